@@ -1,0 +1,216 @@
+"""ctypes wrapper of the C oracle (test infrastructure only).
+
+Every function takes and returns numpy arrays; the arithmetic is all in
+moe_oracle.c.  Only tests/, the smoke check and the benchmark's CPU-baseline
+leg import this module.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+P = C.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = C.CDLL(_build.ensure_built())
+        _lib.oracle_set_threads.argtypes = [C.c_int]
+        _lib.oracle_max_threads.restype = C.c_int
+        _lib.oracle_decode_act.argtypes = [P, C.c_int, C.c_long, P]
+        _lib.oracle_router_logits.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P]
+        _lib.oracle_router_select.argtypes = [C.c_int, C.c_int, C.c_int, P, P, C.c_double, P, P, P, P, P]
+        _lib.oracle_permute.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P, P, P]
+        _lib.oracle_expert_apply.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int] + [P] * 9 + [P, P, P]
+        _lib.oracle_combine.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P]
+        _lib.oracle_moe_layer.argtypes = ([C.c_int] * 7 + [C.c_double, C.c_int] + [P] * 5 + [P] * 12)
+        _lib.oracle_moe_tokens.argtypes = ([C.c_int, P] + [C.c_int] * 6 + [C.c_double, C.c_int] + [P] * 5 + [P] * 4)
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(C.c_void_p)
+
+
+class _QFFN(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in
+                ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down")]
+
+
+def _qffn(ws) -> Optional[_QFFN]:
+    if ws is None:
+        return None
+    s = _QFFN()
+    for n, _ in _QFFN._fields_:
+        setattr(s, n, getattr(ws, n).ctypes.data)
+    return s
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
+
+
+def decode_act(x: np.ndarray, act: int) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    out = np.empty(x.shape, dtype=np.float64)
+    lib().oracle_decode_act(_p(x), int(act), x.size, _p(out))
+    return out
+
+
+def router_logits(xd: np.ndarray, W_r: np.ndarray) -> np.ndarray:
+    xd = np.ascontiguousarray(xd, dtype=np.float64)
+    W_r = np.ascontiguousarray(W_r, dtype=np.float32)
+    T, d = xd.shape
+    E = W_r.shape[1]
+    z = np.empty((T, E), dtype=np.float64)
+    lib().oracle_router_logits(T, d, E, _p(xd), _p(W_r), _p(z))
+    return z
+
+
+@dataclass
+class Routing:
+    idx: np.ndarray   # [T][k] int32
+    w: np.ndarray     # [T][k] fp32
+    gap: np.ndarray   # [T] fp64
+    s: np.ndarray     # [T][E] fp64 sigmoid scores
+    sel: np.ndarray   # [T][E] fp64 selection scores
+
+
+def router_select(z: np.ndarray, bias: np.ndarray, k: int, lam: float) -> Routing:
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    bias = np.ascontiguousarray(bias, dtype=np.float32)
+    T, E = z.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    gap = np.empty(T, dtype=np.float64)
+    s = np.empty((T, E), dtype=np.float64)
+    sel = np.empty((T, E), dtype=np.float64)
+    lib().oracle_router_select(T, E, k, _p(z), _p(bias), float(lam), _p(idx), _p(w), _p(gap), _p(s), _p(sel))
+    return Routing(idx, w, gap, s, sel)
+
+
+@dataclass
+class Permutation:
+    counts: np.ndarray
+    offsets: np.ndarray
+    perm: np.ndarray
+    inv: np.ndarray
+    uniq: np.ndarray
+    n_uniq: int
+
+
+def permute(idx: np.ndarray, E: int) -> Permutation:
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    A = T * k
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(A, np.int32)
+    inv = np.empty(A, np.int32)
+    uniq = np.empty(E, np.int32)
+    n = np.zeros(1, np.int32)
+    lib().oracle_permute(T, k, E, _p(idx), _p(counts), _p(offsets), _p(perm), _p(inv), _p(uniq), _p(n))
+    return Permutation(counts, offsets, perm, inv, uniq, int(n[0]))
+
+
+def expert_apply(X: np.ndarray, d: int, I: int, wbits: int, ws, e: int, return_h: bool = False):
+    """Apply expert e of a stacked expert set (synth.QExpertSet layout) to rows X [n][d] (fp64)."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    n = X.shape[0]
+    Y = np.empty((n, d), dtype=np.float64)
+    H = np.empty((n, I), dtype=np.float64) if return_h else None
+    args = [np.ascontiguousarray(a[e]) for a in
+            (ws.q_gate, ws.s_gate, ws.z_gate, ws.q_up, ws.s_up, ws.z_up, ws.q_down, ws.s_down, ws.z_down)]
+    lib().oracle_expert_apply(n, d, I, wbits, *[_p(a) for a in args], _p(X), _p(Y), _p(H))
+    return (Y, H) if return_h else Y
+
+
+def combine(Y: np.ndarray, S: Optional[np.ndarray], inv: np.ndarray, w: np.ndarray) -> np.ndarray:
+    T, k = w.shape
+    d = Y.shape[1]
+    y = np.empty((T, d), dtype=np.float64)
+    lib().oracle_combine(T, k, d, _p(np.ascontiguousarray(Y, dtype=np.float64)),
+                         _p(None if S is None else np.ascontiguousarray(S, dtype=np.float64)),
+                         _p(np.ascontiguousarray(inv, dtype=np.int32)),
+                         _p(np.ascontiguousarray(w, dtype=np.float32)), _p(y))
+    return y
+
+
+@dataclass
+class LayerResult:
+    idx: np.ndarray
+    w: np.ndarray
+    gap: np.ndarray
+    perm: Permutation
+    Yperm: np.ndarray
+    S: Optional[np.ndarray]
+    y: np.ndarray
+
+
+def moe_layer(spec, x, W_r, bias, routed, shared) -> LayerResult:
+    """Whole layer through the batch union (spec: synth.LayerSpec)."""
+    T = x.shape[0]
+    d, E, k, I, Is = spec.d, spec.E, spec.k, spec.I, spec.I_shared
+    A = T * k
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    gap = np.empty(T, np.float64)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(A, np.int32)
+    inv = np.empty(A, np.int32)
+    uniq = np.empty(E, np.int32)
+    n = np.zeros(1, np.int32)
+    Yperm = np.empty((A, d), np.float64)
+    S = np.empty((T, d), np.float64) if Is > 0 else None
+    y = np.empty((T, d), np.float64)
+    r = _qffn(routed)
+    s = _qffn(shared)
+    lib().oracle_moe_layer(T, d, E, k, I, Is, spec.wbits, float(spec.routed_scale), spec.act,
+                           _p(np.ascontiguousarray(x)), _p(W_r), _p(bias), C.byref(r),
+                           C.byref(s) if s is not None else None,
+                           _p(idx), _p(w), _p(gap), _p(counts), _p(offsets), _p(perm), _p(inv), _p(uniq),
+                           _p(n), _p(Yperm), _p(S), _p(y))
+    return LayerResult(idx, w, gap, Permutation(counts, offsets, perm, inv, uniq, int(n[0])), Yperm, S, y)
+
+
+@dataclass
+class TokenResult:
+    tokens: np.ndarray
+    idx: np.ndarray
+    w: np.ndarray
+    gap: np.ndarray
+    y: np.ndarray
+
+
+def moe_tokens(spec, tokens, x, W_r, bias, routed, shared) -> TokenResult:
+    """Per-token loop (no batch union) over the listed rows of x."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n = tokens.size
+    d, E, k = spec.d, spec.E, spec.k
+    idx = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float32)
+    gap = np.empty(n, np.float64)
+    y = np.empty((n, d), np.float64)
+    r = _qffn(routed)
+    s = _qffn(shared)
+    lib().oracle_moe_tokens(n, _p(tokens), d, E, k, spec.I, spec.I_shared, spec.wbits,
+                            float(spec.routed_scale), spec.act, _p(np.ascontiguousarray(x)), _p(W_r), _p(bias),
+                            C.byref(r), C.byref(s) if s is not None else None,
+                            _p(idx), _p(w), _p(gap), _p(y))
+    return TokenResult(tokens, idx, w, gap, y)

@@ -1,0 +1,315 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a library
+routine (numpy/BLAS matmul, scipy's logistic, torch's per-channel affine
+dequantisation and SiLU, a stable library sort), a closed form, an invariant
+or a special case.  None of them re-types the oracle's formulas.
+"""
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from routed_expert_ffn_sigmoid_amd import synth
+
+# ----------------------------------------------------------------------------
+# helpers (test-side constructions, independent of the oracle)
+# ----------------------------------------------------------------------------
+
+
+def tiny_spec(**kw):
+    base = dict(name="pin", family=100, d=64, E=8, k=2, I=32, I_shared=0, wbits=8,
+                routed_scale=1.0, act=synth.ACT_F32, bias="uniform0.01")
+    base.update(kw)
+    return synth.LayerSpec(**base)
+
+
+def unpack_int4(qb: np.ndarray) -> np.ndarray:
+    """[rows][cols/2] packed bytes -> [rows][cols] values 0..15, even column in the low nibble."""
+    lo = (qb & 0x0F).astype(np.uint8)
+    hi = (qb >> 4).astype(np.uint8)
+    out = np.empty((qb.shape[0], qb.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def torch_dequant(q: np.ndarray, scale: np.ndarray, zp: np.ndarray, wbits: int) -> torch.Tensor:
+    """Per-output-channel affine dequantisation by torch's quantized-tensor machinery."""
+    if wbits == 4:
+        vals = torch.from_numpy(unpack_int4(q))
+        qt = torch._make_per_channel_quantized_tensor(
+            vals, torch.from_numpy(scale.astype(np.float64)),
+            torch.from_numpy(zp.astype(np.int64)), 0)
+    else:
+        qt = torch._make_per_channel_quantized_tensor(
+            torch.from_numpy(q.astype(np.int8)), torch.from_numpy(scale.astype(np.float64)),
+            torch.from_numpy(zp.astype(np.int64)), 0)
+    return qt.dequantize().double()
+
+
+def torch_swiglu(X: np.ndarray, ex, e: int, wbits: int) -> np.ndarray:
+    Wg = torch_dequant(ex.q_gate[e], ex.s_gate[e], ex.z_gate[e], wbits)
+    Wu = torch_dequant(ex.q_up[e], ex.s_up[e], ex.z_up[e], wbits)
+    Wd = torch_dequant(ex.q_down[e], ex.s_down[e], ex.z_down[e], wbits)
+    x = torch.from_numpy(np.asarray(X, dtype=np.float64))
+    h = torch.nn.functional.silu(x @ Wg.T) * (x @ Wu.T)
+    return (h @ Wd.T).numpy()
+
+
+def brute_topk(sel_row: np.ndarray, k: int):
+    order = sorted(range(sel_row.size), key=lambda e: (-sel_row[e], e))
+    return order[:k], order
+
+
+# ----------------------------------------------------------------------------
+# activations and router
+# ----------------------------------------------------------------------------
+
+
+def test_decode_act_matches_torch(orc):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(1000).astype(np.float32) * 10
+    bits = synth.round_to_bf16_bits(x)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(orc.decode_act(bits, synth.ACT_BF16), ref)
+    np.testing.assert_array_equal(orc.decode_act(x, synth.ACT_F32), x.astype(np.float64))
+    # the generator's RNE rounding agrees with torch's
+    ref_bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, ref_bits)
+
+
+@pytest.mark.parametrize("T,d,E", [(5, 64, 8), (8, 7168, 256), (3, 4096, 8)])
+def test_router_logits_match_blas(orc, T, d, E):
+    rng = np.random.default_rng(T + d)
+    x = rng.standard_normal((T, d))
+    W = (rng.standard_normal((d, E)) * 0.02).astype(np.float32)
+    z = orc.router_logits(x, W)
+    ref = x @ W.astype(np.float64)
+    bound = 1e-13 * (np.abs(x) @ np.abs(W.astype(np.float64)))
+    assert np.all(np.abs(z - ref) <= bound)
+
+
+def test_sigmoid_scores_match_scipy_and_bias_is_added(orc):
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((64, 16)) * 4
+    b = rng.uniform(-0.3, 0.3, 16).astype(np.float32)
+    r = orc.router_select(z, b, 4, 1.0)
+    np.testing.assert_allclose(r.s, scipy.special.expit(z), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(r.sel - r.s, np.broadcast_to(b.astype(np.float64), r.s.shape), rtol=0, atol=1e-15)
+    # symmetry of the logistic function
+    r2 = orc.router_select(-z, b, 4, 1.0)
+    np.testing.assert_allclose(r.s + r2.s, 1.0, rtol=0, atol=4.5e-16)
+
+
+@pytest.mark.parametrize("E,k,ties", [(8, 2, False), (16, 4, False), (8, 2, True), (16, 5, True), (6, 6, False)])
+def test_topk_equals_full_sort_brute_force(orc, E, k, ties):
+    rng = np.random.default_rng(E * 10 + k)
+    z = rng.standard_normal((200, E))
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    if ties:  # few distinct logits and no bias -> many exact ties in sel
+        z = np.round(z * 2) / 2
+        b[:] = 0
+    r = orc.router_select(z, b, k, 1.0)
+    for t in range(z.shape[0]):
+        top, order = brute_topk(r.sel[t], k)
+        assert list(r.idx[t]) == top
+        if k < E:
+            assert r.gap[t] == r.sel[t][order[k - 1]] - r.sel[t][order[k]]
+        else:
+            assert np.isinf(r.gap[t])
+
+
+@pytest.mark.parametrize("lam", [1.0, 2.5])
+def test_combine_weights_normalised_scaled_unbiased(orc, lam):
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((100, 32)) * 2
+    b = rng.standard_normal(32).astype(np.float32) * 0.2
+    r = orc.router_select(z, b, 8, lam)
+    assert np.all(r.w > 0)
+    np.testing.assert_allclose(r.w.astype(np.float64).sum(1), lam, rtol=1e-6)
+    # proportional to the unbiased sigmoid score of each chosen expert
+    s_sel = np.take_along_axis(r.s, r.idx.astype(np.int64), 1)
+    np.testing.assert_allclose(r.w / r.w[:, :1], s_sel / s_sel[:, :1], rtol=3e-7)
+
+
+def test_all_tie_router(orc):
+    """W_r = 0 and b = 0: every score is exactly 0.5, so ids 0..k-1 win and w = lambda/k."""
+    T, d, E, k, lam = 4, 32, 8, 3, 2.5
+    z = orc.router_logits(np.ones((T, d)), np.zeros((d, E), np.float32))
+    r = orc.router_select(z, np.zeros(E, np.float32), k, lam)
+    assert np.all(r.s == 0.5)
+    assert np.all(r.idx == np.arange(k))
+    assert np.all(r.w == np.float32(lam / k))
+    assert np.all(r.gap == 0.0)
+
+
+def test_unbiased_selection_follows_logits(orc):
+    """b = 0: the sigmoid is increasing, so the top-k by score equals the top-k by logit."""
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((300, 64)) * 3
+    r = orc.router_select(z, np.zeros(64, np.float32), 8, 1.0)
+    ref = np.argsort(-z, axis=1, kind="stable")[:, :8]
+    np.testing.assert_array_equal(r.idx, ref)
+
+
+# ----------------------------------------------------------------------------
+# permutation
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("T,k,E", [(16, 2, 8), (1, 8, 256), (512, 8, 256), (37, 3, 5), (64, 8, 256)])
+def test_permutation_equals_stable_sort(orc, T, k, E):
+    rng = np.random.default_rng(T * k + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    p = orc.permute(idx, E)
+    flat = idx.reshape(-1)
+    perm_ref = np.argsort(flat, kind="stable").astype(np.int32)
+    np.testing.assert_array_equal(p.perm, perm_ref)
+    counts = np.bincount(flat, minlength=E)
+    np.testing.assert_array_equal(p.counts, counts)
+    np.testing.assert_array_equal(p.offsets, np.concatenate([[0], np.cumsum(counts)]))
+    assert p.counts.sum() == T * k
+    np.testing.assert_array_equal(p.inv[p.perm], np.arange(T * k))
+    u = np.flatnonzero(counts)
+    assert p.n_uniq == u.size
+    np.testing.assert_array_equal(p.uniq[:u.size], u)
+    assert np.all(p.uniq[u.size:] == -1)
+
+
+def test_permutation_skewed_and_single_expert(orc):
+    idx = np.full((10, 1), 3, np.int32)
+    p = orc.permute(idx, 4)
+    assert list(p.counts) == [0, 0, 0, 10] and p.n_uniq == 1 and p.uniq[0] == 3
+    np.testing.assert_array_equal(p.perm, np.arange(10))
+
+
+# ----------------------------------------------------------------------------
+# experts, shared expert, combine, whole layer
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("wbits", [8, 4])
+def test_single_expert_equals_dense_swiglu(orc, wbits):
+    """E=1, k=1, lambda=1, no shared expert: the layer is one dense SwiGLU of the dequantised weights."""
+    spec = tiny_spec(E=1, k=1, d=64, I=96, wbits=wbits)
+    L = synth.gen_layer(spec, 7)
+    res = orc.moe_layer(spec, L.x, L.W_r, L.bias, L.routed, L.shared)
+    assert np.all(res.idx == 0) and np.all(res.w == 1.0)
+    ref = torch_swiglu(L.x.astype(np.float64), L.routed, 0, wbits)
+    np.testing.assert_allclose(res.y, ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("wbits,act", [(8, synth.ACT_F32), (4, synth.ACT_BF16)])
+def test_two_experts_plus_shared_reduces_to_dense(orc, wbits, act):
+    """E=k=2 with a shared expert: y = S + lambda * (s0*Y0 + s1*Y1) / (s0+s1), all from library routines."""
+    spec = tiny_spec(E=2, k=2, d=64, I=32, I_shared=48, wbits=wbits, act=act, routed_scale=2.5)
+    L = synth.gen_layer(spec, 5)
+    res = orc.moe_layer(spec, L.x, L.W_r, L.bias, L.routed, L.shared)
+    xd = orc.decode_act(L.x, act) if act == synth.ACT_BF16 else L.x.astype(np.float64)
+    s = scipy.special.expit(xd @ L.W_r.astype(np.float64))
+    Y0 = torch_swiglu(xd, L.routed, 0, wbits)
+    Y1 = torch_swiglu(xd, L.routed, 1, wbits)
+    S = torch_swiglu(xd, L.shared, 0, wbits)
+    ref = S + 2.5 * (s[:, :1] * Y0 + s[:, 1:] * Y1) / s.sum(1, keepdims=True)
+    np.testing.assert_allclose(res.y, ref, rtol=2e-6, atol=2e-6 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("name", ["tiny"])
+def test_batch_union_bitwise_equals_per_token_loop(orc, name):
+    spec = synth.CONFIGS[name]
+    L = synth.gen_layer(spec, 16)
+    res = orc.moe_layer(spec, L.x, L.W_r, L.bias, L.routed, L.shared)
+    tok = orc.moe_tokens(spec, np.arange(16), L.x, L.W_r, L.bias, L.routed, L.shared)
+    np.testing.assert_array_equal(res.idx, tok.idx)
+    np.testing.assert_array_equal(res.w, tok.w)
+    np.testing.assert_array_equal(res.y, tok.y)
+
+
+def test_batch_union_with_shared_and_int4(orc):
+    spec = tiny_spec(E=16, k=4, d=128, I=64, I_shared=32, wbits=4, act=synth.ACT_BF16, routed_scale=2.5,
+                     bias="normal0.05")
+    L = synth.gen_layer(spec, 24)
+    res = orc.moe_layer(spec, L.x, L.W_r, L.bias, L.routed, L.shared)
+    tok = orc.moe_tokens(spec, np.arange(24), L.x, L.W_r, L.bias, L.routed, L.shared)
+    np.testing.assert_array_equal(res.y, tok.y)
+    # y_perm rows are the per-expert outputs of the routed token
+    for t in (0, 7, 23):
+        for j in range(spec.k):
+            p = res.perm.inv[t * spec.k + j]
+            e = res.idx[t, j]
+            Y = orc.expert_apply(orc.decode_act(L.x[t:t + 1], spec.act), spec.d, spec.I, 4, L.routed, e)
+            np.testing.assert_array_equal(res.Yperm[p], Y[0])
+
+
+def test_expert_byte_sizes():
+    """Three matrices per SwiGLU expert at one byte (int8) or half a byte (int4) per weight."""
+    mid, large = synth.CONFIGS["mid"], synth.CONFIGS["large"]
+    assert 3 * mid.I * mid.d * mid.wbits // 8 == 176_160_768
+    assert 3 * large.I * large.d * large.wbits // 8 == 22_020_096
+    ex = synth.gen_expert(synth.small_spec(large, d=64, I=32), 0)
+    assert ex.gate.q.nbytes + ex.up.q.nbytes + ex.down.q.nbytes == 3 * 64 * 32 // 2
+
+
+@pytest.mark.parametrize("wbits", [8, 4])
+def test_zero_weights_leave_only_shared(orc, wbits):
+    """q == zp everywhere in the routed experts: the routed part vanishes and y = S."""
+    spec = tiny_spec(E=4, k=2, d=64, I=32, I_shared=32, wbits=wbits)
+    L = synth.gen_layer(spec, 6)
+    R = L.routed
+    if wbits == 8:
+        for q, z in ((R.q_gate, R.z_gate), (R.q_up, R.z_up), (R.q_down, R.z_down)):
+            q[:] = z[..., None]
+    else:
+        for q, z in ((R.q_gate, R.z_gate), (R.q_up, R.z_up), (R.q_down, R.z_down)):
+            z[:] = 5.0
+            q[:] = 0x55
+    res = orc.moe_layer(spec, L.x, L.W_r, L.bias, L.routed, L.shared)
+    np.testing.assert_array_equal(res.y, res.S)
+    assert np.abs(res.S).max() > 0
+
+
+def test_routed_scale_is_linear_and_skips_shared(orc):
+    spec1 = tiny_spec(E=8, k=2, d=64, I=32, I_shared=32, routed_scale=1.0)
+    spec2 = synth.small_spec(spec1, routed_scale=2.5)
+    L = synth.gen_layer(spec1, 9)
+    r1 = orc.moe_layer(spec1, L.x, L.W_r, L.bias, L.routed, L.shared)
+    r2 = orc.moe_layer(spec2, L.x, L.W_r, L.bias, L.routed, L.shared)
+    np.testing.assert_array_equal(r1.S, r2.S)
+    ref = 2.5 * (r1.y - r1.S)
+    # w is rounded to fp32 on both sides, so agreement is to fp32 precision
+    np.testing.assert_allclose(r2.y - r2.S, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
+
+
+def test_int4_equals_expanded_int8(orc):
+    """Nibbles expanded to int8 (low nibble = even input index) give a bit-identical layer."""
+    spec4 = tiny_spec(E=4, k=2, d=64, I=32, I_shared=32, wbits=4, act=synth.ACT_BF16)
+    spec8 = synth.small_spec(spec4, wbits=8)
+    L = synth.gen_layer(spec4, 8)
+
+    def expand(ws):
+        def ex(q):
+            return np.ascontiguousarray(np.stack([unpack_int4(m) for m in q]).astype(np.int8))
+        return synth.QExpertSet(ex(ws.q_gate), ex(ws.q_up), ex(ws.q_down), ws.s_gate, ws.s_up, ws.s_down,
+                                ws.z_gate.astype(np.int8), ws.z_up.astype(np.int8), ws.z_down.astype(np.int8))
+    r4 = orc.moe_layer(spec4, L.x, L.W_r, L.bias, L.routed, L.shared)
+    r8 = orc.moe_layer(spec8, L.x, L.W_r, L.bias, expand(L.routed), expand(L.shared))
+    np.testing.assert_array_equal(r4.y, r8.y)
+
+
+def test_thread_count_and_seed_determinism(orc):
+    spec = tiny_spec(E=8, k=2, d=128, I=64, I_shared=32, wbits=4, act=synth.ACT_BF16)
+    L1 = synth.gen_layer(spec, 12)
+    L2 = synth.gen_layer(spec, 12)
+    assert synth.sha256_of(L1.x, L1.W_r, L1.routed.q_gate, L1.routed.s_down) == \
+        synth.sha256_of(L2.x, L2.W_r, L2.routed.q_gate, L2.routed.s_down)
+    n0 = orc.max_threads()
+    try:
+        orc.set_threads(1)
+        a = orc.moe_layer(spec, L1.x, L1.W_r, L1.bias, L1.routed, L1.shared)
+        orc.set_threads(max(4, n0))
+        b = orc.moe_layer(spec, L1.x, L1.W_r, L1.bias, L1.routed, L1.shared)
+    finally:
+        orc.set_threads(n0)
+    np.testing.assert_array_equal(a.y, b.y)
+    np.testing.assert_array_equal(a.Yperm, b.Yperm)
