@@ -1,0 +1,168 @@
+"""MoE-layer forward benchmark on one MI355X.
+
+One step = one pass of the whole layer (moe_route -> moe_permute ->
+moe_forward -> moe_combine) over one batch of seeded synthetic tokens, with
+all inputs already resident in HBM.  Decode workloads rotate over several
+resident layers and a pool of activation batches so that neither the 256 MB
+Infinity Cache nor L2 holds the expert weights between steps.
+
+Prints ONE JSON line (the driver's contract).  `value` is MoE-layer tokens/s.
+`roofline` reports the expert-FFN stage (moe_forward) against HBM bandwidth
+(decode) or the bf16/fp16 MFMA peak (prefill), timed with HIP events on the
+stream the kernels run on.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2516.6  # dense bf16/fp16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="mid", help="workload name (routed_expert_ffn_sigmoid_amd.synth.CONFIGS)")
+    ap.add_argument("--T", type=int, default=None, help="tokens per step (default: first of the workload's T list)")
+    ap.add_argument("--layers", type=int, default=None, help="resident layers rotated per step")
+    ap.add_argument("--pool", type=int, default=16, help="activation batches rotated per step")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(spec, T, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload (tokens of layer 0)."""
+    from oracle import oracle as orc
+    from routed_expert_ffn_sigmoid_amd import synth
+    inp = synth.gen_layer(spec, T, 0, 0, 0)
+    cores = orc.max_threads()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.moe_layer(spec, inp.x, inp.W_r, inp.bias, inp.routed, inp.shared)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or n >= 1000:
+            break
+    return {"value": n * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} full {spec.name} layers at T={T} (layer 0, batch 0), {el:.1f} s, fp64 C with OpenMP"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from routed_expert_ffn_sigmoid_amd import binding as B
+    from routed_expert_ffn_sigmoid_amd import layer as L
+    from routed_expert_ffn_sigmoid_amd import synth
+
+    spec = synth.CONFIGS[args.config]
+    T = args.T or synth.WORKLOAD_T[args.config][0]
+    decode = T * spec.k <= 4 * spec.E or T <= 64
+    n_layers = args.layers or (4 if decode else 1)
+    path = {"auto": B.MOE_PATH_AUTO, "gemv": B.MOE_PATH_GEMV, "gemm": B.MOE_PATH_GEMM}[args.path]
+    dev = torch.device("cuda:0")
+    B.lib()
+
+    t_setup = time.perf_counter()
+    layers = [L.DeviceLayerWeights(spec, 0, l, dev) for l in range(n_layers)]
+    pool = [L.upload_x(spec, synth.gen_x(spec, T, 0, b), dev) for b in range(args.pool)]
+    run = L.MoeRun(spec, T, dev, path)
+    stream = torch.cuda.current_stream()
+    setup_s = time.perf_counter() - t_setup
+
+    # untimed pass over every (layer, batch) pair: realized unique experts per step
+    n_uniq = np.zeros((n_layers, args.pool), dtype=np.int64)
+    for l in range(n_layers):
+        for b in range(args.pool):
+            run.run(pool[b], layers[l])
+            n_uniq[l, b] = int(run.n_uniq.item())
+
+    def step(i):
+        l, b = i % n_layers, i % args.pool
+        W, x = layers[l], pool[b]
+        run.route(x, W)
+        run.permute()
+        ev[i][0].record(stream)
+        run.forward(x, W)
+        ev[i][1].record(stream)
+        run.combine()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.warmup + args.steps)]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    fwd_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, args.warmup + args.steps)])
+    ebytes = spec.expert_bytes()
+    sbytes = spec.expert_bytes(spec.I_shared) if spec.I_shared else 0
+    steps_idx = range(args.warmup, args.warmup + args.steps)
+    bytes_tot = sum(int(n_uniq[i % n_layers, i % args.pool]) * ebytes + sbytes for i in steps_idx)
+    flops_per_step = 2.0 * 3 * spec.d * (T * spec.k * spec.I + T * spec.I_shared)
+    fwd_s = fwd_ms.sum() / 1e3
+    if decode:
+        achieved = bytes_tot / fwd_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "moe_forward (expert-FFN kernels)",
+                "algorithmic_bytes_per_launch": round(bytes_tot / args.steps),
+                "avg_launch_us": round(float(fwd_ms.mean()) * 1e3, 2)}
+    else:
+        achieved = flops_per_step * args.steps / fwd_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "moe_forward (expert-FFN kernels)",
+                "algorithmic_flops_per_launch": flops_per_step,
+                "avg_launch_us": round(float(fwd_ms.mean()) * 1e3, 2)}
+
+    ms_per_step = elapsed / args.steps * 1e3
+    out = {
+        "metric": "MoE-layer tokens/s",
+        "value": round(T * args.steps / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("bf16-act/" if spec.act == synth.ACT_BF16 else "f32-act/") + f"int{spec.wbits}-weights/f32-accum",
+        "data": "synthetic (seeded; random-init quantised weights)",
+        "config": {"workload": f"{spec.name}: d={spec.d} E={spec.E} top-{spec.k} I={spec.I} "
+                               f"shared={spec.I_shared} int{spec.wbits} T={T}",
+                   "T": T, "layers_resident": n_layers, "x_pool": args.pool,
+                   "mean_unique_experts": round(float(np.mean([n_uniq[i % n_layers, i % args.pool]
+                                                                for i in steps_idx])), 2),
+                   "path": args.path, "setup_s": round(setup_s, 1)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, T, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

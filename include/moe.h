@@ -1,0 +1,169 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer forward.
+ *
+ * The layer (pages cited by title):
+ *   1. moe_route   -- a DeepSeek-V3-style sigmoid router: every token keeps k
+ *      of E experts ("25GB 内存跑 744B GLM-5.2 模型" page, section 三.1).  The
+ *      per-expert bias steers selection only, DeepSeek-V3's balancing
+ *      without an auxiliary loss, and routing, selection and scaling must be
+ *      reproduced exactly (same page, section 四.3).
+ *   2. moe_permute -- batch union: assignments that hit the same expert are
+ *      grouped so the expert's weights are read once for all of them (same
+ *      page, section 三.4; gathering the active experts into one batched
+ *      product: "企业官网建设流程全解析" page, Colibri walk-through, section 3.3).
+ *   3. moe_forward -- the routed SwiGLU experts and the always-on shared
+ *      expert, weights quantised per output channel with a scale and a zero
+ *      point (walk-through page, section 3.4); the shared expert belongs to
+ *      the dense, resident part of the model (GLM-5.2 page, section 二).
+ *   4. moe_combine -- y = shared + sum_j w_j * expert_j(x).
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer owned by the caller; only the
+ *     moe_shape / moe_qffn structs are read on the host, during the call.
+ *     The library allocates no memory and keeps no global mutable state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without waiting for it.  Results are valid once
+ *     the stream has reached that point.  Counts, offsets and the unique-
+ *     expert list stay on the device; no call copies them to the host.
+ *   - `ws` is a caller-owned device workspace of at least
+ *     moe_workspace_size(shape) bytes, 256-byte aligned.  Calls that share a
+ *     workspace must be ordered (same stream); concurrent calls need their
+ *     own workspaces.  Workspace contents need no initialisation.
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code.  All arguments
+ *     are validated before anything is enqueued, so a failed call leaves
+ *     every output untouched.  moe_last_error() gives a message for the
+ *     calling thread's last failure.
+ *   - Pointer arguments must be 16-byte aligned (MOE_EALIGN otherwise).
+ *
+ * Shapes and layouts
+ *   T tokens, d hidden size, E routed experts, k experts per token,
+ *   I routed intermediate size, I_shared shared intermediate size (0 = none),
+ *   A = T*k assignments (a = t*k + j is token t's j-th choice).
+ *   x        [T][d] fp32 (MOE_ACT_F32) or bf16 (MOE_ACT_BF16), row-major.
+ *   W_r      [d][E] fp32;  bias [E] fp32.
+ *   Quantised matrices are row-major [out][in], one scale and zero point per
+ *   output row; dequantised weight = scale * (q - zp):
+ *     wbits 8: q int8, zp int8;
+ *     wbits 4: q unsigned 0..15, two per byte, the even input index in the
+ *              low nibble; zp fp32.
+ *   moe_qffn for n experts: q_gate, q_up [n][I][in_bytes],
+ *   q_down [n][d][I*wbits/8], s_* fp32 and z_* as above, [n][out].
+ *   Limits: 1 <= k <= min(E, 32), E <= 1024, T*k < 2^31;
+ *   d and I (and I_shared) multiples of 32 for int4 and of 16 for int8.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* bad shape, NULL required pointer, unknown enum */
+#define MOE_EUNSUPPORTED (-2) /* dtype or bit width not implemented */
+#define MOE_EWORKSPACE (-3)   /* workspace missing or smaller than moe_workspace_size() */
+#define MOE_EALIGN (-4)       /* pointer not 16-byte (workspace: 256-byte) aligned */
+#define MOE_EDEVICE (-5)      /* kernel launch failed */
+
+#define MOE_ACT_F32 0
+#define MOE_ACT_BF16 1
+
+/* moe_forward expert-FFN implementation */
+#define MOE_PATH_AUTO 0 /* choose from T, k and E */
+#define MOE_PATH_GEMV 1 /* bandwidth-bound dequant-GEMV (decode) */
+#define MOE_PATH_GEMM 2 /* MFMA grouped GEMM (prefill) */
+
+typedef struct moe_shape {
+    int32_t T, d, E, k, I, I_shared;
+    float routed_scale; /* lambda: the normalised combine weights are multiplied by it */
+    int32_t act_dtype;  /* MOE_ACT_F32 | MOE_ACT_BF16 */
+    int32_t wbits;      /* 8 | 4 */
+    int32_t path;       /* MOE_PATH_* (moe_forward only) */
+} moe_shape;
+
+typedef struct moe_qffn {
+    const void *q_gate, *q_up, *q_down;
+    const float *s_gate, *s_up, *s_down;
+    const void *z_gate, *z_up, *z_down;
+} moe_qffn;
+
+/* Bytes of workspace that every call below needs for this shape (host only, no device work). */
+MOE_API size_t moe_workspace_size(const moe_shape *shape);
+
+/*
+ * Router ("25GB 内存跑 744B GLM-5.2 模型" page, sections 三.1 and 四.3).
+ *   z[t][e]   = sum_i x[t][i] * W_r[i][e]            (fp64 accumulation)
+ *   s[t][e]   = 1 / (1 + exp(-z[t][e]))              (fp64)
+ *   sel[t][e] = s[t][e] + bias[e]                    (selection score, fp64)
+ *   topk_idx[t][0..k): the k experts of largest sel, in descending sel,
+ *                      equal scores ordered by lower expert id;
+ *   topk_w[t][j] = routed_scale * s[t][idx_j] / sum_j' s[t][idx_j']  (fp32);
+ *   gap[t]    = sel of the k-th choice minus sel of the (k+1)-th, fp64
+ *               (+inf when k == E); optional (NULL).  Tokens with a gap
+ *               below 1e-6 are the near ties a caller may want to log.
+ * Outputs: topk_idx [T][k] int32, topk_w [T][k] fp32, gap [T] fp64 or NULL.
+ */
+MOE_API int moe_route(const moe_shape *shape, const void *x, const float *W_r, const float *bias, int32_t *topk_idx,
+              float *topk_w, double *gap, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Batch union (GLM-5.2 page, section 三.4): a stable counting sort of the A
+ * assignments by expert.
+ *   counts[e]      assignments routed to e                      [E]
+ *   offsets[e]     exclusive prefix sum of counts               [E+1]
+ *   perm[p]        assignment a = t*k + j at sorted position p  [A]
+ *                  (ascending a within an expert)
+ *   inv[a]         sorted position of assignment a              [A]
+ *   uniq[0..n)     experts with counts > 0, ascending; -1 after [E]
+ *   n_uniq[0]      number of unique experts                     [1]
+ * Integer work, bit-exact and independent of scheduling.  topk_idx entries
+ * outside [0, E) are not counted and set n_uniq to -1.
+ */
+MOE_API int moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t *counts, int32_t *offsets, int32_t *perm,
+                int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Routed and shared SwiGLU experts (walk-through page, section 3.4):
+ *   g = s_g * ((q_g - z_g) . x),  u = s_u * ((q_u - z_u) . x),
+ *   h = silu(g) * u,  out = s_d * ((q_d - z_d) . h),  silu(v) = v / (1 + exp(-v)).
+ * Each unique expert e (uniq/n_uniq/offsets/perm from moe_permute) is applied
+ * to the tokens t = perm[p] / k of its rows p in [offsets[e], offsets[e+1]),
+ * reading its weights once for all of them; results go to y_perm[p] (fp32,
+ * [A][d]).  The shared expert (shared != NULL, shape->I_shared > 0) is
+ * applied to every token; its output goes to y_shared [T][d] fp32.
+ * Accumulation is fp32; the MFMA path rounds h to fp16 between the two
+ * products.  `routed` describes E experts, `shared` one.
+ */
+MOE_API int moe_forward(const moe_shape *shape, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                float *y_perm, float *y_shared, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Weighted combine:
+ *   y[t] = y_shared[t] + sum_{j=0}^{k-1} topk_w[t][j] * y_perm[inv[t*k + j]]
+ * summed in this order in fp32 (y_shared NULL = no shared term).
+ * Output y [T][d] fp32.
+ */
+MOE_API int moe_combine(const moe_shape *shape, const float *y_perm, const float *y_shared, const int32_t *inv,
+                const float *topk_w, float *y, void *stream);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+MOE_API const char *moe_last_error(void);
+
+/* ABI version: increases when a signature or a layout changes. */
+MOE_API int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,146 @@
+"""ctypes binding of libmoe_hip.so (argument marshalling only).
+
+Every function has the name and argument order of the C ABI in
+include/moe.h and takes torch tensors (device memory) or raw device pointers.
+All computation happens in the HIP library; if it cannot be loaded, import of
+this module's functions raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EWORKSPACE = -3
+MOE_EALIGN = -4
+MOE_EDEVICE = -5
+
+MOE_ACT_F32 = 0
+MOE_ACT_BF16 = 1
+
+MOE_PATH_AUTO = 0
+MOE_PATH_GEMV = 1
+MOE_PATH_GEMM = 2
+
+# names declared in include/moe.h
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_combine",
+           "moe_last_error", "moe_abi_version")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class moe_shape(C.Structure):
+    _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("E", C.c_int32), ("k", C.c_int32), ("I", C.c_int32),
+                ("I_shared", C.c_int32), ("routed_scale", C.c_float), ("act_dtype", C.c_int32),
+                ("wbits", C.c_int32), ("path", C.c_int32)]
+
+
+class moe_qffn(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in
+                ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down")]
+
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library (raises if it is missing: there is no other implementation)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(python -m routed_expert_ffn_sigmoid_amd.build)")
+        L = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        S = C.POINTER(moe_shape)
+        Q = C.POINTER(moe_qffn)
+        L.moe_workspace_size.argtypes = [S]
+        L.moe_workspace_size.restype = C.c_size_t
+        L.moe_route.argtypes = [S, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_permute.argtypes = [S, P, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_forward.argtypes = [S, P, Q, Q, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_combine.argtypes = [S, P, P, P, P, P, P]
+        for f in ("moe_route", "moe_permute", "moe_forward", "moe_combine", "moe_abi_version"):
+            getattr(L, f).restype = C.c_int
+        L.moe_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def make_shape(T, d, E, k, I, I_shared=0, routed_scale=1.0, act_dtype=MOE_ACT_BF16, wbits=4,
+               path=MOE_PATH_AUTO) -> moe_shape:
+    return moe_shape(T, d, E, k, I, I_shared, routed_scale, act_dtype, wbits, path)
+
+
+def make_qffn(q_gate, q_up, q_down, s_gate, s_up, s_down, z_gate, z_up, z_down) -> moe_qffn:
+    return moe_qffn(*[_ptr(t) for t in (q_gate, q_up, q_down, s_gate, s_up, s_down, z_gate, z_up, z_down)])
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_workspace_size(shape: moe_shape) -> int:
+    return int(lib().moe_workspace_size(C.byref(shape)))
+
+
+def moe_route(shape, x, W_r, bias, topk_idx, topk_w, gap, ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().moe_route(C.byref(shape), _ptr(x), _ptr(W_r), _ptr(bias), _ptr(topk_idx), _ptr(topk_w),
+                           _ptr(gap), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_permute(shape, topk_idx, counts, offsets, perm, inv, uniq, n_uniq, ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().moe_permute(C.byref(shape), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
+                             _ptr(uniq), _ptr(n_uniq), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_forward(shape, x, routed: moe_qffn, shared: Optional[moe_qffn], offsets, perm, uniq, n_uniq, y_perm,
+                y_shared, ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().moe_forward(C.byref(shape), _ptr(x), C.byref(routed),
+                             C.byref(shared) if shared is not None else None, _ptr(offsets), _ptr(perm),
+                             _ptr(uniq), _ptr(n_uniq), _ptr(y_perm), _ptr(y_shared), _ptr(ws), ws_bytes,
+                             _stream(stream)))
+
+
+def moe_combine(shape, y_perm, y_shared, inv, topk_w, y, stream=None) -> None:
+    _check(lib().moe_combine(C.byref(shape), _ptr(y_perm), _ptr(y_shared), _ptr(inv), _ptr(topk_w), _ptr(y),
+                             _stream(stream)))

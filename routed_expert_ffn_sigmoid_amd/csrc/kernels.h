@@ -1,0 +1,51 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Weights of n quantised SwiGLU experts, stacked per matrix (see include/moe.h).
+struct QW {
+    const uint8_t *qg, *qu, *qd;
+    const float *sg, *su, *sd;
+    const void *zg, *zu, *zd;
+};
+
+// Everything the expert-FFN kernels read or write.
+struct FfnParams {
+    const void *x;
+    int T, d, k, E, A;
+    int I, Is;  // routed and shared intermediate sizes (Is = 0: no shared expert)
+    int wbits, act;
+    QW routed, shared;
+    const int32_t *offsets, *perm, *uniq, *n_uniq;
+    int n_routed_slots;  // min(E, A): grid slots reserved for routed experts
+    float *y_perm, *y_sh;
+};
+
+// router.hip
+size_t router_workspace_bytes(int T, int d, int E);
+hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
+                         float lambda, int32_t *idx, float *w, double *gap, void *ws, hipStream_t stream);
+
+// permute.hip
+size_t permute_lds_bytes(int E);
+hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
+                          int32_t *inv, int32_t *uniq, int32_t *n_uniq, hipStream_t stream);
+
+// ffn_gemv.hip: decode path (h kept in fp32 in the workspace)
+size_t gemv_workspace_bytes(const FfnParams &P);
+hipError_t launch_ffn_gemv(const FfnParams &P, void *ws, hipStream_t stream);
+
+// ffn_gemm.hip: MFMA grouped-GEMM path
+size_t gemm_workspace_bytes(const FfnParams &P);
+hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const float *y_perm, const float *y_shared, const int32_t *inv, const float *w, int T,
+                          int d, int k, float *y, hipStream_t stream);
+
+}  // namespace moe

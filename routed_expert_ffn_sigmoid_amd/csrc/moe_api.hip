@@ -1,0 +1,221 @@
+// C ABI of the MoE-layer forward: argument validation, workspace layout and kernel launches.
+// Nothing here allocates device memory or waits on the device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE_PTR(p, name)                                                     \
+    do {                                                                         \
+        if (!(p)) return fail(MOE_EINVAL, "%s: %s is NULL", fn, name);           \
+        if (!aligned((p), 16)) return fail(MOE_EALIGN, "%s: %s is not 16-byte aligned", fn, name); \
+    } while (0)
+
+int check_shape(const char *fn, const moe_shape *s) {
+    if (!s) return fail(MOE_EINVAL, "%s: shape is NULL", fn);
+    if (s->T < 1 || s->d < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->I_shared < 0)
+        return fail(MOE_EINVAL, "%s: T, d, E, k, I must be >= 1 and I_shared >= 0", fn);
+    if (s->k > s->E || s->k > 32) return fail(MOE_EINVAL, "%s: k=%d must be <= min(E, 32)", fn, s->k);
+    if (s->E > 1024) return fail(MOE_EINVAL, "%s: E=%d exceeds 1024", fn, s->E);
+    if ((long)s->T * s->k >= (1L << 31)) return fail(MOE_EINVAL, "%s: T*k overflows int32", fn);
+    if (s->act_dtype != MOE_ACT_F32 && s->act_dtype != MOE_ACT_BF16)
+        return fail(MOE_EUNSUPPORTED, "%s: act_dtype %d not supported", fn, s->act_dtype);
+    if (s->wbits != 8 && s->wbits != 4) return fail(MOE_EUNSUPPORTED, "%s: wbits %d not supported", fn, s->wbits);
+    const int m = s->wbits == 4 ? 32 : 16;
+    if (s->d % m || s->I % m || s->I_shared % m)
+        return fail(MOE_EINVAL, "%s: d, I and I_shared must be multiples of %d for %d-bit weights", fn, m, s->wbits);
+    if (s->path != MOE_PATH_AUTO && s->path != MOE_PATH_GEMV && s->path != MOE_PATH_GEMM)
+        return fail(MOE_EINVAL, "%s: unknown path %d", fn, s->path);
+    return MOE_OK;
+}
+
+int check_ws(const char *fn, const moe_shape *s, void *ws, size_t ws_bytes) {
+    size_t need = moe_workspace_size(s);
+    if (need == 0) return MOE_OK;
+    if (!ws) return fail(MOE_EWORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (!aligned(ws, 256)) return fail(MOE_EALIGN, "%s: workspace is not 256-byte aligned", fn);
+    if (ws_bytes < need) return fail(MOE_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    return MOE_OK;
+}
+
+int check_qffn(const char *fn, const moe_qffn *q, const char *which) {
+    if (!q) return fail(MOE_EINVAL, "%s: %s weights are NULL", fn, which);
+    const void *ptrs[9] = {q->q_gate, q->q_up, q->q_down, q->s_gate, q->s_up, q->s_down, q->z_gate, q->z_up, q->z_down};
+    static const char *names[9] = {"q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down"};
+    for (int i = 0; i < 9; i++) {
+        if (!ptrs[i]) return fail(MOE_EINVAL, "%s: %s.%s is NULL", fn, which, names[i]);
+        if (!aligned(ptrs[i], 16)) return fail(MOE_EALIGN, "%s: %s.%s is not 16-byte aligned", fn, which, names[i]);
+    }
+    return MOE_OK;
+}
+
+moe::QW to_qw(const moe_qffn *q) {
+    moe::QW w{};
+    if (!q) return w;
+    w.qg = (const uint8_t *)q->q_gate;
+    w.qu = (const uint8_t *)q->q_up;
+    w.qd = (const uint8_t *)q->q_down;
+    w.sg = q->s_gate;
+    w.su = q->s_up;
+    w.sd = q->s_down;
+    w.zg = q->z_gate;
+    w.zu = q->z_up;
+    w.zd = q->z_down;
+    return w;
+}
+
+moe::FfnParams ffn_params(const moe_shape *s) {
+    moe::FfnParams P{};
+    P.T = s->T;
+    P.d = s->d;
+    P.k = s->k;
+    P.E = s->E;
+    P.A = s->T * s->k;
+    P.I = s->I;
+    P.Is = s->I_shared;
+    P.wbits = s->wbits;
+    P.act = s->act_dtype;
+    P.n_routed_slots = s->E < P.A ? s->E : P.A;
+    return P;
+}
+
+// Path the forward call takes for this shape.
+int forward_path(const moe_shape *s) {
+    if (s->path != MOE_PATH_AUTO) return s->path;
+    return MOE_PATH_GEMV;
+}
+
+int launch_status(const char *fn, hipError_t err) {
+    if (err != hipSuccess) return fail(MOE_EDEVICE, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return 1; }
+
+const char *moe_last_error(void) { return g_err; }
+
+size_t moe_workspace_size(const moe_shape *s) {
+    if (check_shape("moe_workspace_size", s) != MOE_OK) return 0;
+    moe::FfnParams P = ffn_params(s);
+    size_t r = moe::router_workspace_bytes(s->T, s->d, s->E);
+    size_t g = moe::gemv_workspace_bytes(P);
+    size_t need = r > g ? r : g;
+    size_t m = moe::gemm_workspace_bytes(P);
+    if (m > need) need = m;
+    return (need + 255) & ~(size_t)255;
+}
+
+int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *bias, int32_t *topk_idx,
+              float *topk_w, double *gap, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_route";
+    int rc = check_shape(fn, s);
+    if (rc) return rc;
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(W_r, "W_r");
+    REQUIRE_PTR(bias, "bias");
+    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR(topk_w, "topk_w");
+    if (gap && !aligned(gap, 16)) return fail(MOE_EALIGN, "%s: gap is not 16-byte aligned", fn);
+    rc = check_ws(fn, s, ws, ws_bytes);
+    if (rc) return rc;
+    return launch_status(fn, moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
+                                                topk_idx, topk_w, gap, ws, (hipStream_t)stream));
+}
+
+int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, int32_t *offsets, int32_t *perm,
+                int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_permute";
+    int rc = check_shape(fn, s);
+    if (rc) return rc;
+    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR(counts, "counts");
+    REQUIRE_PTR(offsets, "offsets");
+    REQUIRE_PTR(perm, "perm");
+    REQUIRE_PTR(inv, "inv");
+    REQUIRE_PTR(uniq, "uniq");
+    REQUIRE_PTR(n_uniq, "n_uniq");
+    rc = check_ws(fn, s, ws, ws_bytes);
+    if (rc) return rc;
+    return launch_status(fn, moe::launch_permute(topk_idx, s->T * s->k, s->E, counts, offsets, perm, inv, uniq,
+                                                 n_uniq, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                float *y_perm, float *y_shared, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_forward";
+    int rc = check_shape(fn, s);
+    if (rc) return rc;
+    REQUIRE_PTR(x, "x");
+    rc = check_qffn(fn, routed, "routed");
+    if (rc) return rc;
+    if (s->I_shared > 0) {
+        rc = check_qffn(fn, shared, "shared");
+        if (rc) return rc;
+        REQUIRE_PTR(y_shared, "y_shared");
+    }
+    REQUIRE_PTR(offsets, "offsets");
+    REQUIRE_PTR(perm, "perm");
+    REQUIRE_PTR(uniq, "uniq");
+    REQUIRE_PTR(n_uniq, "n_uniq");
+    REQUIRE_PTR(y_perm, "y_perm");
+    rc = check_ws(fn, s, ws, ws_bytes);
+    if (rc) return rc;
+    moe::FfnParams P = ffn_params(s);
+    P.x = x;
+    P.routed = to_qw(routed);
+    P.shared = to_qw(s->I_shared > 0 ? shared : nullptr);
+    P.offsets = offsets;
+    P.perm = perm;
+    P.uniq = uniq;
+    P.n_uniq = n_uniq;
+    P.y_perm = y_perm;
+    P.y_sh = s->I_shared > 0 ? y_shared : nullptr;
+    const int path = forward_path(s);
+    hipError_t err;
+    if (path == MOE_PATH_GEMM) {
+        err = moe::launch_ffn_gemm(P, ws, (hipStream_t)stream);
+        if (err == hipErrorNotSupported)
+            return fail(MOE_EUNSUPPORTED, "%s: the MFMA path does not support this shape", fn);
+    } else {
+        err = moe::launch_ffn_gemv(P, ws, (hipStream_t)stream);
+    }
+    return launch_status(fn, err);
+}
+
+int moe_combine(const moe_shape *s, const float *y_perm, const float *y_shared, const int32_t *inv,
+                const float *topk_w, float *y, void *stream) {
+    const char *fn = "moe_combine";
+    int rc = check_shape(fn, s);
+    if (rc) return rc;
+    REQUIRE_PTR(y_perm, "y_perm");
+    REQUIRE_PTR(inv, "inv");
+    REQUIRE_PTR(topk_w, "topk_w");
+    REQUIRE_PTR(y, "y");
+    if (y_shared && !aligned(y_shared, 16)) return fail(MOE_EALIGN, "%s: y_shared is not 16-byte aligned", fn);
+    return launch_status(fn, moe::launch_combine(y_perm, y_shared, inv, topk_w, s->T, s->d, s->k, y,
+                                                 (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+"""Shared test helpers: tolerance checks and oracle evaluations of sampled tokens."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from routed_expert_ffn_sigmoid_amd import synth
+
+# Layer-output tolerance: relative L2 <= 1e-3 and max-abs <= 2e-3 * RMS(output).
+REL_L2 = 1e-3
+MAX_ABS_RMS = 2e-3
+NEAR_TIE = 1e-6
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def close_report(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = got - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(err) / nref if nref > 0 else np.linalg.norm(err)
+    rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    mx = np.abs(err).max() if err.size else 0.0
+    return rel, (mx / rms if rms > 0 else mx)
+
+
+def assert_layer_close(got, ref, what: str):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rel, mx = close_report(got, ref)
+    assert rel <= REL_L2 and mx <= MAX_ABS_RMS, f"{what}: rel-L2 {rel:.3e} (<= {REL_L2}), max-abs {mx:.3e} RMS (<= {MAX_ABS_RMS})"
+    return rel, mx
+
+
+class SampledOracle:
+    """Oracle evaluation of a subset of tokens, regenerating only the experts they hit."""
+
+    def __init__(self, orc, spec: synth.LayerSpec, seed: int = 0, layer: int = 0):
+        self.orc, self.spec, self.seed, self.layer = orc, spec, seed, layer
+        self._experts = {}
+
+    def expert(self, e: int) -> synth.QExpertSet:
+        if e not in self._experts:
+            self._experts[e] = synth.stack_experts([synth.gen_expert(self.spec, e, self.seed, self.layer)])
+        return self._experts[e]
+
+    def run(self, x: np.ndarray, W_r: np.ndarray, bias: np.ndarray, tokens):
+        orc, spec = self.orc, self.spec
+        tokens = np.asarray(tokens, dtype=np.int64)
+        n, k, d = tokens.size, spec.k, spec.d
+        xd = orc.decode_act(np.ascontiguousarray(x[tokens]), spec.act)
+        z = orc.router_logits(xd, W_r)
+        r = orc.router_select(z, bias, k, spec.routed_scale)
+        Y = np.zeros((n, k, d))
+        for e in sorted(set(int(v) for v in r.idx.reshape(-1))):
+            rows = [(i, j) for i in range(n) for j in range(k) if r.idx[i, j] == e]
+            Ye = orc.expert_apply(xd[[i for i, _ in rows]], d, spec.I, spec.wbits, self.expert(e), 0)
+            for (i, j), yrow in zip(rows, Ye):
+                Y[i, j] = yrow
+        S = None
+        if spec.I_shared > 0:
+            S = orc.expert_apply(xd, d, spec.I_shared, spec.wbits, self.expert(-1), 0)
+        y = orc.combine(Y.reshape(n * k, d), S, np.arange(n * k, dtype=np.int32), r.w)
+        return r, Y, S, y

@@ -1,0 +1,246 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Expert indices and the permutation must match bit for bit; layer outputs
+within relative L2 <= 1e-3 and max-abs <= 2e-3 * RMS(output).  Small cases
+run the whole oracle layer; the full-size workloads compare every routed
+index and the whole permutation, and the layer output on sampled tokens
+(tokens are independent, so a sample is an exact check of those rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import SampledOracle, assert_layer_close, say, NEAR_TIE
+from routed_expert_ffn_sigmoid_amd import binding as B
+from routed_expert_ffn_sigmoid_amd import layer as L
+from routed_expert_ffn_sigmoid_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    return torch.device("cuda:0")
+
+
+def spec_of(name=None, **kw):
+    if name is not None:
+        base = synth.CONFIGS[name]
+        return synth.small_spec(base, **kw) if kw else base
+    d = dict(name="case", family=200, d=512, E=16, k=4, I=352, I_shared=0, wbits=4, routed_scale=1.0,
+             act=synth.ACT_BF16, bias="normal0.05")
+    d.update(kw)
+    return synth.LayerSpec(**d)
+
+
+class HostLayer:
+    """numpy inputs of one layer plus their device copies."""
+
+    def __init__(self, spec, T, dev, seed=0, layer=0, batch=0, tweak=None):
+        self.spec, self.T = spec, T
+        self.inp = synth.gen_layer(spec, T, seed, layer, batch)
+        if tweak:
+            tweak(self.inp)
+        self.x = L.upload_x(spec, self.inp.x, dev)
+        self.W = L.DeviceLayerWeights.__new__(L.DeviceLayerWeights)
+        self.W.spec = spec
+        self.W.W_r = torch.from_numpy(self.inp.W_r).to(dev)
+        self.W.bias = torch.from_numpy(self.inp.bias).to(dev)
+        self.W.routed = L.DeviceExperts.from_set(spec, self.inp.routed, spec.I, dev)
+        self.W.shared = (L.DeviceExperts.from_set(spec, self.inp.shared, spec.I_shared, dev)
+                         if self.inp.shared is not None else None)
+        self.W.routed_q = self.W.routed.qffn()
+        self.W.shared_q = self.W.shared.qffn() if self.W.shared is not None else None
+
+
+def run_full_case(orc, dev, spec, T, path=B.MOE_PATH_AUTO, tweak=None, label=""):
+    say(f"[case] {label or spec.name} T={T} d={spec.d} E={spec.E} k={spec.k} I={spec.I} Is={spec.I_shared} "
+        f"w{spec.wbits} act={spec.act} path={path}")
+    H = HostLayer(spec, T, dev, tweak=tweak)
+    run = L.MoeRun(spec, T, dev, path)
+    run.run(H.x, H.W)
+    torch.cuda.synchronize()
+    ref = orc.moe_layer(spec, H.inp.x, H.inp.W_r, H.inp.bias, H.inp.routed, H.inp.shared)
+    np.testing.assert_array_equal(run.idx.cpu().numpy(), ref.idx, err_msg="topk_idx")
+    np.testing.assert_allclose(run.w.cpu().numpy(), ref.w, rtol=1e-6, atol=0, err_msg="topk_w")
+    gap = run.gap.cpu().numpy()
+    fin = np.isfinite(ref.gap)
+    np.testing.assert_allclose(gap[fin], ref.gap[fin], rtol=0, atol=1e-12, err_msg="gap")
+    assert np.all(np.isinf(gap[~fin]))
+    assert list(np.flatnonzero(gap < NEAR_TIE)) == list(np.flatnonzero(ref.gap < NEAR_TIE))
+    p = ref.perm
+    for name in ("counts", "offsets", "perm", "inv"):
+        np.testing.assert_array_equal(getattr(run, name).cpu().numpy(), getattr(p, name), err_msg=name)
+    assert int(run.n_uniq.item()) == p.n_uniq
+    np.testing.assert_array_equal(run.uniq.cpu().numpy(), p.uniq, err_msg="uniq")
+    assert_layer_close(run.y_perm.cpu().numpy(), ref.Yperm, "y_perm")
+    if spec.I_shared:
+        assert_layer_close(run.y_shared.cpu().numpy(), ref.S, "y_shared")
+    rel, mx = assert_layer_close(run.y.cpu().numpy(), ref.y, "y")
+    say(f"   ok rel-L2 {rel:.2e} max-abs/RMS {mx:.2e} n_uniq {p.n_uniq}")
+    return run, ref
+
+
+# ---------------------------------------------------------------------------
+# small cases: whole oracle layer
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    "tiny_cfg": (dict(name="tiny"), 16),
+    "int4_bf16_shared_ragged_T": (dict(d=512, E=16, k=4, I=352, I_shared=96, routed_scale=2.5), 7),
+    "int8_f32": (dict(d=1024, E=8, k=2, I=1536, wbits=8, act=synth.ACT_F32, bias="uniform0.01"), 5),
+    "int4_f32_split": (dict(d=256, E=8, k=3, I=64, I_shared=128, act=synth.ACT_F32), 9),
+    "int8_bf16_shared": (dict(d=768, E=32, k=8, I=256, I_shared=512, wbits=8, routed_scale=2.5), 3),
+    "int8_f32_k_ranges": (dict(d=8192, E=4, k=2, I=64, wbits=8, act=synth.ACT_F32), 4),
+    "int4_f32_down_k_ranges": (dict(d=256, E=4, k=2, I=8192, act=synth.ACT_F32), 4),
+    "E_equals_k": (dict(d=256, E=4, k=4, I=128, I_shared=64), 3),
+    "T1": (dict(d=512, E=64, k=6, I=256, I_shared=256, routed_scale=2.5), 1),
+    "tiny_short_rows": (dict(d=64, E=8, k=2, I=32, wbits=8, act=synth.ACT_F32), 6),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_layer_parity(orc, dev, case):
+    kw, T = SMALL[case]
+    spec = spec_of(**kw) if "name" not in kw else spec_of(kw["name"])
+    run_full_case(orc, dev, spec, T, label=case)
+
+
+def test_all_tie_router(orc, dev):
+    """W_r = 0 and b = 0: every selection score is 0.5; ids 0..k-1 win with w = lambda/k."""
+    spec = spec_of(d=256, E=8, k=3, I=64, routed_scale=2.5)
+
+    def tweak(inp):
+        inp.W_r[:] = 0
+        inp.bias[:] = 0
+    run, ref = run_full_case(orc, dev, spec, 5, tweak=tweak, label="all_tie")
+    assert np.all(run.idx.cpu().numpy() == np.arange(3))
+    assert np.all(run.w.cpu().numpy() == np.float32(2.5 / 3))
+
+
+def test_one_expert_takes_all(orc, dev):
+    spec = spec_of(d=256, E=16, k=2, I=64, I_shared=64)
+
+    def tweak(inp):
+        inp.bias[:] = 0
+        inp.bias[5] = 10.0
+    run, ref = run_full_case(orc, dev, spec, 11, tweak=tweak, label="one_expert_hot")
+    assert run.counts.cpu().numpy()[5] == 11
+
+
+def test_zero_weights_give_shared_only(orc, dev):
+    spec = spec_of(d=256, E=8, k=2, I=64, I_shared=64, wbits=8, act=synth.ACT_F32)
+
+    def tweak(inp):
+        R = inp.routed
+        for q, z in ((R.q_gate, R.z_gate), (R.q_up, R.z_up), (R.q_down, R.z_down)):
+            q[:] = z[..., None]
+    run, ref = run_full_case(orc, dev, spec, 4, tweak=tweak, label="zero_routed")
+    np.testing.assert_allclose(run.y.cpu().numpy(), run.y_shared.cpu().numpy(), rtol=0, atol=1e-5)
+
+
+def test_repeat_is_bitwise_deterministic(dev):
+    spec = spec_of(d=512, E=16, k=4, I=352, I_shared=96)
+    H = HostLayer(spec, 13, dev)
+    run = L.MoeRun(spec, 13, dev)
+    outs = []
+    for _ in range(3):
+        run.run(H.x, H.W)
+        torch.cuda.synchronize()
+        outs.append((run.perm.cpu().numpy().copy(), run.y.cpu().numpy().copy()))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o[0], outs[0][0])
+        np.testing.assert_array_equal(o[1], outs[0][1])
+
+
+def test_permute_adversarial(orc, dev):
+    """moe_permute on hand-made index arrays: skewed, single expert, all experts, large A."""
+    rng = np.random.default_rng(7)
+    cases = [
+        (np.full((300, 1), 2, np.int32), 4),
+        (np.stack([rng.permutation(256)[:8] for _ in range(4096)]).astype(np.int32), 256),
+        (np.tile(np.arange(8, dtype=np.int32), (5, 1)), 8),
+        (np.stack([rng.permutation(1024)[:32] for _ in range(70)]).astype(np.int32), 1024),
+    ]
+    for idx, E in cases:
+        T, k = idx.shape
+        say(f"[permute] T={T} k={k} E={E}")
+        spec = spec_of(d=64, E=E, k=k, I=32)
+        run = L.MoeRun(spec, T, dev)
+        run.idx.copy_(torch.from_numpy(idx))
+        run.permute()
+        torch.cuda.synchronize()
+        p = orc.permute(idx, E)
+        for name in ("counts", "offsets", "perm", "inv", "uniq"):
+            np.testing.assert_array_equal(getattr(run, name).cpu().numpy(), getattr(p, name), err_msg=name)
+        assert int(run.n_uniq.item()) == p.n_uniq
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+
+_WEIGHTS = {}
+
+
+def weights_for(spec, dev, layer=0):
+    """Expert weights are shared by the workloads of one family; the bias is per workload."""
+    key = (spec.family, spec.wbits, layer)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        torch.cuda.empty_cache()
+        say(f"[upload] family={spec.family} w{spec.wbits} layer={layer}")
+        _WEIGHTS[key] = L.DeviceLayerWeights(spec, 0, layer, dev)
+    W = _WEIGHTS[key]
+    W.bias = torch.from_numpy(synth.gen_bias(spec, 0, layer)).to(dev)
+    W.W_r = torch.from_numpy(synth.gen_router(spec, 0, layer)).to(dev)
+    return W
+
+
+FULL = [("mid", 1, None), ("mid", 4, None), ("large", 1, None), ("large_zipf", 4, None),
+        ("large_zipf", 512, 24), ("prefill_int4_uniform", 8192, 8), ("prefill_int4_zipf", 8192, 8),
+        ("prefill_int8_uniform", 8192, 8), ("prefill_int8_zipf", 8192, 8)]
+
+
+@pytest.mark.parametrize("name,T,nsample", FULL, ids=[f"{n}-T{t}" for n, t, _ in FULL])
+def test_full_workload_parity(orc, dev, name, T, nsample):
+    spec = synth.CONFIGS[name]
+    say(f"[full] {name} T={T} sample={nsample}")
+    W = weights_for(spec, dev)
+    x_np = synth.gen_x(spec, T)
+    x = L.upload_x(spec, x_np, dev)
+    run = L.MoeRun(spec, T, dev)
+    run.run(x, W)
+    torch.cuda.synchronize()
+    W_r = synth.gen_router(spec)
+    bias = synth.gen_bias(spec)
+    idx = run.idx.cpu().numpy()
+    # every routed index is checked when the oracle router is cheap enough (all of T <= 8192)
+    z = orc.router_logits(orc.decode_act(x_np, spec.act), W_r)
+    r = orc.router_select(z, bias, spec.k, spec.routed_scale)
+    np.testing.assert_array_equal(idx, r.idx, err_msg="topk_idx")
+    np.testing.assert_allclose(run.w.cpu().numpy(), r.w, rtol=1e-6, atol=0)
+    near = np.flatnonzero(r.gap < NEAR_TIE)
+    assert list(np.flatnonzero(run.gap.cpu().numpy() < NEAR_TIE)) == list(near)
+    if near.size:
+        say(f"   near-tie tokens (gap < 1e-6): {near.tolist()[:20]}{' ...' if near.size > 20 else ''}")
+    p = orc.permute(r.idx, spec.E)
+    for nm in ("counts", "offsets", "perm", "inv", "uniq"):
+        np.testing.assert_array_equal(getattr(run, nm).cpu().numpy(), getattr(p, nm), err_msg=nm)
+    assert int(run.n_uniq.item()) == p.n_uniq
+    say(f"   indices+permutation bit-exact; n_uniq={p.n_uniq} max count={p.counts.max()}")
+    tokens = np.arange(T) if nsample is None else np.unique(
+        np.concatenate([[0, T - 1], np.random.default_rng(T).choice(T, nsample - 2, replace=False)]))
+    so = SampledOracle(orc, spec)
+    ro, Y, S, y = so.run(x_np, W_r, bias, tokens)
+    y_gpu = run.y.cpu().numpy()[tokens]
+    rel, mx = assert_layer_close(y_gpu, y, f"{name} T={T} y (sampled {tokens.size})")
+    inv = run.inv.cpu().numpy()
+    yp = run.y_perm.cpu().numpy()
+    for i, t in enumerate(tokens[:4]):
+        for j in range(spec.k):
+            assert_layer_close(yp[inv[t * spec.k + j]], Y[i, j], f"y_perm t={t} j={j}")
+    say(f"   ok rel-L2 {rel:.2e} max-abs/RMS {mx:.2e}")
