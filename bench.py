@@ -6,16 +6,20 @@ all inputs already resident in HBM.  Decode workloads rotate over several
 resident layers and a pool of activation batches so that neither the 256 MB
 Infinity Cache nor L2 holds the expert weights between steps.
 
+Each step of the rotation is captured once as a HIP graph (the four ABI
+calls) and replayed, so host launch overhead does not enter the timing.
+
 Prints ONE JSON line (the driver's contract).  `value` is MoE-layer tokens/s.
 `roofline` reports the expert-FFN stage (moe_forward) against HBM bandwidth
 (decode) or the bf16/fp16 MFMA peak (prefill), timed with HIP events on the
-stream the kernels run on.  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload.
+stream the kernels run on around replays of a graph of moe_forward calls.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -37,7 +41,7 @@ def parse():
     ap.add_argument("--config", default="mid", help="workload name (routed_expert_ffn_sigmoid_amd.synth.CONFIGS)")
     ap.add_argument("--T", type=int, default=None, help="tokens per step (default: first of the workload's T list)")
     ap.add_argument("--layers", type=int, default=None, help="resident layers rotated per step")
-    ap.add_argument("--pool", type=int, default=16, help="activation batches rotated per step")
+    ap.add_argument("--pool", type=int, default=None, help="activation batches rotated per step (16 decode, 2 prefill)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -76,6 +80,7 @@ def main():
     T = args.T or synth.WORKLOAD_T[args.config][0]
     decode = T * spec.k <= 4 * spec.E or T <= 64
     n_layers = args.layers or (4 if decode else 1)
+    args.pool = args.pool or (16 if decode else 2)
     path = {"auto": B.MOE_PATH_AUTO, "gemv": B.MOE_PATH_GEMV, "gemm": B.MOE_PATH_GEMM}[args.path]
     dev = torch.device("cuda:0")
     B.lib()
@@ -83,59 +88,81 @@ def main():
     t_setup = time.perf_counter()
     layers = [L.DeviceLayerWeights(spec, 0, l, dev) for l in range(n_layers)]
     pool = [L.upload_x(spec, synth.gen_x(spec, T, 0, b), dev) for b in range(args.pool)]
-    run = L.MoeRun(spec, T, dev, path)
-    stream = torch.cuda.current_stream()
+    cycle = n_layers * args.pool // math.gcd(n_layers, args.pool)
+    # one set of output/workspace buffers per step of the rotation, so each step can be a captured graph
+    runs = [L.MoeRun(spec, T, dev, path) for _ in range(cycle)]
     setup_s = time.perf_counter() - t_setup
 
-    # untimed pass over every (layer, batch) pair: realized unique experts per step
-    n_uniq = np.zeros((n_layers, args.pool), dtype=np.int64)
-    for l in range(n_layers):
-        for b in range(args.pool):
-            run.run(pool[b], layers[l])
-            n_uniq[l, b] = int(run.n_uniq.item())
+    def operands(i):
+        return pool[i % args.pool], layers[i % n_layers]
 
-    def step(i):
-        l, b = i % n_layers, i % args.pool
-        W, x = layers[l], pool[b]
-        run.route(x, W)
-        run.permute()
-        ev[i][0].record(stream)
-        run.forward(x, W)
-        ev[i][1].record(stream)
-        run.combine()
+    # eager pass over the rotation: realized unique experts per step
+    n_uniq = np.zeros(cycle, dtype=np.int64)
+    for i in range(cycle):
+        x, W = operands(i)
+        runs[i].run(x, W)
+        n_uniq[i] = int(runs[i].n_uniq.item())
+    torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.warmup + args.steps)]
+    # HIP graphs: one per step of the rotation (the four ABI calls), and one of a whole rotation of
+    # moe_forward calls for the expert-FFN stage timing
+    side = torch.cuda.Stream()
+    step_graphs = []
+    for i in range(cycle):
+        g = torch.cuda.CUDAGraph()
+        x, W = operands(i)
+        with torch.cuda.graph(g, stream=side):
+            runs[i].run(x, W)
+        step_graphs.append(g)
+    fwd_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(fwd_graph, stream=side):
+        for i in range(cycle):
+            x, W = operands(i)
+            runs[i].forward(x, W)
+    torch.cuda.synchronize()
+
     for i in range(args.warmup):
-        step(i)
+        step_graphs[i % cycle].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
-        step(i)
+        step_graphs[i % cycle].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    fwd_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, args.warmup + args.steps)])
+    # expert-FFN stage alone, timed with HIP events on the stream the kernels run on
+    fwd_reps = max(1, (args.steps + cycle - 1) // cycle)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fwd_graph.replay()
+    e0.record(stream)
+    for _ in range(fwd_reps):
+        fwd_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_s = e0.elapsed_time(e1) / 1e3
+    n_fwd = fwd_reps * cycle
+    fwd_us = fwd_s / n_fwd * 1e6
+
     ebytes = spec.expert_bytes()
     sbytes = spec.expert_bytes(spec.I_shared) if spec.I_shared else 0
-    steps_idx = range(args.warmup, args.warmup + args.steps)
-    bytes_tot = sum(int(n_uniq[i % n_layers, i % args.pool]) * ebytes + sbytes for i in steps_idx)
+    bytes_per_fwd = float(np.mean(n_uniq)) * ebytes + sbytes
     flops_per_step = 2.0 * 3 * spec.d * (T * spec.k * spec.I + T * spec.I_shared)
-    fwd_s = fwd_ms.sum() / 1e3
     if decode:
-        achieved = bytes_tot / fwd_s / 1e9
+        achieved = bytes_per_fwd / (fwd_s / n_fwd) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "moe_forward (expert-FFN kernels)",
-                "algorithmic_bytes_per_launch": round(bytes_tot / args.steps),
-                "avg_launch_us": round(float(fwd_ms.mean()) * 1e3, 2)}
+                "kernel": "moe_forward (gate/up + down expert-FFN kernels)",
+                "algorithmic_bytes_per_launch": round(bytes_per_fwd),
+                "avg_launch_us": round(fwd_us, 2)}
     else:
-        achieved = flops_per_step * args.steps / fwd_s / 1e12
+        achieved = flops_per_step / (fwd_s / n_fwd) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "moe_forward (expert-FFN kernels)",
+                "kernel": "moe_forward (gate/up + down expert-FFN kernels)",
                 "algorithmic_flops_per_launch": flops_per_step,
-                "avg_launch_us": round(float(fwd_ms.mean()) * 1e3, 2)}
+                "avg_launch_us": round(fwd_us, 2)}
+    steps_idx = range(args.warmup, args.warmup + args.steps)
 
     ms_per_step = elapsed / args.steps * 1e3
     out = {
@@ -154,8 +181,8 @@ def main():
         "config": {"workload": f"{spec.name}: d={spec.d} E={spec.E} top-{spec.k} I={spec.I} "
                                f"shared={spec.I_shared} int{spec.wbits} T={T}",
                    "T": T, "layers_resident": n_layers, "x_pool": args.pool,
-                   "mean_unique_experts": round(float(np.mean([n_uniq[i % n_layers, i % args.pool]
-                                                                for i in steps_idx])), 2),
+                   "mean_unique_experts": round(float(np.mean([n_uniq[i % cycle] for i in steps_idx])), 2),
+                   "timing": "HIP graph per step (the four ABI calls), replayed",
                    "path": args.path, "setup_s": round(setup_s, 1)},
         "roofline": roof,
     }

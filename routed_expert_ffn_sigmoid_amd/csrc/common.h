@@ -45,4 +45,34 @@ __device__ __forceinline__ T wave_sum(T v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Raw buffer loads: an offset at or beyond the descriptor's byte count returns zeros without touching
+// memory, so loads that may fall outside their row stay branch-free and keep many requests in flight.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // offset that is always out of range
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor, 32-bit data
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+__device__ __forceinline__ double buf_load_f64(rsrc_t r, uint32_t off) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return __builtin_bit_cast(double, v);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t buf_load2(rsrc_t r, uint32_t off) {
+    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 }  // namespace moe

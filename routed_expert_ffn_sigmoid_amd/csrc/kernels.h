@@ -36,9 +36,9 @@ size_t permute_lds_bytes(int E);
 hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
                           int32_t *inv, int32_t *uniq, int32_t *n_uniq, hipStream_t stream);
 
-// ffn_gemv.hip: decode path (h kept in fp32 in the workspace)
-size_t gemv_workspace_bytes(const FfnParams &P);
-hipError_t launch_ffn_gemv(const FfnParams &P, void *ws, hipStream_t stream);
+// ffn_decode.hip: decode path, int8 MFMA with exact integer accumulation (h kept in fp32 in the workspace)
+size_t decode_workspace_bytes(const FfnParams &P);
+hipError_t launch_ffn_decode(const FfnParams &P, void *ws, hipStream_t stream);
 
 // ffn_gemm.hip: MFMA grouped-GEMM path
 size_t gemm_workspace_bytes(const FfnParams &P);

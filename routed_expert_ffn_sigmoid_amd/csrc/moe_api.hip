@@ -119,7 +119,7 @@ size_t moe_workspace_size(const moe_shape *s) {
     if (check_shape("moe_workspace_size", s) != MOE_OK) return 0;
     moe::FfnParams P = ffn_params(s);
     size_t r = moe::router_workspace_bytes(s->T, s->d, s->E);
-    size_t g = moe::gemv_workspace_bytes(P);
+    size_t g = moe::decode_workspace_bytes(P);
     size_t need = r > g ? r : g;
     size_t m = moe::gemm_workspace_bytes(P);
     if (m > need) need = m;
@@ -199,7 +199,7 @@ int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const
         if (err == hipErrorNotSupported)
             return fail(MOE_EUNSUPPORTED, "%s: the MFMA path does not support this shape", fn);
     } else {
-        err = moe::launch_ffn_gemv(P, ws, (hipStream_t)stream);
+        err = moe::launch_ffn_decode(P, ws, (hipStream_t)stream);
     }
     return launch_status(fn, err);
 }

@@ -1,13 +1,15 @@
 // Sigmoid + bias top-k router ("25GB 内存跑 744B GLM-5.2 模型" page, sections 三.1 and 四.3).
 //
 // Two kernels:
-//   router_logits  z = x . W_r in fp64, tiled 64 tokens x 64 experts per
-//                  workgroup with a K split so small T still spreads the
-//                  W_r read over the whole chip; partial sums per split go to
-//                  the workspace (no atomics: the reduction order is fixed).
-//   router_select  one wavefront per token: sums the splits in order, takes
-//                  the sigmoid, adds the bias, and picks the top k+1 by
-//                  repeated wave-wide argmax with ties to the lower id.
+//   logits  z = x . W_r in fp64, split over blocks of d rows so that even one
+//           token spreads the W_r read over the whole chip.  T <= 4: each
+//           workgroup streams a block of >= 64 KB of W_r rows once for all tokens;
+//           larger T: 64 tokens x 64 experts register tiles.  At most 32 blocks
+//           at small T, so the partials are few.  Partial sums per
+//           block go to the workspace (no atomics: the reduction order is fixed).
+//   select  one workgroup per token: adds the partials in a fixed order, takes
+//           the sigmoid, adds the bias, and picks the top k+1 by repeated
+//           wave-wide argmax with ties to the lower id.
 // Products of an fp32/bf16 activation and an fp32 weight are exact in fp64,
 // so the logit differs from any other fp64 summation order only by fp64
 // rounding; the choice of experts therefore matches a plain fp64 evaluation
@@ -87,6 +89,90 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restri
     }
 }
 
+// Small-T logits: 1024-thread workgroups each stream a block of W_r rows once for all T <= RS_TMAX
+// tokens.  Thread (row group rg, expert quad q) handles rows rg, rg+R, ... (at most RSK_MAXR) of the
+// block for experts 4q..4q+3; all of its W_r loads are issued before the block's activations are
+// staged in LDS.  At most RSK_SPLITS blocks, so the select kernel reads few partials.
+constexpr int RS_TMAX = 4;
+constexpr int RSK_THREADS = 1024;
+constexpr int RSK_SPLITS = 32;
+constexpr int RSK_MIN_BYTES = 64 * 1024;  // W_r bytes per workgroup at least
+constexpr int RSK_MAXR = 12;              // W_r rows per thread (1024 threads: 128 VGPRs each)
+constexpr int RSK_MAX_ROWS = 2048;        // rows per block (LDS holds RS_TMAX x rows activations)
+
+template <int ACT>
+__global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const void *__restrict__ x,
+                                                                           const float *__restrict__ Wr, int T,
+                                                                           int d, int E, int rows,
+                                                                           double *__restrict__ part) {
+    __shared__ double red[RSK_THREADS / 64][256];
+    __shared__ float xs[RS_TMAX * RSK_MAX_ROWS];  // [t][row in block], row pitch = rows
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nq = E >> 2;             // expert quads: a power of two <= 64
+    const int R = RSK_THREADS / nq;    // row groups (>= 16: every wave holds at least one)
+    const int q = tid % nq, rg = tid / nq;
+    const int i0 = blockIdx.x * rows, i1 = min(d, i0 + rows);
+    const rsrc_t wsrc = make_rsrc(Wr, (uint32_t)((long)d * E * 4));
+    const rsrc_t xsrc = make_rsrc(x, (uint32_t)((long)T * d * (ACT == 0 ? 4 : 2)));
+    // activations first (few, branch-free), then every W_r row of this thread: waiting for the
+    // activations does not wait for the weights
+    constexpr int XPT = RS_TMAX * RSK_MAX_ROWS / RSK_THREADS;
+    uint32_t xr[XPT];
+#pragma unroll
+    for (int c = 0; c < XPT; c++) {
+        const int o = tid + c * RSK_THREADS;
+        const int t = o / rows, i = i0 + o % rows;
+        const uint32_t xo = (t < T && i < i1) ? (uint32_t)(((long)t * d + i) * (ACT == 0 ? 4 : 2)) : kOOB;
+        xr[c] = ACT == 0 ? buf_load4(xsrc, xo) : (uint32_t)buf_load2(xsrc, xo);
+    }
+    uint4 w[RSK_MAXR];
+#pragma unroll
+    for (int u = 0; u < RSK_MAXR; u++) {
+        const int i = i0 + rg + u * R;
+        w[u] = buf_load16(wsrc, i < i1 ? (uint32_t)(((long)i * E + 4 * q) * 4) : kOOB);
+    }
+#pragma unroll
+    for (int c = 0; c < XPT; c++)  // unconditional: entries past T*rows are zeros nobody reads
+        xs[tid + c * RSK_THREADS] = ACT == 0 ? __uint_as_float(xr[c]) : bf16_to_f32((uint16_t)xr[c]);
+    __syncthreads();
+    double acc[RS_TMAX][4];
+#pragma unroll
+    for (int t = 0; t < RS_TMAX; t++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc[t][v] = 0.0;
+#pragma unroll
+    for (int u = 0; u < RSK_MAXR; u++) {
+        const int li = rg + u * R;  // row inside the block (the weights are zero past its end)
+        if (li < rows) {
+            const double w4[4] = {(double)__uint_as_float(w[u].x), (double)__uint_as_float(w[u].y),
+                                  (double)__uint_as_float(w[u].z), (double)__uint_as_float(w[u].w)};
+#pragma unroll
+            for (int t = 0; t < RS_TMAX; t++) {
+                const double xd = (double)xs[t * rows + li];
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[t][v] = fma(xd, w4[v], acc[t][v]);
+            }
+        }
+    }
+    // fixed-order reduction over row groups: lanes holding the same quad inside a wave
+    // (xor offsets nq, 2nq, ..., 32), then the 16 waves in order, one token at a time
+    for (int t = 0; t < T; t++) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            double a = acc[t][v];
+            for (int o = nq; o < 64; o <<= 1) a += __shfl_xor(a, o, 64);
+            if (lane < nq) red[wv][lane * 4 + v] = a;
+        }
+        __syncthreads();
+        if (tid < E) {
+            double z = 0.0;
+            for (int w2 = 0; w2 < RSK_THREADS / 64; w2++) z += red[w2][tid];
+            part[((long)blockIdx.x * T + t) * E + tid] = z;
+        }
+        __syncthreads();
+    }
+}
+
 constexpr int RS_MAXJ = 16;  // experts per lane: E <= 1024
 
 // (v, id) is better than (v2, id2): larger score, then lower id
@@ -94,14 +180,44 @@ __device__ __forceinline__ bool better(double v, int id, double v2, int id2) {
     return v > v2 || (v == v2 && id < id2);
 }
 
-// grid: ceil(T/4); block 256 (one wavefront per token)
-__global__ __launch_bounds__(256) void router_select_kernel(const double *__restrict__ part, int nsplit, int T,
-                                                            int E, int k, const float *__restrict__ bias,
-                                                            float lambda, int32_t *__restrict__ idx,
-                                                            float *__restrict__ w, double *__restrict__ gap) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+// One workgroup (1024 threads) per token.  Thread (e, g) sums the splits s = g, g+4, ... of expert e with
+// eight independent accumulators (fixed order), the four groups are added in order, then the first
+// wavefront takes sigmoid, bias and the top k+1 by repeated wave-wide argmax (ties to the lower id).
+constexpr int RSEL_THREADS = 1024;
+constexpr int RSEL_LOADS = 8;
+
+__global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const double *__restrict__ part, int nsplit,
+                                                                     int T, int E, int k,
+                                                                     const float *__restrict__ bias, float lambda,
+                                                                     int32_t *__restrict__ idx,
+                                                                     float *__restrict__ w,
+                                                                     double *__restrict__ gap) {
+    extern __shared__ double zs[];  // [4][E]
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ept = (E + 255) / 256;  // experts per thread column
+    const rsrc_t psrc = make_rsrc(part, (uint32_t)((long)nsplit * T * E * 8));
+    for (int j = 0; j < ept; j++) {
+        const int e = (tid & 255) + 256 * j;
+        const int g = tid >> 8;
+        if (e >= E) continue;
+        double z = 0.0;
+        int sp = g;
+        // batches of RSEL_LOADS independent loads, added in split order
+        for (; sp < nsplit; sp += 4 * RSEL_LOADS) {
+            double a[RSEL_LOADS];
+#pragma unroll
+            for (int m = 0; m < RSEL_LOADS; m++) {
+                const int s2 = sp + 4 * m;
+                a[m] = buf_load_f64(psrc, s2 < nsplit ? (uint32_t)((((long)s2 * T + t) * E + e) * 8) : kOOB);
+            }
+#pragma unroll
+            for (int m = 0; m < RSEL_LOADS; m++) z += a[m];
+        }
+        zs[g * E + e] = z;
+    }
+    __syncthreads();
+    if (tid >= 64) return;
     const int nj = (E + 63) >> 6;
     double sel[RS_MAXJ], s[RS_MAXJ];
 #pragma unroll
@@ -110,8 +226,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double *__rest
         sel[j] = -INFINITY;
         s[j] = 0.0;
         if (j < nj && e < E) {
-            double z = 0.0;
-            for (int sp = 0; sp < nsplit; sp++) z += part[((long)sp * T + t) * E + e];
+            const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
             s[j] = 1.0 / (1.0 + exp(-z));
             sel[j] = s[j] + (double)bias[e];
         }
@@ -134,7 +249,6 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double *__rest
                 bj = j;
             }
         }
-        // wave-wide argmax of (bv, bid)
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
             double ov = __shfl_xor(bv, o, 64);
@@ -147,7 +261,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double *__rest
             }
         }
         if (r < k) {
-            if ((bid & 63) == lane && bj >= 0 && lane + 64 * bj == bid) taken |= 1u << bj;
+            if (bj >= 0 && lane + 64 * bj == bid) taken |= 1u << bj;
             sum_s += bs;
             if (lane == r) {
                 my_s = bs;
@@ -165,7 +279,25 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double *__rest
     }
 }
 
+static bool use_skinny(int T, int E) { return T <= RS_TMAX && E >= 4 && E <= 256 && (E & (E - 1)) == 0; }
+
+static int skinny_rows(int d, int E) {
+    const long wbytes = (long)d * E * 4;
+    long nsplit = wbytes / RSK_MIN_BYTES;
+    if (nsplit > RSK_SPLITS) nsplit = RSK_SPLITS;
+    if (nsplit < 1) nsplit = 1;
+    long rows = (d + nsplit - 1) / nsplit;
+    const long cap = (long)RSK_MAXR * (RSK_THREADS / (E / 4));  // rows the threads of a block can hold
+    if (rows > cap) rows = cap;
+    if (rows > RSK_MAX_ROWS) rows = RSK_MAX_ROWS;
+    return (int)rows;
+}
+
 int router_nsplit(int T, int d, int E) {
+    if (use_skinny(T, E)) {
+        const int rows = skinny_rows(d, E);
+        return (d + rows - 1) / rows;
+    }
     int gx = (E + RL_TE - 1) / RL_TE, gy = (T + RL_TT - 1) / RL_TT;
     int ksteps = (d + RL_KS - 1) / RL_KS;
     int want = 512 / (gx * gy);
@@ -180,20 +312,32 @@ size_t router_workspace_bytes(int T, int d, int E) {
 
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
                          float lambda, int32_t *idx, float *w, double *gap, void *ws, hipStream_t stream) {
-    int nsplit = router_nsplit(T, d, E);
-    int ksteps = (d + RL_KS - 1) / RL_KS;
-    int chunk = ((ksteps + nsplit - 1) / nsplit) * RL_KS;
-    nsplit = (d + chunk - 1) / chunk;
     double *part = (double *)ws;
-    dim3 grid((E + RL_TE - 1) / RL_TE, (T + RL_TT - 1) / RL_TT, nsplit);
-    if (act == 0)
-        hipLaunchKernelGGL(router_logits_kernel<0>, grid, dim3(256), 0, stream, x, Wr, T, d, E, chunk, part);
-    else
-        hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, stream, x, Wr, T, d, E, chunk, part);
+    int nsplit;
+    if (use_skinny(T, E)) {
+        const int rows = skinny_rows(d, E);
+        nsplit = (d + rows - 1) / rows;
+        if (act == 0)
+            hipLaunchKernelGGL(router_logits_skinny_kernel<0>, dim3(nsplit), dim3(RSK_THREADS), 0, stream, x, Wr, T,
+                               d, E, rows, part);
+        else
+            hipLaunchKernelGGL(router_logits_skinny_kernel<1>, dim3(nsplit), dim3(RSK_THREADS), 0, stream, x, Wr, T,
+                               d, E, rows, part);
+    } else {
+        nsplit = router_nsplit(T, d, E);
+        int ksteps = (d + RL_KS - 1) / RL_KS;
+        int chunk = ((ksteps + nsplit - 1) / nsplit) * RL_KS;
+        nsplit = (d + chunk - 1) / chunk;
+        dim3 grid((E + RL_TE - 1) / RL_TE, (T + RL_TT - 1) / RL_TT, nsplit);
+        if (act == 0)
+            hipLaunchKernelGGL(router_logits_kernel<0>, grid, dim3(256), 0, stream, x, Wr, T, d, E, chunk, part);
+        else
+            hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, stream, x, Wr, T, d, E, chunk, part);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, part, nsplit, T, E, k, bias,
-                       lambda, idx, w, gap);
+    hipLaunchKernelGGL(router_select_kernel, dim3(T), dim3(RSEL_THREADS), 4 * E * sizeof(double), stream, part,
+                       nsplit, T, E, k, bias, lambda, idx, w, gap);
     return hipGetLastError();
 }
 
