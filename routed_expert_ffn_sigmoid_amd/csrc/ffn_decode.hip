@@ -41,8 +41,6 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int DK_THREADS = 256;
 constexpr int DK_GMAX = 16;               // tokens per pass: the MFMA M dimension
 constexpr int DK_LDS_BUDGET = 150 * 1024; // digit planes + reduction buffer
-constexpr int DK_RED_BYTES = 4 * 64 * 4 * 8 * 2;
-constexpr int DK_STAGE_MAX = 4;           // 8-input groups per thread kept in registers while staging
 
 struct DSlot {
     int e, I;
@@ -94,39 +92,37 @@ __device__ __forceinline__ void load8(rsrc_t src, uint32_t off, float (&v)[8]) {
     }
 }
 
-// Stage ng source rows (fp32 or bf16) as three signed 8-bit digit planes of their 24-bit fixed point
-// values.  expo[i] = e (x ~= X * 2^-e), xsum[i] = sum of X (exact).  Rows past K up to Kp are zero.
+// Wave-private staging: the inputs [k0, k0 + kpart) of ng source rows (fp32 or bf16) become three
+// signed 8-bit digit planes of their 24-bit fixed-point values, with one power-of-two scale per
+// (row, wavefront): x ~= X * 2^-expo[i], |X| < 2^22.  xsum[i] = sum of X (exact).  Positions past
+// kpart up to the padded length are zero.  Only this wavefront reads what it writes, so the only
+// synchronisation is the wavefront's own LDS ordering.
 template <int WBITS, int SRC>
-__device__ void dk_stage(rsrc_t src, const long *rowoff, int ng, int K, int Kp, int stride,
-                         long plane_bytes, int8_t *planes, int *expo, double *xsum, float *redf, double *redd) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int ngr = Kp / 8;
+__device__ void wave_stage(rsrc_t src, long rowoff_lane, int ng, int k0, int kpart, int kpad, int stride,
+                           long plane_bytes, int8_t *planes, int *expo, double *xsum) {
+    const int lane = threadIdx.x & 63;
+    const int ngr = kpad / 8;  // groups of 8 inputs, zero past kpart
+    constexpr int MAXG = 2;    // groups per lane held in registers (kpart <= 1024)
+    const int esz = SRC == 0 ? 4 : 2;
     for (int i = 0; i < ng; i++) {
-        float v[DK_STAGE_MAX][8];
+        const long ro = __shfl(rowoff_lane, i, 64) + k0;  // element offset of this row's first input
+        float v[MAXG][8];
         float mx = 0.f;
 #pragma unroll
-        for (int c = 0; c < DK_STAGE_MAX; c++) {
-            const int m = tid + c * DK_THREADS;
-#pragma unroll
-            for (int t = 0; t < 8; t++) v[c][t] = 0.f;
-            const bool ok = m < ngr && m * 8 < K;
-            load8<SRC>(src, ok ? (uint32_t)((rowoff[i] + (long)m * 8) * (SRC == 0 ? 4 : 2)) : kOOB, v[c]);
+        for (int c = 0; c < MAXG; c++) {
+            const int m = lane + 64 * c;
+            load8<SRC>(src, (m < ngr && m * 8 < kpart) ? (uint32_t)((ro + (long)m * 8) * esz) : kOOB, v[c]);
 #pragma unroll
             for (int t = 0; t < 8; t++) mx = fmaxf(mx, fabsf(v[c][t]));
         }
-        // rows longer than DK_STAGE_MAX * 8 * 256 inputs: the tail is read in a second sweep below
-        for (int m = tid + DK_STAGE_MAX * DK_THREADS; m < ngr; m += DK_THREADS) {
-            if (m * 8 >= K) break;
+        for (int m = lane + 64 * MAXG; m < ngr; m += 64) {  // K parts longer than 1024 inputs
             float xv[8];
-            load8<SRC>(src, (uint32_t)((rowoff[i] + (long)m * 8) * (SRC == 0 ? 4 : 2)), xv);
+            load8<SRC>(src, m * 8 < kpart ? (uint32_t)((ro + (long)m * 8) * esz) : kOOB, xv);
 #pragma unroll
             for (int t = 0; t < 8; t++) mx = fmaxf(mx, fabsf(xv[t]));
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (lane == 0) redf[wv] = mx;
-        __syncthreads();
-        mx = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
         int e = 0;
         if (mx > 0.f) {
             int ex;
@@ -184,27 +180,27 @@ __device__ void dk_stage(rsrc_t src, const long *rowoff, int ng, int K, int Kp, 
             }
         };
 #pragma unroll
-        for (int c = 0; c < DK_STAGE_MAX; c++) {
-            const int m = tid + c * DK_THREADS;
-            if (m < ngr) put(m, v[c]);  // groups past K hold zeros
+        for (int c = 0; c < MAXG; c++) {
+            const int m = lane + 64 * c;
+            if (m < ngr) put(m, v[c]);
         }
-        for (int m = tid + DK_STAGE_MAX * DK_THREADS; m < ngr; m += DK_THREADS) {
+        for (int m = lane + 64 * MAXG; m < ngr; m += 64) {
             float xv[8];
-            load8<SRC>(src, m * 8 < K ? (uint32_t)((rowoff[i] + (long)m * 8) * (SRC == 0 ? 4 : 2)) : kOOB, xv);
+            load8<SRC>(src, m * 8 < kpart ? (uint32_t)((ro + (long)m * 8) * esz) : kOOB, xv);
             put(m, xv);
         }
-        // exact sum of the fixed-point values (fp64 holds integers below 2^53 exactly)
-        double ds = (double)ssum;
+        double ds = (double)ssum;  // exact: integers below 2^53
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) ds += __shfl_xor(ds, o, 64);
-        __syncthreads();  // everyone has read redf
-        if (lane == 0) redd[wv] = ds;
-        __syncthreads();
-        if (tid == 0) {
-            xsum[i] = ((redd[0] + redd[1]) + redd[2]) + redd[3];
+        if (lane == 0) {
+            xsum[i] = ds;
             expo[i] = e;
         }
     }
+    // make this wavefront's LDS writes visible to its own later reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ float zp_val(const void *z, int wbits, long i) {
@@ -215,16 +211,13 @@ __device__ __forceinline__ float zp_val(const void *z, int wbits, long i) {
 // grid: (ceil(rows / (16 * 4/S)), slots); block 256; dynamic LDS from dk_lds_bytes.
 template <int MODE, int WBITS, int SRC, int S>
 __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, float *__restrict__ h,
-                                                            float *__restrict__ h_sh, int gmax, int Kp) {
+                                                            float *__restrict__ h_sh, int gmax, int kpad) {
     constexpr int TPW = 4 / S;
     constexpr int NM = MODE == 0 ? 2 : 1;  // matrices per wave: gate and up, or down
     constexpr int PF = MODE == 0 ? 4 : 8;  // 64-byte segments in flight per row
     extern __shared__ __align__(16) uint8_t dk_lds[];
-    __shared__ long rowoff[DK_GMAX];
-    __shared__ int expo[DK_GMAX];
-    __shared__ double xsum[DK_GMAX];
-    __shared__ float redf[4];
-    __shared__ double redd[4];
+    __shared__ int wexpo[4][DK_GMAX];
+    __shared__ double wxsum[4][DK_GMAX];
     __shared__ uint32_t zero_area[8];
 
     DSlot s;
@@ -266,14 +259,23 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
 
     const int p0 = s.shared ? 0 : P.offsets[s.e];
     const int n = s.shared ? P.T : P.offsets[s.e + 1] - p0;
-    const int stride = Kp + 16;
-    const long pb = (long)gmax * stride;  // bytes per digit plane
-    int8_t *planes = (int8_t *)dk_lds;
-    double *red = (double *)(dk_lds + 3 * pb);
+    const int stride = kpad + 16;
+    const long pb = (long)gmax * stride;             // bytes per digit plane of one wavefront
+    int8_t *planes = (int8_t *)dk_lds + (long)wv * 3 * pb;
+    double *red = (double *)dk_lds;                  // cross-wave partials, after the planes are done
     if (tid < 8) zero_area[tid] = 0u;
     const rsrc_t src = MODE == 0 ? make_rsrc(P.x, (uint32_t)((long)P.T * P.d * (SRC == 0 ? 4 : 2)))
                                  : make_rsrc(s.shared ? h_sh : h,
                                              (uint32_t)((long)(s.shared ? P.T : P.A) * K * 4));
+    // z of this lane's output row (the same row for every token)
+    float zrow[NM];
+    if (MODE == 0) {
+        zrow[0] = zp_val(W.zg, WBITS, (long)s.e * s.I + row);
+        zrow[NM - 1] = zp_val(W.zu, WBITS, (long)s.e * s.I + row);
+    } else {
+        zrow[0] = zp_val(W.zd, WBITS, (long)s.e * P.d + row);
+    }
+    __syncthreads();  // zero_area
 
     for (int g0 = 0; g0 < n; g0 += gmax) {
         const int ng = min(gmax, n - g0);
@@ -281,20 +283,21 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
 #pragma unroll
             for (int b = 0; b < PF; b++) ldw(b, b);
         }
-        if (tid < ng) {
+        long rowoff_lane = 0;  // lane i < ng: element offset of token i's source row
+        if (lane < ng) {
             if (MODE == 0) {
-                const int t = s.shared ? (g0 + tid) : (P.perm[p0 + g0 + tid] / P.k);
-                rowoff[tid] = (long)t * P.d;
+                const int t = s.shared ? (g0 + lane) : (P.perm[p0 + g0 + lane] / P.k);
+                rowoff_lane = (long)t * P.d;
             } else {
-                rowoff[tid] = (long)((s.shared ? 0 : p0) + g0 + tid) * K;
+                rowoff_lane = (long)((s.shared ? 0 : p0) + g0 + lane) * K;
             }
         }
-        __syncthreads();
         if (MODE == 0)
-            dk_stage<WBITS, SRC>(src, rowoff, ng, K, Kp, stride, pb, planes, expo, xsum, redf, redd);
+            wave_stage<WBITS, SRC>(src, rowoff_lane, ng, kp * kpart, kpart, kpad, stride, pb, planes,
+                                   wexpo[wv], wxsum[wv]);
         else
-            dk_stage<WBITS, 0>(src, rowoff, ng, K, Kp, stride, pb, planes, expo, xsum, redf, redd);
-        __syncthreads();
+            wave_stage<WBITS, 0>(src, rowoff_lane, ng, kp * kpart, kpart, kpad, stride, pb, planes, wexpo[wv],
+                                 wxsum[wv]);
 
         // ---- stream the wavefront's K part through the matrix cores
         i32x4_t C[NM][3];
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
             for (int p = 0; p < 3; p++) C[m][p] = (i32x4_t){0, 0, 0, 0};
         // A-operand rows: token j of this lane; lanes without a token read a zeroed LDS area
         const bool tok_ok = j < ng;
-        const int8_t *xrow = tok_ok ? planes + (long)j * stride + (long)kp * kpart : (const int8_t *)zero_area;
+        const int8_t *xrow = tok_ok ? planes + (long)j * stride : (const int8_t *)zero_area;
         const long pstep = tok_ok ? pb : 0;
         const int gstep = tok_ok ? 1 : 0;
         for (int seg0 = 0; seg0 < nseg_pad; seg0 += PF) {
@@ -359,15 +362,23 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // ---- exact partial dot products in fp64; the S wavefronts of a tile add theirs in order
+        // ---- this wavefront's exact partial, zero point applied and scale undone, in fp64
         double v[NM][4];
 #pragma unroll
-        for (int m = 0; m < NM; m++)
+        for (int r = 0; r < 4; r++) {
+            const int i = 4 * g + r;  // token of this register
+            const bool ok = i < ng;
+            const double unit = ok ? ldexp(1.0, -wexpo[wv][i]) : 0.0;
+            const double xs = ok ? wxsum[wv][i] : 0.0;
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-                v[m][r] = (double)C[m][2][r] * 65536.0 + (double)C[m][1][r] * 256.0 + (double)C[m][0][r];
+            for (int m = 0; m < NM; m++) {
+                const double dot = (double)C[m][2][r] * 65536.0 + (double)C[m][1][r] * 256.0 + (double)C[m][0][r];
+                v[m][r] = (dot - (double)zrow[m] * xs) * unit;
+            }
+        }
+        // the S wavefronts of a tile add their partials in a fixed order
         if (S > 1) {
-            __syncthreads();  // red is free
+            __syncthreads();  // every wavefront is done with its planes: red may overwrite them
 #pragma unroll
             for (int m = 0; m < NM; m++)
 #pragma unroll
@@ -391,33 +402,28 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
                 for (int r = 0; r < 4; r++) {
                     const int i = 4 * g + r;  // token of this register
                     if (i < ng) {
-                        const double unit = ldexp(1.0, -expo[i]);
                         if (MODE == 0) {
                             const long ch = (long)s.e * s.I + o;
-                            const double gg = (double)W.sg[ch] *
-                                              ((v[0][r] - (double)zp_val(W.zg, WBITS, ch) * xsum[i]) * unit);
-                            const double uu = (double)W.su[ch] *
-                                              ((v[NM - 1][r] - (double)zp_val(W.zu, WBITS, ch) * xsum[i]) * unit);
-                            const float gf = (float)gg;
-                            const float hv = gf / (1.f + expf(-gf)) * (float)uu;
+                            const float gf = (float)((double)W.sg[ch] * v[0][r]);
+                            const float uf = (float)((double)W.su[ch] * v[NM - 1][r]);
+                            const float hv = gf / (1.f + expf(-gf)) * uf;
                             if (s.shared)
                                 h_sh[(long)(g0 + i) * s.I + o] = hv;
                             else
                                 h[(long)(p0 + g0 + i) * s.I + o] = hv;
                         } else {
                             const long ch = (long)s.e * P.d + o;
-                            const double y = (double)W.sd[ch] *
-                                             ((v[0][r] - (double)zp_val(W.zd, WBITS, ch) * xsum[i]) * unit);
+                            const float y = (float)((double)W.sd[ch] * v[0][r]);
                             if (s.shared)
-                                P.y_sh[(long)(g0 + i) * P.d + o] = (float)y;
+                                P.y_sh[(long)(g0 + i) * P.d + o] = y;
                             else
-                                P.y_perm[(long)(p0 + g0 + i) * P.d + o] = (float)y;
+                                P.y_perm[(long)(p0 + g0 + i) * P.d + o] = y;
                         }
                     }
                 }
             }
         }
-        __syncthreads();  // LDS planes and token metadata are reused by the next token group
+        if (S > 1 || g0 + gmax < n) __syncthreads();  // red / planes are reused by the next token group
     }
 }
 
@@ -441,15 +447,22 @@ static int pick_s(int mode, int K, int wbits) {
     return 1;
 }
 
-// Tokens per pass: as many as the digit planes of one workgroup can hold, at most DK_GMAX.
-static int dk_gmax(int T, int Kp) {
-    int fit = (DK_LDS_BUDGET - DK_RED_BYTES) / (3 * (Kp + 16));
+// bytes of cross-wave partials (fp64): 4 wavefronts x NM matrices x 4 registers x 64 lanes
+static size_t dk_red_bytes(int mode) { return (size_t)4 * (mode == 0 ? 2 : 1) * 4 * 64 * 8; }
+
+// Tokens per pass: as many as the digit planes of the four wavefronts can hold, at most DK_GMAX.
+static int dk_gmax(int T, int kpad) {
+    int fit = DK_LDS_BUDGET / (4 * 3 * (kpad + 16));
     if (fit > DK_GMAX) fit = DK_GMAX;
     if (fit < 1) fit = 1;
     return T < fit ? T : fit;
 }
 
-static size_t dk_lds_bytes(int Kp, int gmax) { return 3L * gmax * (Kp + 16) + DK_RED_BYTES; }
+static size_t dk_lds_bytes(int mode, int kpad, int gmax) {
+    const size_t planes = (size_t)4 * 3 * gmax * (kpad + 16);
+    const size_t red = dk_red_bytes(mode);
+    return planes > red ? planes : red;
+}
 
 size_t decode_workspace_bytes(const FfnParams &P) {
     const size_t hb = ((size_t)P.A * P.I * sizeof(float) + 255) & ~(size_t)255;
@@ -466,9 +479,9 @@ static hipError_t dk_launch_mode(const FfnParams &P, float *h, float *h_sh, hipS
     const int Kmin = MODE == 0 ? P.d : (P.Is > 0 && P.Is < P.I ? P.Is : P.I);
     const int S = pick_s(MODE, Kmin, WBITS) < pick_s(MODE, K, WBITS) ? pick_s(MODE, Kmin, WBITS)
                                                                         : pick_s(MODE, K, WBITS);
-    const int Kp = pad_k(K, WBITS);
-    const int gmax = dk_gmax(P.T, Kp);
-    const size_t lds = dk_lds_bytes(Kp, gmax);
+    const int kpad = pad_k(K / S, WBITS);  // the largest wavefront K part, padded to whole segments
+    const int gmax = dk_gmax(P.T, kpad);
+    const size_t lds = dk_lds_bytes(MODE, kpad, gmax);
     const int nout = MODE == 0 ? Imax : P.d;
     const int rows_per_wg = 16 * (4 / S);
     dim3 grid((nout + rows_per_wg - 1) / rows_per_wg, slots);
@@ -485,13 +498,13 @@ static hipError_t dk_launch_mode(const FfnParams &P, float *h, float *h_sh, hipS
     }
     if (S == 4)
         hipLaunchKernelGGL((decode_kernel<MODE, WBITS, SRC, 4>), grid, dim3(DK_THREADS), lds, stream, P, h, h_sh,
-                           gmax, Kp);
+                           gmax, kpad);
     else if (S == 2)
         hipLaunchKernelGGL((decode_kernel<MODE, WBITS, SRC, 2>), grid, dim3(DK_THREADS), lds, stream, P, h, h_sh,
-                           gmax, Kp);
+                           gmax, kpad);
     else
         hipLaunchKernelGGL((decode_kernel<MODE, WBITS, SRC, 1>), grid, dim3(DK_THREADS), lds, stream, P, h, h_sh,
-                           gmax, Kp);
+                           gmax, kpad);
     return hipGetLastError();
 }
 

@@ -173,19 +173,47 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
     }
 }
 
-constexpr int RS_MAXJ = 16;  // experts per lane: E <= 1024
-
 // (v, id) is better than (v2, id2): larger score, then lower id
 __device__ __forceinline__ bool better(double v, int id, double v2, int id2) {
     return v > v2 || (v == v2 && id < id2);
 }
 
-// One workgroup (1024 threads) per token.  Thread (e, g) sums the splits s = g, g+4, ... of expert e with
-// eight independent accumulators (fixed order), the four groups are added in order, then the first
-// wavefront takes sigmoid, bias and the top k+1 by repeated wave-wide argmax (ties to the lower id).
+// One DPP step of a wave-wide argmax of (v, id): take the partner's pair when it is better.
+// bound_ctrl off and old = own value: lanes without a partner keep what they have.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(double &v, int &id) {
+    const int2 b = __builtin_bit_cast(int2, v);
+    const int lo = __builtin_amdgcn_update_dpp(b.x, b.x, CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(b.y, b.y, CTRL, ROW_MASK, 0xF, false);
+    const int oid = __builtin_amdgcn_update_dpp(id, id, CTRL, ROW_MASK, 0xF, false);
+    const double ov = __builtin_bit_cast(double, make_int2(lo, hi));
+    if (better(ov, oid, v, id)) {
+        v = ov;
+        id = oid;
+    }
+}
+
+// Wave-wide argmax (larger v, then lower id); the result is returned to every lane.
+__device__ __forceinline__ void wave_argmax(double &v, int &id) {
+    argmax_step<0xB1, 0xF>(v, id);   // quad_perm [1,0,3,2]
+    argmax_step<0x4E, 0xF>(v, id);   // quad_perm [2,3,0,1]
+    argmax_step<0x141, 0xF>(v, id);  // row_half_mirror
+    argmax_step<0x140, 0xF>(v, id);  // row_mirror: lane 15 of each row holds the row's best
+    argmax_step<0x142, 0xA>(v, id);  // row_bcast15: rows 1 and 3 take the last lane of rows 0 and 2
+    argmax_step<0x143, 0xC>(v, id);  // row_bcast31: rows 2 and 3 take lane 31
+    const int2 b = __builtin_bit_cast(int2, v);
+    v = __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(b.x, 63), __builtin_amdgcn_readlane(b.y, 63)));
+    id = __builtin_amdgcn_readlane(id, 63);
+}
+
+// One workgroup (1024 threads) per token.  Thread (e, g) sums the splits s = g, g+4, ... of expert e
+// (fixed order), the four groups are added in order; then the first wavefront takes sigmoid and bias
+// and picks the top k+1.  Each lane holds EJ experts (e = lane + 64 j), sorts them once, and exposes
+// its best unchosen one; each round is one wave-wide argmax and the winning lane moves to its next.
 constexpr int RSEL_THREADS = 1024;
 constexpr int RSEL_LOADS = 8;
 
+template <int EJ>
 __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const double *__restrict__ part, int nsplit,
                                                                      int T, int E, int k,
                                                                      const float *__restrict__ bias, float lambda,
@@ -218,50 +246,60 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
     }
     __syncthreads();
     if (tid >= 64) return;
-    const int nj = (E + 63) >> 6;
-    double sel[RS_MAXJ], s[RS_MAXJ];
+    // this lane's candidates, sorted best first
+    double cv[EJ], cs[EJ];
+    int ci[EJ];
 #pragma unroll
-    for (int j = 0; j < RS_MAXJ; j++) {
-        int e = lane + 64 * j;
-        sel[j] = -INFINITY;
-        s[j] = 0.0;
-        if (j < nj && e < E) {
+    for (int j = 0; j < EJ; j++) {
+        const int e = lane + 64 * j;
+        cv[j] = -INFINITY;
+        cs[j] = 0.0;
+        ci[j] = 0x7fffffff;
+        if (e < E) {
             const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
-            s[j] = 1.0 / (1.0 + exp(-z));
-            sel[j] = s[j] + (double)bias[e];
+            cs[j] = 1.0 / (1.0 + exp(-z));
+            cv[j] = cs[j] + (double)bias[e];
+            ci[j] = e;
         }
     }
-    uint32_t taken = 0;  // bit j: slot j of this lane already chosen
+#pragma unroll
+    for (int a2 = 0; a2 < EJ; a2++)  // insertion sort, fully unrolled (EJ <= 16)
+#pragma unroll
+        for (int b2 = EJ - 1; b2 > a2; b2--)
+            if (better(cv[b2], ci[b2], cv[b2 - 1], ci[b2 - 1])) {
+                const double tv = cv[b2], ts = cs[b2];
+                const int ti = ci[b2];
+                cv[b2] = cv[b2 - 1];
+                cs[b2] = cs[b2 - 1];
+                ci[b2] = ci[b2 - 1];
+                cv[b2 - 1] = tv;
+                cs[b2 - 1] = ts;
+                ci[b2 - 1] = ti;
+            }
+    int head = 0;  // next unchosen candidate of this lane
     double sum_s = 0.0, prev_v = 0.0;
-    double my_s = 0.0;  // lane j' < k keeps the score of choice j'
+    double my_s = 0.0;  // lane r < k keeps the score of choice r
     int my_id = 0;
     const int rounds = (k < E) ? k + 1 : k;
     for (int r = 0; r < rounds; r++) {
-        double bv = -INFINITY, bs = 0.0;
-        int bid = 0x7fffffff, bj = -1;
+        double hv = -INFINITY, hs = 0.0;
+        int hid = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < RS_MAXJ; j++) {
-            int e = lane + 64 * j;
-            if (j < nj && e < E && !((taken >> j) & 1u) && better(sel[j], e, bv, bid)) {
-                bv = sel[j];
-                bid = e;
-                bs = s[j];
-                bj = j;
+        for (int j = 0; j < EJ; j++)
+            if (head == j) {
+                hv = cv[j];
+                hs = cs[j];
+                hid = ci[j];
             }
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            double ov = __shfl_xor(bv, o, 64);
-            int oid = __shfl_xor(bid, o, 64);
-            double os = __shfl_xor(bs, o, 64);
-            if (better(ov, oid, bv, bid)) {
-                bv = ov;
-                bid = oid;
-                bs = os;
-            }
-        }
+        double bv = hv;
+        int bid = hid;
+        wave_argmax(bv, bid);
+        const int wl = bid & 63;  // lane that owns the winner
+        const int2 sb = __builtin_bit_cast(int2, hs);
+        const double bs = __builtin_bit_cast(
+            double, make_int2(__builtin_amdgcn_readlane(sb.x, wl), __builtin_amdgcn_readlane(sb.y, wl)));
         if (r < k) {
-            if (bj >= 0 && lane + 64 * bj == bid) taken |= 1u << bj;
+            if (lane == wl) head++;
             sum_s += bs;
             if (lane == r) {
                 my_s = bs;
@@ -336,8 +374,16 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_select_kernel, dim3(T), dim3(RSEL_THREADS), 4 * E * sizeof(double), stream, part,
-                       nsplit, T, E, k, bias, lambda, idx, w, gap);
+    const size_t lds = 4 * E * sizeof(double);
+    if (E <= 64)
+        hipLaunchKernelGGL(router_select_kernel<1>, dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T, E, k,
+                           bias, lambda, idx, w, gap);
+    else if (E <= 256)
+        hipLaunchKernelGGL(router_select_kernel<4>, dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T, E, k,
+                           bias, lambda, idx, w, gap);
+    else
+        hipLaunchKernelGGL(router_select_kernel<16>, dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T, E,
+                           k, bias, lambda, idx, w, gap);
     return hipGetLastError();
 }
 

@@ -99,6 +99,9 @@ SMALL = {
     "E_equals_k": (dict(d=256, E=4, k=4, I=128, I_shared=64), 3),
     "T1": (dict(d=512, E=64, k=6, I=256, I_shared=256, routed_scale=2.5), 1),
     "tiny_short_rows": (dict(d=64, E=8, k=2, I=32, wbits=8, act=synth.ACT_F32), 6),
+    "E512_k16_router": (dict(d=256, E=512, k=16, I=64, routed_scale=2.5), 5),
+    "E1000_k32_router": (dict(d=128, E=1000, k=32, I=32), 3),
+    "E12_nonpow2": (dict(d=256, E=12, k=3, I=64, wbits=8, act=synth.ACT_F32), 8),
 }
 
 
