@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run three plain 1 GiB device-to-device copies (torch copy_), whose HBM counter "
+                         "readings scale the counters read for the MoE kernels")
     return ap.parse_args()
 
 
@@ -84,6 +87,13 @@ def main():
     path = {"auto": B.MOE_PATH_AUTO, "gemv": B.MOE_PATH_GEMV, "gemm": B.MOE_PATH_GEMM}[args.path]
     dev = torch.device("cuda:0")
     B.lib()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     t_setup = time.perf_counter()
     layers = [L.DeviceLayerWeights(spec, 0, l, dev) for l in range(n_layers)]

@@ -45,6 +45,13 @@ __device__ __forceinline__ T wave_sum(T v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Read of a value that no kernel of the launch writes, through the constant address space: with a
+// wave-uniform index it becomes a scalar-unit load, which leaves the vector-memory counter (and so the
+// weight loads in flight) alone.
+__device__ __forceinline__ int32_t ld_const(const int32_t *p, long i) {
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+
 // Raw buffer loads: an offset at or beyond the descriptor's byte count returns zeros without touching
 // memory, so loads that may fall outside their row stay branch-free and keep many requests in flight.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

@@ -97,114 +97,221 @@ __device__ __forceinline__ void load8(rsrc_t src, uint32_t off, float (&v)[8]) {
 // (row, wavefront): x ~= X * 2^-expo[i], |X| < 2^22.  xsum[i] = sum of X (exact).  Positions past
 // kpart up to the padded length are zero.  Only this wavefront reads what it writes, so the only
 // synchronisation is the wavefront's own LDS ordering.
-template <int WBITS, int SRC>
-__device__ void wave_stage(rsrc_t src, long rowoff_lane, int ng, int k0, int kpart, int kpad, int stride,
-                           long plane_bytes, int8_t *planes, int *expo, double *xsum) {
+//
+// A row is staged in two steps so that its loads can be issued ahead of other memory traffic:
+// stage_issue requests the row's first 4 x 64 groups of 8 inputs (all in flight at once) and
+// stage_finish turns them into digits; longer K parts are loaded there in further rounds of 4 groups
+// per lane (read twice: once for the maximum, once for the digits).
+template <int SRC>
+struct StageRaw {
+    static constexpr int G = 4;  // groups of 8 inputs per lane
+    static constexpr int W = SRC == 0 ? 2 : 1;  // 16-byte loads per group
+    uint4 q[G][W];
+};
+
+template <int SRC>
+__device__ __forceinline__ void stage_issue(rsrc_t src, long ro, int m0, int ngr, int kpart, StageRaw<SRC> &r) {
     const int lane = threadIdx.x & 63;
-    const int ngr = kpad / 8;  // groups of 8 inputs, zero past kpart
-    constexpr int MAXG = 2;    // groups per lane held in registers (kpart <= 1024)
     const int esz = SRC == 0 ? 4 : 2;
-    for (int i = 0; i < ng; i++) {
-        const long ro = __shfl(rowoff_lane, i, 64) + k0;  // element offset of this row's first input
-        float v[MAXG][8];
-        float mx = 0.f;
 #pragma unroll
-        for (int c = 0; c < MAXG; c++) {
-            const int m = lane + 64 * c;
-            load8<SRC>(src, (m < ngr && m * 8 < kpart) ? (uint32_t)((ro + (long)m * 8) * esz) : kOOB, v[c]);
+    for (int c = 0; c < StageRaw<SRC>::G; c++) {
+        const int m = m0 + lane + 64 * c;
+        const uint32_t off = (m < ngr && m * 8 < kpart) ? (uint32_t)((ro + (long)m * 8) * esz) : kOOB;
 #pragma unroll
-            for (int t = 0; t < 8; t++) mx = fmaxf(mx, fabsf(v[c][t]));
-        }
-        for (int m = lane + 64 * MAXG; m < ngr; m += 64) {  // K parts longer than 1024 inputs
-            float xv[8];
-            load8<SRC>(src, m * 8 < kpart ? (uint32_t)((ro + (long)m * 8) * esz) : kOOB, xv);
+        for (int w = 0; w < StageRaw<SRC>::W; w++) r.q[c][w] = buf_load16(src, off == kOOB ? kOOB : off + 16 * w);
+    }
+}
+
+template <int SRC>
+__device__ __forceinline__ void raw_to_f32(const uint4 (&q)[StageRaw<SRC>::W], float (&v)[8]) {
+    if (SRC == 0) {
+        const uint4 a = q[0], b = q[StageRaw<SRC>::W - 1];
+        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z);
+        v[3] = __uint_as_float(a.w); v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+        v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    } else {
+        const uint32_t qq[4] = {q[0].x, q[0].y, q[0].z, q[0].w};
 #pragma unroll
-            for (int t = 0; t < 8; t++) mx = fmaxf(mx, fabsf(xv[t]));
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        int e = 0;
-        if (mx > 0.f) {
-            int ex;
-            frexpf(mx, &ex);  // mx < 2^ex
-            e = 22 - ex;
-        }
-        const float sc = ldexpf(1.f, e);
-        long ssum = 0;
-        int8_t *p0 = planes + (long)i * stride, *p1 = p0 + plane_bytes, *p2 = p1 + plane_bytes;
-        auto put = [&](int m, const float (&xv)[8]) {
-            int d0[8], d1[8], d2[8];
-#pragma unroll
-            for (int t = 0; t < 8; t++) {
-                const int X = (int)rintf(xv[t] * sc);
-                ssum += X;
-                d0[t] = (X << 24) >> 24;
-                const int r = (X - d0[t]) >> 8;
-                d1[t] = (r << 24) >> 24;
-                d2[t] = (r - d1[t]) >> 8;
-            }
-            auto pack4 = [](const int *d) {
-                return (uint32_t)(d[0] & 255) | ((uint32_t)(d[1] & 255) << 8) | ((uint32_t)(d[2] & 255) << 16) |
-                       ((uint32_t)(d[3] & 255) << 24);
-            };
-            if (WBITS == 8) {
-                const int pos = m * 8;
-                *(uint2 *)(p0 + pos) = make_uint2(pack4(d0), pack4(d0 + 4));
-                *(uint2 *)(p1 + pos) = make_uint2(pack4(d1), pack4(d1 + 4));
-                *(uint2 *)(p2 + pos) = make_uint2(pack4(d2), pack4(d2 + 4));
-            } else {
-                // inputs 8m..8m+7: evens go to plane_pos(8m), odds to plane_pos(8m+1)
-                const int pe = plane_pos<4>(m * 8), po = plane_pos<4>(m * 8 + 1);
-                int ev[4], od[4];
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    ev[t] = d0[2 * t];
-                    od[t] = d0[2 * t + 1];
-                }
-                *(uint32_t *)(p0 + pe) = pack4(ev);
-                *(uint32_t *)(p0 + po) = pack4(od);
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    ev[t] = d1[2 * t];
-                    od[t] = d1[2 * t + 1];
-                }
-                *(uint32_t *)(p1 + pe) = pack4(ev);
-                *(uint32_t *)(p1 + po) = pack4(od);
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    ev[t] = d2[2 * t];
-                    od[t] = d2[2 * t + 1];
-                }
-                *(uint32_t *)(p2 + pe) = pack4(ev);
-                *(uint32_t *)(p2 + po) = pack4(od);
-            }
-        };
-#pragma unroll
-        for (int c = 0; c < MAXG; c++) {
-            const int m = lane + 64 * c;
-            if (m < ngr) put(m, v[c]);
-        }
-        for (int m = lane + 64 * MAXG; m < ngr; m += 64) {
-            float xv[8];
-            load8<SRC>(src, m * 8 < kpart ? (uint32_t)((ro + (long)m * 8) * esz) : kOOB, xv);
-            put(m, xv);
-        }
-        double ds = (double)ssum;  // exact: integers below 2^53
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) ds += __shfl_xor(ds, o, 64);
-        if (lane == 0) {
-            xsum[i] = ds;
-            expo[i] = e;
+        for (int j = 0; j < 4; j++) {
+            v[2 * j] = __uint_as_float(qq[j] << 16);
+            v[2 * j + 1] = __uint_as_float(qq[j] & 0xFFFF0000u);
         }
     }
-    // make this wavefront's LDS writes visible to its own later reads
+}
+
+template <int SRC>
+__device__ __forceinline__ float raw_absmax(const StageRaw<SRC> &r, float mx) {
+#pragma unroll
+    for (int c = 0; c < StageRaw<SRC>::G; c++) {
+        float v[8];
+        raw_to_f32<SRC>(r.q[c], v);
+#pragma unroll
+        for (int t = 0; t < 8; t++) mx = fmaxf(mx, fabsf(v[t]));
+    }
+    return mx;
+}
+
+template <int WBITS, int SRC>
+__device__ void stage_finish(const StageRaw<SRC> &r, rsrc_t src, long ro, int i, int ngr, int kpart, int stride,
+                             long plane_bytes, int8_t *planes, int *expo, double *xsum) {
+    constexpr int RG = 64 * StageRaw<SRC>::G;  // groups per round
+    const int lane = threadIdx.x & 63;
+    float mx = raw_absmax<SRC>(r, 0.f);
+    for (int m0 = RG; m0 < ngr; m0 += RG) {
+        StageRaw<SRC> r2;
+        stage_issue<SRC>(src, ro, m0, ngr, kpart, r2);
+        mx = raw_absmax<SRC>(r2, mx);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    int e = 0;
+    if (mx > 0.f) {
+        int ex;
+        frexpf(mx, &ex);  // mx < 2^ex
+        e = 22 - ex;
+    }
+    const float sc = ldexpf(1.f, e);
+    long ssum = 0;
+    int8_t *p0 = planes + (long)i * stride, *p1 = p0 + plane_bytes, *p2 = p1 + plane_bytes;
+    auto put = [&](int m, const float (&xv)[8]) {
+        // digits of the 8 inputs, packed as they are produced: for int8 weights two words per plane in
+        // input order; for int4 weights one word of even inputs and one of odd inputs per plane
+        uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const int X = (int)rintf(xv[t] * sc);
+            ssum += X;
+            const int d0 = (X << 24) >> 24;
+            const int rr = (X - d0) >> 8;
+            const int d1 = (rr << 24) >> 24;
+            const int d2 = (rr - d1) >> 8;
+            const int word = WBITS == 8 ? (t >> 2) : (t & 1);
+            const int sh = WBITS == 8 ? 8 * (t & 3) : 8 * (t >> 1);
+            w[0][word] |= (uint32_t)(d0 & 255) << sh;
+            w[1][word] |= (uint32_t)(d1 & 255) << sh;
+            w[2][word] |= (uint32_t)(d2 & 255) << sh;
+        }
+        if (WBITS == 8) {
+            const int pos = m * 8;
+            *(uint2 *)(p0 + pos) = make_uint2(w[0][0], w[0][1]);
+            *(uint2 *)(p1 + pos) = make_uint2(w[1][0], w[1][1]);
+            *(uint2 *)(p2 + pos) = make_uint2(w[2][0], w[2][1]);
+        } else {
+            // inputs 8m..8m+7: evens go to plane_pos(8m), odds to plane_pos(8m+1)
+            const int pe = plane_pos<4>(m * 8), po = plane_pos<4>(m * 8 + 1);
+            *(uint32_t *)(p0 + pe) = w[0][0];
+            *(uint32_t *)(p0 + po) = w[0][1];
+            *(uint32_t *)(p1 + pe) = w[1][0];
+            *(uint32_t *)(p1 + po) = w[1][1];
+            *(uint32_t *)(p2 + pe) = w[2][0];
+            *(uint32_t *)(p2 + po) = w[2][1];
+        }
+    };
+    auto put_round = [&](const StageRaw<SRC> &rr, int m0) {
+#pragma unroll
+        for (int c = 0; c < StageRaw<SRC>::G; c++) {
+            const int m = m0 + lane + 64 * c;
+            float v[8];
+            raw_to_f32<SRC>(rr.q[c], v);
+            if (m < ngr) put(m, v);
+        }
+    };
+    put_round(r, 0);
+    for (int m0 = RG; m0 < ngr; m0 += RG) {
+        StageRaw<SRC> r2;
+        stage_issue<SRC>(src, ro, m0, ngr, kpart, r2);
+        put_round(r2, m0);
+    }
+    double ds = (double)ssum;  // exact: integers below 2^53
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ds += __shfl_xor(ds, o, 64);
+    if (lane == 0) {
+        xsum[i] = ds;
+        expo[i] = e;
+    }
+}
+
+// make this wavefront's LDS writes visible to its own later reads
+__device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Source row of staged token i: through the permutation (gate/up of a routed expert reads row
+// perm[base + i] / k of x), or directly (row base + i of h, or of x for the shared expert).  The index
+// is wave-uniform, so the permutation is read with scalar loads.
+struct RowMap {
+    const int32_t *perm;  // nullptr: direct
+    int base, k;
+    long len;  // elements per source row
+    __device__ __forceinline__ long row_off(int i) const {
+        return perm ? (long)(ld_const(perm, base + i) / k) * len : (long)(base + i) * len;
+    }
+};
+
+// All ng rows, one after the other (each row's loads in flight together).
+template <int WBITS, int SRC>
+__device__ void wave_stage(rsrc_t src, const RowMap &rm, int ng, int k0, int kpart, int kpad, int stride,
+                           long plane_bytes, int8_t *planes, int *expo, double *xsum) {
+    const int ngr = kpad / 8;  // groups of 8 inputs, zero past kpart
+    for (int i = 0; i < ng; i++) {
+        const long ro = rm.row_off(i) + k0;  // element offset of this row's first input
+        StageRaw<SRC> r;
+        stage_issue<SRC>(src, ro, 0, ngr, kpart, r);
+        stage_finish<WBITS, SRC>(r, src, ro, i, ngr, kpart, stride, plane_bytes, planes, expo, xsum);
+    }
+    wave_lds_sync();
+}
+
 __device__ __forceinline__ float zp_val(const void *z, int wbits, long i) {
     return wbits == 8 ? (float)((const int8_t *)z)[i] : ((const float *)z)[i];
+}
+
+// One 64-byte segment of a wavefront's 16 rows (NM matrices) through the matrix cores:
+// C[m][p] += digits of plane p (A, 16 tokens x 64 inputs) . weights of matrix m (B, 64 inputs x 16 rows).
+template <int WBITS, int NM>
+__device__ __forceinline__ void consume_segment(const uint4 (&wq)[NM], const int8_t *xrow, long pstep, int gstep,
+                                                int seg, int g, i32x4_t (&C)[NM][3]) {
+    if (WBITS == 8) {
+        i32x4_t A[3];
+        const int8_t *xa = xrow + gstep * (64 * seg + 16 * g);
+#pragma unroll
+        for (int p = 0; p < 3; p++) {
+            const uint4 v = *(const uint4 *)(xa + p * pstep);
+            A[p] = (i32x4_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        }
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+            const uint4 q = wq[m];
+            const i32x4_t Bq = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+#pragma unroll
+            for (int p = 0; p < 3; p++) C[m][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[p], Bq, C[m][p], 0, 0, 0);
+        }
+    } else {
+        i32x4_t Ae[3], Ao[3];
+        const int8_t *xa = xrow + gstep * (128 * seg + 32 * g);
+#pragma unroll
+        for (int p = 0; p < 3; p++) {
+            const uint4 ve = *(const uint4 *)(xa + p * pstep);
+            const uint4 vo = *(const uint4 *)(xa + p * pstep + 16);
+            Ae[p] = (i32x4_t){(int)ve.x, (int)ve.y, (int)ve.z, (int)ve.w};
+            Ao[p] = (i32x4_t){(int)vo.x, (int)vo.y, (int)vo.z, (int)vo.w};
+        }
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+            const uint4 q = wq[m];
+            const i32x4_t Be = {(int)(q.x & 0x0F0F0F0Fu), (int)(q.y & 0x0F0F0F0Fu), (int)(q.z & 0x0F0F0F0Fu),
+                                (int)(q.w & 0x0F0F0F0Fu)};
+            const i32x4_t Bo = {(int)((q.x >> 4) & 0x0F0F0F0Fu), (int)((q.y >> 4) & 0x0F0F0F0Fu),
+                                (int)((q.z >> 4) & 0x0F0F0F0Fu), (int)((q.w >> 4) & 0x0F0F0F0Fu)};
+#pragma unroll
+            for (int p = 0; p < 3; p++) {
+                C[m][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ae[p], Be, C[m][p], 0, 0, 0);
+                C[m][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ao[p], Bo, C[m][p], 0, 0, 0);
+            }
+        }
+    }
 }
 
 // MODE 0: gate/up -> h (fp32); MODE 1: down -> y_perm / y_shared.
@@ -283,21 +390,15 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
 #pragma unroll
             for (int b = 0; b < PF; b++) ldw(b, b);
         }
-        long rowoff_lane = 0;  // lane i < ng: element offset of token i's source row
-        if (lane < ng) {
-            if (MODE == 0) {
-                const int t = s.shared ? (g0 + lane) : (P.perm[p0 + g0 + lane] / P.k);
-                rowoff_lane = (long)t * P.d;
-            } else {
-                rowoff_lane = (long)((s.shared ? 0 : p0) + g0 + lane) * K;
-            }
-        }
+        RowMap rm;
+        rm.perm = (MODE == 0 && !s.shared) ? P.perm : nullptr;
+        rm.base = (s.shared ? 0 : p0) + g0;
+        rm.k = P.k;
+        rm.len = MODE == 0 ? P.d : K;
         if (MODE == 0)
-            wave_stage<WBITS, SRC>(src, rowoff_lane, ng, kp * kpart, kpart, kpad, stride, pb, planes,
-                                   wexpo[wv], wxsum[wv]);
+            wave_stage<WBITS, SRC>(src, rm, ng, kp * kpart, kpart, kpad, stride, pb, planes, wexpo[wv], wxsum[wv]);
         else
-            wave_stage<WBITS, 0>(src, rowoff_lane, ng, kp * kpart, kpart, kpad, stride, pb, planes, wexpo[wv],
-                                 wxsum[wv]);
+            wave_stage<WBITS, 0>(src, rm, ng, kp * kpart, kpart, kpad, stride, pb, planes, wexpo[wv], wxsum[wv]);
 
         // ---- stream the wavefront's K part through the matrix cores
         i32x4_t C[NM][3];
@@ -314,46 +415,7 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
 #pragma unroll
             for (int b = 0; b < PF; b++) {
                 const int seg = seg0 + b;
-                if (WBITS == 8) {
-                    i32x4_t A[3];
-                    const int8_t *xa = xrow + gstep * (64 * seg + 16 * g);
-#pragma unroll
-                    for (int p = 0; p < 3; p++) {
-                        const uint4 v = *(const uint4 *)(xa + p * pstep);
-                        A[p] = (i32x4_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-                    }
-#pragma unroll
-                    for (int m = 0; m < NM; m++) {
-                        const uint4 q = wbuf[b][m];
-                        const i32x4_t Bq = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-#pragma unroll
-                        for (int p = 0; p < 3; p++)
-                            C[m][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[p], Bq, C[m][p], 0, 0, 0);
-                    }
-                } else {
-                    i32x4_t Ae[3], Ao[3];
-                    const int8_t *xa = xrow + gstep * (128 * seg + 32 * g);
-#pragma unroll
-                    for (int p = 0; p < 3; p++) {
-                        const uint4 ve = *(const uint4 *)(xa + p * pstep);
-                        const uint4 vo = *(const uint4 *)(xa + p * pstep + 16);
-                        Ae[p] = (i32x4_t){(int)ve.x, (int)ve.y, (int)ve.z, (int)ve.w};
-                        Ao[p] = (i32x4_t){(int)vo.x, (int)vo.y, (int)vo.z, (int)vo.w};
-                    }
-#pragma unroll
-                    for (int m = 0; m < NM; m++) {
-                        const uint4 q = wbuf[b][m];
-                        const i32x4_t Be = {(int)(q.x & 0x0F0F0F0Fu), (int)(q.y & 0x0F0F0F0Fu),
-                                            (int)(q.z & 0x0F0F0F0Fu), (int)(q.w & 0x0F0F0F0Fu)};
-                        const i32x4_t Bo = {(int)((q.x >> 4) & 0x0F0F0F0Fu), (int)((q.y >> 4) & 0x0F0F0F0Fu),
-                                            (int)((q.z >> 4) & 0x0F0F0F0Fu), (int)((q.w >> 4) & 0x0F0F0F0Fu)};
-#pragma unroll
-                        for (int p = 0; p < 3; p++) {
-                            C[m][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ae[p], Be, C[m][p], 0, 0, 0);
-                            C[m][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ao[p], Bo, C[m][p], 0, 0, 0);
-                        }
-                    }
-                }
+                consume_segment<WBITS, NM>(wbuf[b], xrow, pstep, gstep, seg, g, C);
                 // refill this slot right away (past the end: out of range, zeros, no memory traffic);
                 // the scheduling barrier keeps the compiler from sinking the refill to the end of the
                 // unrolled block, which would let the in-flight queue drain every PF segments
@@ -427,6 +489,349 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
     }
 }
 
+// ---------------------------------------------------------------------------- persistent variant
+// Decode with one workgroup of DKP_WAVES wavefronts per CU.  Work items are (slot, row tile) pairs,
+// slot-major over the unique experts and then the shared expert; CU c takes the contiguous items
+// [c*N/ncu, (c+1)*N/ncu).  The S wavefronts of a tile split its K range and TPW = DKP_WAVES / S
+// tiles share an item, so every wavefront of a CU works on the same item and the CU's items end
+// together.  Each wavefront's weight stream runs across items: while it consumes the last batch of
+// an item, the refills already fetch the first segments of the next item.
+//
+// Start-up takes two memory round trips: the routing tables (unique list, offsets, permutation) go to
+// LDS in one round together with the first activation rows; the weight stream starts right after.
+// Gate/up stages the digit planes of all T tokens once (slots only remap lanes to tokens); down
+// stages the rows of h of each slot when the slot changes.  Requires T <= DK_GMAX.
+struct DItem {
+    int slot, e, tile, I, kpart_bytes, nseg_pad, row, p0, ng;
+    bool shared, row_ok;
+};
+
+constexpr int DKP_WAVES = 8;
+constexpr int DKP_TAB_PER_THREAD = 6;  // routing-table words loaded per thread (>= 1 + 1024 + 1025 + 512)
+
+// Words of the routing table kept in LDS: n_uniq, uniq[n_routed_slots], offsets[E + 1], perm[A] (gate/up).
+__host__ __device__ inline int dkp_tab_words(int mode, int n_routed_slots, int E, int A) {
+    return 1 + n_routed_slots + E + 1 + (mode == 0 ? A : 0);
+}
+
+template <int MODE, int WBITS, int SRC, int S>
+__global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(FfnParams P, float *__restrict__ h,
+                                                                           float *__restrict__ h_sh, int kpad,
+                                                                           int tiles_r, int tiles_s, int ncu) {
+    constexpr int NW = DKP_WAVES;
+    constexpr int TPW = NW / S;
+    constexpr int NM = MODE == 0 ? 2 : 1;
+    constexpr int PF = MODE == 0 ? 8 : 16;  // 16 weight loads in flight per wavefront
+    constexpr int SRCX = MODE == 0 ? SRC : 0;
+    extern __shared__ __align__(16) uint8_t dk_lds[];
+    __shared__ int wexpo[NW][DK_GMAX];
+    __shared__ double wxsum[NW][DK_GMAX];
+    __shared__ uint32_t zero_area[8];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave indices stay scalar
+    const int tile_w = wv / S, kp = wv % S;
+    const int g = lane >> 4, j = lane & 15;
+    const int T = P.T;
+
+    // ---- LDS layout: routing table, digit planes (one copy per K part), cross-wave partials
+    const int nrs = P.n_routed_slots;
+    const int tab_words = dkp_tab_words(MODE, nrs, P.E, P.A);
+    int *tab = (int *)dk_lds;
+    const int *t_uniq = tab + 1, *t_off = tab + 1 + nrs, *t_perm = tab + 2 + nrs + P.E;
+    const int stride = kpad + 16;
+    const long pb = (long)T * stride;  // bytes per digit plane of one K part
+    int8_t *planes = (int8_t *)dk_lds + ((tab_words * 4 + 15) & ~15) + (long)kp * 3 * pb;
+    double *red = (double *)(dk_lds + ((tab_words * 4 + 15) & ~15) + (long)S * 3 * pb);
+
+    // ---- round 1: routing table and (gate/up) this wavefront's first activation row, all requested
+    // before any of them is waited for
+    const int kd = MODE == 0 ? P.d : 0;
+    const rsrc_t xsrc0 = make_rsrc(P.x, (uint32_t)((long)T * P.d * (SRC == 0 ? 4 : 2)));
+    StageRaw<SRCX> raw0;
+    {
+        const rsrc_t r_nu = make_rsrc(P.n_uniq, 4), r_uq = make_rsrc(P.uniq, (uint32_t)nrs * 4);
+        const rsrc_t r_of = make_rsrc(P.offsets, (uint32_t)(P.E + 1) * 4);
+        const rsrc_t r_pm = make_rsrc(P.perm, (uint32_t)P.A * 4);
+        uint32_t v[DKP_TAB_PER_THREAD];
+#pragma unroll
+        for (int q = 0; q < DKP_TAB_PER_THREAD; q++) {
+            const int w = tid + q * NW * 64;
+            // one source per word; words past the table read nothing
+            const int b1 = 1, b2 = 1 + nrs, b3 = 2 + nrs + P.E;
+            rsrc_t r = r_nu;
+            uint32_t off = kOOB;
+            if (w < b1) { r = r_nu; off = 0; }
+            else if (w < b2) { r = r_uq; off = (uint32_t)(w - b1) * 4; }
+            else if (w < b3) { r = r_of; off = (uint32_t)(w - b2) * 4; }
+            else if (w < tab_words) { r = r_pm; off = (uint32_t)(w - b3) * 4; }
+            v[q] = buf_load4(r, off);
+        }
+        if (MODE == 0) {
+            // token row tile_w (if any), this wavefront's K part
+            const int kpart = kd / S;
+            const long ro = (long)tile_w * kd + kp * kpart;
+            stage_issue<SRCX>(xsrc0, ro, tile_w < T ? 0 : kpad, kpad / 8, kpart, raw0);
+        }
+#pragma unroll
+        for (int q = 0; q < DKP_TAB_PER_THREAD; q++) {
+            const int w = tid + q * NW * 64;
+            if (w < tab_words) tab[w] = (int)v[q];
+        }
+    }
+    if (tid < 8) zero_area[tid] = 0u;
+    __syncthreads();  // table in LDS (the compiler waits for the table loads before the stores)
+
+    int nu = __builtin_amdgcn_readfirstlane(tab[0]);
+    nu = nu < 0 ? 0 : (nu > nrs ? nrs : nu);
+    // item counts stay far below 2^31 / ncu (at most 1025 slots x 2^16 tiles), so 32-bit index math
+    const int N = nu * tiles_r + (P.Is > 0 ? tiles_s : 0);
+    int i0, i1;
+    {
+        const int G = gridDim.x, b = blockIdx.x;
+        if (G % ncu == 0 && N >= G) {
+            const int m = G / ncu, c = b % ncu, r = b / ncu;
+            const int c0 = c * N / ncu, c1 = (c + 1) * N / ncu;
+            i0 = c0 + r * (c1 - c0) / m;
+            i1 = c0 + (r + 1) * (c1 - c0) / m;
+        } else {
+            i0 = b * N / G;
+            i1 = (b + 1) * N / G;
+        }
+    }
+    if (i0 >= i1) return;  // uniform over the workgroup
+
+    auto decode = [&](int i) {
+        DItem it;
+        if (i < nu * tiles_r) {
+            it.slot = i / tiles_r;
+            it.tile = i % tiles_r;
+            it.e = __builtin_amdgcn_readfirstlane(t_uniq[it.slot]);
+            it.shared = false;
+            it.I = P.I;
+            it.p0 = __builtin_amdgcn_readfirstlane(t_off[it.e]);
+            it.ng = __builtin_amdgcn_readfirstlane(t_off[it.e + 1]) - it.p0;
+        } else {
+            it.slot = nrs;
+            it.tile = i - nu * tiles_r;
+            it.e = 0;
+            it.shared = true;
+            it.I = P.Is;
+            it.p0 = 0;
+            it.ng = T;
+        }
+        const int K = MODE == 0 ? P.d : it.I;
+        const int nout = MODE == 0 ? it.I : P.d;
+        it.kpart_bytes = K / S * WBITS / 8;
+        it.nseg_pad = ((it.kpart_bytes + 63) / 64 + PF - 1) / PF * PF;
+        it.row = (it.tile * TPW + tile_w) * 16 + j;
+        it.row_ok = it.row < nout;
+        return it;
+    };
+    auto weights = [&](const DItem &it, rsrc_t (&wr)[NM], uint32_t &lane_off) {
+        const QW &W = it.shared ? P.shared : P.routed;
+        const int K = MODE == 0 ? P.d : it.I;
+        const int nout = MODE == 0 ? it.I : P.d;
+        const long rb = (long)K * WBITS / 8;
+        const uint32_t mbytes = (uint32_t)((long)nout * rb);
+        if (MODE == 0) {
+            wr[0] = make_rsrc(W.qg + (long)it.e * it.I * rb, mbytes);
+            wr[NM - 1] = make_rsrc(W.qu + (long)it.e * it.I * rb, mbytes);
+        } else {
+            wr[0] = make_rsrc(W.qd + (long)it.e * P.d * rb, mbytes);
+        }
+        lane_off = (uint32_t)((long)min(it.row, nout - 1) * rb) + (uint32_t)(kp * it.kpart_bytes + 16 * g);
+    };
+    // down: rows of h of a slot (row r of the slot is h row p0 + r, or h_sh row r)
+    auto h_src = [&](const DItem &it) {
+        return make_rsrc(it.shared ? h_sh : h, (uint32_t)((long)(it.shared ? T : P.A) * it.I * 4));
+    };
+
+    DItem cur = decode(i0);
+    rsrc_t wr_cur[NM], wr_nxt[NM];
+    uint32_t off_cur, off_nxt;
+    weights(cur, wr_cur, off_cur);
+    uint4 wbuf[PF][NM];
+    auto ld = [&](int b, const rsrc_t (&wr)[NM], uint32_t lane_off, int kpart_bytes, int seg) {
+        const uint32_t off = (64 * seg + 16 * g < kpart_bytes) ? lane_off + 64 * seg : kOOB;
+#pragma unroll
+        for (int m = 0; m < NM; m++) wbuf[b][m] = buf_load16(wr[m], off);
+    };
+
+    // ---- activations of the first item, then the weight stream.  Staging runs first: its code is
+    // cold at launch, and fetching it behind the whole chip's first burst of weight requests costs
+    // more than the short gap before the stream starts.
+    if (MODE == 0) {
+        const int kpart = kd / S;
+        if (tile_w < T)
+            stage_finish<WBITS, SRCX>(raw0, xsrc0, (long)tile_w * kd + kp * kpart, tile_w, kpad / 8, kpart, stride, pb,
+                                      planes, wexpo[kp], wxsum[kp]);
+        for (int r = tile_w + TPW; r < T; r += TPW) {
+            const long ro = (long)r * kd + kp * kpart;
+            StageRaw<SRCX> raw;
+            stage_issue<SRCX>(xsrc0, ro, 0, kpad / 8, kpart, raw);
+            stage_finish<WBITS, SRCX>(raw, xsrc0, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp], wxsum[kp]);
+        }
+    } else {
+        const rsrc_t src = h_src(cur);
+        const int kpart = cur.I / S;
+        const long base = cur.shared ? 0 : cur.p0;
+        for (int r = tile_w; r < cur.ng; r += TPW) {
+            const long ro = (base + r) * cur.I + kp * kpart;
+            StageRaw<SRCX> raw;
+            stage_issue<SRCX>(src, ro, 0, kpad / 8, kpart, raw);
+            stage_finish<WBITS, SRCX>(raw, src, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp], wxsum[kp]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < PF; b++) ld(b, wr_cur, off_cur, cur.kpart_bytes, b);
+    __syncthreads();  // planes and exponents
+
+    int staged_slot = cur.slot;
+    for (int i = i0; i < i1; i++) {
+        const bool has_next = i + 1 < i1;
+        DItem nxt = cur;
+        if (has_next) {
+            nxt = decode(i + 1);
+            weights(nxt, wr_nxt, off_nxt);
+        } else {
+            // no next item: keep a valid descriptor; its refills use an out-of-range offset
+#pragma unroll
+            for (int m = 0; m < NM; m++) wr_nxt[m] = wr_cur[m];
+            off_nxt = off_cur;
+        }
+        // ---- down: the rows of h of a new slot
+        if (MODE == 1 && cur.slot != staged_slot) {
+            const rsrc_t src = h_src(cur);
+            const int kpart = cur.I / S;
+            const long base = cur.shared ? 0 : cur.p0;
+            __syncthreads();  // every wavefront is done reading the previous planes
+            for (int r = tile_w; r < cur.ng; r += TPW) {
+                const long ro = (base + r) * cur.I + kp * kpart;
+                StageRaw<SRCX> raw;
+                stage_issue<SRCX>(src, ro, 0, kpad / 8, kpart, raw);
+                stage_finish<WBITS, SRCX>(raw, src, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp],
+                                          wxsum[kp]);
+            }
+            __syncthreads();
+        }
+        staged_slot = cur.slot;
+
+        // ---- A-operand row of this lane: the token (gate/up) or slot row (down) at position j
+        int trow = -1;
+        if (j < cur.ng) trow = MODE == 0 ? (cur.shared ? j : t_perm[cur.p0 + j] / P.k) : j;
+        const bool tok_ok = trow >= 0;
+        const int8_t *xrow = tok_ok ? planes + (long)trow * stride : (const int8_t *)zero_area;
+        const long pstep = tok_ok ? pb : 0;
+        const int gstep = tok_ok ? 1 : 0;
+
+        // ---- the item's segments
+        i32x4_t C[NM][3];
+#pragma unroll
+        for (int m = 0; m < NM; m++)
+#pragma unroll
+            for (int p = 0; p < 3; p++) C[m][p] = (i32x4_t){0, 0, 0, 0};
+        int seg0 = 0;
+        for (; seg0 + PF < cur.nseg_pad; seg0 += PF) {
+#pragma unroll
+            for (int b = 0; b < PF; b++) {
+                consume_segment<WBITS, NM>(wbuf[b], xrow, pstep, gstep, seg0 + b, g, C);
+                __builtin_amdgcn_sched_barrier(0);
+                ld(b, wr_cur, off_cur, cur.kpart_bytes, seg0 + PF + b);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // last batch, peeled: the per-row zero points and scales are requested first, then the refills
+        // start the next item (or read nothing), so the epilogue waits only for what it uses
+        const QW &W = cur.shared ? P.shared : P.routed;
+        const int nout = MODE == 0 ? cur.I : P.d;
+        const int rowc = min(cur.row, nout - 1);
+        float zrow[NM], srow[NM];
+        if (MODE == 0) {
+            const long ch = (long)cur.e * cur.I + rowc;
+            zrow[0] = zp_val(W.zg, WBITS, ch);
+            zrow[NM - 1] = zp_val(W.zu, WBITS, ch);
+            srow[0] = W.sg[ch];
+            srow[NM - 1] = W.su[ch];
+        } else {
+            const long ch = (long)cur.e * P.d + rowc;
+            zrow[0] = zp_val(W.zd, WBITS, ch);
+            srow[0] = W.sd[ch];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int kpb_nxt = has_next ? nxt.kpart_bytes : 0;
+#pragma unroll
+        for (int b = 0; b < PF; b++) {
+            consume_segment<WBITS, NM>(wbuf[b], xrow, pstep, gstep, seg0 + b, g, C);
+            __builtin_amdgcn_sched_barrier(0);
+            ld(b, wr_nxt, off_nxt, kpb_nxt, b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- exact partial of this wavefront, zero point applied and scale undone, in fp64; register r
+        // of lane group g holds position 4g + r of the slot
+        double v[NM][4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int i2 = 4 * g + r;
+            const bool ok = i2 < cur.ng;
+            const int pr = ok ? (MODE == 0 ? (cur.shared ? i2 : t_perm[cur.p0 + i2] / P.k) : i2) : 0;
+            const double unit = ok ? ldexp(1.0, -wexpo[kp][pr]) : 0.0;
+            const double xs = ok ? wxsum[kp][pr] : 0.0;
+#pragma unroll
+            for (int m = 0; m < NM; m++) {
+                const double dot = (double)C[m][2][r] * 65536.0 + (double)C[m][1][r] * 256.0 + (double)C[m][0][r];
+                v[m][r] = (dot - (double)zrow[m] * xs) * unit;
+            }
+        }
+        if (S > 1) {
+            __syncthreads();  // the previous item's partials have been read
+#pragma unroll
+            for (int m = 0; m < NM; m++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) red[((wv * NM + m) * 4 + r) * 64 + lane] = v[m][r];
+            __syncthreads();
+            if (kp == 0) {
+#pragma unroll
+                for (int m = 0; m < NM; m++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        double a = v[m][r];
+                        for (int q = 1; q < S; q++) a += red[(((wv + q) * NM + m) * 4 + r) * 64 + lane];
+                        v[m][r] = a;
+                    }
+            }
+        }
+        if (kp == 0 && cur.row_ok) {
+            const int o = cur.row;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int i2 = 4 * g + r;
+                if (i2 < cur.ng) {
+                    if (MODE == 0) {
+                        const float gf = (float)((double)srow[0] * v[0][r]);
+                        const float uf = (float)((double)srow[NM - 1] * v[NM - 1][r]);
+                        const float hv = gf / (1.f + expf(-gf)) * uf;
+                        if (cur.shared)
+                            h_sh[(long)i2 * cur.I + o] = hv;
+                        else
+                            h[(long)(cur.p0 + i2) * cur.I + o] = hv;
+                    } else {
+                        const float y = (float)((double)srow[0] * v[0][r]);
+                        if (cur.shared)
+                            P.y_sh[(long)i2 * P.d + o] = y;
+                        else
+                            P.y_perm[(long)(cur.p0 + i2) * P.d + o] = y;
+                    }
+                }
+            }
+        }
+        cur = nxt;
+#pragma unroll
+        for (int m = 0; m < NM; m++) wr_cur[m] = wr_nxt[m];
+        off_cur = off_nxt;
+    }
+}
+
 // ---------------------------------------------------------------------------- host side
 
 static int pad_k(int K, int wbits) {
@@ -434,14 +839,16 @@ static int pad_k(int K, int wbits) {
     return (K + seg_inputs - 1) / seg_inputs * seg_inputs;
 }
 
-// K split: the largest S in {4, 2, 1} that keeps whole 16-byte chunks per wavefront and, for the
-// down projection, at least 8 segments per wavefront.
+// K split: the largest S in {4, 2, 1} that keeps whole 16-byte chunks per wavefront and leaves each
+// wavefront at least 16 segments of 64 bytes per row (short rows: one wavefront per tile over the
+// whole row, no cross-wave reduction).
 static int pick_s(int mode, int K, int wbits) {
+    (void)mode;
     const int chunk_inputs = wbits == 8 ? 16 : 32;
     const int nseg_full = (K * wbits / 8 + 63) / 64;
     for (int S = 4; S >= 2; S >>= 1) {
         if (K % (S * chunk_inputs)) continue;
-        if (mode == 1 && nseg_full / S < 8) continue;
+        if (nseg_full / S < 16) continue;
         return S;
     }
     return 1;
@@ -470,9 +877,123 @@ size_t decode_workspace_bytes(const FfnParams &P) {
     return hb + hs;
 }
 
+static int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    return n;
+}
+
+template <typename F>
+static hipError_t allow_lds(F fn, size_t lds) {
+    if (lds <= 65536) return hipSuccess;
+    return hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+// ---- persistent path (every slot's tokens fit one pass of the digit-plane LDS)
+
+constexpr size_t DKP_LDS_BUDGET = 150 * 1024;  // routing table + digit planes (one copy per K part) + partials
+
+static size_t dkp_red_bytes(int mode) { return (size_t)DKP_WAVES * (mode == 0 ? 2 : 1) * 4 * 64 * 8; }
+
+static int dkp_pf(int mode) { return mode == 0 ? 8 : 16; }
+
+// K split of the persistent kernel: the S in {8, 4, 2, 1} (whole 16-byte chunks per wavefront) with the
+// least work on the busiest CU, counted in wavefront segments including the padding to the prefetch
+// depth; ties go to the smaller S (less cross-wave reduction).
+static int dkp_pick_s(int mode, int K, int nout, int slots, int wbits, int ncu) {
+    const int chunk_inputs = wbits == 8 ? 16 : 32;
+    const int nseg_full = (K * wbits / 8 + 63) / 64;
+    const int pf = dkp_pf(mode);
+    int best = 1;
+    long best_cost = -1;
+    for (int S = 1; S <= DKP_WAVES; S <<= 1) {
+        if (K % (S * chunk_inputs)) continue;
+        const int tpw = DKP_WAVES / S;
+        const int nseg = (nseg_full + S - 1) / S;
+        const int nseg_pad = (nseg + pf - 1) / pf * pf;
+        const long items = (long)slots * ((nout + 16 * tpw - 1) / (16 * tpw));
+        const long per_cu = (items + ncu - 1) / ncu;
+        const long cost = per_cu * tpw * nseg_pad;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = S;
+        }
+    }
+    return best;
+}
+
+static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad) {
+    const size_t tab = ((size_t)dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) * 4 + 15) & ~(size_t)15;
+    return tab + (size_t)S * 3 * P.T * (kpad + 16) + dkp_red_bytes(mode);
+}
+
+template <int MODE, int WBITS, int SRC, int S>
+static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, hipStream_t stream) {
+    const int rows_per_item = 16 * (DKP_WAVES / S);
+    const int tiles_r = ((MODE == 0 ? P.I : P.d) + rows_per_item - 1) / rows_per_item;
+    const int tiles_s = P.Is > 0 ? ((MODE == 0 ? P.Is : P.d) + rows_per_item - 1) / rows_per_item : 0;
+    const size_t lds = dkp_lds_bytes(MODE, S, P, kpad);
+    auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S>;
+    hipError_t err = allow_lds(fn, lds);
+    if (err != hipSuccess) return err;
+    const int ncu = device_cus();
+    const long items = (long)P.n_routed_slots * tiles_r + tiles_s;
+    long grid = ncu;
+    if (grid > items) grid = items;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(DKP_WAVES * 64), lds, stream, P, h, h_sh, kpad, tiles_r,
+                       tiles_s, ncu);
+    return hipGetLastError();
+}
+
+// Launches the persistent kernel if the digit planes of all T tokens fit; *done tells whether it did.
+template <int MODE, int WBITS, int SRC>
+static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t stream, bool *done) {
+    *done = false;
+    const int Imax = P.I > P.Is ? P.I : P.Is;
+    const int K = MODE == 0 ? P.d : Imax;
+    const int Kmin = MODE == 0 ? P.d : (P.Is > 0 && P.Is < P.I ? P.Is : P.I);
+    const int nout = MODE == 0 ? Imax : P.d;
+    const int slots = P.n_routed_slots + (P.Is > 0 ? 1 : 0);
+    // routed and shared expert split alike: the split must divide both K ranges
+    int S = dkp_pick_s(MODE, K, nout, slots, WBITS, device_cus());
+    while (S > 1 && (Kmin % (S * (WBITS == 8 ? 16 : 32)))) S >>= 1;
+    const int kpad = pad_k(K / S, WBITS);
+    if (P.T > DK_GMAX || dkp_tab_words(MODE, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64 ||
+        dkp_lds_bytes(MODE, S, P, kpad) > DKP_LDS_BUDGET)
+        return hipSuccess;
+    *done = true;
+    switch (S) {
+        case 8: return dkp_launch_s<MODE, WBITS, SRC, 8>(P, h, h_sh, kpad, stream);
+        case 4: return dkp_launch_s<MODE, WBITS, SRC, 4>(P, h, h_sh, kpad, stream);
+        case 2: return dkp_launch_s<MODE, WBITS, SRC, 2>(P, h, h_sh, kpad, stream);
+        default: return dkp_launch_s<MODE, WBITS, SRC, 1>(P, h, h_sh, kpad, stream);
+    }
+}
+
+// ---- token-group path (large T): one workgroup per (row block, slot), tokens in passes of gmax
+
+template <int MODE, int WBITS, int SRC, int S>
+static hipError_t dk_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, int gmax, hipStream_t stream) {
+    const int slots = P.n_routed_slots + (P.Is > 0 ? 1 : 0);
+    const int Imax = P.I > P.Is ? P.I : P.Is;
+    const int rows_per_item = 16 * (4 / S);
+    const size_t lds = dk_lds_bytes(MODE, kpad, gmax);
+    auto fn = decode_kernel<MODE, WBITS, SRC, S>;
+    hipError_t err = allow_lds(fn, lds);
+    if (err != hipSuccess) return err;
+    const int nout = MODE == 0 ? Imax : P.d;
+    dim3 grid((nout + rows_per_item - 1) / rows_per_item, slots);
+    hipLaunchKernelGGL(fn, grid, dim3(DK_THREADS), lds, stream, P, h, h_sh, gmax, kpad);
+    return hipGetLastError();
+}
+
 template <int MODE, int WBITS, int SRC>
 static hipError_t dk_launch_mode(const FfnParams &P, float *h, float *h_sh, hipStream_t stream) {
-    const int slots = P.n_routed_slots + (P.Is > 0 ? 1 : 0);
+    bool done = false;
+    hipError_t err = dkp_try<MODE, WBITS, SRC>(P, h, h_sh, stream, &done);
+    if (done || err != hipSuccess) return err;
     const int Imax = P.I > P.Is ? P.I : P.Is;
     const int K = MODE == 0 ? P.d : Imax;
     // both the routed and the shared expert must split the same way: use the smaller intermediate size
@@ -481,31 +1002,9 @@ static hipError_t dk_launch_mode(const FfnParams &P, float *h, float *h_sh, hipS
                                                                         : pick_s(MODE, K, WBITS);
     const int kpad = pad_k(K / S, WBITS);  // the largest wavefront K part, padded to whole segments
     const int gmax = dk_gmax(P.T, kpad);
-    const size_t lds = dk_lds_bytes(MODE, kpad, gmax);
-    const int nout = MODE == 0 ? Imax : P.d;
-    const int rows_per_wg = 16 * (4 / S);
-    dim3 grid((nout + rows_per_wg - 1) / rows_per_wg, slots);
-    const void *fn;
-    if (S == 4)
-        fn = (const void *)decode_kernel<MODE, WBITS, SRC, 4>;
-    else if (S == 2)
-        fn = (const void *)decode_kernel<MODE, WBITS, SRC, 2>;
-    else
-        fn = (const void *)decode_kernel<MODE, WBITS, SRC, 1>;
-    if (lds > 65536) {
-        hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return err;
-    }
-    if (S == 4)
-        hipLaunchKernelGGL((decode_kernel<MODE, WBITS, SRC, 4>), grid, dim3(DK_THREADS), lds, stream, P, h, h_sh,
-                           gmax, kpad);
-    else if (S == 2)
-        hipLaunchKernelGGL((decode_kernel<MODE, WBITS, SRC, 2>), grid, dim3(DK_THREADS), lds, stream, P, h, h_sh,
-                           gmax, kpad);
-    else
-        hipLaunchKernelGGL((decode_kernel<MODE, WBITS, SRC, 1>), grid, dim3(DK_THREADS), lds, stream, P, h, h_sh,
-                           gmax, kpad);
-    return hipGetLastError();
+    if (S == 4) return dk_launch_s<MODE, WBITS, SRC, 4>(P, h, h_sh, kpad, gmax, stream);
+    if (S == 2) return dk_launch_s<MODE, WBITS, SRC, 2>(P, h, h_sh, kpad, gmax, stream);
+    return dk_launch_s<MODE, WBITS, SRC, 1>(P, h, h_sh, kpad, gmax, stream);
 }
 
 template <int WBITS, int SRC>
