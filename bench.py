@@ -18,6 +18,7 @@ stream the kernels run on around replays of a graph of moe_forward calls.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -49,6 +50,28 @@ def parse():
                     help="first run three plain 1 GiB device-to-device copies (torch copy_), whose HBM counter "
                          "readings scale the counters read for the MoE kernels")
     return ap.parse_args()
+
+
+def measured_traffic(config, T):
+    """HBM bytes per moe_forward launch from the committed rocprofv3 counter summary of this workload
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none or when the kernel sources
+    have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_decode_{config}_T{T}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        for key in ("source_sha256:", "traffic_bytes_per_launch:"):
+            if line.startswith(key):
+                vals[key[:-1]] = line[len(key):].strip()
+    h = hashlib.sha256()
+    for f in ("ffn_decode.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "routed_expert_ffn_sigmoid_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(spec, T, target_s):
@@ -160,8 +183,10 @@ def main():
     flops_per_step = 2.0 * 3 * spec.d * (T * spec.k * spec.I + T * spec.I_shared)
     if decode:
         achieved = bytes_per_fwd / (fwd_s / n_fwd) / 1e9
+        traffic = measured_traffic(args.config, T)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "kernel": "moe_forward (gate/up + down expert-FFN kernels)",
                 "algorithmic_bytes_per_launch": round(bytes_per_fwd),
                 "avg_launch_us": round(fwd_us, 2)}
