@@ -40,7 +40,8 @@ hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int
 size_t decode_workspace_bytes(const FfnParams &P);
 hipError_t launch_ffn_decode(const FfnParams &P, void *ws, hipStream_t stream);
 
-// ffn_gemm.hip: MFMA grouped-GEMM path
+// ffn_gemm.hip: MFMA grouped-GEMM path (bf16 activations, d and I multiples of 64)
+bool gemm_supported(const FfnParams &P);
 size_t gemm_workspace_bytes(const FfnParams &P);
 hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream);
 

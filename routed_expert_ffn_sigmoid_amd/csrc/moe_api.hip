@@ -95,9 +95,12 @@ moe::FfnParams ffn_params(const moe_shape *s) {
     return P;
 }
 
-// Path the forward call takes for this shape.
+// Path the forward call takes for this shape: the matrix-core grouped GEMM once there are enough rows
+// per expert to reuse each weight (more than 16 tokens), the bandwidth-bound decode kernels otherwise.
 int forward_path(const moe_shape *s) {
     if (s->path != MOE_PATH_AUTO) return s->path;
+    moe::FfnParams P = ffn_params(s);
+    if (s->T > 16 && moe::gemm_supported(P)) return MOE_PATH_GEMM;
     return MOE_PATH_GEMV;
 }
 

@@ -112,6 +112,24 @@ def test_small_layer_parity(orc, dev, case):
     run_full_case(orc, dev, spec, T, label=case)
 
 
+# the matrix-core grouped GEMM path (bf16 activations; d, I multiples of 64): several 128-row tiles per
+# expert with ragged ends, experts with a handful of rows, I_shared above and below I
+GEMM = {
+    "gemm_int4_shared": (dict(d=512, E=16, k=4, I=384, I_shared=192, routed_scale=2.5), 70),
+    "gemm_int8_shared": (dict(d=768, E=8, k=2, I=512, I_shared=256, wbits=8, routed_scale=2.5), 200),
+    "gemm_int4_row_tiles": (dict(d=256, E=4, k=2, I=256), 300),
+    "gemm_int8_one_expert_many_rows": (dict(d=128, E=2, k=1, I=64, I_shared=64, wbits=8), 400),
+    "gemm_int4_shared_wider": (dict(d=320, E=8, k=3, I=128, I_shared=320), 45),
+    "gemm_int4_T1": (dict(d=512, E=64, k=6, I=256, I_shared=256, routed_scale=2.5), 1),
+}
+
+
+@pytest.mark.parametrize("case", list(GEMM))
+def test_gemm_path_parity(orc, dev, case):
+    kw, T = GEMM[case]
+    run_full_case(orc, dev, spec_of(**kw), T, path=B.MOE_PATH_GEMM, label=case)
+
+
 def test_all_tie_router(orc, dev):
     """W_r = 0 and b = 0: every selection score is 0.5; ids 0..k-1 win with w = lambda/k."""
     spec = spec_of(d=256, E=8, k=3, I=64, routed_scale=2.5)
