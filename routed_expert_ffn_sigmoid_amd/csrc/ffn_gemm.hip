@@ -35,24 +35,35 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16v_t __attribute__((ext_vector_type(16)));
 
-constexpr int GG_M = 128;       // rows per tile
-constexpr int GG_WAVES = 8;
-constexpr int GG_K = 64;        // K per pipeline step
-constexpr int GG_LDA = 72;      // LDS row stride of an activation plane, in halfs (64 + 8 of padding)
+constexpr int GG_M = 128;          // rows per tile
+constexpr int GG_WAVES = 8;        // wavefronts per workgroup, one workgroup per CU
+constexpr int GG_K = 64;           // K per pipeline step
+constexpr int GG_NW = 64;          // weight rows per wavefront and tile (two 32-column subtiles)
 constexpr int GG_MAXSLOTS = 1025;
+constexpr int GG_RING = 152 * 1024;  // LDS for the staging ring (the rest of the 160 KB holds the tables)
 
 // storage position, within its group of 8, of input i of the group (int4 weights)
 __device__ __forceinline__ int pos8(int i) { return ((i & 3) << 1) | (i >> 2); }
 
-// fp16 values of eight int4 weights from one word of packed nibbles (input k in the low nibble of byte
-// k/2), in the order k = 0,4,1,5,2,6,3,7: 0x6400 | n is the fp16 bit pattern of 1024 + n, and off is
-// -(1024 + z) with z the integral zero point folded in (or 0).  Exact: |q - z| <= 1024 + 15.
-__device__ __forceinline__ h8_t deq_int4(uint32_t w, h2_t off) {
-    const uint32_t M = 0x000F000Fu, B = 0x64006400u;
-    const h2_t p0 = __builtin_bit_cast(h2_t, (w & M) | B) + off;
-    const h2_t p1 = __builtin_bit_cast(h2_t, ((w >> 4) & M) | B) + off;
-    const h2_t p2 = __builtin_bit_cast(h2_t, ((w >> 8) & M) | B) + off;
-    const h2_t p3 = __builtin_bit_cast(h2_t, ((w >> 12) & M) | B) + off;
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "s"(o));
+    return r;
+}
+
+// fp16 values of eight int4 weights from one word (input k in the low nibble of byte k/2 for even k, the
+// high nibble for odd k), in the order k = 0,4,1,5,2,6,3,7.  A nibble under the exponent of 1024
+// (0x6400) is the fp16 value 1024 + n; a high nibble is left in place, giving 1024 + 16 n, and scaled
+// by 1/16 in a fused multiply-add.  off = -(1024 + z), off16 = -(64 + z), z the folded integral zero
+// point (or 0).  Exact: every intermediate is an integer or a multiple of 1/16 below 2048.
+__device__ __forceinline__ h8_t deq_int4(uint32_t w, uint32_t mlo, uint32_t mhi, h2_t off, h2_t off16) {
+    const uint32_t B = 0x64006400u;
+    const h2_t sixteenth = (h2_t){(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t w8 = w >> 8;
+    const h2_t p0 = __builtin_bit_cast(h2_t, and_or(w, mlo, B)) + off;
+    const h2_t p1 = __builtin_bit_cast(h2_t, and_or(w, mhi, B)) * sixteenth + off16;
+    const h2_t p2 = __builtin_bit_cast(h2_t, and_or(w8, mlo, B)) + off;
+    const h2_t p3 = __builtin_bit_cast(h2_t, and_or(w8, mhi, B)) * sixteenth + off16;
     return (h8_t){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
@@ -71,6 +82,28 @@ __device__ __forceinline__ h8_t deq_int8(uint32_t w0, uint32_t w1, h2_t off) {
 __device__ __forceinline__ float gg_zp(const void *z, int wbits, long i) {
     return wbits == 8 ? (float)((const int8_t *)z)[i] : ((const float *)z)[i];
 }
+
+// Buffer -> LDS copy of one wavefront: lane L's 16 bytes at voff land at LDS address lds + 16 L.  Written
+// as inline assembly so that the compiler's wait-count pass, which cannot tell the stages of the ring
+// apart, does not make every LDS read wait for every copy in flight; the pipeline below waits for the
+// exact count itself.  M0 (the LDS base of the copy) is saved and restored, with a wait state after
+// each write of it.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(lds), "s"(r)
+        : "memory");
+}
+
+// s_waitcnt with only the vector-memory count (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+#define GG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // x (bf16 [T][d]) -> x16 (fp16 [T][d], int4 order within groups of 8).
 template <int WBITS>
@@ -95,7 +128,7 @@ __global__ __launch_bounds__(256) void x16_kernel(const uint16_t *__restrict__ x
 }
 
 template <int V>
-struct GgSet {
+struct GgInt {
     static constexpr int value = V;
 };
 
@@ -105,42 +138,55 @@ struct GemmBufs {
     _Float16 *hshi, *hslo;     // [T][I_shared]
 };
 
-// MODE 0: gate/up (A = x16 rows through the permutation; B = the gate and up rows of 32 channels per
-// wavefront; output h as fp16 hi/lo planes).  MODE 1: down (A = h hi/lo rows of the slot; B = 64 down
-// rows per wavefront; output y_perm / y_shared in fp32).
+// Stage layout of the LDS ring.  Activation planes: 128 rows x 128 bytes (64 fp16), 16-byte chunk c of
+// row m stored at chunk c ^ (m & 7).  Weights: each wavefront's 64 rows x RB bytes, 16-byte chunk c of
+// row r stored at c ^ ((r >> 2) & 1) (int4, 32-byte rows) or c ^ ((r >> 1) & 3) (int8, 64-byte rows).
+// With these swizzles each group of 8 lanes of a fragment read covers all 32 banks once.
+template <int MODE, int WBITS>
+struct GgCfg {
+    static constexpr int NA = MODE == 0 ? 1 : 2;            // activation planes: x, or h hi and lo
+    static constexpr int RB = GG_K * WBITS / 8;             // weight bytes per row and step
+    static constexpr int PLANE = GG_M * GG_K * 2;           // bytes per activation plane
+    static constexpr int A_BYTES = NA * PLANE;
+    static constexpr int B_BYTES = GG_WAVES * GG_NW * RB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int STAGES = GG_RING / STAGE > 4 ? 4 : GG_RING / STAGE;
+    static constexpr int NLA = 2;                           // 1 KB copies per wavefront, plane and step
+    static constexpr int NLB = GG_NW * RB / 1024;           // 1 KB weight copies per wavefront and step
+    static constexpr int NL = NA * NLA + NLB;
+    static constexpr int NOUT_W = MODE == 0 ? 32 : 64;      // distinct output columns per wavefront
+    static constexpr int NOUT_G = NOUT_W * GG_WAVES;        // per tile
+    static_assert(STAGES >= 2, "LDS ring");
+    static_assert(GG_M * 128 / 1024 == NLA * GG_WAVES, "activation copies");
+};
+
+// MODE 0: gate/up (A = x16 rows through the permutation; each wavefront owns 32 channels, subtile 0 their
+// gate rows and subtile 1 their up rows; output h as fp16 hi/lo planes).  MODE 1: down (A = h hi/lo rows
+// of the slot; 64 down rows per wavefront; output y_perm / y_shared in fp32).
 //
 // Zero points: when every zero point of the tile's weight rows is an integer (int8 always; int4 when
 // its fp32 zero points are integral), it is folded into the dequantisation (B = q - z, exact in fp16);
-// otherwise B = q and the epilogue subtracts z times the row sum of the activations, which the
-// staging threads then accumulate.
-template <int MODE, int WBITS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBufs G, int tiles_n) {
-    constexpr int NA = MODE == 0 ? 1 : 2;         // activation planes: x, or h hi and lo
-    constexpr int MM = WAVES == 4 ? 4 : 2;        // 32-row blocks per wavefront
-    constexpr int NJ = WAVES == 4 ? 4 : 2;        // 32-column subtiles per wavefront
-    constexpr int WM = 4 / MM;                    // wavefront rows
-    constexpr int WN = WAVES / WM;                // wavefront columns
-    constexpr int NOUT_W = MODE == 0 ? 16 * NJ : 32 * NJ;  // distinct output columns per wavefront
-    constexpr int NOUT_G = NOUT_W * WN;           // per tile
-    constexpr int CPT = 1024 / (WAVES * 64);      // activation chunks per thread per plane and step
-    constexpr int TPR = 8 / CPT;                  // staging threads per row
-    constexpr int ACH = CPT * NA;                 // 16-byte activation chunks per thread per step
-    constexpr int WL = WBITS == 8 ? 2 : 1;        // 16-byte weight loads per subtile per step
-    constexpr int PLANE = GG_M * GG_LDA;          // halfs per activation plane
+// otherwise B = q and the epilogue subtracts z times the row sum of the activations, summed from the
+// staged tiles.
+template <int MODE, int WBITS>
+__global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBufs G, int tiles_n) {
+    using C = GgCfg<MODE, WBITS>;
+    constexpr int NA = C::NA, RB = C::RB, PLANE = C::PLANE, STAGE = C::STAGE, STAGES = C::STAGES;
+    constexpr int NLB = C::NLB, NL = C::NL;
+    constexpr int WL = WBITS == 8 ? 2 : 1;   // 16-byte weight fragments per subtile and step
     constexpr float QBIAS = WBITS == 8 ? 1152.f : 1024.f;
-    // activation planes in dynamic LDS: [2 stages][NA planes][GG_M rows][GG_LDA halfs]
-    extern __shared__ __align__(16) _Float16 As_dyn[];
+    extern __shared__ __align__(16) unsigned char gg_ring[];
+    __shared__ int s_t0[GG_MAXSLOTS + 1];
     __shared__ float rsum[GG_M];
-    __shared__ int s_e[GG_MAXSLOTS], s_p0[GG_MAXSLOTS], s_c[GG_MAXSLOTS], s_t0[GG_MAXSLOTS + 1];
     __shared__ int s_nslot;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 5, lr = lane & 31;
-    const int wm = wv / WN, wn = wv % WN;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)gg_ring;
 
     // ---- tile table: slot s (used experts in uniq order, then the shared expert) has
-    // mt_s = ceil(c_s / 128) row tiles and tiles_n output tiles; s_t0 is the exclusive prefix
+    // ceil(c_s / 128) row tiles times tiles_n output tiles; s_t0 is the exclusive prefix
     if (wv == 0) {
         int nu = *P.n_uniq;
         nu = nu < 0 ? 0 : (nu > P.n_routed_slots ? P.n_routed_slots : nu);
@@ -150,15 +196,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBu
             const int s = b + lane;
             int mt = 0;
             if (s < ns) {
-                int e = 0, p0 = 0, c = P.T;
+                int c = P.T;
                 if (s < nu) {
-                    e = P.uniq[s];
-                    p0 = P.offsets[e];
-                    c = P.offsets[e + 1] - p0;
+                    const int e = P.uniq[s];
+                    c = P.offsets[e + 1] - P.offsets[e];
                 }
-                s_e[s] = e;
-                s_p0[s] = p0;
-                s_c[s] = c;
                 mt = (c + GG_M - 1) / GG_M;
             }
             const int v = mt * tiles_n;
@@ -177,215 +219,253 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBu
         }
     }
     __syncthreads();
-    const int nslot = s_nslot;
-    const int ntiles = s_t0[nslot];
+    const int nslot = __builtin_amdgcn_readfirstlane(s_nslot);
+    const int ntiles = __builtin_amdgcn_readfirstlane(s_t0[nslot]);
 
-    // staging thread map: row srow of the tile, chunks CPT*sq .. CPT*sq + CPT - 1 (of 8 per row and
-    // step) of every plane
-    const int srow = tid / TPR, sq = tid % TPR;
+    // Workgroups are dealt round-robin to the 8 XCDs: number them XCD-major so that consecutive tiles
+    // (the row tiles of one weight block) run on the same XCD and share its L2.
+    const int nwg = gridDim.x;
+    const int vwg = nwg % 8 == 0 ? (int)(blockIdx.x % 8) * (nwg / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
 
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (int tile = vwg; tile < ntiles; tile += nwg) {
         // ---- locate the tile: slot (binary search), output tile, row tile
         int lo = 0, hi = nslot - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_t0[mid] <= tile) lo = mid; else hi = mid - 1;
         }
-        const int slot = lo;
+        const int slot = __builtin_amdgcn_readfirstlane(lo);
         const bool shared = P.Is > 0 && slot == nslot - 1;
-        const int e = s_e[slot], p0 = s_p0[slot], cnt = s_c[slot];
+        int e = 0, p0 = 0, cnt = P.T;
+        if (!shared) {
+            e = ld_const(P.uniq, slot);
+            p0 = ld_const(P.offsets, e);
+            cnt = ld_const(P.offsets, e + 1) - p0;
+        }
         const int mt_n = (cnt + GG_M - 1) / GG_M;
-        const int local = tile - s_t0[slot];
+        const int local = tile - __builtin_amdgcn_readfirstlane(s_t0[slot]);
         const int ntile = local / mt_n, mtile = local % mt_n;
         const int r0 = mtile * GG_M;                     // first row of the tile within the slot
         const int rows = min(GG_M, cnt - r0);
-        const int nm32 = (rows + 31) >> 5;               // 32-row MFMA blocks with data
         const int I = shared ? P.Is : P.I;
         const int KK = MODE == 0 ? P.d : I;              // contraction length
         const int nout = MODE == 0 ? I : P.d;
         const int nsteps = KK / GG_K;
-        const QW &W = shared ? P.shared : P.routed;
+        // field by field: a reference into the by-value parameter block would make the compiler copy it
+        // to private memory and read these pointers back into vector registers
+        QW W;
+        W.qg = shared ? P.shared.qg : P.routed.qg;
+        W.qu = shared ? P.shared.qu : P.routed.qu;
+        W.qd = shared ? P.shared.qd : P.routed.qd;
+        W.sg = shared ? P.shared.sg : P.routed.sg;
+        W.su = shared ? P.shared.su : P.routed.su;
+        W.sd = shared ? P.shared.sd : P.routed.sd;
+        W.zg = shared ? P.shared.zg : P.routed.zg;
+        W.zu = shared ? P.shared.zu : P.routed.zu;
+        W.zd = shared ? P.shared.zd : P.routed.zd;
+        const long rbf = (long)KK * WBITS / 8;           // bytes per weight row
 
-        // ---- activation source of this thread's staging row
-        rsrc_t asrc[NA];
-        long arow = -1;  // element offset of the row, -1: padding
-        if (MODE == 0) {
-            asrc[0] = make_rsrc(G.x16, (uint32_t)((long)P.T * P.d * 2));
-            if (srow < rows) {
-                const int t = shared ? (r0 + srow) : (P.perm[p0 + r0 + srow] / P.k);
-                arow = (long)t * P.d;
+        // ---- copy sources.  Activations: this lane moves chunk (lane & 7) ^ (lane >> 3) of row
+        // 8 (2 wv + i) + lane / 8 (i = 0, 1), landing at its swizzled place.
+        rsrc_t ars[NA];
+        uint32_t asrc[2];
+        {
+            if (MODE == 0) {
+                ars[0] = make_rsrc(G.x16, (uint32_t)((long)P.T * P.d * 2));
+            } else {
+                const uint32_t nb = (uint32_t)((long)(shared ? P.T : P.A) * I * 2);
+                ars[0] = make_rsrc(shared ? G.hshi : G.hhi, nb);
+                ars[NA - 1] = make_rsrc(shared ? G.hslo : G.hlo, nb);
             }
-        } else {
-            const uint32_t nb = (uint32_t)((long)(shared ? P.T : P.A) * I * 2);
-            asrc[0] = make_rsrc(shared ? G.hshi : G.hhi, nb);
-            asrc[NA - 1] = make_rsrc(shared ? G.hslo : G.hlo, nb);
-            if (srow < rows) arow = (long)((shared ? 0 : p0) + r0 + srow) * I;
+            const uint32_t alc = (uint32_t)((lane & 7) ^ (lane >> 3));
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int m = 8 * (2 * wv + i) + (lane >> 3);
+                uint32_t off = kOOB;
+                if (m < rows) {
+                    long row;
+                    if (MODE == 0) row = shared ? (r0 + m) : (P.perm[p0 + r0 + m] / P.k);
+                    else row = (long)(shared ? 0 : p0) + r0 + m;
+                    off = (uint32_t)(row * KK * 2) + 16 * alc;
+                }
+                asrc[i] = off;
+            }
+        }
+        // Weights: 1 KB copy i of this wavefront holds rows 32 i + lane / 2 (int4) or 16 i + lane / 4
+        // (int8) of its 64; row r of subtile j = r / 32 is column 32 j + r % 32 of the wavefront.
+        rsrc_t brs[2];
+        uint32_t bsrc[NLB];
+        const int nbase = ntile * C::NOUT_G + wv * C::NOUT_W;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const uint8_t *base = MODE == 0 ? (j == 0 ? W.qg : W.qu) + (long)e * I * rbf : W.qd + (long)e * P.d * rbf;
+            brs[j] = make_rsrc(base, (uint32_t)(nout * rbf));
+        }
+#pragma unroll
+        for (int i = 0; i < NLB; i++) {
+            int rl, lc;
+            if (WBITS == 4) {
+                rl = 32 * i + (lane >> 1);
+                lc = (lane & 1) ^ ((lane >> 3) & 1);
+            } else {
+                rl = 16 * i + (lane >> 2);
+                lc = (lane & 3) ^ ((lane >> 3) & 3);
+            }
+            const int j = rl >> 5, col = rl & 31;
+            const int o = MODE == 0 ? nbase + col : nbase + 32 * j + col;
+            bsrc[i] = o < nout ? (uint32_t)(o * rbf) + 16 * lc : kOOB;
         }
 
-        // ---- weight rows of this lane: subtile j.  Gate/up: j < NJ/2 the gate rows of channels
-        // c0 + 32 j + lr, j >= NJ/2 the up rows of the same channels; down: outputs o0 + 32 j + lr.
-        const long rb = (long)KK * WBITS / 8;  // bytes per weight row
-        rsrc_t wsrc[NJ];
-        uint32_t wrow[NJ];
-        int ocol[NJ];
-        float sc[NJ], zp[NJ];
-        {
-            const int nbase = ntile * NOUT_G + wn * NOUT_W;
+        // ---- epilogue columns, scales and zero points of this lane (column lr of subtile j)
+        int ocol[2];
+        float sc[2], zp[2];
 #pragma unroll
-            for (int j = 0; j < NJ; j++) {
-                const bool gate = j < NJ / 2;
-                const int o = MODE == 0 ? nbase + 32 * (j % (NJ / 2)) + lr : nbase + 32 * j + lr;
-                ocol[j] = o;
-                const long ncol = MODE == 0 ? I : P.d;
-                const uint8_t *base = MODE == 0 ? (gate ? W.qg : W.qu) + (long)e * I * rb : W.qd + (long)e * P.d * rb;
-                wsrc[j] = make_rsrc(base, (uint32_t)(ncol * rb));
-                wrow[j] = o < nout ? (uint32_t)(o * rb) : kOOB;
-                const long ch = (long)e * ncol + min(o, nout - 1);
-                if (MODE == 0) {
-                    sc[j] = gate ? W.sg[ch] : W.su[ch];
-                    zp[j] = gg_zp(gate ? W.zg : W.zu, WBITS, ch);
-                } else {
-                    sc[j] = W.sd[ch];
-                    zp[j] = gg_zp(W.zd, WBITS, ch);
-                }
+        for (int j = 0; j < 2; j++) {
+            const int o = MODE == 0 ? nbase + lr : nbase + 32 * j + lr;
+            ocol[j] = o;
+            const long ncol = MODE == 0 ? I : P.d;
+            const long ch = (long)e * ncol + min(o, nout - 1);
+            if (MODE == 0) {
+                sc[j] = j == 0 ? W.sg[ch] : W.su[ch];
+                zp[j] = gg_zp(j == 0 ? W.zg : W.zu, WBITS, ch);
+            } else {
+                sc[j] = W.sd[ch];
+                zp[j] = gg_zp(W.zd, WBITS, ch);
             }
         }
         bool my_int = true;
 #pragma unroll
-        for (int j = 0; j < NJ; j++) my_int = my_int && zp[j] == rintf(zp[j]) && fabsf(zp[j]) <= 512.f;
+        for (int j = 0; j < 2; j++) my_int = my_int && zp[j] == rintf(zp[j]) && fabsf(zp[j]) <= 512.f;
         const bool fold = __syncthreads_and(my_int);  // uniform over the workgroup
-        h2_t boff[NJ];
+        h2_t boff[2], boff16[2];
 #pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            const _Float16 o = (_Float16)(-(QBIAS + (fold ? zp[j] : 0.f)));
+        for (int j = 0; j < 2; j++) {
+            const float z = fold ? zp[j] : 0.f;
+            const _Float16 o = (_Float16)(-(QBIAS + z)), o16 = (_Float16)(-(64.f + z));
             boff[j] = (h2_t){o, o};
+            boff16[j] = (h2_t){o16, o16};
         }
+        // nibble masks kept in registers (the three-operand and-or cannot take two literals)
+        const uint32_t mlo = __builtin_amdgcn_readfirstlane(0x000F000Fu), mhi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
 
-        // ---- two-step register pipeline (set = step parity).  Steps past the end (the prefetch of the
-        // last two steps, and the padding step of an odd count) load nothing and read as zeros, so every
-        // step issues the same number of loads.
-        uint4 araw[2][ACH];
-        uint4 wraw[2][NJ][WL];
-        auto issue = [&](int step, int set) {
-            const bool live = step < nsteps;
-            const uint32_t ao =
-                (arow < 0 || !live) ? kOOB : (uint32_t)((arow + (long)step * GG_K + 8 * CPT * sq) * 2);
+        // ---- LDS read offsets within a stage
+        uint32_t ard[4];  // activation fragment of substep s: row lr (+ 32 mm), chunk 4 kg + s
+#pragma unroll
+        for (int s = 0; s < 4; s++) ard[s] = (uint32_t)(lr * 128 + (((4 * kg + s) ^ (lr & 7)) * 16));
+        uint32_t brd[2][WL];  // weight fragment of subtile j: row 32 j + lr of the wavefront, bytes 32 kg ...
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int h = 0; h < WL; h++) {
+                const int rl = 32 * j + lr;
+                const int pc = WBITS == 4 ? (kg ^ ((rl >> 2) & 1)) : ((2 * kg + h) ^ ((rl >> 1) & 3));
+                brd[j][h] = (uint32_t)(C::A_BYTES + wv * GG_NW * RB + rl * RB + pc * 16);
+            }
+
+        auto issue = [&](int step, int stg) {
+            const uint32_t sb = ring0 + (uint32_t)(stg * STAGE);
 #pragma unroll
             for (int pl = 0; pl < NA; pl++)
 #pragma unroll
-                for (int c = 0; c < CPT; c++)
-                    araw[set][CPT * pl + c] = buf_load16(asrc[pl], ao == kOOB ? kOOB : ao + 16 * c);
+                for (int i = 0; i < 2; i++)
+                    dma16(ars[pl], sb + pl * PLANE + (2 * wv + i) * 1024, asrc[i] + (uint32_t)(step * 128));
 #pragma unroll
-            for (int j = 0; j < NJ; j++)
-#pragma unroll
-                for (int q = 0; q < WL; q++)
-                    wraw[set][j][q] = buf_load16(
-                        wsrc[j], (wrow[j] == kOOB || !live)
-                                     ? kOOB
-                                     : wrow[j] + (uint32_t)(step * (GG_K * WBITS / 8) + kg * (16 * WL) + 16 * q));
+            for (int i = 0; i < NLB; i++)
+                dma16(brs[WBITS == 4 ? i : i >> 1],
+                      sb + C::A_BYTES + wv * GG_NW * RB + i * 1024, bsrc[i] + (uint32_t)(step * RB));
         };
-        float rs = 0.f;
-        f32x16v_t acc[MM][NJ];
-#pragma unroll
-        for (int mm = 0; mm < MM; mm++)
-#pragma unroll
-            for (int j = 0; j < NJ; j++) acc[mm][j] = (f32x16v_t){};
 
-        issue(0, 0);
-        issue(1, 1);
-        // one pipeline step; the register set is a compile-time constant (the loop runs two steps per
-        // iteration) so that every wait counts only the loads it needs
-        auto one_step = [&](int step, auto setc) {
-            constexpr int set = decltype(setc)::value;
-            _Float16 *Ab = As_dyn + set * NA * PLANE;
-            // activation chunks of this step -> LDS (and, without folded zero points, their row sums)
+        // ---- the tile, with the number of 32-row blocks that hold data as a compile-time constant
+        auto run = [&](auto muc) {
+            constexpr int MU = decltype(muc)::value;
+            f32x16v_t acc[MU][2];
 #pragma unroll
-            for (int pl = 0; pl < NA; pl++)
+            for (int mm = 0; mm < MU; mm++)
 #pragma unroll
-                for (int c = 0; c < CPT; c++)
-                    *(uint4 *)(Ab + pl * PLANE + srow * GG_LDA + 8 * (CPT * sq + c)) = araw[set][CPT * pl + c];
+                for (int j = 0; j < 2; j++) acc[mm][j] = (f32x16v_t){};
+            float rs = 0.f;
+
+#pragma unroll
+            for (int i = 0; i < STAGES - 1; i++) issue(i, i);
+            int stg = 0;
+            for (int step = 0; step < nsteps; step++) {
+                GG_WAIT_VM((STAGES - 2) * NL);  // this wavefront's copies of this step have landed
+                __syncthreads();                // everyone's have; the stage read last step is free
+                issue(step + STAGES - 1, stg == 0 ? STAGES - 1 : stg - 1);
+                const unsigned char *sp = gg_ring + stg * STAGE;
+                uint4 braw[2][WL];
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int h = 0; h < WL; h++) braw[j][h] = *(const uint4 *)(sp + brd[j][h]);
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    h8_t bq[2];
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        if (WBITS == 4) {
+                            const uint32_t ww[4] = {braw[j][0].x, braw[j][0].y, braw[j][0].z, braw[j][0].w};
+                            bq[j] = deq_int4(ww[s], mlo, mhi, boff[j], boff16[j]);
+                        } else {
+                            const uint4 q = braw[j][s >> 1];
+                            bq[j] = (s & 1) ? deq_int8(q.z, q.w, boff[j]) : deq_int8(q.x, q.y, boff[j]);
+                        }
+                    }
+#pragma unroll
+                    for (int mm = 0; mm < MU; mm++)
+#pragma unroll
+                        for (int pl = 0; pl < NA; pl++) {
+                            const h8_t a = *(const h8_t *)(sp + pl * PLANE + mm * 4096 + ard[s]);
+#pragma unroll
+                            for (int j = 0; j < 2; j++)
+                                acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq[j], acc[mm][j], 0, 0, 0);
+                        }
+                }
+                if (!fold) {
+                    // row sums of the staged activations: row tid / 4, chunks 2 (tid % 4) and 2 (tid % 4) + 1
+                    const int m = tid >> 2;
+#pragma unroll
+                    for (int pl = 0; pl < NA; pl++)
+#pragma unroll
+                        for (int h = 0; h < 2; h++) {
+                            const int pc = (2 * (tid & 3) + h) ^ (m & 7);
+                            const h8_t v = *(const h8_t *)(sp + pl * PLANE + m * 128 + pc * 16);
+#pragma unroll
+                            for (int i = 0; i < 8; i++) rs += (float)v[i];
+                        }
+                }
+                stg = stg + 1 == STAGES ? 0 : stg + 1;
+            }
+            GG_WAIT_VM(0);  // the copies issued past the end land before the ring is reused
             if (!fold) {
-#pragma unroll
-                for (int q = 0; q < ACH; q++) {
-                    const uint32_t ww[4] = {araw[set][q].x, araw[set][q].y, araw[set][q].z, araw[set][q].w};
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const h2_t hh = __builtin_bit_cast(h2_t, ww[i]);
-                        rs += (float)hh.x + (float)hh.y;
-                    }
-                }
+                float t = rs;
+                t += __shfl_xor(t, 1, 64);
+                t += __shfl_xor(t, 2, 64);
+                if ((tid & 3) == 0) rsum[tid >> 2] = t;
             }
-            uint4 wcur[NJ][WL];
-#pragma unroll
-            for (int j = 0; j < NJ; j++)
-#pragma unroll
-                for (int q = 0; q < WL; q++) wcur[j][q] = wraw[set][j][q];
-            __syncthreads();  // this step's activations are in LDS; the other stage is free
-            issue(step + 2, set);
+            __syncthreads();
 
+            // ---- epilogue: lane column ocol[j]; register r holds row 8 (r / 4) + 4 kg + r % 4 of block mm.
+            // The lane's row offset is made opaque here so that the compiler does not hoist the 64 row
+            // indices that derive from it out of the tile loop (they would occupy registers throughout).
+            int mk = 4 * kg;
+            asm volatile("" : "+v"(mk));
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                h8_t bq[NJ];
+            for (int mm = 0; mm < MU; mm++) {
 #pragma unroll
-                for (int j = 0; j < NJ; j++) {
-                    if (WBITS == 4) {
-                        const uint32_t ww[4] = {wcur[j][0].x, wcur[j][0].y, wcur[j][0].z, wcur[j][0].w};
-                        bq[j] = deq_int4(ww[s], boff[j]);
-                    } else {
-                        const uint4 q = wcur[j][s >> 1];
-                        bq[j] = (s & 1) ? deq_int8(q.z, q.w, boff[j]) : deq_int8(q.x, q.y, boff[j]);
-                    }
-                }
-                // every block runs, also the all-padding ones of a short row tile (their rows are zero): a
-                // branch around an MFMA would make the compiler copy the accumulator to merge the paths
-#pragma unroll
-                for (int mm = 0; mm < MM; mm++) {
-#pragma unroll
-                    for (int pl = 0; pl < NA; pl++) {
-                        const h8_t a = *(const h8_t *)(Ab + pl * PLANE + ((MM * wm + mm) * 32 + lr) * GG_LDA +
-                                                       32 * kg + 8 * s);
-#pragma unroll
-                        for (int j = 0; j < NJ; j++)
-                            acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq[j], acc[mm][j], 0, 0, 0);
-                    }
-                }
-                // keep each substep's fragment loads next to its MFMAs (bounded register use)
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        for (int step = 0; step < nsteps; step += 2) {
-            one_step(step, GgSet<0>{});
-            one_step(step + 1, GgSet<1>{});
-        }
-
-        // ---- row sums (the staging threads of a row, fixed order), only without folded zero points
-        if (!fold) {
-            float t = rs;
-#pragma unroll
-            for (int o = 1; o < TPR; o <<= 1) t = t + __shfl_xor(t, o, 64);
-            if (sq == 0) rsum[srow] = t;
-        }
-        __syncthreads();
-
-        // ---- epilogue: lane column ocol[j]; register r holds row 8*(r/4) + 4*kg + (r%4) of block mm
-#pragma unroll
-        for (int mm = 0; mm < MM; mm++) {
-            if (MM * wm + mm >= nm32) continue;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = (MM * wm + mm) * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-                if (m >= rows) continue;
-                const float xs = fold ? 0.f : rsum[m];
-                const long prow = (long)(shared ? 0 : p0) + r0 + m;  // output row
-                if (MODE == 0) {
-#pragma unroll
-                    for (int jj = 0; jj < NJ / 2; jj++) {
-                        const int c = ocol[jj];
+                for (int r = 0; r < 16; r++) {
+                    const int m = mm * 32 + 8 * (r >> 2) + mk + (r & 3);
+                    if (m >= rows) continue;
+                    const float xs = fold ? 0.f : rsum[m];
+                    const long prow = (long)(shared ? 0 : p0) + r0 + m;  // output row
+                    if (MODE == 0) {
+                        const int c = ocol[0];
                         if (c < nout) {
-                            const int ju = jj + NJ / 2;
-                            const float gv = sc[jj] * (acc[mm][jj][r] - (fold ? 0.f : zp[jj]) * xs);
-                            const float uv = sc[ju] * (acc[mm][ju][r] - (fold ? 0.f : zp[ju]) * xs);
-                            const float hv = gv / (1.f + expf(-gv)) * uv;
+                            const float gv = sc[0] * (acc[mm][0][r] - (fold ? 0.f : zp[0]) * xs);
+                            const float uv = sc[1] * (acc[mm][1][r] - (fold ? 0.f : zp[1]) * xs);
+                            // silu through the hardware exp2 and reciprocal (relative error ~1e-6, below the
+                            // 22 bits that h keeps)
+                            const float hv = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * gv)) * uv;
                             const _Float16 h_hi = (_Float16)hv;
                             const _Float16 h_lo = (_Float16)(hv - (float)h_hi);
                             // stored at the planes' position of channel c (int4 order within groups of 8)
@@ -393,19 +473,24 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBu
                             (shared ? G.hshi : G.hhi)[prow * I + hp] = h_hi;
                             (shared ? G.hslo : G.hlo)[prow * I + hp] = h_lo;
                         }
-                    }
-                } else {
+                    } else {
 #pragma unroll
-                    for (int j = 0; j < NJ; j++) {
-                        if (ocol[j] < nout) {
-                            const float y = sc[j] * (acc[mm][j][r] - (fold ? 0.f : zp[j]) * xs);
-                            (shared ? P.y_sh : P.y_perm)[prow * P.d + ocol[j]] = y;
+                        for (int j = 0; j < 2; j++) {
+                            if (ocol[j] < nout) {
+                                const float y = sc[j] * (acc[mm][j][r] - (fold ? 0.f : zp[j]) * xs);
+                                (shared ? P.y_sh : P.y_perm)[prow * P.d + ocol[j]] = y;
+                            }
                         }
                     }
                 }
             }
-        }
-        __syncthreads();  // rsum and the activation stages are reused by the next tile
+        };
+        const int nm32 = (rows + 31) >> 5;  // 32-row MFMA blocks with data
+        if (nm32 >= 4) run(GgInt<4>{});
+        else if (nm32 == 3) run(GgInt<3>{});
+        else if (nm32 == 2) run(GgInt<2>{});
+        else run(GgInt<1>{});
+        __syncthreads();  // rsum and the ring are reused by the next tile
     }
 }
 
@@ -436,20 +521,16 @@ static int gg_cus() {
     return n;
 }
 
-template <int MODE, int WBITS, int WAVES>
+template <int MODE, int WBITS>
 static hipError_t gg_launch_mode(const FfnParams &P, const GemmBufs &G, hipStream_t stream) {
-    constexpr int NJ = WAVES == 4 ? 4 : 2, MM = WAVES == 4 ? 4 : 2;
-    constexpr int WN = WAVES / (4 / MM);
-    constexpr int NOUT_G = (MODE == 0 ? 16 * NJ : 32 * NJ) * WN;
+    using C = GgCfg<MODE, WBITS>;
     const int Imax = P.I > P.Is ? P.I : P.Is;
-    const int tiles_n = ((MODE == 0 ? Imax : P.d) + NOUT_G - 1) / NOUT_G;
-    const size_t lds = (size_t)2 * (MODE == 0 ? 1 : 2) * GG_M * GG_LDA * sizeof(_Float16);
-    auto fn = gemm_kernel<MODE, WBITS, WAVES>;
-    if (lds > 65536) {
-        hipError_t err = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return err;
-    }
-    hipLaunchKernelGGL(fn, dim3(gg_cus()), dim3(WAVES * 64), lds, stream, P, G, tiles_n);
+    const int tiles_n = ((MODE == 0 ? Imax : P.d) + C::NOUT_G - 1) / C::NOUT_G;
+    const size_t lds = (size_t)C::STAGES * C::STAGE;
+    auto fn = gemm_kernel<MODE, WBITS>;
+    hipError_t err = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(fn, dim3(gg_cus()), dim3(GG_WAVES * 64), lds, stream, P, G, tiles_n);
     return hipGetLastError();
 }
 
@@ -462,9 +543,9 @@ static hipError_t gg_launch(const FfnParams &P, const GemmBufs &G, hipStream_t s
                        (_Float16 *)G.x16, nchunks);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    err = gg_launch_mode<0, WBITS, GG_WAVES>(P, G, stream);
+    err = gg_launch_mode<0, WBITS>(P, G, stream);
     if (err != hipSuccess) return err;
-    return gg_launch_mode<1, WBITS, GG_WAVES>(P, G, stream);
+    return gg_launch_mode<1, WBITS>(P, G, stream);
 }
 
 hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream) {
