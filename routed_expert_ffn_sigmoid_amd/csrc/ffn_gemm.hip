@@ -138,10 +138,15 @@ struct GemmBufs {
     _Float16 *hshi, *hslo;     // [T][I_shared]
 };
 
-// Stage layout of the LDS ring.  Activation planes: 128 rows x 128 bytes (64 fp16), 16-byte chunk c of
-// row m stored at chunk c ^ (m & 7).  Weights: each wavefront's 64 rows x RB bytes, 16-byte chunk c of
-// row r stored at c ^ ((r >> 2) & 1) (int4, 32-byte rows) or c ^ ((r >> 1) & 3) (int8, 64-byte rows).
-// With these swizzles each group of 8 lanes of a fragment read covers all 32 banks once.
+// Stage layout of the LDS ring.  Activation planes: 128 rows x 128 bytes (64 fp16); weights: each
+// wavefront's 64 rows x RB bytes.  The 16-byte chunks of a row are permuted (XOR with a function of the
+// row) so that the 16 lanes that a 128-bit LDS read serves together (16 consecutive rows, one chunk
+// column) hit 16 different 16-byte slots of the 64 banks.  XOR is its own inverse: the same map takes a
+// logical chunk to its slot and a slot back to the chunk.
+__device__ __forceinline__ int swz_a(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
+__device__ __forceinline__ int swz_b4(int r, int c) { return c ^ ((r >> 3) & 1); }  // 32-byte rows
+__device__ __forceinline__ int swz_b8(int r, int c) { return c ^ ((r >> 2) & 3); }  // 64-byte rows
+
 template <int MODE, int WBITS>
 struct GgCfg {
     static constexpr int NA = MODE == 0 ? 1 : 2;            // activation planes: x, or h hi and lo
@@ -265,8 +270,8 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         W.zd = shared ? P.shared.zd : P.routed.zd;
         const long rbf = (long)KK * WBITS / 8;           // bytes per weight row
 
-        // ---- copy sources.  Activations: this lane moves chunk (lane & 7) ^ (lane >> 3) of row
-        // 8 (2 wv + i) + lane / 8 (i = 0, 1), landing at its swizzled place.
+        // ---- copy sources.  Activations: this lane fills slot lane & 7 of row 8 (2 wv + i) + lane / 8
+        // (i = 0, 1), i.e. it moves the logical chunk that the swizzle puts there.
         rsrc_t ars[NA];
         uint32_t asrc[2];
         {
@@ -277,10 +282,10 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 ars[0] = make_rsrc(shared ? G.hshi : G.hhi, nb);
                 ars[NA - 1] = make_rsrc(shared ? G.hslo : G.hlo, nb);
             }
-            const uint32_t alc = (uint32_t)((lane & 7) ^ (lane >> 3));
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 const int m = 8 * (2 * wv + i) + (lane >> 3);
+                const uint32_t alc = (uint32_t)swz_a(m, lane & 7);
                 uint32_t off = kOOB;
                 if (m < rows) {
                     long row;
@@ -306,10 +311,10 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
             int rl, lc;
             if (WBITS == 4) {
                 rl = 32 * i + (lane >> 1);
-                lc = (lane & 1) ^ ((lane >> 3) & 1);
+                lc = swz_b4(rl, lane & 1);
             } else {
                 rl = 16 * i + (lane >> 2);
-                lc = (lane & 3) ^ ((lane >> 3) & 3);
+                lc = swz_b8(rl, lane & 3);
             }
             const int j = rl >> 5, col = rl & 31;
             const int o = MODE == 0 ? nbase + col : nbase + 32 * j + col;
@@ -351,14 +356,14 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         // ---- LDS read offsets within a stage
         uint32_t ard[4];  // activation fragment of substep s: row lr (+ 32 mm), chunk 4 kg + s
 #pragma unroll
-        for (int s = 0; s < 4; s++) ard[s] = (uint32_t)(lr * 128 + (((4 * kg + s) ^ (lr & 7)) * 16));
+        for (int s = 0; s < 4; s++) ard[s] = (uint32_t)(lr * 128 + swz_a(lr, 4 * kg + s) * 16);
         uint32_t brd[2][WL];  // weight fragment of subtile j: row 32 j + lr of the wavefront, bytes 32 kg ...
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int h = 0; h < WL; h++) {
                 const int rl = 32 * j + lr;
-                const int pc = WBITS == 4 ? (kg ^ ((rl >> 2) & 1)) : ((2 * kg + h) ^ ((rl >> 1) & 3));
+                const int pc = WBITS == 4 ? swz_b4(rl, kg) : swz_b8(rl, 2 * kg + h);
                 brd[j][h] = (uint32_t)(C::A_BYTES + wv * GG_NW * RB + rl * RB + pc * 16);
             }
 
@@ -385,42 +390,61 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 for (int j = 0; j < 2; j++) acc[mm][j] = (f32x16v_t){};
             float rs = 0.f;
 
-#pragma unroll
-            for (int i = 0; i < STAGES - 1; i++) issue(i, i);
-            int stg = 0;
-            for (int step = 0; step < nsteps; step++) {
-                GG_WAIT_VM((STAGES - 2) * NL);  // this wavefront's copies of this step have landed
-                __syncthreads();                // everyone's have; the stage read last step is free
-                issue(step + STAGES - 1, stg == 0 ? STAGES - 1 : stg - 1);
-                const unsigned char *sp = gg_ring + stg * STAGE;
-                uint4 braw[2][WL];
+            // Operand registers: activation fragments of two phases (a phase is substep s of the 4 in a
+            // step and plane pl), dequantised weights of two substeps, the raw weights of a step.
+            constexpr int NPH = 4 * NA;
+            constexpr int NBR = 2 * WL;  // raw weight reads per step
+            uint4 braw[2][WL];
+            h8_t af[2][MU];
+            h8_t bq[2][2];
+            auto rd_b = [&](const unsigned char *p) {
 #pragma unroll
                 for (int j = 0; j < 2; j++)
 #pragma unroll
-                    for (int h = 0; h < WL; h++) braw[j][h] = *(const uint4 *)(sp + brd[j][h]);
+                    for (int h = 0; h < WL; h++) braw[j][h] = *(const uint4 *)(p + brd[j][h]);
+            };
+            auto rd_a = [&](const unsigned char *p, int ph, int buf) {
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    h8_t bq[2];
+                for (int mm = 0; mm < MU; mm++)
+                    af[buf][mm] = *(const h8_t *)(p + (ph % NA) * PLANE + mm * 4096 + ard[ph / NA]);
+            };
+            auto deq = [&](int sub, int buf) {
 #pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        if (WBITS == 4) {
-                            const uint32_t ww[4] = {braw[j][0].x, braw[j][0].y, braw[j][0].z, braw[j][0].w};
-                            bq[j] = deq_int4(ww[s], mlo, mhi, boff[j], boff16[j]);
-                        } else {
-                            const uint4 q = braw[j][s >> 1];
-                            bq[j] = (s & 1) ? deq_int8(q.z, q.w, boff[j]) : deq_int8(q.x, q.y, boff[j]);
-                        }
+                for (int j = 0; j < 2; j++) {
+                    if (WBITS == 4) {
+                        const uint32_t ww[4] = {braw[j][0].x, braw[j][0].y, braw[j][0].z, braw[j][0].w};
+                        bq[buf][j] = deq_int4(ww[sub], mlo, mhi, boff[j], boff16[j]);
+                    } else {
+                        const uint4 q = braw[j][sub >> 1];
+                        bq[buf][j] = (sub & 1) ? deq_int8(q.z, q.w, boff[j]) : deq_int8(q.x, q.y, boff[j]);
                     }
-#pragma unroll
-                    for (int mm = 0; mm < MU; mm++)
-#pragma unroll
-                        for (int pl = 0; pl < NA; pl++) {
-                            const h8_t a = *(const h8_t *)(sp + pl * PLANE + mm * 4096 + ard[s]);
-#pragma unroll
-                            for (int j = 0; j < 2; j++)
-                                acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq[j], acc[mm][j], 0, 0, 0);
-                        }
                 }
+            };
+            auto mfmas = [&](int ph) {
+#pragma unroll
+                for (int mm = 0; mm < MU; mm++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+                        acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ph & 1][mm], bq[(ph / NA) & 1][j],
+                                                                            acc[mm][j], 0, 0, 0);
+            };
+
+            // ---- prologue: STAGES steps in flight, the operands of step 0 in registers
+#pragma unroll
+            for (int i = 0; i < STAGES; i++) issue(i, i);
+            GG_WAIT_VM((STAGES - 1) * NL);
+            __syncthreads();
+            rd_b(gg_ring);
+            rd_a(gg_ring, 0, 0);
+            deq(0, 0);
+
+            // ---- K loop.  Step t's data sit in stage t % STAGES.  The copies of step t + STAGES are issued
+            // into the stage of step t once every wavefront has passed the barrier of step t, which comes
+            // after the last read of that stage (the fragments of the last phase are read one phase ahead).
+            int stg = 0;
+            for (int step = 0; step < nsteps; step++) {
+                const unsigned char *sp = gg_ring + stg * STAGE;
+                const int nstg = stg + 1 == STAGES ? 0 : stg + 1;
                 if (!fold) {
                     // row sums of the staged activations: row tid / 4, chunks 2 (tid % 4) and 2 (tid % 4) + 1
                     const int m = tid >> 2;
@@ -428,13 +452,46 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                     for (int pl = 0; pl < NA; pl++)
 #pragma unroll
                         for (int h = 0; h < 2; h++) {
-                            const int pc = (2 * (tid & 3) + h) ^ (m & 7);
+                            const int pc = swz_a(m, 2 * (tid & 3) + h);
                             const h8_t v = *(const h8_t *)(sp + pl * PLANE + m * 128 + pc * 16);
 #pragma unroll
                             for (int i = 0; i < 8; i++) rs += (float)v[i];
                         }
                 }
-                stg = stg + 1 == STAGES ? 0 : stg + 1;
+                __builtin_amdgcn_sched_barrier(0);
+                // phases but the last: the MFMAs of phase ph run interleaved with the fragment reads of phase
+                // ph + 1 and, when ph + 1 starts a substep, the dequantisation of its weights
+#pragma unroll
+                for (int ph = 0; ph < NPH - 1; ph++) {
+                    rd_a(sp, ph + 1, (ph + 1) & 1);
+                    if ((ph + 1) % NA == 0) deq((ph + 1) / NA, ((ph + 1) / NA) & 1);
+                    mfmas(ph);
+#pragma unroll
+                    for (int i = 0; i < 2 * MU; i++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+                        if (i < MU) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);           // VALU
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // last phase: step + 1 has landed everywhere after the barrier; its operands are read while
+                // the MFMAs of this phase run
+                GG_WAIT_VM((STAGES - 2) * NL);
+                __syncthreads();
+                issue(step + STAGES, stg);
+                const unsigned char *np = gg_ring + nstg * STAGE;
+                rd_b(np);
+                rd_a(np, 0, 0);
+                mfmas(NPH - 1);
+                deq(0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, NBR + MU, 0);  // the reads first
+#pragma unroll
+                for (int i = 0; i < 2 * MU; i++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i >= MU / 2) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                stg = nstg;
             }
             GG_WAIT_VM(0);  // the copies issued past the end land before the ring is reused
             if (!fold) {
