@@ -40,6 +40,8 @@ constexpr int GG_WAVES = 8;        // wavefronts per workgroup, one workgroup pe
 constexpr int GG_K = 64;           // K per pipeline step
 constexpr int GG_NW = 64;          // weight rows per wavefront and tile (two 32-column subtiles)
 constexpr int GG_MAXSLOTS = 1025;
+constexpr int GG_XCDS = 8;         // XCDs of the chip; workgroups are dealt to them round-robin
+constexpr int GG_GROUP = 16;       // consecutive tiles handed to one XCD at a time
 constexpr int GG_RING = 152 * 1024;  // LDS for the staging ring (the rest of the 160 KB holds the tables)
 
 // storage position, within its group of 8, of input i of the group (int4 weights)
@@ -108,7 +110,9 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff) {
 // x (bf16 [T][d]) -> x16 (fp16 [T][d], int4 order within groups of 8).
 template <int WBITS>
 __global__ __launch_bounds__(256) void x16_kernel(const uint16_t *__restrict__ x, _Float16 *__restrict__ x16,
-                                                  long nchunks) {
+                                                  long nchunks, int *__restrict__ tile_ctr) {
+    // the tile queues of the two GEMM launches that follow start empty
+    if (blockIdx.x == 0 && threadIdx.x < 2 * GG_XCDS) tile_ctr[threadIdx.x] = 0;
     for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (long)gridDim.x * 256) {
         const uint4 q = ((const uint4 *)x)[c];
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -136,6 +140,7 @@ struct GemmBufs {
     const _Float16 *x16;       // [T][d]
     _Float16 *hhi, *hlo;       // [A][I]
     _Float16 *hshi, *hslo;     // [T][I_shared]
+    int *tile_ctr;             // [2][GG_XCDS] tile queue counters (zeroed by the x16 pass)
 };
 
 // Stage layout of the LDS ring.  Activation planes: 128 rows x 128 bytes (64 fp16); weights: each
@@ -227,12 +232,30 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
     const int nslot = __builtin_amdgcn_readfirstlane(s_nslot);
     const int ntiles = __builtin_amdgcn_readfirstlane(s_t0[nslot]);
 
-    // Workgroups are dealt round-robin to the 8 XCDs: number them XCD-major so that consecutive tiles
-    // (the row tiles of one weight block) run on the same XCD and share its L2.
-    const int nwg = gridDim.x;
-    const int vwg = nwg % 8 == 0 ? (int)(blockIdx.x % 8) * (nwg / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
-
-    for (int tile = vwg; tile < ntiles; tile += nwg) {
+    // Tile queue.  The tile list (slot-major, then output tile, then row tile: consecutive tiles share
+    // weights or activations) is cut into groups of GG_GROUP tiles, dealt round-robin to the XCDs; each
+    // XCD's workgroups take the tiles of its groups in order from its own counter, so the data that
+    // neighbouring tiles share is read through one L2.  A workgroup whose XCD has run out takes tiles
+    // from the other XCDs' queues.  The next tile is claimed while the current one runs.
+    __shared__ int s_tile[2];
+    int *ctr = G.tile_ctr + MODE * GG_XCDS;
+    const int xcd = (int)(blockIdx.x % GG_XCDS);
+    auto claim = [&]() -> int {
+        for (int k = 0; k < GG_XCDS; k++) {
+            const int xx = (xcd + k) % GG_XCDS;
+            const int c = atomicAdd(ctr + xx, 1);
+            const long t = ((long)(c / GG_GROUP) * GG_XCDS + xx) * GG_GROUP + c % GG_GROUP;
+            if (t < ntiles) return (int)t;
+        }
+        return -1;
+    };
+    if (tid == 0) s_tile[0] = claim();
+    __syncthreads();
+    int tsel = 0;
+    for (int tile = __builtin_amdgcn_readfirstlane(s_tile[0]); tile >= 0;
+         tile = __builtin_amdgcn_readfirstlane(s_tile[tsel])) {
+        if (tid == 0) s_tile[tsel ^ 1] = claim();  // read after the barriers of this tile
+        tsel ^= 1;
         // ---- locate the tile: slot (binary search), output tile, row tile
         int lo = 0, hi = nslot - 1;
         while (lo < hi) {
@@ -556,7 +579,8 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
 static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t gemm_workspace_bytes(const FfnParams &P) {
-    return al256((size_t)P.T * P.d * 2) + 2 * al256((size_t)P.A * P.I * 2) + 2 * al256((size_t)P.T * P.Is * 2);
+    return al256((size_t)P.T * P.d * 2) + 2 * al256((size_t)P.A * P.I * 2) + 2 * al256((size_t)P.T * P.Is * 2) +
+           al256(2 * GG_XCDS * sizeof(int));
 }
 
 bool gemm_supported(const FfnParams &P) {
@@ -597,7 +621,7 @@ static hipError_t gg_launch(const FfnParams &P, const GemmBufs &G, hipStream_t s
     long grid = (nchunks + 255) / 256;
     if (grid > (long)gg_cus() * 8) grid = (long)gg_cus() * 8;
     hipLaunchKernelGGL(x16_kernel<WBITS>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t *)P.x,
-                       (_Float16 *)G.x16, nchunks);
+                       (_Float16 *)G.x16, nchunks, G.tile_ctr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     err = gg_launch_mode<0, WBITS>(P, G, stream);
@@ -618,6 +642,8 @@ hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream) {
     G.hshi = (_Float16 *)p;
     p += al256((size_t)P.T * P.Is * 2);
     G.hslo = (_Float16 *)p;
+    p += al256((size_t)P.T * P.Is * 2);
+    G.tile_ctr = (int *)p;
     return P.wbits == 4 ? gg_launch<4>(P, G, stream) : gg_launch<8>(P, G, stream);
 }
 
