@@ -19,74 +19,118 @@
 
 namespace moe {
 
-constexpr int RL_TT = 64;  // tokens per tile
-constexpr int RL_TE = 64;  // experts per tile
-constexpr int RL_KS = 32;  // d rows per LDS stage
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int RM_TT = 64;           // tokens per workgroup tile
+constexpr int RM_TE = 256;          // experts per workgroup tile (4 wavefronts x 64)
+constexpr int RM_KS = 16;           // d rows per LDS stage
+constexpr int RM_XP = RM_TT + 16;   // LDS row pitch of the activation tile, floats
+constexpr int RM_WP = RM_TE + 16;   // LDS row pitch of the W_r tile, floats
+constexpr int RM_MAXSPLIT = 64;
 
 template <int ACT>
-__device__ __forceinline__ double load_act(const void *x, long i) {
-    if (ACT == 0) return (double)((const float *)x)[i];
-    return (double)bf16_to_f32(((const uint16_t *)x)[i]);
+__device__ __forceinline__ float load_act(const void *x, long i) {
+    if (ACT == 0) return ((const float *)x)[i];
+    return bf16_to_f32(((const uint16_t *)x)[i]);
 }
 
-// grid: (ceil(E/64), ceil(T/64), nsplit); block 256.
-// part[s][t][e] = sum over d rows [s*chunk, min(d,(s+1)*chunk)) of x[t][i]*W_r[i][e]
+// Logits on the fp64 matrix cores (v_mfma_f64_16x16x4f64; lane l holds A[l % 16][l / 16] and
+// B[l / 16][l % 16], and D[4 i + l / 16][l % 16] in register i).  grid: (ceil(E/256), ceil(T/64), nsplit),
+// block 256: wavefront w owns experts 64 w .. 64 w + 63 of the tile for all 64 tokens, as 4 x 4 blocks of
+// 16 x 16.  The d rows [s*chunk, min(d,(s+1)*chunk)) go through a double-buffered LDS stage of 16 rows
+// (fp32: both operands convert to fp64 exactly).  part[s][t][e] = the partial dot product.
 template <int ACT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restrict__ x,
                                                             const float *__restrict__ Wr, int T, int d, int E,
                                                             int chunk, double *__restrict__ part) {
-    __shared__ double xs[RL_KS][RL_TT + 2];
-    __shared__ double wsm[RL_KS][RL_TE + 2];
-    const int tid = threadIdx.x;
-    const int e0 = blockIdx.x * RL_TE, t0 = blockIdx.y * RL_TT;
+    __shared__ float xs[2][RM_KS][RM_XP];  // [stage][row][token]
+    __shared__ float wsm[2][RM_KS][RM_WP]; // [stage][row][expert]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int e0 = blockIdx.x * RM_TE, t0 = blockIdx.y * RM_TT;
     const int i_begin = blockIdx.z * chunk;
     const int i_end = min(d, i_begin + chunk);
-    const int tx = tid & 15, ty = tid >> 4;  // 16 x 16 threads, 4 x 4 outputs each
-    double acc[4][4];
+    const int nsteps = (i_end - i_begin + RM_KS - 1) / RM_KS;
+    // staging map: activations of token tid / 4, rows 4 (tid % 4) .. + 3; W_r row tid / 16, experts
+    // 16 (tid % 16) .. + 15
+    const int xt = tid >> 2, xk = 4 * (tid & 3);
+    const int wk = tid >> 4, we = 16 * (tid & 15);
+    const bool vec4 = (E & 3) == 0;
+    float xr[4], wr[16];
+    auto load = [&](int step) {
+        const int i = i_begin + step * RM_KS;
+        const int t = t0 + xt;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int k = i + xk + u;
+            xr[u] = (t < T && k < i_end) ? load_act<ACT>(x, (long)t * d + k) : 0.f;
+        }
+        const int k = i + wk;
+        const float *row = Wr + (long)k * E + e0 + we;
+        if (vec4 && k < i_end && e0 + we + 16 <= E) {
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const float4 q = ((const float4 *)row)[v];
+                wr[4 * v] = q.x;
+                wr[4 * v + 1] = q.y;
+                wr[4 * v + 2] = q.z;
+                wr[4 * v + 3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; v++) wr[v] = (k < i_end && e0 + we + v < E) ? row[v] : 0.f;
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) xs[buf][xk + u][xt] = xr[u];
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+            *(float4 *)&wsm[buf][wk][we + 4 * v] = make_float4(wr[4 * v], wr[4 * v + 1], wr[4 * v + 2], wr[4 * v + 3]);
+    };
+
+    f64x4_t acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; a++)
 #pragma unroll
-        for (int b = 0; b < 4; b++) acc[a][b] = 0.0;
+        for (int b = 0; b < 4; b++) acc[a][b] = (f64x4_t){0.0, 0.0, 0.0, 0.0};
 
-    for (int i0 = i_begin; i0 < i_end; i0 += RL_KS) {
-        // x tile: RL_TT tokens x RL_KS rows (stored transposed: [k][token])
-        for (int q = tid; q < RL_TT * RL_KS; q += 256) {
-            int tt = q / RL_KS, kk = q % RL_KS;
-            int t = t0 + tt, i = i0 + kk;
-            xs[kk][tt] = (t < T && i < i_end) ? load_act<ACT>(x, (long)t * d + i) : 0.0;
-        }
-        // W tile: RL_KS rows x RL_TE experts
-        for (int q = tid; q < RL_TE * RL_KS; q += 256) {
-            int kk = q / RL_TE, ee = q % RL_TE;
-            int i = i0 + kk, e = e0 + ee;
-            wsm[kk][ee] = (i < i_end && e < E) ? (double)Wr[(long)i * E + e] : 0.0;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < RL_KS; kk++) {
+    const int kr = lane >> 4, cl = lane & 15;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int step = 0; step < nsteps; step++) {
+        const int buf = step & 1;
+        if (step + 1 < nsteps) load(step + 1);
+#pragma unroll
+        for (int q = 0; q < RM_KS / 4; q++) {
             double a[4], b[4];
 #pragma unroll
-            for (int u = 0; u < 4; u++) a[u] = xs[kk][ty * 4 + u];
+            for (int tb = 0; tb < 4; tb++) a[tb] = (double)xs[buf][4 * q + kr][16 * tb + cl];
 #pragma unroll
-            for (int u = 0; u < 4; u++) b[u] = wsm[kk][tx * 4 + u];
+            for (int eb = 0; eb < 4; eb++) b[eb] = (double)wsm[buf][4 * q + kr][64 * wv + 16 * eb + cl];
 #pragma unroll
-            for (int u = 0; u < 4; u++)
+            for (int tb = 0; tb < 4; tb++)
 #pragma unroll
-                for (int v = 0; v < 4; v++) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+                for (int eb = 0; eb < 4; eb++)
+                    acc[tb][eb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[tb], b[eb], acc[tb][eb], 0, 0, 0);
         }
+        if (step + 1 < nsteps) store(buf ^ 1);
         __syncthreads();
     }
     double *out = part + (long)blockIdx.z * T * E;
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-        int t = t0 + ty * 4 + u;
-        if (t >= T) continue;
+    for (int tb = 0; tb < 4; tb++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            int e = e0 + tx * 4 + v;
-            if (e < E) out[(long)t * E + e] = acc[u][v];
+        for (int i = 0; i < 4; i++) {
+            const int t = t0 + 16 * tb + 4 * i + kr;
+            if (t >= T) continue;
+#pragma unroll
+            for (int eb = 0; eb < 4; eb++) {
+                const int e = e0 + 64 * wv + 16 * eb + cl;
+                if (e < E) out[(long)t * E + e] = acc[tb][eb][i];
+            }
         }
-    }
 }
 
 // Small-T logits: 1024-thread workgroups each stream a block of W_r rows once for all T <= RS_TMAX
@@ -336,12 +380,15 @@ int router_nsplit(int T, int d, int E) {
         const int rows = skinny_rows(d, E);
         return (d + rows - 1) / rows;
     }
-    int gx = (E + RL_TE - 1) / RL_TE, gy = (T + RL_TT - 1) / RL_TT;
-    int ksteps = (d + RL_KS - 1) / RL_KS;
-    int want = 512 / (gx * gy);
+    // about two workgroups per CU, at least 4 stages of rows per split
+    const int gx = (E + RM_TE - 1) / RM_TE, gy = (T + RM_TT - 1) / RM_TT;
+    const int ksteps = (d + RM_KS - 1) / RM_KS;
+    int want = (512 + gx * gy - 1) / (gx * gy);
+    if (want > ksteps / 4) want = ksteps / 4;
+    if (want > RM_MAXSPLIT) want = RM_MAXSPLIT;
     if (want < 1) want = 1;
-    if (want > ksteps) want = ksteps;
-    return want;
+    const int chunk = ((ksteps + want - 1) / want) * RM_KS;
+    return (d + chunk - 1) / chunk;
 }
 
 size_t router_workspace_bytes(int T, int d, int E) {
@@ -363,10 +410,8 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
                                d, E, rows, part);
     } else {
         nsplit = router_nsplit(T, d, E);
-        int ksteps = (d + RL_KS - 1) / RL_KS;
-        int chunk = ((ksteps + nsplit - 1) / nsplit) * RL_KS;
-        nsplit = (d + chunk - 1) / chunk;
-        dim3 grid((E + RL_TE - 1) / RL_TE, (T + RL_TT - 1) / RL_TT, nsplit);
+        const int chunk = (((d + RM_KS - 1) / RM_KS + nsplit - 1) / nsplit) * RM_KS;
+        dim3 grid((E + RM_TE - 1) / RM_TE, (T + RM_TT - 1) / RM_TT, nsplit);
         if (act == 0)
             hipLaunchKernelGGL(router_logits_kernel<0>, grid, dim3(256), 0, stream, x, Wr, T, d, E, chunk, part);
         else
