@@ -130,6 +130,25 @@ def test_gemm_path_parity(orc, dev, case):
     run_full_case(orc, dev, spec_of(**kw), T, path=B.MOE_PATH_GEMM, label=case)
 
 
+def _fractional_zero_points(inp):
+    """Non-integral int4 zero points on the even experts and the shared expert (the odd experts keep integral
+    ones): the GEMM path then mixes tiles that fold z into the dequantisation with tiles that subtract z times
+    the activation row sums."""
+    for s, every in ((inp.routed, 2), (inp.shared, 1)):
+        if s is None:
+            continue
+        for name in ("z_gate", "z_up", "z_down"):
+            z = getattr(s, name)
+            z[::every] += np.float32(0.37)
+
+
+@pytest.mark.parametrize("case,path", [("gemm_int4_shared", B.MOE_PATH_GEMM), ("gemm_int4_row_tiles", B.MOE_PATH_GEMM),
+                                       ("gemm_int4_shared_wider", B.MOE_PATH_GEMV)])
+def test_fractional_int4_zero_points(orc, dev, case, path):
+    kw, T = GEMM[case]
+    run_full_case(orc, dev, spec_of(**kw), T, path=path, tweak=_fractional_zero_points, label=case + "_frac_zp")
+
+
 def test_all_tie_router(orc, dev):
     """W_r = 0 and b = 0: every selection score is 0.5; ids 0..k-1 win with w = lambda/k."""
     spec = spec_of(d=256, E=8, k=3, I=64, routed_scale=2.5)
