@@ -11,21 +11,26 @@
 // 3.4): w = s (q - z).  They enter the MFMA as fp16 values of q, exact for int8 and int4, dequantised in
 // registers from the packed bytes; the zero point is applied once per output through the row sum of the
 // activations, and the scale in the epilogue.  Activations: x is bf16 and is converted once to fp16
-// (exact save for magnitudes below 2^-14); h enters the down GEMM as fp16 hi + lo planes (two MFMAs into
-// one accumulator, about 22 significant bits: a single fp16 rounding of h moves the largest down outputs
-// by up to 3e-3 of their RMS).  Accumulation is fp32.
+// (exact save for magnitudes below 2^-14).  h enters the down GEMM as an fp16 plane plus the residual
+// h - fp16(h) in e4m3 under one E8M0 exponent per row and 32 channels (the block form of the scaled
+// matrix-core product), about 16 significant bits in all: a single fp16 rounding of h would move the
+// largest down outputs by up to 3e-3 of their RMS.  The residual product is one scaled e4m3 MFMA per K
+// step and 32x32 block, half the matrix-core time of the fp16 plane's four; its weights are the same
+// dequantised values in e4m3 (exact for int4, 4 significant bits for larger int8 values, which the
+// residual's own 4 bits already bound).  Accumulation is fp32.
 //
-// Layout of the activation planes (x16, h hi/lo): row-major, and for int4 weights the 8 inputs of each
-// group are stored in the order 0,4,1,5,2,6,3,7, the order in which the nibble dequantisation below
-// produces the weights.
+// Layout of the activation planes (x16, h and its residual): row-major, and for int4 weights the 8
+// inputs of each group are stored in the order 0,4,1,5,2,6,3,7, the order in which the nibble
+// dequantisation below produces the weights.  Residual exponents: per row tile (over all slots) and K
+// step, 256 bytes [block][row % 32][row / 32], the order in which one 32-bit LDS read gives a lane the
+// exponents of its four row blocks.
 //
 // Tiles: 128 rows; 8 wavefronts as 2 (rows) x 4 (columns), each 64 rows x 2 subtiles of 32 columns.
 // Gate/up pairs the gate and up rows of the same 32 channels in one wavefront (128 channels per tile),
 // down takes 64 outputs per wavefront (256 per tile).  A persistent grid (one workgroup per CU) walks
 // the tiles (slot-major, then output tile, then row tile) from a table built on the device from
-// n_uniq / uniq / offsets, so one launch shape
-// serves every routing.  Activations go through registers to LDS and weights to registers, both two
-// K steps ahead.
+// n_uniq / uniq / offsets, so one launch shape serves every routing.  Activations and weights are
+// copied from memory straight into an LDS ring of 2-4 K steps.
 #include "common.h"
 #include "kernels.h"
 
@@ -79,6 +84,45 @@ __device__ __forceinline__ h8_t deq_int8(uint32_t w0, uint32_t w1, h2_t off) {
     const h2_t p2 = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) + off;
     const h2_t p3 = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) + off;
     return (h8_t){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+typedef int i4v_t __attribute__((ext_vector_type(4)));
+typedef int i8v_t __attribute__((ext_vector_type(8)));
+typedef short s2_t __attribute__((ext_vector_type(2)));
+
+// e4m3 bytes of eight fp16 values, in order, as two words (round to nearest even; integers up to 16 in
+// magnitude are exact, larger ones up to 448 keep 4 significant bits)
+__device__ __forceinline__ void fp8x8(h8_t v, int &d0, int &d1) {
+    s2_t w0 = {0, 0}, w1 = {0, 0};
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w0, (h2_t){v[0], v[1]}, 1.f, false);
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w0, (h2_t){v[2], v[3]}, 1.f, true);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w1, (h2_t){v[4], v[5]}, 1.f, false);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w1, (h2_t){v[6], v[7]}, 1.f, true);
+    d0 = __builtin_bit_cast(int, w0);
+    d1 = __builtin_bit_cast(int, w1);
+}
+
+// maximum of each v[i] over the 32 lanes of each half of the wavefront (row-local DPP steps: neighbours,
+// pairs, mirrored halves of 8 and of 16 lanes; then the other 16 lanes through a swizzle within 32).  The
+// four reductions advance together, so each DPP read finds its operand written a few instructions back.
+__device__ __forceinline__ void max_half_wave4(uint32_t (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0xB1, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0x4E, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0x141, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0x140, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_ds_swizzle((int)v[i], 0x401F));
+}
+
+// one scaled e4m3 x e4m3 product of a 32x32x64 block: A scaled per row and 32-long K block by byte OPS of
+// sa (an E8M0 exponent), B unscaled
+template <int OPS>
+__device__ __forceinline__ f32x16v_t mfma_lo(i8v_t a, i8v_t b, f32x16v_t c, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPS, sa, 0, 127);
 }
 
 __device__ __forceinline__ float gg_zp(const void *z, int wbits, long i) {
@@ -138,8 +182,13 @@ struct GgInt {
 
 struct GemmBufs {
     const _Float16 *x16;       // [T][d]
-    _Float16 *hhi, *hlo;       // [A][I]
-    _Float16 *hshi, *hslo;     // [T][I_shared]
+    _Float16 *hhi;             // [A][I] h rounded to fp16
+    uint8_t *hlo;              // [A][I] its residual h - hi, e4m3 under the block exponents of hsc
+    _Float16 *hshi;            // [T][I_shared], the same for the shared expert
+    uint8_t *hslo;
+    uint8_t *hsc;              // residual exponents (E8M0): [row tile][K step][block 2][row 32][row block 4]
+    uint32_t hsc_bytes;
+    int ksmax;                 // K steps per row tile in hsc
     int *tile_ctr;             // [2][GG_XCDS] tile queue counters (zeroed by the x16 pass)
 };
 
@@ -154,16 +203,18 @@ __device__ __forceinline__ int swz_b8(int r, int c) { return c ^ ((r >> 2) & 3);
 
 template <int MODE, int WBITS>
 struct GgCfg {
-    static constexpr int NA = MODE == 0 ? 1 : 2;            // activation planes: x, or h hi and lo
+    static constexpr bool LO8 = MODE == 1;                  // h residual plane (e4m3 + block exponents)
     static constexpr int RB = GG_K * WBITS / 8;             // weight bytes per row and step
-    static constexpr int PLANE = GG_M * GG_K * 2;           // bytes per activation plane
-    static constexpr int A_BYTES = NA * PLANE;
+    static constexpr int PLANE = GG_M * GG_K * 2;           // bytes of the fp16 activation plane (x or h hi)
+    static constexpr int LO_BYTES = LO8 ? GG_M * GG_K : 0;  // residual plane: 128 rows x 64 bytes
+    static constexpr int SC_BYTES = LO8 ? 1024 : 0;         // its 256 exponent bytes, in a 1 KB copy
+    static constexpr int A_BYTES = PLANE + LO_BYTES + SC_BYTES;
     static constexpr int B_BYTES = GG_WAVES * GG_NW * RB;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int STAGES = GG_RING / STAGE > 4 ? 4 : GG_RING / STAGE;
-    static constexpr int NLA = 2;                           // 1 KB copies per wavefront, plane and step
+    static constexpr int NLA = 2;                           // 1 KB copies per wavefront and step, fp16 plane
     static constexpr int NLB = GG_NW * RB / 1024;           // 1 KB weight copies per wavefront and step
-    static constexpr int NL = NA * NLA + NLB;
+    static constexpr int NL = NLA + (LO8 ? 1 : 0) + NLB;    // wavefront 0 also copies the exponents
     static constexpr int NOUT_W = MODE == 0 ? 32 : 64;      // distinct output columns per wavefront
     static constexpr int NOUT_G = NOUT_W * GG_WAVES;        // per tile
     static_assert(STAGES >= 2, "LDS ring");
@@ -171,8 +222,10 @@ struct GgCfg {
 };
 
 // MODE 0: gate/up (A = x16 rows through the permutation; each wavefront owns 32 channels, subtile 0 their
-// gate rows and subtile 1 their up rows; output h as fp16 hi/lo planes).  MODE 1: down (A = h hi/lo rows
-// of the slot; 64 down rows per wavefront; output y_perm / y_shared in fp32).
+// gate rows and subtile 1 their up rows; output h as an fp16 plane plus the e4m3 residual plane and its
+// exponents).  MODE 1: down (A = the h planes of the slot's rows; 64 down rows per wavefront; output
+// y_perm / y_shared in fp32).  Its K step is four fp16 MFMAs on h hi and one scaled e4m3 MFMA on the
+// residual, whose weights are the same dequantised values converted to e4m3.
 //
 // Zero points: when every zero point of the tile's weight rows is an integer (int8 always; int4 when
 // its fp32 zero points are integral), it is folded into the dequantisation (B = q - z, exact in fp16);
@@ -181,7 +234,8 @@ struct GgCfg {
 template <int MODE, int WBITS>
 __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBufs G, int tiles_n) {
     using C = GgCfg<MODE, WBITS>;
-    constexpr int NA = C::NA, RB = C::RB, PLANE = C::PLANE, STAGE = C::STAGE, STAGES = C::STAGES;
+    constexpr bool LO8 = C::LO8;
+    constexpr int RB = C::RB, PLANE = C::PLANE, STAGE = C::STAGE, STAGES = C::STAGES;
     constexpr int NLB = C::NLB, NL = C::NL;
     constexpr int WL = WBITS == 8 ? 2 : 1;   // 16-byte weight fragments per subtile and step
     constexpr float QBIAS = WBITS == 8 ? 1152.f : 1024.f;
@@ -275,6 +329,9 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         const int ntile = local / mt_n, mtile = local % mt_n;
         const int r0 = mtile * GG_M;                     // first row of the tile within the slot
         const int rows = min(GG_M, cnt - r0);
+        // row tile number over all slots (the same in both passes: the prefix counts row tiles times
+        // tiles_n); it indexes the residual exponents
+        const int rt = __builtin_amdgcn_readfirstlane(s_t0[slot]) / tiles_n + mtile;
         const int I = shared ? P.Is : P.I;
         const int KK = MODE == 0 ? P.d : I;              // contraction length
         const int nout = MODE == 0 ? I : P.d;
@@ -293,17 +350,24 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         W.zd = shared ? P.shared.zd : P.routed.zd;
         const long rbf = (long)KK * WBITS / 8;           // bytes per weight row
 
-        // ---- copy sources.  Activations: this lane fills slot lane & 7 of row 8 (2 wv + i) + lane / 8
-        // (i = 0, 1), i.e. it moves the logical chunk that the swizzle puts there.
-        rsrc_t ars[NA];
-        uint32_t asrc[2];
+        // ---- copy sources.  fp16 activations: this lane fills slot lane & 7 of row 8 (2 wv + i) + lane / 8
+        // (i = 0, 1), i.e. it moves the logical chunk that the swizzle puts there.  Residual plane: slot
+        // lane & 3 of row 16 wv + lane / 4.  Exponents (wavefront 0): lanes 0..15 copy the 256 bytes of the
+        // step, the other lanes' out-of-range copies fill the rest of the 1 KB with zeros.
+        rsrc_t ars, alrs, scrs;
+        uint32_t asrc[2], alsrc = kOOB, scsrc = kOOB;
         {
             if (MODE == 0) {
-                ars[0] = make_rsrc(G.x16, (uint32_t)((long)P.T * P.d * 2));
+                ars = make_rsrc(G.x16, (uint32_t)((long)P.T * P.d * 2));
+                alrs = scrs = ars;  // unused
             } else {
-                const uint32_t nb = (uint32_t)((long)(shared ? P.T : P.A) * I * 2);
-                ars[0] = make_rsrc(shared ? G.hshi : G.hhi, nb);
-                ars[NA - 1] = make_rsrc(shared ? G.hslo : G.hlo, nb);
+                const long nr = shared ? P.T : P.A;
+                ars = make_rsrc(shared ? G.hshi : G.hhi, (uint32_t)(nr * I * 2));
+                alrs = make_rsrc(shared ? G.hslo : G.hlo, (uint32_t)(nr * I));
+                scrs = make_rsrc(G.hsc, G.hsc_bytes);
+                const int m = 16 * wv + (lane >> 2);
+                if (m < rows) alsrc = (uint32_t)(((long)(shared ? 0 : p0) + r0 + m) * I) + 16 * swz_b8(m, lane & 3);
+                if (lane < 16) scsrc = (uint32_t)rt * (uint32_t)G.ksmax * 256u + 16 * lane;
             }
 #pragma unroll
             for (int i = 0; i < 2; i++) {
@@ -361,9 +425,10 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 zp[j] = gg_zp(W.zd, WBITS, ch);
             }
         }
+        // (|z| <= 256 keeps the folded int8 weights q - z inside the e4m3 range of the residual product)
         bool my_int = true;
 #pragma unroll
-        for (int j = 0; j < 2; j++) my_int = my_int && zp[j] == rintf(zp[j]) && fabsf(zp[j]) <= 512.f;
+        for (int j = 0; j < 2; j++) my_int = my_int && zp[j] == rintf(zp[j]) && fabsf(zp[j]) <= 256.f;
         const bool fold = __syncthreads_and(my_int);  // uniform over the workgroup
         h2_t boff[2], boff16[2];
 #pragma unroll
@@ -380,6 +445,12 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         uint32_t ard[4];  // activation fragment of substep s: row lr (+ 32 mm), chunk 4 kg + s
 #pragma unroll
         for (int s = 0; s < 4; s++) ard[s] = (uint32_t)(lr * 128 + swz_a(lr, 4 * kg + s) * 16);
+        // residual fragment: row lr (+ 32 mm), chunks kg and 2 + kg (inputs 16 kg.. and 32 + 16 kg..); the
+        // exponent word of row block kg, rows lr + 32 mm in byte mm
+        uint32_t ald[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) ald[h] = (uint32_t)(PLANE + lr * 64 + swz_b8(lr, 2 * h + kg) * 16);
+        const uint32_t scd = (uint32_t)(PLANE + C::LO_BYTES + kg * 128 + lr * 4);
         uint32_t brd[2][WL];  // weight fragment of subtile j: row 32 j + lr of the wavefront, bytes 32 kg ...
 #pragma unroll
         for (int j = 0; j < 2; j++)
@@ -393,10 +464,11 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         auto issue = [&](int step, int stg) {
             const uint32_t sb = ring0 + (uint32_t)(stg * STAGE);
 #pragma unroll
-            for (int pl = 0; pl < NA; pl++)
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-                    dma16(ars[pl], sb + pl * PLANE + (2 * wv + i) * 1024, asrc[i] + (uint32_t)(step * 128));
+            for (int i = 0; i < 2; i++) dma16(ars, sb + (2 * wv + i) * 1024, asrc[i] + (uint32_t)(step * 128));
+            if constexpr (LO8) {
+                dma16(alrs, sb + PLANE + wv * 1024, alsrc + (uint32_t)(step * 64));
+                if (wv == 0) dma16(scrs, sb + PLANE + C::LO_BYTES, scsrc + (uint32_t)(step * 256));
+            }
 #pragma unroll
             for (int i = 0; i < NLB; i++)
                 dma16(brs[WBITS == 4 ? i : i >> 1],
@@ -413,23 +485,24 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 for (int j = 0; j < 2; j++) acc[mm][j] = (f32x16v_t){};
             float rs = 0.f;
 
-            // Operand registers: activation fragments of two phases (a phase is substep s of the 4 in a
-            // step and plane pl), dequantised weights of two substeps, the raw weights of a step.
-            constexpr int NPH = 4 * NA;
+            // Operand registers: activation fragments of two substeps, dequantised weights of two substeps,
+            // the raw weights of a step; with the residual plane, its fragments, its exponent word and the
+            // e4m3 weights of the whole step.
             constexpr int NBR = 2 * WL;  // raw weight reads per step
             uint4 braw[2][WL];
             h8_t af[2][MU];
             h8_t bq[2][2];
+            i8v_t al[MU], bl[2];
+            int scw = 0;
             auto rd_b = [&](const unsigned char *p) {
 #pragma unroll
                 for (int j = 0; j < 2; j++)
 #pragma unroll
                     for (int h = 0; h < WL; h++) braw[j][h] = *(const uint4 *)(p + brd[j][h]);
             };
-            auto rd_a = [&](const unsigned char *p, int ph, int buf) {
+            auto rd_a = [&](const unsigned char *p, int sub, int buf) {
 #pragma unroll
-                for (int mm = 0; mm < MU; mm++)
-                    af[buf][mm] = *(const h8_t *)(p + (ph % NA) * PLANE + mm * 4096 + ard[ph / NA]);
+                for (int mm = 0; mm < MU; mm++) af[buf][mm] = *(const h8_t *)(p + mm * 4096 + ard[sub]);
             };
             auto deq = [&](int sub, int buf) {
 #pragma unroll
@@ -443,19 +516,69 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                     }
                 }
             };
-            auto mfmas = [&](int ph) {
+            auto mfmas = [&](int sub) {
 #pragma unroll
                 for (int mm = 0; mm < MU; mm++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
-                        acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ph & 1][mm], bq[(ph / NA) & 1][j],
+                        acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[sub & 1][mm], bq[sub & 1][j],
                                                                             acc[mm][j], 0, 0, 0);
+            };
+            // Residual product.  Lane half kg dequantises inputs 32 kg + 8 s .. + 7 in substep s; as e4m3 they
+            // fill words 2 s, 2 s + 1 of bl, i.e. the lane holds inputs 32 kg .. 32 kg + 31 in order.  The
+            // scaled MFMA wants inputs 16 kg .. + 15 in words 0-3 and 32 + 16 kg .. + 15 in words 4-7, the same
+            // order as the residual fragments: words 4-7 of the low half and words 0-3 of the high half trade
+            // places (one 32-lane swap per word pair).
+            auto cvt = [&](int sub, int buf) {
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    int d0, d1;
+                    fp8x8(bq[buf][j], d0, d1);
+                    bl[j][2 * sub] = d0;
+                    bl[j][2 * sub + 1] = d1;
+                }
+            };
+            auto swap_halves = [&]() {
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)bl[j][i], (uint32_t)bl[j][i + 4], false, false);
+                        bl[j][i] = (int)r[0];
+                        bl[j][i + 4] = (int)r[1];
+                    }
+            };
+            auto rd_lo = [&](const unsigned char *p) {
+#pragma unroll
+                for (int mm = 0; mm < MU; mm++) {
+                    const i4v_t u0 = *(const i4v_t *)(p + mm * 2048 + ald[0]);
+                    const i4v_t u1 = *(const i4v_t *)(p + mm * 2048 + ald[1]);
+                    al[mm] = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+                scw = *(const int *)(p + scd);
+            };
+            auto mfmas_lo = [&]() {
+#pragma unroll
+                for (int mm = 0; mm < MU; mm++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        if (mm == 0) acc[mm][j] = mfma_lo<0>(al[mm], bl[j], acc[mm][j], scw);
+                        else if (mm == 1) acc[mm][j] = mfma_lo<1>(al[mm], bl[j], acc[mm][j], scw);
+                        else if (mm == 2) acc[mm][j] = mfma_lo<2>(al[mm], bl[j], acc[mm][j], scw);
+                        else acc[mm][j] = mfma_lo<3>(al[mm], bl[j], acc[mm][j], scw);
+                    }
+            };
+            // wavefront 0 has one copy more per step (the exponents)
+            auto wait_steps = [&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                if (LO8 && wv == 0) GG_WAIT_VM(n * (NL + 1));
+                else GG_WAIT_VM(n * NL);
             };
 
             // ---- prologue: STAGES steps in flight, the operands of step 0 in registers
 #pragma unroll
             for (int i = 0; i < STAGES; i++) issue(i, i);
-            GG_WAIT_VM((STAGES - 1) * NL);
+            wait_steps(GgInt<STAGES - 1>{});
             __syncthreads();
             rd_b(gg_ring);
             rd_a(gg_ring, 0, 0);
@@ -469,55 +592,100 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 const unsigned char *sp = gg_ring + stg * STAGE;
                 const int nstg = stg + 1 == STAGES ? 0 : stg + 1;
                 if (!fold) {
-                    // row sums of the staged activations: row tid / 4, chunks 2 (tid % 4) and 2 (tid % 4) + 1
+                    // row sums of the staged activations: row tid / 4, fp16 chunks 2 (tid % 4) and
+                    // 2 (tid % 4) + 1, residual chunk tid % 4 (times its block exponent)
                     const int m = tid >> 2;
 #pragma unroll
-                    for (int pl = 0; pl < NA; pl++)
+                    for (int h = 0; h < 2; h++) {
+                        const int pc = swz_a(m, 2 * (tid & 3) + h);
+                        const h8_t v = *(const h8_t *)(sp + m * 128 + pc * 16);
 #pragma unroll
-                        for (int h = 0; h < 2; h++) {
-                            const int pc = swz_a(m, 2 * (tid & 3) + h);
-                            const h8_t v = *(const h8_t *)(sp + pl * PLANE + m * 128 + pc * 16);
+                        for (int i = 0; i < 8; i++) rs += (float)v[i];
+                    }
+                    if constexpr (LO8) {
+                        const int q = tid & 3;
+                        const uint4 v = *(const uint4 *)(sp + PLANE + m * 64 + swz_b8(m, q) * 16);
+                        const int ex = sp[PLANE + C::LO_BYTES + (q >> 1) * 128 + (m & 31) * 4 + (m >> 5)];
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                        float t = 0.f;
 #pragma unroll
-                            for (int i = 0; i < 8; i++) rs += (float)v[i];
-                        }
+                        for (int i = 0; i < 4; i++)
+                            t += (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 0) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1)) +
+                                 (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 2) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3));
+                        rs += __builtin_ldexpf(t, ex - 127);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // phases but the last: the MFMAs of phase ph run interleaved with the fragment reads of phase
-                // ph + 1 and, when ph + 1 starts a substep, the dequantisation of its weights
+                // substeps but the last: the MFMAs of substep s run interleaved with the fragment reads and
+                // the dequantisation of substep s + 1 (and the e4m3 conversion of substep s)
 #pragma unroll
-                for (int ph = 0; ph < NPH - 1; ph++) {
+                for (int ph = 0; ph < 3; ph++) {
                     rd_a(sp, ph + 1, (ph + 1) & 1);
-                    if ((ph + 1) % NA == 0) deq((ph + 1) / NA, ((ph + 1) / NA) & 1);
+                    deq(ph + 1, (ph + 1) & 1);
+                    if constexpr (LO8) cvt(ph, ph & 1);
                     mfmas(ph);
 #pragma unroll
                     for (int i = 0; i < 2 * MU; i++) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
                         if (i < MU) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);           // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x002, LO8 ? 4 : 3, 0);  // VALU
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                // last phase: step + 1 has landed everywhere after the barrier; its operands are read while
-                // the MFMAs of this phase run
-                GG_WAIT_VM((STAGES - 2) * NL);
-                __syncthreads();
-                issue(step + STAGES, stg);
-                const unsigned char *np = gg_ring + nstg * STAGE;
-                rd_b(np);
-                rd_a(np, 0, 0);
-                mfmas(NPH - 1);
-                deq(0, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, NBR + MU, 0);  // the reads first
+                if constexpr (LO8) {
+                    // substep 3 (with the reads of the residual fragments), then the residual product: its
+                    // e4m3 weights are complete once substep 3 is converted; step + 1 has landed everywhere
+                    // after the barrier, and its operands are read while the residual MFMAs run
+                    rd_lo(sp);
+                    cvt(3, 1);
+                    swap_halves();
+                    mfmas(3);
 #pragma unroll
-                for (int i = 0; i < 2 * MU; i++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i >= MU / 2) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                    for (int i = 0; i < 2 * MU; i++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (i < MU) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_steps(GgInt<STAGES - 2>{});
+                    __syncthreads();
+                    issue(step + STAGES, stg);
+                    const unsigned char *np = gg_ring + nstg * STAGE;
+                    rd_b(np);
+                    rd_a(np, 0, 0);
+                    mfmas_lo();
+                    deq(0, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NBR + MU, 0);  // the reads first
+#pragma unroll
+                    for (int i = 0; i < 2 * MU; i++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (i >= MU / 2) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+                    // last substep: step + 1 has landed everywhere after the barrier; its operands are read
+                    // while the MFMAs of this substep run
+                    wait_steps(GgInt<STAGES - 2>{});
+                    __syncthreads();
+                    issue(step + STAGES, stg);
+                    const unsigned char *np = gg_ring + nstg * STAGE;
+                    rd_b(np);
+                    rd_a(np, 0, 0);
+                    mfmas(3);
+                    deq(0, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NBR + MU, 0);  // the reads first
+#pragma unroll
+                    for (int i = 0; i < 2 * MU; i++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (i >= MU / 2) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
                 stg = nstg;
             }
             GG_WAIT_VM(0);  // the copies issued past the end land before the ring is reused
-            if (!fold) {
+            {
+                // row sums (zeros when the zero points are folded: the epilogue reads them either way)
                 float t = rs;
                 t += __shfl_xor(t, 1, 64);
                 t += __shfl_xor(t, 2, 64);
@@ -528,38 +696,84 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
             // ---- epilogue: lane column ocol[j]; register r holds row 8 (r / 4) + 4 kg + r % 4 of block mm.
             // The lane's row offset is made opaque here so that the compiler does not hoist the 64 row
             // indices that derive from it out of the tile loop (they would occupy registers throughout).
+            // Stores go through buffer descriptors based at the tile's first row and ending after its last,
+            // so rows past the tile fall out of range, as do columns past the output (their offsets are
+            // made out of range): the bounds check drops them, with no branch around the stores.
             int mk = 4 * kg;
             asm volatile("" : "+v"(mk));
+            const long prow0 = (long)(shared ? 0 : p0) + r0;  // output row of tile row 0
+            float zpe[2];  // zero point still to apply (0 when folded)
 #pragma unroll
-            for (int mm = 0; mm < MU; mm++) {
+            for (int j = 0; j < 2; j++) zpe[j] = fold ? 0.f : zp[j];
+            // tile row of register r of block mm: the lane part mk plus a uniform part
+            auto mrow = [](int mm, int r) { return mm * 32 + 8 * (r >> 2) + (r & 3); };
+            if constexpr (MODE == 0) {
+                const int c = ocol[0];
+                // stored at the planes' position of channel c (int4 order within groups of 8)
+                const uint32_t hp = (uint32_t)(WBITS == 4 ? ((c & ~7) | pos8(c & 7)) : c);
+                const uint32_t o2 = c < nout ? 2 * hp : kOOB, o1 = c < nout ? hp : kOOB;
+                const rsrc_t hhr = make_rsrc((shared ? G.hshi : G.hhi) + prow0 * I, (uint32_t)(rows * I * 2));
+                const rsrc_t hlr = make_rsrc((shared ? G.hslo : G.hlo) + prow0 * I, (uint32_t)(rows * I));
+                // the 32 channels of this wavefront form one residual block of K step nbase / 64 of the down
+                // pass (block (nbase / 32) % 2); lane lr = 0 of each half stores the exponents of its rows
+                const long scbase = ((long)rt * G.ksmax + (nbase >> 6)) * 256 + ((nbase >> 5) & 1) * 128;
+                const rsrc_t hsr = make_rsrc(G.hsc + scbase, 128);
+                const uint32_t os = (lr == 0 && nbase < nout) ? 0u : kOOB;
+                const uint32_t mkI = (uint32_t)mk * (uint32_t)I;
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int m = mm * 32 + 8 * (r >> 2) + mk + (r & 3);
-                    if (m >= rows) continue;
-                    const float xs = fold ? 0.f : rsum[m];
-                    const long prow = (long)(shared ? 0 : p0) + r0 + m;  // output row
-                    if (MODE == 0) {
-                        const int c = ocol[0];
-                        if (c < nout) {
-                            const float gv = sc[0] * (acc[mm][0][r] - (fold ? 0.f : zp[0]) * xs);
-                            const float uv = sc[1] * (acc[mm][1][r] - (fold ? 0.f : zp[1]) * xs);
+                for (int mm = 0; mm < MU; mm++) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 16; r4 += 4) {  // four consecutive rows at a time
+                        _Float16 h_hi[4];
+                        float lo[4];
+                        uint32_t lb[4];
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int r = r4 + i, m = mrow(mm, r) + mk;
+                            const float xs = rsum[m];
+                            const float gv = sc[0] * (acc[mm][0][r] - zpe[0] * xs);
+                            const float uv = sc[1] * (acc[mm][1][r] - zpe[1] * xs);
                             // silu through the hardware exp2 and reciprocal (relative error ~1e-6, below the
-                            // 22 bits that h keeps)
+                            // precision that h keeps)
                             const float hv = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * gv)) * uv;
-                            const _Float16 h_hi = (_Float16)hv;
-                            const _Float16 h_lo = (_Float16)(hv - (float)h_hi);
-                            // stored at the planes' position of channel c (int4 order within groups of 8)
-                            const int hp = WBITS == 4 ? ((c & ~7) | pos8(c & 7)) : c;
-                            (shared ? G.hshi : G.hhi)[prow * I + hp] = h_hi;
-                            (shared ? G.hslo : G.hlo)[prow * I + hp] = h_lo;
+                            h_hi[i] = (_Float16)hv;
+                            lo[i] = hv - (float)h_hi[i];
+                            // rows past the tile contribute zeros to the block maximum
+                            lb[i] = (c < nout && m < rows) ? (__builtin_bit_cast(uint32_t, lo[i]) & 0x7FFFFFFFu) : 0u;
                         }
-                    } else {
+                        // block exponent (every lane of a half-wavefront holds the same row): the largest
+                        // residual of the block scaled into [128, 256), e4m3 values below 448; S is the
+                        // E8M0 byte of the inverse scaling
+                        max_half_wave4(lb);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int r = r4 + i, m = mrow(mm, r) + mk;
+                            const int S = max((int)(lb[i] >> 23) - 7, 0);
+                            const float mult = __builtin_bit_cast(float, (uint32_t)(254 - S) << 23);
+                            const int q8 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[i] * mult, 0.f, 0, false);
+                            const uint32_t mo = mkI + (uint32_t)mrow(mm, r) * (uint32_t)I;
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h_hi[i]), hhr, (int)(2 * mo + o2), 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)q8, hlr, (int)(mo + o1), 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)S, hsr, (int)((m & 31) * 4 + (m >> 5) + os), 0, 0);
+                        }
+                    }
+                }
+            } else {
+                const rsrc_t yr = make_rsrc((shared ? P.y_sh : P.y_perm) + prow0 * P.d, (uint32_t)(rows * P.d * 4));
+                uint32_t yo[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++) yo[j] = ocol[j] < nout ? 4 * (uint32_t)ocol[j] : kOOB;
+                const uint32_t rowb = 4 * (uint32_t)P.d, mkd = (uint32_t)mk * rowb;
+#pragma unroll
+                for (int mm = 0; mm < MU; mm++) {
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const float xs = rsum[mrow(mm, r) + mk];
+                        const uint32_t mo = mkd + (uint32_t)mrow(mm, r) * rowb;
 #pragma unroll
                         for (int j = 0; j < 2; j++) {
-                            if (ocol[j] < nout) {
-                                const float y = sc[j] * (acc[mm][j][r] - (fold ? 0.f : zp[j]) * xs);
-                                (shared ? P.y_sh : P.y_perm)[prow * P.d + ocol[j]] = y;
-                            }
+                            const float y = sc[j] * (acc[mm][j][r] - zpe[j] * xs);
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, y), yr, (int)(mo + yo[j]), 0, 0);
                         }
                     }
                 }
@@ -578,8 +792,16 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
 
 static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Row tiles over all slots: at most A / 128 + (used experts) routed ones, plus T / 128 shared ones.
+static long gg_row_tiles(const FfnParams &P) {
+    return ((long)P.A + GG_M - 1) / GG_M + P.n_routed_slots + (P.Is > 0 ? ((long)P.T + GG_M - 1) / GG_M : 0);
+}
+static long gg_ksmax(const FfnParams &P) { return (P.I > P.Is ? P.I : P.Is) / GG_K; }
+static size_t gg_hsc_bytes(const FfnParams &P) { return (size_t)gg_row_tiles(P) * gg_ksmax(P) * 256; }
+
 size_t gemm_workspace_bytes(const FfnParams &P) {
-    return al256((size_t)P.T * P.d * 2) + 2 * al256((size_t)P.A * P.I * 2) + 2 * al256((size_t)P.T * P.Is * 2) +
+    return al256((size_t)P.T * P.d * 2) + al256((size_t)P.A * P.I * 2) + al256((size_t)P.A * P.I) +
+           al256((size_t)P.T * P.Is * 2) + al256((size_t)P.T * P.Is) + al256(gg_hsc_bytes(P)) +
            al256(2 * GG_XCDS * sizeof(int));
 }
 
@@ -591,6 +813,9 @@ bool gemm_supported(const FfnParams &P) {
     const long Imax = P.I > P.Is ? P.I : P.Is;
     if (Imax * ((long)P.d * P.wbits / 8) > 0x7FFFFFFFL) return false;
     if ((long)P.A * Imax * 2 > 0x7FFFFFFFL || (long)P.T * P.d * 2 > 0x7FFFFFFFL) return false;
+    if ((long)gg_hsc_bytes(P) > 0x7FFFFFFFL) return false;
+    // epilogue stores: 32-bit offsets within one 128-row tile (out-of-range marker added on top)
+    if ((long)GG_M * Imax * 2 > 0x7FFFFFFFL || (long)GG_M * P.d * 4 > 0x7FFFFFFFL) return false;
     return true;
 }
 
@@ -637,12 +862,16 @@ hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream) {
     p += al256((size_t)P.T * P.d * 2);
     G.hhi = (_Float16 *)p;
     p += al256((size_t)P.A * P.I * 2);
-    G.hlo = (_Float16 *)p;
-    p += al256((size_t)P.A * P.I * 2);
+    G.hlo = (uint8_t *)p;
+    p += al256((size_t)P.A * P.I);
     G.hshi = (_Float16 *)p;
     p += al256((size_t)P.T * P.Is * 2);
-    G.hslo = (_Float16 *)p;
-    p += al256((size_t)P.T * P.Is * 2);
+    G.hslo = (uint8_t *)p;
+    p += al256((size_t)P.T * P.Is);
+    G.hsc = (uint8_t *)p;
+    G.hsc_bytes = (uint32_t)gg_hsc_bytes(P);
+    G.ksmax = (int)gg_ksmax(P);
+    p += al256(gg_hsc_bytes(P));
     G.tile_ctr = (int *)p;
     return P.wbits == 4 ? gg_launch<4>(P, G, stream) : gg_launch<8>(P, G, stream);
 }

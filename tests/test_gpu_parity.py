@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import SampledOracle, assert_layer_close, say, NEAR_TIE
+from helpers import SampledOracle, assert_layer_close, close_report, say, NEAR_TIE, GEMM_REL_L2
 from routed_expert_ffn_sigmoid_amd import binding as B
 from routed_expert_ffn_sigmoid_amd import layer as L
 from routed_expert_ffn_sigmoid_amd import synth
@@ -81,6 +81,10 @@ def run_full_case(orc, dev, spec, T, path=B.MOE_PATH_AUTO, tweak=None, label="")
         assert_layer_close(run.y_shared.cpu().numpy(), ref.S, "y_shared")
     rel, mx = assert_layer_close(run.y.cpu().numpy(), ref.y, "y")
     say(f"   ok rel-L2 {rel:.2e} max-abs/RMS {mx:.2e} n_uniq {p.n_uniq}")
+    if path == B.MOE_PATH_GEMM:
+        relp, _ = close_report(run.y_perm.cpu().numpy(), ref.Yperm)
+        assert relp <= GEMM_REL_L2, f"y_perm rel-L2 {relp:.3e} above the matrix-core path's {GEMM_REL_L2}"
+        assert rel <= GEMM_REL_L2, f"y rel-L2 {rel:.3e} above the matrix-core path's {GEMM_REL_L2}"
     return run, ref
 
 
@@ -278,6 +282,8 @@ def test_full_workload_parity(orc, dev, name, T, nsample):
     ro, Y, S, y = so.run(x_np, W_r, bias, tokens)
     y_gpu = run.y.cpu().numpy()[tokens]
     rel, mx = assert_layer_close(y_gpu, y, f"{name} T={T} y (sampled {tokens.size})")
+    if T > 16:  # these run on the matrix-core path
+        assert rel <= GEMM_REL_L2, f"y rel-L2 {rel:.3e} above the matrix-core path's {GEMM_REL_L2}"
     inv = run.inv.cpu().numpy()
     yp = run.y_perm.cpu().numpy()
     for i, t in enumerate(tokens[:4]):
