@@ -31,6 +31,9 @@
 // list is read and before the activations are staged; the segment loop is
 // padded to a multiple of PF with out-of-range (zero) loads, so it is
 // straight-line code with PF segments in flight per row.
+#include <algorithm>
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -585,19 +588,54 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     nu = nu < 0 ? 0 : (nu > nrs ? nrs : nu);
     // item counts stay far below 2^31 / ncu (at most 1025 slots x 2^16 tiles), so 32-bit index math
     const int N = nu * tiles_r + (P.Is > 0 ? tiles_s : 0);
-    int i0, i1;
-    {
+    // With one tile per item (S = NW) the ranges are cut in half tiles (8 rows): every CU gets the same
+    // number of rows to within 8, and a range may begin or end in the middle of a tile, whose rows
+    // outside it read and store nothing.  Otherwise the ranges are cut in items.
+    constexpr bool HALVES = TPW == 1;
+    const int NU = HALVES ? 2 * N : N;
+    int u0, u1;
+    if (MODE == 0 || HALVES) {
         const int G = gridDim.x, b = blockIdx.x;
-        if (G % ncu == 0 && N >= G) {
+        if (G % ncu == 0 && NU >= G) {
             const int m = G / ncu, c = b % ncu, r = b / ncu;
-            const int c0 = c * N / ncu, c1 = (c + 1) * N / ncu;
-            i0 = c0 + r * (c1 - c0) / m;
-            i1 = c0 + (r + 1) * (c1 - c0) / m;
+            const int c0 = c * NU / ncu, c1 = (c + 1) * NU / ncu;
+            u0 = c0 + r * (c1 - c0) / m;
+            u1 = c0 + (r + 1) * (c1 - c0) / m;
         } else {
-            i0 = b * N / G;
-            i1 = (b + 1) * N / G;
+            u0 = b * NU / G;
+            u1 = (b + 1) * NU / G;
         }
+    } else {
+        // Down with items of several tiles: it restages the rows of h whenever a range moves to another
+        // slot, and that request would queue behind the weights already in flight, a long delay next to
+        // coarse items.  So the range boundaries are moved to slot starts: each slot is shared by the
+        // workgroups whose plain boundary c * NU / G falls inside it, in equal parts; a slot that no
+        // boundary falls into goes to the workgroup before it.  (With half-tile units the plain split is
+        // kept: it balances to 8 rows, and one restage per crossing range costs less than the rounding
+        // of slot-aligned shares.)
+        const int G = gridDim.x;
+        const int ur = HALVES ? 2 * tiles_r : tiles_r;
+        const int us = P.Is > 0 ? (HALVES ? 2 * tiles_s : tiles_s) : 0;
+        auto bound = [&](int c) -> int {
+            if (c <= 0 || NU == 0) return 0;
+            if (c >= G) return NU;
+            const int p = (int)((long)c * NU / G);
+            int st, len;
+            if (p < nu * ur) {
+                st = p / ur * ur;
+                len = ur;
+            } else {
+                st = nu * ur;
+                len = us;
+            }
+            const int first = (int)(((long)st * G + NU - 1) / NU);
+            const int n = (int)(((long)(st + len) * G + NU - 1) / NU) - first;  // >= 1: c is one of them
+            return st + (int)((long)(c - first) * len / n);
+        };
+        u0 = bound(blockIdx.x);
+        u1 = bound(blockIdx.x + 1);
     }
+    const int i0 = HALVES ? u0 >> 1 : u0, i1 = HALVES ? (u1 + 1) >> 1 : u1;
     if (i0 >= i1) return;  // uniform over the workgroup
 
     auto decode = [&](int i) {
@@ -624,7 +662,8 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         it.kpart_bytes = K / S * WBITS / 8;
         it.nseg_pad = ((it.kpart_bytes + 63) / 64 + PF - 1) / PF * PF;
         it.row = (it.tile * TPW + tile_w) * 16 + j;
-        it.row_ok = it.row < nout;
+        const int u = 2 * i + (j >> 3);  // half tile of this lane's row
+        it.row_ok = it.row < nout && (!HALVES || (u >= u0 && u < u1));
         return it;
     };
     auto weights = [&](const DItem &it, rsrc_t (&wr)[NM], uint32_t &lane_off) {
@@ -639,7 +678,8 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         } else {
             wr[0] = make_rsrc(W.qd + (long)it.e * P.d * rb, mbytes);
         }
-        lane_off = (uint32_t)((long)min(it.row, nout - 1) * rb) + (uint32_t)(kp * it.kpart_bytes + 16 * g);
+        // rows past the output or outside this CU's half tiles read nothing
+        lane_off = it.row_ok ? (uint32_t)((long)it.row * rb) + (uint32_t)(kp * it.kpart_bytes + 16 * g) : kOOB;
     };
     // down: rows of h of a slot (row r of the slot is h row p0 + r, or h_sh row r)
     auto h_src = [&](const DItem &it) {
@@ -657,9 +697,9 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         for (int m = 0; m < NM; m++) wbuf[b][m] = buf_load16(wr[m], off);
     };
 
-    // ---- activations of the first item, then the weight stream.  Staging runs first: its code is
-    // cold at launch, and fetching it behind the whole chip's first burst of weight requests costs
-    // more than the short gap before the stream starts.
+    // ---- activations of the first item and the weight stream.  Gate/up stages first (its rows were
+    // requested with the table): the staging code is cold at launch, and fetching it behind the whole
+    // chip's first burst of weight requests costs more than the short gap before the stream starts.
     if (MODE == 0) {
         const int kpart = kd / S;
         if (tile_w < T)
@@ -671,20 +711,35 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             stage_issue<SRCX>(xsrc0, ro, 0, kpad / 8, kpart, raw);
             stage_finish<WBITS, SRCX>(raw, xsrc0, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp], wxsum[kp]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < PF; b++) ld(b, wr_cur, off_cur, cur.kpart_bytes, b);
     } else {
+        // Rows of h: those of the slot are known only after the table round.  Each staging wavefront's
+        // first row is requested before any wavefront starts its weights (when fewer rows than tiles
+        // per item leave wavefronts without staging work, their weight requests would otherwise
+        // queue ahead of the rows in the CU's memory pipeline); the digits are made while the weight
+        // stream starts.
         const rsrc_t src = h_src(cur);
         const int kpart = cur.I / S;
         const long base = cur.shared ? 0 : cur.p0;
-        for (int r = tile_w; r < cur.ng; r += TPW) {
+        StageRaw<SRCX> raw1;
+        const bool st1 = tile_w < cur.ng;
+        const long ro1 = (base + tile_w) * cur.I + kp * kpart;
+        stage_issue<SRCX>(src, ro1, st1 ? 0 : kpad, kpad / 8, kpart, raw1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < PF; b++) ld(b, wr_cur, off_cur, cur.kpart_bytes, b);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st1) stage_finish<WBITS, SRCX>(raw1, src, ro1, tile_w, kpad / 8, kpart, stride, pb, planes, wexpo[kp], wxsum[kp]);
+        for (int r = tile_w + TPW; r < cur.ng; r += TPW) {
             const long ro = (base + r) * cur.I + kp * kpart;
             StageRaw<SRCX> raw;
             stage_issue<SRCX>(src, ro, 0, kpad / 8, kpart, raw);
             stage_finish<WBITS, SRCX>(raw, src, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp], wxsum[kp]);
         }
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < PF; b++) ld(b, wr_cur, off_cur, cur.kpart_bytes, b);
     __syncthreads();  // planes and exponents
 
     int staged_slot = cur.slot;
@@ -899,23 +954,35 @@ static size_t dkp_red_bytes(int mode) { return (size_t)DKP_WAVES * (mode == 0 ? 
 
 static int dkp_pf(int mode) { return mode == 0 ? 8 : 16; }
 
-// K split of the persistent kernel: the S in {8, 4, 2, 1} (whole 16-byte chunks per wavefront) with the
-// least work on the busiest CU, counted in wavefront segments including the padding to the prefetch
-// depth; ties go to the smaller S (less cross-wave reduction).
-static int dkp_pick_s(int mode, int K, int nout, int slots, int wbits, int ncu) {
+// K split of the persistent kernel: the S in {8, 4, 2, 1} (whole 16-byte chunks per wavefront).
+// Gate/up: the least work on the busiest CU at the largest possible slot count, counted as items x tiles
+// per item x segments padded to the prefetch depth; ties go to the smaller S.  Down: a wavefront streams
+// items x segments padded to the prefetch depth (a padded segment costs its place in the stream though it
+// reads nothing), at the expected number of slots -- uniform routing hits E (1 - (1 - k/E)^T) experts, and
+// skewed routing fewer -- with items counted in half tiles when a tile is an item (its ranges are cut in
+// half tiles); ties go to the larger S.
+static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, int wbits, int ncu) {
     const int chunk_inputs = wbits == 8 ? 16 : 32;
     const int nseg_full = (K * wbits / 8 + 63) / 64;
     const int pf = dkp_pf(mode);
     int best = 1;
-    long best_cost = -1;
-    for (int S = 1; S <= DKP_WAVES; S <<= 1) {
+    double best_cost = -1;
+    for (int i = 0; i < 4; i++) {
+        const int S = mode == 0 ? 1 << i : DKP_WAVES >> i;
         if (K % (S * chunk_inputs)) continue;
         const int tpw = DKP_WAVES / S;
         const int nseg = (nseg_full + S - 1) / S;
         const int nseg_pad = (nseg + pf - 1) / pf * pf;
-        const long items = (long)slots * ((nout + 16 * tpw - 1) / (16 * tpw));
-        const long per_cu = (items + ncu - 1) / ncu;
-        const long cost = per_cu * tpw * nseg_pad;
+        const long tiles = (nout + 16 * tpw - 1) / (16 * tpw);
+        double cost;
+        if (mode == 0) {
+            const long items = (long)slots * tiles;
+            cost = (double)((items + ncu - 1) / ncu) * tpw * nseg_pad;
+        } else {
+            const double items = slots_exp * (double)tiles;
+            const double per_cu = tpw == 1 ? std::ceil(2.0 * items / ncu) / 2.0 : std::ceil(items / ncu);
+            cost = per_cu * nseg_pad;
+        }
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
             best = S;
@@ -956,8 +1023,10 @@ static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t
     const int Kmin = MODE == 0 ? P.d : (P.Is > 0 && P.Is < P.I ? P.Is : P.I);
     const int nout = MODE == 0 ? Imax : P.d;
     const int slots = P.n_routed_slots + (P.Is > 0 ? 1 : 0);
+    const double uniq_exp = (double)P.E * (1.0 - std::pow(1.0 - (double)P.k / P.E, (double)P.T));
+    const double slots_exp = std::min((double)P.n_routed_slots, uniq_exp) + (P.Is > 0 ? 1 : 0);
     // routed and shared expert split alike: the split must divide both K ranges
-    int S = dkp_pick_s(MODE, K, nout, slots, WBITS, device_cus());
+    int S = dkp_pick_s(MODE, K, nout, slots, slots_exp, WBITS, device_cus());
     while (S > 1 && (Kmin % (S * (WBITS == 8 ? 16 : 32)))) S >>= 1;
     const int kpad = pad_k(K / S, WBITS);
     if (P.T > DK_GMAX || dkp_tab_words(MODE, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64 ||
