@@ -154,6 +154,40 @@ __device__ __forceinline__ float raw_absmax(const StageRaw<SRC> &r, float mx) {
     return mx;
 }
 
+// Wave-wide reductions in DPP steps (neighbours, pairs, mirrored halves of 8 and 16 lanes, then rows 0-1
+// into 1 and 2-3 into 3, then row 1 into rows 2-3): lane 63 ends with the result.  Low latency next to
+// shuffles through LDS, which matters on the start-up path.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ float wave_max_nonneg(float x) {  // x >= 0: the bit patterns order as the values
+    uint32_t v = __float_as_uint(x);
+    v = max(v, dpp_u32<0xB1, 0xF>(v, v));
+    v = max(v, dpp_u32<0x4E, 0xF>(v, v));
+    v = max(v, dpp_u32<0x141, 0xF>(v, v));
+    v = max(v, dpp_u32<0x140, 0xF>(v, v));
+    v = max(v, dpp_u32<0x142, 0xA>(v, v));
+    v = max(v, dpp_u32<0x143, 0xC>(v, v));
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 63));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+    const int2 b = __builtin_bit_cast(int2, v);
+    const int2 o = make_int2((int)dpp_u32<CTRL, ROWS>((uint32_t)b.x, 0u), (int)dpp_u32<CTRL, ROWS>((uint32_t)b.y, 0u));
+    return v + __builtin_bit_cast(double, o);  // lanes of rows outside ROWS add +0
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {  // exact when every partial sum is (integers below 2^53)
+    v = dpp_add_f64<0xB1, 0xF>(v);
+    v = dpp_add_f64<0x4E, 0xF>(v);
+    v = dpp_add_f64<0x141, 0xF>(v);
+    v = dpp_add_f64<0x140, 0xF>(v);
+    v = dpp_add_f64<0x142, 0xA>(v);
+    v = dpp_add_f64<0x143, 0xC>(v);
+    const int2 b = __builtin_bit_cast(int2, v);
+    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(b.x, 63), __builtin_amdgcn_readlane(b.y, 63)));
+}
+
 template <int WBITS, int SRC>
 __device__ void stage_finish(const StageRaw<SRC> &r, rsrc_t src, long ro, int i, int ngr, int kpart, int stride,
                              long plane_bytes, int8_t *planes, int *expo, double *xsum) {
@@ -165,8 +199,7 @@ __device__ void stage_finish(const StageRaw<SRC> &r, rsrc_t src, long ro, int i,
         stage_issue<SRC>(src, ro, m0, ngr, kpart, r2);
         mx = raw_absmax<SRC>(r2, mx);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx = wave_max_nonneg(mx);
     int e = 0;
     if (mx > 0.f) {
         int ex;
@@ -177,22 +210,32 @@ __device__ void stage_finish(const StageRaw<SRC> &r, rsrc_t src, long ro, int i,
     long ssum = 0;
     int8_t *p0 = planes + (long)i * stride, *p1 = p0 + plane_bytes, *p2 = p1 + plane_bytes;
     auto put = [&](int m, const float (&xv)[8]) {
-        // digits of the 8 inputs, packed as they are produced: for int8 weights two words per plane in
-        // input order; for int4 weights one word of even inputs and one of odd inputs per plane
-        uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+        // Digits: for |X| < 2^22 the bytes of (X + 0x808080) ^ 0x808080 are the signed base-256 digits
+        // d0, d1, d2 of X (each in [-128, 127], the representation being unique).  Planes are packed with
+        // byte permutes: for int8 weights two words per plane in input order, for int4 weights one word
+        // of even inputs and one of odd inputs.
+        uint32_t V[8];
+        int gs = 0;  // |sum| < 2^25
 #pragma unroll
         for (int t = 0; t < 8; t++) {
             const int X = (int)rintf(xv[t] * sc);
-            ssum += X;
-            const int d0 = (X << 24) >> 24;
-            const int rr = (X - d0) >> 8;
-            const int d1 = (rr << 24) >> 24;
-            const int d2 = (rr - d1) >> 8;
-            const int word = WBITS == 8 ? (t >> 2) : (t & 1);
-            const int sh = WBITS == 8 ? 8 * (t & 3) : 8 * (t >> 1);
-            w[0][word] |= (uint32_t)(d0 & 255) << sh;
-            w[1][word] |= (uint32_t)(d1 & 255) << sh;
-            w[2][word] |= (uint32_t)(d2 & 255) << sh;
+            gs += X;
+            V[t] = ((uint32_t)X + 0x808080u) ^ 0x808080u;
+        }
+        ssum += gs;
+        uint32_t w[3][2];
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            // the four inputs of word q: q*4 + 0..3 (int8) or q, q + 2, q + 4, q + 6 (int4)
+            const uint32_t a0 = WBITS == 8 ? V[4 * q] : V[q], a1 = WBITS == 8 ? V[4 * q + 1] : V[q + 2];
+            const uint32_t a2 = WBITS == 8 ? V[4 * q + 2] : V[q + 4], a3 = WBITS == 8 ? V[4 * q + 3] : V[q + 6];
+            const uint32_t A = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.b0 a1.b0 a0.b1 a1.b1
+            const uint32_t B = __builtin_amdgcn_perm(a3, a2, 0x05010400u);  // a2.b0 a3.b0 a2.b1 a3.b1
+            const uint32_t C = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.b2 a1.b2 ...
+            const uint32_t D = __builtin_amdgcn_perm(a3, a2, 0x07030602u);  // a2.b2 a3.b2 ...
+            w[0][q] = __builtin_amdgcn_perm(B, A, 0x05040100u);             // byte 0 of a0..a3
+            w[1][q] = __builtin_amdgcn_perm(B, A, 0x07060302u);             // byte 1
+            w[2][q] = __builtin_amdgcn_perm(D, C, 0x05040100u);             // byte 2
         }
         if (WBITS == 8) {
             const int pos = m * 8;
@@ -225,9 +268,7 @@ __device__ void stage_finish(const StageRaw<SRC> &r, rsrc_t src, long ro, int i,
         stage_issue<SRC>(src, ro, m0, ngr, kpart, r2);
         put_round(r2, m0);
     }
-    double ds = (double)ssum;  // exact: integers below 2^53
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ds += __shfl_xor(ds, o, 64);
+    const double ds = wave_sum_f64((double)ssum);  // exact: integers below 2^53
     if (lane == 0) {
         xsum[i] = ds;
         expo[i] = e;
@@ -701,15 +742,19 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     // requested with the table): the staging code is cold at launch, and fetching it behind the whole
     // chip's first burst of weight requests costs more than the short gap before the stream starts.
     if (MODE == 0) {
+        // rows tile_w, tile_w + TPW, ...: the next row is requested before this one is turned into digits
         const int kpart = kd / S;
-        if (tile_w < T)
-            stage_finish<WBITS, SRCX>(raw0, xsrc0, (long)tile_w * kd + kp * kpart, tile_w, kpad / 8, kpart, stride, pb,
-                                      planes, wexpo[kp], wxsum[kp]);
-        for (int r = tile_w + TPW; r < T; r += TPW) {
-            const long ro = (long)r * kd + kp * kpart;
-            StageRaw<SRCX> raw;
-            stage_issue<SRCX>(xsrc0, ro, 0, kpad / 8, kpart, raw);
-            stage_finish<WBITS, SRCX>(raw, xsrc0, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp], wxsum[kp]);
+        StageRaw<SRCX> rb;
+        for (int r = tile_w; r < T; r += 2 * TPW) {
+            const int r1 = r + TPW, r2 = r + 2 * TPW;
+            if (r1 < T) stage_issue<SRCX>(xsrc0, (long)r1 * kd + kp * kpart, 0, kpad / 8, kpart, rb);
+            stage_finish<WBITS, SRCX>(raw0, xsrc0, (long)r * kd + kp * kpart, r, kpad / 8, kpart, stride, pb, planes,
+                                      wexpo[kp], wxsum[kp]);
+            if (r1 < T) {
+                if (r2 < T) stage_issue<SRCX>(xsrc0, (long)r2 * kd + kp * kpart, 0, kpad / 8, kpart, raw0);
+                stage_finish<WBITS, SRCX>(rb, xsrc0, (long)r1 * kd + kp * kpart, r1, kpad / 8, kpart, stride, pb,
+                                          planes, wexpo[kp], wxsum[kp]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
