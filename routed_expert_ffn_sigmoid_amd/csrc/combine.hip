@@ -8,7 +8,11 @@
 
 namespace moe {
 
-// grid: (T, ceil(d/1024)); block 256
+// grid: (T, ceil(d/1024)); block 256.  The k routed rows are taken in batches of CB: the batch's row
+// numbers and weights are read together (one round trip), then its row loads are issued together (a
+// second), then added in order j = 0, 1, ...; with k <= CB the whole gather is two round trips deep.
+constexpr int CB = 8;
+
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_perm,
                                                       const float *__restrict__ y_shared,
                                                       const int32_t *__restrict__ inv, const float *__restrict__ w,
@@ -16,17 +20,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const int t = blockIdx.x;
     const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (c >= d) return;
-    float4 acc = y_shared ? *(const float4 *)(y_shared + (long)t * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; j++) {
-        const float wj = w[(long)t * k + j];
-        const int p = inv[(long)t * k + j];
-        if (p < 0) continue;  // assignment dropped by moe_permute (invalid expert id)
-        const float4 v = *(const float4 *)(y_perm + (long)p * d + c);
-        acc.x = fmaf(wj, v.x, acc.x);
-        acc.y = fmaf(wj, v.y, acc.y);
-        acc.z = fmaf(wj, v.z, acc.z);
-        acc.w = fmaf(wj, v.w, acc.w);
+    // the shared row is requested unconditionally (from y itself when there is none, then discarded), so
+    // that it travels with the first batch instead of ahead of it
+    const float4 s4 = *(const float4 *)((y_shared ? y_shared : y) + (long)t * d + c);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < k; j0 += CB) {
+        int p[CB];
+        float wj[CB];
+#pragma unroll
+        for (int u = 0; u < CB; u++) {
+            const int j = j0 + u;
+            p[u] = j < k ? inv[(long)t * k + j] : -1;
+            wj[u] = j < k ? w[(long)t * k + j] : 0.f;
+        }
+        float4 v[CB];
+#pragma unroll
+        for (int u = 0; u < CB; u++)  // p < 0: assignment dropped by moe_permute (invalid expert id), or past k
+            v[u] = p[u] >= 0 ? *(const float4 *)(y_perm + (long)p[u] * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j0 == 0 && y_shared) acc = s4;
+#pragma unroll
+        for (int u = 0; u < CB; u++) {
+            if (p[u] < 0) continue;
+            acc.x = fmaf(wj[u], v[u].x, acc.x);
+            acc.y = fmaf(wj[u], v[u].y, acc.y);
+            acc.z = fmaf(wj[u], v[u].z, acc.z);
+            acc.w = fmaf(wj[u], v[u].w, acc.w);
+        }
     }
+    if (k <= 0 && y_shared) acc = s4;
     *(float4 *)(y + (long)t * d + c) = acc;
 }
 

@@ -153,6 +153,15 @@ def test_fractional_int4_zero_points(orc, dev, case, path):
     run_full_case(orc, dev, spec_of(**kw), T, path=path, tweak=_fractional_zero_points, label=case + "_frac_zp")
 
 
+def test_more_used_experts_than_cus(orc, dev):
+    """Decode with more used experts than the chip has CUs (256): the down pass's slot-aligned ranges then meet
+    slots that no range boundary falls into, which go to the neighbouring range.  With a small selection bias
+    the 512 assignments spread over about 390 experts."""
+    _, ref = run_full_case(orc, dev, spec_of(d=128, E=1000, k=32, I=64, I_shared=64, bias="uniform0.01"), 16,
+                           label="more_used_experts_than_cus")
+    assert ref.perm.n_uniq > 256, ref.perm.n_uniq
+
+
 def test_all_tie_router(orc, dev):
     """W_r = 0 and b = 0: every selection score is 0.5; ids 0..k-1 win with w = lambda/k."""
     spec = spec_of(d=256, E=8, k=3, I=64, routed_scale=2.5)
