@@ -52,11 +52,12 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(config, T):
+def measured_traffic(config, T, gemm=False):
     """HBM bytes per moe_forward launch from the committed rocprofv3 counter summary of this workload
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none or when the kernel sources
     have changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_decode_{config}_T{T}.md")
+    kind = "gemm" if gemm else "decode"
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kind}_{config}_T{T}.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -66,7 +67,7 @@ def measured_traffic(config, T):
             if line.startswith(key):
                 vals[key[:-1]] = line[len(key):].strip()
     h = hashlib.sha256()
-    for f in ("ffn_decode.hip", "common.h", "kernels.h"):
+    for f in ("ffn_gemm.hip" if gemm else "ffn_decode.hip", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "routed_expert_ffn_sigmoid_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if vals.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
@@ -152,6 +153,10 @@ def main():
         for i in range(cycle):
             x, W = operands(i)
             runs[i].forward(x, W)
+    perm_graph = torch.cuda.CUDAGraph()  # the permutation alone (it rewrites the same outputs)
+    with torch.cuda.graph(perm_graph, stream=side):
+        for i in range(cycle):
+            runs[i].permute()
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -176,14 +181,26 @@ def main():
     fwd_s = e0.elapsed_time(e1) / 1e3
     n_fwd = fwd_reps * cycle
     fwd_us = fwd_s / n_fwd * 1e6
+    perm_graph.replay()
+    e0.record(stream)
+    for _ in range(fwd_reps):
+        perm_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    perm_us = e0.elapsed_time(e1) * 1e3 / n_fwd
 
     ebytes = spec.expert_bytes()
     sbytes = spec.expert_bytes(spec.I_shared) if spec.I_shared else 0
     bytes_per_fwd = float(np.mean(n_uniq)) * ebytes + sbytes
     flops_per_step = 2.0 * 3 * spec.d * (T * spec.k * spec.I + T * spec.I_shared)
-    if decode:
+    # the roof that binds: HBM when the expert FFNs do fewer flops per expert-weight byte than the ridge
+    # point of the two peaks (2516.6 TFLOP/s / 8 TB/s = 315 flop/B), the matrix cores otherwise
+    ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops_per_step / bytes_per_fwd < ridge:
         achieved = bytes_per_fwd / (fwd_s / n_fwd) / 1e9
-        traffic = measured_traffic(args.config, T)
+        # the auto path runs the matrix-core GEMM for T > 16 with bf16 activations
+        gemm = args.path == "gemm" or (args.path == "auto" and T > 16 and spec.act == synth.ACT_BF16)
+        traffic = measured_traffic(args.config, T, gemm)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
@@ -217,6 +234,8 @@ def main():
                                f"shared={spec.I_shared} int{spec.wbits} T={T}",
                    "T": T, "layers_resident": n_layers, "x_pool": args.pool,
                    "mean_unique_experts": round(float(np.mean([n_uniq[i % cycle] for i in steps_idx])), 2),
+                   "assignments_per_unique_expert": round(T * spec.k / float(np.mean(n_uniq)), 2),
+                   "permute_us_alone": round(perm_us, 2),
                    "timing": "HIP graph per step (the four ABI calls), replayed",
                    "path": args.path, "setup_s": round(setup_s, 1)},
         "roofline": roof,
