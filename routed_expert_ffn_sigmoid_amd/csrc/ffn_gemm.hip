@@ -48,6 +48,7 @@ constexpr int GG_MAXSLOTS = 1025;
 constexpr int GG_XCDS = 8;         // XCDs of the chip; workgroups are dealt to them round-robin
 constexpr int GG_GROUP = 16;       // consecutive tiles handed to one XCD at a time
 constexpr int GG_RING = 152 * 1024;  // LDS for the staging ring (the rest of the 160 KB holds the tables)
+constexpr int GG_JUNK = 1024;        // end of the ring: sink of the copies a tile does not need (they read nothing)
 
 // storage position, within its group of 8, of input i of the group (int4 weights)
 __device__ __forceinline__ int pos8(int i) { return ((i & 3) << 1) | (i >> 2); }
@@ -205,20 +206,29 @@ template <int MODE, int WBITS>
 struct GgCfg {
     static constexpr bool LO8 = MODE == 1;                  // h residual plane (e4m3 + block exponents)
     static constexpr int RB = GG_K * WBITS / 8;             // weight bytes per row and step
-    static constexpr int PLANE = GG_M * GG_K * 2;           // bytes of the fp16 activation plane (x or h hi)
-    static constexpr int LO_BYTES = LO8 ? GG_M * GG_K : 0;  // residual plane: 128 rows x 64 bytes
-    static constexpr int SC_BYTES = LO8 ? 1024 : 0;         // its 256 exponent bytes, in a 1 KB copy
-    static constexpr int A_BYTES = PLANE + LO_BYTES + SC_BYTES;
     static constexpr int B_BYTES = GG_WAVES * GG_NW * RB;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int STAGES = GG_RING / STAGE > 4 ? 4 : GG_RING / STAGE;
     static constexpr int NLA = 2;                           // 1 KB copies per wavefront and step, fp16 plane
     static constexpr int NLB = GG_NW * RB / 1024;           // 1 KB weight copies per wavefront and step
-    static constexpr int NL = NLA + (LO8 ? 1 : 0) + NLB;    // wavefront 0 also copies the exponents
+    static constexpr int NL = NLA + (LO8 ? 2 : 0) + NLB;    // + one residual and one exponent copy
     static constexpr int NOUT_W = MODE == 0 ? 32 : 64;      // distinct output columns per wavefront
     static constexpr int NOUT_G = NOUT_W * GG_WAVES;        // per tile
-    static_assert(STAGES >= 2, "LDS ring");
     static_assert(GG_M * 128 / 1024 == NLA * GG_WAVES, "activation copies");
+    // Stage layout of a tile with MU blocks of 32 rows: the fp16 plane (x or h hi; MU x 32 rows x 128 bytes),
+    // the residual plane (MU x 32 rows x 64 bytes) and the 1 KB exponent copy, then the weights (each
+    // wavefront's 64 rows x RB bytes); as many stages as the ring holds, at most 8.  Short tiles thus keep
+    // more steps of weights in flight, which is what bounds them.
+    template <int MU>
+    struct Lay {
+        static constexpr int PLANE = MU * 32 * GG_K * 2;
+        static constexpr int LO_BYTES = LO8 ? MU * 32 * GG_K : 0;
+        static constexpr int SC_BYTES = LO8 ? 1024 : 0;
+        static constexpr int A_BYTES = PLANE + LO_BYTES + SC_BYTES;
+        static constexpr int STAGE = A_BYTES + B_BYTES;
+        static constexpr int STAGES = (GG_RING - GG_JUNK) / STAGE > 8 ? 8 : (GG_RING - GG_JUNK) / STAGE;
+        static constexpr int NAC = 4 * MU;           // 1 KB copies of the fp16 plane per step
+        static constexpr int NLC = LO8 ? 2 * MU : 0;  // of the residual plane
+        static_assert(STAGES >= 2, "LDS ring");
+    };
 };
 
 // MODE 0: gate/up (A = x16 rows through the permutation; each wavefront owns 32 channels, subtile 0 their
@@ -235,7 +245,7 @@ template <int MODE, int WBITS>
 __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBufs G, int tiles_n) {
     using C = GgCfg<MODE, WBITS>;
     constexpr bool LO8 = C::LO8;
-    constexpr int RB = C::RB, PLANE = C::PLANE, STAGE = C::STAGE, STAGES = C::STAGES;
+    constexpr int RB = C::RB;
     constexpr int NLB = C::NLB, NL = C::NL;
     constexpr int WL = WBITS == 8 ? 2 : 1;   // 16-byte weight fragments per subtile and step
     constexpr float QBIAS = WBITS == 8 ? 1152.f : 1024.f;
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 scrs = make_rsrc(G.hsc, G.hsc_bytes);
                 const int m = 16 * wv + (lane >> 2);
                 if (m < rows) alsrc = (uint32_t)(((long)(shared ? 0 : p0) + r0 + m) * I) + 16 * swz_b8(m, lane & 3);
-                if (lane < 16) scsrc = (uint32_t)rt * (uint32_t)G.ksmax * 256u + 16 * lane;
+                if (wv == 0 && lane < 16) scsrc = (uint32_t)rt * (uint32_t)G.ksmax * 256u + 16 * lane;
             }
 #pragma unroll
             for (int i = 0; i < 2; i++) {
@@ -445,39 +455,48 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         uint32_t ard[4];  // activation fragment of substep s: row lr (+ 32 mm), chunk 4 kg + s
 #pragma unroll
         for (int s = 0; s < 4; s++) ard[s] = (uint32_t)(lr * 128 + swz_a(lr, 4 * kg + s) * 16);
-        // residual fragment: row lr (+ 32 mm), chunks kg and 2 + kg (inputs 16 kg.. and 32 + 16 kg..); the
-        // exponent word of row block kg, rows lr + 32 mm in byte mm
-        uint32_t ald[2];
-#pragma unroll
-        for (int h = 0; h < 2; h++) ald[h] = (uint32_t)(PLANE + lr * 64 + swz_b8(lr, 2 * h + kg) * 16);
-        const uint32_t scd = (uint32_t)(PLANE + C::LO_BYTES + kg * 128 + lr * 4);
-        uint32_t brd[2][WL];  // weight fragment of subtile j: row 32 j + lr of the wavefront, bytes 32 kg ...
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int h = 0; h < WL; h++) {
-                const int rl = 32 * j + lr;
-                const int pc = WBITS == 4 ? swz_b4(rl, kg) : swz_b8(rl, 2 * kg + h);
-                brd[j][h] = (uint32_t)(C::A_BYTES + wv * GG_NW * RB + rl * RB + pc * 16);
-            }
-
-        auto issue = [&](int step, int stg) {
-            const uint32_t sb = ring0 + (uint32_t)(stg * STAGE);
-#pragma unroll
-            for (int i = 0; i < 2; i++) dma16(ars, sb + (2 * wv + i) * 1024, asrc[i] + (uint32_t)(step * 128));
-            if constexpr (LO8) {
-                dma16(alrs, sb + PLANE + wv * 1024, alsrc + (uint32_t)(step * 64));
-                if (wv == 0) dma16(scrs, sb + PLANE + C::LO_BYTES, scsrc + (uint32_t)(step * 256));
-            }
-#pragma unroll
-            for (int i = 0; i < NLB; i++)
-                dma16(brs[WBITS == 4 ? i : i >> 1],
-                      sb + C::A_BYTES + wv * GG_NW * RB + i * 1024, bsrc[i] + (uint32_t)(step * RB));
-        };
-
         // ---- the tile, with the number of 32-row blocks that hold data as a compile-time constant
         auto run = [&](auto muc) {
             constexpr int MU = decltype(muc)::value;
+            using Y = typename C::template Lay<MU>;
+            constexpr int PLANE = Y::PLANE, STAGE = Y::STAGE, STAGES = Y::STAGES;
+            // residual fragment: row lr (+ 32 mm), chunks kg and 2 + kg (inputs 16 kg.. and 32 + 16 kg..); the
+            // exponent word of row block kg, rows lr + 32 mm in byte mm
+            uint32_t ald[2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) ald[h] = (uint32_t)(PLANE + lr * 64 + swz_b8(lr, 2 * h + kg) * 16);
+            const uint32_t scd = (uint32_t)(PLANE + Y::LO_BYTES + kg * 128 + lr * 4);
+            uint32_t brd[2][WL];  // weight fragment of subtile j: row 32 j + lr of the wavefront, bytes 32 kg ...
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int h = 0; h < WL; h++) {
+                    const int rl = 32 * j + lr;
+                    const int pc = WBITS == 4 ? swz_b4(rl, kg) : swz_b8(rl, 2 * kg + h);
+                    brd[j][h] = (uint32_t)(Y::A_BYTES + wv * GG_NW * RB + rl * RB + pc * 16);
+                }
+            // Copies of step `step` into stage `stg`.  Every wavefront issues the same number per step (so one
+            // wait count serves all): the activation rows past MU x 32 and the exponents of wavefronts other
+            // than 0 go to the junk area and read nothing, and so does every copy of a step past the end of K.
+            const uint32_t junk = ring0 + (uint32_t)(GG_RING - GG_JUNK);
+            auto issue = [&](int step, int stg) {
+                const uint32_t sb = ring0 + (uint32_t)(stg * STAGE);
+                const bool live = step < nsteps;
+                auto src = [&](uint32_t base, uint32_t adv) { return live ? base + adv : kOOB; };
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const int c = 2 * wv + i;
+                    dma16(ars, c < Y::NAC ? sb + c * 1024 : junk, src(asrc[i], (uint32_t)(step * 128)));
+                }
+                if constexpr (LO8) {
+                    dma16(alrs, wv < Y::NLC ? sb + PLANE + wv * 1024 : junk, src(alsrc, (uint32_t)(step * 64)));
+                    dma16(scrs, wv == 0 ? sb + PLANE + Y::LO_BYTES : junk, src(scsrc, (uint32_t)(step * 256)));
+                }
+#pragma unroll
+                for (int i = 0; i < NLB; i++)
+                    dma16(brs[WBITS == 4 ? i : i >> 1], sb + Y::A_BYTES + wv * GG_NW * RB + i * 1024,
+                          src(bsrc[i], (uint32_t)(step * RB)));
+            };
             f32x16v_t acc[MU][2];
 #pragma unroll
             for (int mm = 0; mm < MU; mm++)
@@ -568,11 +587,9 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                         else acc[mm][j] = mfma_lo<3>(al[mm], bl[j], acc[mm][j], scw);
                     }
             };
-            // wavefront 0 has one copy more per step (the exponents)
-            auto wait_steps = [&](auto nc) {
+            auto wait_steps = [&](auto nc) {  // all but the copies of the last n steps issued have landed
                 constexpr int n = decltype(nc)::value;
-                if (LO8 && wv == 0) GG_WAIT_VM(n * (NL + 1));
-                else GG_WAIT_VM(n * NL);
+                GG_WAIT_VM(n * NL);
             };
 
             // ---- prologue: STAGES steps in flight, the operands of step 0 in registers
@@ -595,24 +612,26 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                     // row sums of the staged activations: row tid / 4, fp16 chunks 2 (tid % 4) and
                     // 2 (tid % 4) + 1, residual chunk tid % 4 (times its block exponent)
                     const int m = tid >> 2;
+                    if (m < MU * 32) {
 #pragma unroll
-                    for (int h = 0; h < 2; h++) {
-                        const int pc = swz_a(m, 2 * (tid & 3) + h);
-                        const h8_t v = *(const h8_t *)(sp + m * 128 + pc * 16);
+                        for (int h = 0; h < 2; h++) {
+                            const int pc = swz_a(m, 2 * (tid & 3) + h);
+                            const h8_t v = *(const h8_t *)(sp + m * 128 + pc * 16);
 #pragma unroll
-                        for (int i = 0; i < 8; i++) rs += (float)v[i];
-                    }
-                    if constexpr (LO8) {
-                        const int q = tid & 3;
-                        const uint4 v = *(const uint4 *)(sp + PLANE + m * 64 + swz_b8(m, q) * 16);
-                        const int ex = sp[PLANE + C::LO_BYTES + (q >> 1) * 128 + (m & 31) * 4 + (m >> 5)];
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                        float t = 0.f;
+                            for (int i = 0; i < 8; i++) rs += (float)v[i];
+                        }
+                        if constexpr (LO8) {
+                            const int q = tid & 3;
+                            const uint4 v = *(const uint4 *)(sp + PLANE + m * 64 + swz_b8(m, q) * 16);
+                            const int ex = sp[PLANE + Y::LO_BYTES + (q >> 1) * 128 + (m & 31) * 4 + (m >> 5)];
+                            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                            float t = 0.f;
 #pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            t += (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 0) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1)) +
-                                 (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 2) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3));
-                        rs += __builtin_ldexpf(t, ex - 127);
+                            for (int i = 0; i < 4; i++)
+                                t += (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 0) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1)) +
+                                     (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 2) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3));
+                            rs += __builtin_ldexpf(t, ex - 127);
+                        }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -832,7 +851,7 @@ static hipError_t gg_launch_mode(const FfnParams &P, const GemmBufs &G, hipStrea
     using C = GgCfg<MODE, WBITS>;
     const int Imax = P.I > P.Is ? P.I : P.Is;
     const int tiles_n = ((MODE == 0 ? Imax : P.d) + C::NOUT_G - 1) / C::NOUT_G;
-    const size_t lds = (size_t)C::STAGES * C::STAGE;
+    const size_t lds = GG_RING;  // every tile shape lays its stages (and the junk area) out in the ring
     auto fn = gemm_kernel<MODE, WBITS>;
     hipError_t err = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
