@@ -30,7 +30,7 @@
 // down takes 64 outputs per wavefront (256 per tile).  A persistent grid (one workgroup per CU) walks
 // the tiles (slot-major, then output tile, then row tile) from a table built on the device from
 // n_uniq / uniq / offsets, so one launch shape serves every routing.  Activations and weights are
-// copied from memory straight into an LDS ring of 2-4 K steps.
+// copied from memory straight into an LDS ring of 2-8 K steps (more for tiles with fewer rows).
 #include "common.h"
 #include "kernels.h"
 
