@@ -133,16 +133,58 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restri
         }
 }
 
-// Small-T logits: 1024-thread workgroups each stream a block of W_r rows once for all T <= RS_TMAX
-// tokens.  Thread (row group rg, expert quad q) handles rows rg, rg+R, ... (at most RSK_MAXR) of the
-// block for experts 4q..4q+3; all of its W_r loads are issued before the block's activations are
-// staged in LDS.  At most RSK_SPLITS blocks, so the select kernel reads few partials.
+// Small-T logits: 1024-thread workgroups each stream a block of W_r (a range of rows, and of the experts a
+// block of at most RSK_EB columns) once for all T <= RS_TMAX tokens.  Thread (row group rg, expert quad q)
+// handles rows rg, rg+R, ... (at most RSK_MAXR) of the block for the block's experts 4q..4q+3; all of its
+// W_r loads are issued before the block's activations are staged in LDS.  Splitting the experts as well as
+// the rows spreads the read over about RSK_WGS workgroups of at least RSK_MIN_BYTES each (one CU streams
+// only about 20 GB/s), while the row splits stay at most RSK_SPLITS, so the select kernel reads few
+// partials.
 constexpr int RS_TMAX = 4;
 constexpr int RSK_THREADS = 1024;
 constexpr int RSK_SPLITS = 32;
-constexpr int RSK_MIN_BYTES = 64 * 1024;  // W_r bytes per workgroup at least
+constexpr int RSK_MIN_BYTES = 8 * 1024;   // W_r bytes per workgroup at least
+constexpr int RSK_EB = 32;                // experts per workgroup column block
+constexpr int RSK_WGS = 256;              // workgroups aimed at
 constexpr int RSK_MAXR = 12;              // W_r rows per thread (1024 threads: 128 VGPRs each)
 constexpr int RSK_MAX_ROWS = 2048;        // rows per block (LDS holds RS_TMAX x rows activations)
+
+// Sum of a over the lanes whose index is congruent to this lane's modulo nq (a power of two <= 64), every
+// lane getting the result, in a fixed order: neighbours and pairs inside quads (DPP quad permutes), lanes 4
+// and 8 apart inside rows of 16 (DPP row rotations), then the other row of each 32 and the other half of the
+// wavefront (16- and 32-lane swaps).  All steps are register moves; the steps below nq are skipped.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double a) {
+    const int2 b = __builtin_bit_cast(int2, a);
+    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_update_dpp(0, b.x, CTRL, 0xF, 0xF, false),
+                                                __builtin_amdgcn_update_dpp(0, b.y, CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ double swap_add_f64(double a, bool sixteen) {
+    const int2 b = __builtin_bit_cast(int2, a);
+    int2 p, q;
+    if (sixteen) {
+        const auto x = __builtin_amdgcn_permlane16_swap((uint32_t)b.x, (uint32_t)b.x, false, false);
+        const auto y = __builtin_amdgcn_permlane16_swap((uint32_t)b.y, (uint32_t)b.y, false, false);
+        p = make_int2((int)x[0], (int)y[0]);
+        q = make_int2((int)x[1], (int)y[1]);
+    } else {
+        const auto x = __builtin_amdgcn_permlane32_swap((uint32_t)b.x, (uint32_t)b.x, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap((uint32_t)b.y, (uint32_t)b.y, false, false);
+        p = make_int2((int)x[0], (int)y[0]);
+        q = make_int2((int)x[1], (int)y[1]);
+    }
+    // the two results hold this lane's value and its partner's, the lower row or half first
+    return __builtin_bit_cast(double, p) + __builtin_bit_cast(double, q);
+}
+__device__ __forceinline__ double sum_congruent(double a, int nq) {
+    if (nq <= 1) a += dpp_f64<0xB1>(a);   // quad_perm 1,0,3,2
+    if (nq <= 2) a += dpp_f64<0x4E>(a);   // quad_perm 2,3,0,1
+    if (nq <= 4) a += dpp_f64<0x124>(a);  // row_ror:4
+    if (nq <= 8) a += dpp_f64<0x128>(a);  // row_ror:8
+    if (nq <= 16) a = swap_add_f64(a, true);
+    if (nq <= 32) a = swap_add_f64(a, false);
+    return a;
+}
 
 template <int ACT>
 __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const void *__restrict__ x,
@@ -152,7 +194,8 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
     __shared__ double red[RSK_THREADS / 64][256];
     __shared__ float xs[RS_TMAX * RSK_MAX_ROWS];  // [t][row in block], row pitch = rows
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int nq = E >> 2;             // expert quads: a power of two <= 64
+    const int EB = E < RSK_EB ? E : RSK_EB, e0 = blockIdx.y * EB;  // this workgroup's experts
+    const int nq = EB >> 2;            // expert quads: a power of two <= 8
     const int R = RSK_THREADS / nq;    // row groups (>= 16: every wave holds at least one)
     const int q = tid % nq, rg = tid / nq;
     const int i0 = blockIdx.x * rows, i1 = min(d, i0 + rows);
@@ -173,7 +216,7 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
 #pragma unroll
     for (int u = 0; u < RSK_MAXR; u++) {
         const int i = i0 + rg + u * R;
-        w[u] = buf_load16(wsrc, i < i1 ? (uint32_t)(((long)i * E + 4 * q) * 4) : kOOB);
+        w[u] = buf_load16(wsrc, i < i1 ? (uint32_t)(((long)i * E + e0 + 4 * q) * 4) : kOOB);
     }
 #pragma unroll
     for (int c = 0; c < XPT; c++)  // unconditional: entries past T*rows are zeros nobody reads
@@ -198,20 +241,19 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
             }
         }
     }
-    // fixed-order reduction over row groups: lanes holding the same quad inside a wave
-    // (xor offsets nq, 2nq, ..., 32), then the 16 waves in order, one token at a time
+    // fixed-order reduction over row groups: the lanes holding the same quad inside a wave, then the 16
+    // waves in order, one token at a time
     for (int t = 0; t < T; t++) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            double a = acc[t][v];
-            for (int o = nq; o < 64; o <<= 1) a += __shfl_xor(a, o, 64);
+            const double a = sum_congruent(acc[t][v], nq);
             if (lane < nq) red[wv][lane * 4 + v] = a;
         }
         __syncthreads();
-        if (tid < E) {
+        if (tid < EB) {
             double z = 0.0;
             for (int w2 = 0; w2 < RSK_THREADS / 64; w2++) z += red[w2][tid];
-            part[((long)blockIdx.x * T + t) * E + tid] = z;
+            part[((long)blockIdx.x * T + t) * E + e0 + tid] = z;
         }
         __syncthreads();
     }
@@ -363,13 +405,17 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
 
 static bool use_skinny(int T, int E) { return T <= RS_TMAX && E >= 4 && E <= 256 && (E & (E - 1)) == 0; }
 
+static int skinny_eb(int E) { return E < RSK_EB ? E : RSK_EB; }
+
 static int skinny_rows(int d, int E) {
-    const long wbytes = (long)d * E * 4;
-    long nsplit = wbytes / RSK_MIN_BYTES;
+    const int eb = skinny_eb(E), neb = E / eb;
+    long nsplit = (RSK_WGS + neb - 1) / neb;                // about RSK_WGS workgroups in all
+    const long by_bytes = (long)d * eb * 4 / RSK_MIN_BYTES;  // each with at least RSK_MIN_BYTES
+    if (nsplit > by_bytes) nsplit = by_bytes;
     if (nsplit > RSK_SPLITS) nsplit = RSK_SPLITS;
     if (nsplit < 1) nsplit = 1;
     long rows = (d + nsplit - 1) / nsplit;
-    const long cap = (long)RSK_MAXR * (RSK_THREADS / (E / 4));  // rows the threads of a block can hold
+    const long cap = (long)RSK_MAXR * (RSK_THREADS / (eb / 4));  // rows the threads of a block can hold
     if (rows > cap) rows = cap;
     if (rows > RSK_MAX_ROWS) rows = RSK_MAX_ROWS;
     return (int)rows;
@@ -403,10 +449,12 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
         const int rows = skinny_rows(d, E);
         nsplit = (d + rows - 1) / rows;
         if (act == 0)
-            hipLaunchKernelGGL(router_logits_skinny_kernel<0>, dim3(nsplit), dim3(RSK_THREADS), 0, stream, x, Wr, T,
+            hipLaunchKernelGGL(router_logits_skinny_kernel<0>, dim3(nsplit, E / skinny_eb(E)), dim3(RSK_THREADS), 0,
+                               stream, x, Wr, T,
                                d, E, rows, part);
         else
-            hipLaunchKernelGGL(router_logits_skinny_kernel<1>, dim3(nsplit), dim3(RSK_THREADS), 0, stream, x, Wr, T,
+            hipLaunchKernelGGL(router_logits_skinny_kernel<1>, dim3(nsplit, E / skinny_eb(E)), dim3(RSK_THREADS), 0,
+                               stream, x, Wr, T,
                                d, E, rows, part);
     } else {
         nsplit = router_nsplit(T, d, E);
