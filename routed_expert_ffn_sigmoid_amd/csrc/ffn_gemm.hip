@@ -12,25 +12,29 @@
 // registers from the packed bytes; the zero point is applied once per output through the row sum of the
 // activations, and the scale in the epilogue.  Activations: x is bf16 and is converted once to fp16
 // (exact save for magnitudes below 2^-14).  h enters the down GEMM as an fp16 plane plus the residual
-// h - fp16(h) in e4m3 under one E8M0 exponent per row and 32 channels (the block form of the scaled
-// matrix-core product), about 16 significant bits in all: a single fp16 rounding of h would move the
-// largest down outputs by up to 3e-3 of their RMS.  The residual product is one scaled e4m3 MFMA per K
-// step and 32x32 block, half the matrix-core time of the fp16 plane's four; its weights are the same
-// dequantised values in e4m3 (exact for int4, 4 significant bits for larger int8 values, which the
-// residual's own 4 bits already bound).  Accumulation is fp32.
+// h - fp16(h) in fp6 e2m3 under one E8M0 exponent per row and 32 channels (the block form of the scaled
+// matrix-core product), about 15-16 significant bits for the larger values of a block: a single fp16
+// rounding of h would move the largest down outputs by up to 3e-3 of their RMS.  The residual product
+// is one scaled e2m3 MFMA per K step and 32x32 block, a quarter of the matrix-core time of the fp16
+// plane's four; its weights are the same dequantised values in e2m3 under a per-column power of two
+// (exact for int4 with zero points in 0..15, 4 significant bits for larger values, which the residual's
+// own 4 bits already bound).  Accumulation is fp32.
 //
 // Layout of the activation planes (x16, h and its residual): row-major, and for int4 weights the 8
 // inputs of each group are stored in the order 0,4,1,5,2,6,3,7, the order in which the nibble
-// dequantisation below produces the weights.  Residual exponents: per row tile (over all slots) and K
-// step, 256 bytes [block][row % 32][row / 32], the order in which one 32-bit LDS read gives a lane the
-// exponents of its four row blocks.
+// dequantisation below produces the weights.  The residual plane keeps one byte per channel: each block
+// of 32 channels holds their 24 bytes of e2m3 codes, then the fp32 sum of the rounded residuals, then 4
+// unused bytes.  Residual exponents: per row tile (over all slots) and K step, 256 bytes
+// [block][row % 32][row / 32], the order in which one 32-bit LDS read gives a lane the exponents of its
+// four row blocks.
 //
-// Tiles: 128 rows; 8 wavefronts as 2 (rows) x 4 (columns), each 64 rows x 2 subtiles of 32 columns.
-// Gate/up pairs the gate and up rows of the same 32 channels in one wavefront (128 channels per tile),
-// down takes 64 outputs per wavefront (256 per tile).  A persistent grid (one workgroup per CU) walks
-// the tiles (slot-major, then output tile, then row tile) from a table built on the device from
-// n_uniq / uniq / offsets, so one launch shape serves every routing.  Activations and weights are
-// copied from memory straight into an LDS ring of 2-8 K steps (more for tiles with fewer rows).
+// Tiles: 128 rows x 512 weight rows; each of the 8 wavefronts covers all 128 rows (as up to 4 blocks of
+// 32) and 64 weight rows as 2 subtiles of 32 columns.  Gate/up pairs the gate and up rows of the same 32
+// channels in one wavefront (256 channels per tile), down takes 64 outputs per wavefront (512 per tile).
+// A persistent grid (one workgroup per CU) walks the tiles (slot-major, then output tile, then row tile)
+// from a table built on the device from n_uniq / uniq / offsets, so one launch shape serves every
+// routing.  Activations and weights are copied from memory straight into an LDS ring of 2-8 K steps
+// (more for tiles with fewer rows).
 #include "common.h"
 #include "kernels.h"
 
@@ -87,43 +91,25 @@ __device__ __forceinline__ h8_t deq_int8(uint32_t w0, uint32_t w1, h2_t off) {
     return (h8_t){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+typedef int i2v_t __attribute__((ext_vector_type(2)));
 typedef int i4v_t __attribute__((ext_vector_type(4)));
 typedef int i8v_t __attribute__((ext_vector_type(8)));
-typedef short s2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h32_t __attribute__((ext_vector_type(32)));
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u6v_t __attribute__((ext_vector_type(6)));
+typedef float f32x32v_t __attribute__((ext_vector_type(32)));
 
-// e4m3 bytes of eight fp16 values, in order, as two words (round to nearest even; integers up to 16 in
-// magnitude are exact, larger ones up to 448 keep 4 significant bits)
-__device__ __forceinline__ void fp8x8(h8_t v, int &d0, int &d1) {
-    s2_t w0 = {0, 0}, w1 = {0, 0};
-    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w0, (h2_t){v[0], v[1]}, 1.f, false);
-    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w0, (h2_t){v[2], v[3]}, 1.f, true);
-    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w1, (h2_t){v[4], v[5]}, 1.f, false);
-    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w1, (h2_t){v[6], v[7]}, 1.f, true);
-    d0 = __builtin_bit_cast(int, w0);
-    d1 = __builtin_bit_cast(int, w1);
-}
+// fp6 e2m3 (1 sign, 2 exponent bits of bias 1, 3 mantissa bits): magnitudes 0.125 m below 1 and
+// (1 + m/8) 2^(e-1) up to 7.5, i.e. 4 significant bits over three binades.  32 values of one lane
+// take six words, value i at bits 6i..6i+5 of their little-endian concatenation; the conversions
+// divide by their scale, round to nearest even and saturate at 7.5.
 
-// maximum of each v[i] over the 32 lanes of each half of the wavefront (row-local DPP steps: neighbours,
-// pairs, mirrored halves of 8 and of 16 lanes; then the other 16 lanes through a swizzle within 32).  The
-// four reductions advance together, so each DPP read finds its operand written a few instructions back.
-__device__ __forceinline__ void max_half_wave4(uint32_t (&v)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0xB1, 0xF, 0xF, false));
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0x4E, 0xF, 0xF, false));
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0x141, 0xF, 0xF, false));
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0x140, 0xF, 0xF, false));
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = max(v[i], (uint32_t)__builtin_amdgcn_ds_swizzle((int)v[i], 0x401F));
-}
-
-// one scaled e4m3 x e4m3 product of a 32x32x64 block: A scaled per row and 32-long K block by byte OPS of
-// sa (an E8M0 exponent), B unscaled
-template <int OPS>
-__device__ __forceinline__ f32x16v_t mfma_lo(i8v_t a, i8v_t b, f32x16v_t c, int sa) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPS, sa, 0, 127);
+// One scaled e2m3 x e2m3 product of a 32x32x64 block (format code 2 for both operands).  Lane half h
+// holds the 32 inputs 32h..32h+31 of its row (A) or column (B) in order, and scales them by an E8M0
+// exponent: byte OPS of sa for A, byte OPB of sb for B.
+template <int OPS, int OPB>
+__device__ __forceinline__ f32x16v_t mfma_lo(i8v_t a, i8v_t b, f32x16v_t c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, OPS, sa, OPB, sb);
 }
 
 __device__ __forceinline__ float gg_zp(const void *z, int wbits, long i) {
@@ -184,7 +170,7 @@ struct GgInt {
 struct GemmBufs {
     const _Float16 *x16;       // [T][d]
     _Float16 *hhi;             // [A][I] h rounded to fp16
-    uint8_t *hlo;              // [A][I] its residual h - hi, e4m3 under the block exponents of hsc
+    uint8_t *hlo;              // [A][I] its residual h - hi: per 32 channels, 24 bytes of e2m3, their sum (fp32), 4 unused
     _Float16 *hshi;            // [T][I_shared], the same for the shared expert
     uint8_t *hslo;
     uint8_t *hsc;              // residual exponents (E8M0): [row tile][K step][block 2][row 32][row block 4]
@@ -204,12 +190,12 @@ __device__ __forceinline__ int swz_b8(int r, int c) { return c ^ ((r >> 2) & 3);
 
 template <int MODE, int WBITS>
 struct GgCfg {
-    static constexpr bool LO8 = MODE == 1;                  // h residual plane (e4m3 + block exponents)
+    static constexpr bool RES = MODE == 1;                  // h residual plane (e2m3 + block exponents)
     static constexpr int RB = GG_K * WBITS / 8;             // weight bytes per row and step
     static constexpr int B_BYTES = GG_WAVES * GG_NW * RB;
     static constexpr int NLA = 2;                           // 1 KB copies per wavefront and step, fp16 plane
     static constexpr int NLB = GG_NW * RB / 1024;           // 1 KB weight copies per wavefront and step
-    static constexpr int NL = NLA + (LO8 ? 2 : 0) + NLB;    // + one residual and one exponent copy
+    static constexpr int NL = NLA + (RES ? 2 : 0) + NLB;    // + one residual and one exponent copy
     static constexpr int NOUT_W = MODE == 0 ? 32 : 64;      // distinct output columns per wavefront
     static constexpr int NOUT_G = NOUT_W * GG_WAVES;        // per tile
     static_assert(GG_M * 128 / 1024 == NLA * GG_WAVES, "activation copies");
@@ -220,22 +206,22 @@ struct GgCfg {
     template <int MU>
     struct Lay {
         static constexpr int PLANE = MU * 32 * GG_K * 2;
-        static constexpr int LO_BYTES = LO8 ? MU * 32 * GG_K : 0;
-        static constexpr int SC_BYTES = LO8 ? 1024 : 0;
+        static constexpr int LO_BYTES = RES ? MU * 32 * GG_K : 0;
+        static constexpr int SC_BYTES = RES ? 1024 : 0;
         static constexpr int A_BYTES = PLANE + LO_BYTES + SC_BYTES;
         static constexpr int STAGE = A_BYTES + B_BYTES;
         static constexpr int STAGES = (GG_RING - GG_JUNK) / STAGE > 8 ? 8 : (GG_RING - GG_JUNK) / STAGE;
         static constexpr int NAC = 4 * MU;           // 1 KB copies of the fp16 plane per step
-        static constexpr int NLC = LO8 ? 2 * MU : 0;  // of the residual plane
+        static constexpr int NLC = RES ? 2 * MU : 0;  // of the residual plane
         static_assert(STAGES >= 2, "LDS ring");
     };
 };
 
 // MODE 0: gate/up (A = x16 rows through the permutation; each wavefront owns 32 channels, subtile 0 their
-// gate rows and subtile 1 their up rows; output h as an fp16 plane plus the e4m3 residual plane and its
+// gate rows and subtile 1 their up rows; output h as an fp16 plane plus the e2m3 residual plane and its
 // exponents).  MODE 1: down (A = the h planes of the slot's rows; 64 down rows per wavefront; output
-// y_perm / y_shared in fp32).  Its K step is four fp16 MFMAs on h hi and one scaled e4m3 MFMA on the
-// residual, whose weights are the same dequantised values converted to e4m3.
+// y_perm / y_shared in fp32).  Its K step is four fp16 MFMAs on h hi and one scaled e2m3 MFMA on the
+// residual, whose weights are the same dequantised values converted to e2m3.
 //
 // Zero points: when every zero point of the tile's weight rows is an integer (int8 always; int4 when
 // its fp32 zero points are integral), it is folded into the dequantisation (B = q - z, exact in fp16);
@@ -244,7 +230,7 @@ struct GgCfg {
 template <int MODE, int WBITS>
 __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBufs G, int tiles_n) {
     using C = GgCfg<MODE, WBITS>;
-    constexpr bool LO8 = C::LO8;
+    constexpr bool RES = C::RES;
     constexpr int RB = C::RB;
     constexpr int NLB = C::NLB, NL = C::NL;
     constexpr int WL = WBITS == 8 ? 2 : 1;   // 16-byte weight fragments per subtile and step
@@ -435,7 +421,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 zp[j] = gg_zp(W.zd, WBITS, ch);
             }
         }
-        // (|z| <= 256 keeps the folded int8 weights q - z inside the e4m3 range of the residual product)
+        // (|z| <= 256 keeps the folded weights q - z and the offsets below exact in fp16)
         bool my_int = true;
 #pragma unroll
         for (int j = 0; j < 2; j++) my_int = my_int && zp[j] == rintf(zp[j]) && fabsf(zp[j]) <= 256.f;
@@ -447,6 +433,19 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
             const _Float16 o = (_Float16)(-(QBIAS + z)), o16 = (_Float16)(-(64.f + z));
             boff[j] = (h2_t){o, o};
             boff16[j] = (h2_t){o16, o16};
+        }
+        // Weights of the residual product: the dequantised values divided by 2^be, the smallest power of two
+        // that brings the column's largest possible |B| to 7.5 or less (e2m3 keeps no more); exact for int4
+        // with an integral z in 0..15 (be = 1), 4 significant bits above 2^be otherwise.
+        // Its E8M0 exponent 127 + be of subtile j sits in byte j of sbp.
+        int sbp = 0;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const float z = fold ? zp[j] : 0.f;
+            const float mx = WBITS == 4 ? fmaxf(fabsf(z), fabsf(15.f - z)) : 128.f + fabsf(z);
+            int be = -1;
+            while (7.5f * __builtin_ldexpf(1.f, be) < mx) be++;
+            sbp |= (127 + be) << (8 * j);
         }
         // nibble masks kept in registers (the three-operand and-or cannot take two literals)
         const uint32_t mlo = __builtin_amdgcn_readfirstlane(0x000F000Fu), mhi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
@@ -460,12 +459,6 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
             constexpr int MU = decltype(muc)::value;
             using Y = typename C::template Lay<MU>;
             constexpr int PLANE = Y::PLANE, STAGE = Y::STAGE, STAGES = Y::STAGES;
-            // residual fragment: row lr (+ 32 mm), chunks kg and 2 + kg (inputs 16 kg.. and 32 + 16 kg..); the
-            // exponent word of row block kg, rows lr + 32 mm in byte mm
-            uint32_t ald[2];
-#pragma unroll
-            for (int h = 0; h < 2; h++) ald[h] = (uint32_t)(PLANE + lr * 64 + swz_b8(lr, 2 * h + kg) * 16);
-            const uint32_t scd = (uint32_t)(PLANE + Y::LO_BYTES + kg * 128 + lr * 4);
             uint32_t brd[2][WL];  // weight fragment of subtile j: row 32 j + lr of the wavefront, bytes 32 kg ...
 #pragma unroll
             for (int j = 0; j < 2; j++)
@@ -488,7 +481,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                     const int c = 2 * wv + i;
                     dma16(ars, c < Y::NAC ? sb + c * 1024 : junk, src(asrc[i], (uint32_t)(step * 128)));
                 }
-                if constexpr (LO8) {
+                if constexpr (RES) {
                     dma16(alrs, wv < Y::NLC ? sb + PLANE + wv * 1024 : junk, src(alsrc, (uint32_t)(step * 64)));
                     dma16(scrs, wv == 0 ? sb + PLANE + Y::LO_BYTES : junk, src(scsrc, (uint32_t)(step * 256)));
                 }
@@ -504,15 +497,17 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 for (int j = 0; j < 2; j++) acc[mm][j] = (f32x16v_t){};
             float rs = 0.f;
 
-            // Operand registers: activation fragments of two substeps, dequantised weights of two substeps,
-            // the raw weights of a step; with the residual plane, its fragments, its exponent word and the
-            // e4m3 weights of the whole step.
+            // Operand registers: activation fragments of two substeps, the raw weights of a step and their
+            // dequantised values (two substeps; with the residual plane all four, which its e2m3 weights are
+            // converted from at once); with the residual plane, its fragments and its exponent word.
             constexpr int NBR = 2 * WL;  // raw weight reads per step
+            constexpr int NBQ = RES ? 4 : 2;
             uint4 braw[2][WL];
             h8_t af[2][MU];
-            h8_t bq[2][2];
+            h8_t bq[NBQ][2];
             i8v_t al[MU], bl[2];
             int scw = 0;
+            auto bqi = [](int sub) { return RES ? sub : (sub & 1); };
             auto rd_b = [&](const unsigned char *p) {
 #pragma unroll
                 for (int j = 0; j < 2; j++)
@@ -540,39 +535,41 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 for (int mm = 0; mm < MU; mm++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
-                        acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[sub & 1][mm], bq[sub & 1][j],
+                        acc[mm][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[sub & 1][mm], bq[bqi(sub)][j],
                                                                             acc[mm][j], 0, 0, 0);
             };
-            // Residual product.  Lane half kg dequantises inputs 32 kg + 8 s .. + 7 in substep s; as e4m3 they
-            // fill words 2 s, 2 s + 1 of bl, i.e. the lane holds inputs 32 kg .. 32 kg + 31 in order.  The
-            // scaled MFMA wants inputs 16 kg .. + 15 in words 0-3 and 32 + 16 kg .. + 15 in words 4-7, the same
-            // order as the residual fragments: words 4-7 of the low half and words 0-3 of the high half trade
-            // places (one 32-lane swap per word pair).
-            auto cvt = [&](int sub, int buf) {
+            // Residual product.  Lane half kg dequantises inputs 32 kg + 8 s .. + 7 in substep s, so after four
+            // substeps it holds inputs 32 kg .. 32 kg + 31 in order: the operand layout of the e2m3 product.
+            auto pk6 = [&]() {
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
-                    int d0, d1;
-                    fp8x8(bq[buf][j], d0, d1);
-                    bl[j][2 * sub] = d0;
-                    bl[j][2 * sub + 1] = d1;
+                    h32_t v;
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+#pragma unroll
+                        for (int i = 0; i < 8; i++) v[8 * q + i] = bq[q][j][i];
+                    const float bx = __builtin_bit_cast(float, (((uint32_t)sbp >> (8 * j)) & 0xFFu) << 23);  // 2^be
+                    const u6v_t r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(v, bx);
+                    bl[j] = (i8v_t){(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], (int)r[5], 0, 0};
                 }
             };
-            auto swap_halves = [&]() {
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)bl[j][i], (uint32_t)bl[j][i + 4], false, false);
-                        bl[j][i] = (int)r[0];
-                        bl[j][i + 4] = (int)r[1];
-                    }
-            };
+            // residual fragment: row lr (+ 32 mm), the 24 bytes of inputs 32 kg .. 32 kg + 31 (chunk 2 kg and the
+            // first 8 bytes of chunk 2 kg + 1); the exponent word of row block kg, rows lr + 32 mm in byte mm.
+            // The offsets are recomputed at each use (from an opaque copy of the lane index), which costs a few
+            // instructions per step instead of registers held across the loop.
             auto rd_lo = [&](const unsigned char *p) {
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int r = ln & 31, h = ln >> 5;
+                uint32_t ald[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) ald[i] = (uint32_t)(PLANE + r * 64 + swz_b8(r, 2 * h + i) * 16);
+                const uint32_t scd = (uint32_t)(PLANE + Y::LO_BYTES + h * 128 + r * 4);
 #pragma unroll
                 for (int mm = 0; mm < MU; mm++) {
                     const i4v_t u0 = *(const i4v_t *)(p + mm * 2048 + ald[0]);
-                    const i4v_t u1 = *(const i4v_t *)(p + mm * 2048 + ald[1]);
-                    al[mm] = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const i2v_t u1 = *(const i2v_t *)(p + mm * 2048 + ald[1]);
+                    al[mm] = (i8v_t){u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], 0, 0};
                 }
                 scw = *(const int *)(p + scd);
             };
@@ -581,10 +578,10 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 for (int mm = 0; mm < MU; mm++)
 #pragma unroll
                     for (int j = 0; j < 2; j++) {
-                        if (mm == 0) acc[mm][j] = mfma_lo<0>(al[mm], bl[j], acc[mm][j], scw);
-                        else if (mm == 1) acc[mm][j] = mfma_lo<1>(al[mm], bl[j], acc[mm][j], scw);
-                        else if (mm == 2) acc[mm][j] = mfma_lo<2>(al[mm], bl[j], acc[mm][j], scw);
-                        else acc[mm][j] = mfma_lo<3>(al[mm], bl[j], acc[mm][j], scw);
+                        if (mm == 0) acc[mm][j] = j == 0 ? mfma_lo<0, 0>(al[mm], bl[j], acc[mm][j], scw, sbp) : mfma_lo<0, 1>(al[mm], bl[j], acc[mm][j], scw, sbp);
+                        else if (mm == 1) acc[mm][j] = j == 0 ? mfma_lo<1, 0>(al[mm], bl[j], acc[mm][j], scw, sbp) : mfma_lo<1, 1>(al[mm], bl[j], acc[mm][j], scw, sbp);
+                        else if (mm == 2) acc[mm][j] = j == 0 ? mfma_lo<2, 0>(al[mm], bl[j], acc[mm][j], scw, sbp) : mfma_lo<2, 1>(al[mm], bl[j], acc[mm][j], scw, sbp);
+                        else acc[mm][j] = j == 0 ? mfma_lo<3, 0>(al[mm], bl[j], acc[mm][j], scw, sbp) : mfma_lo<3, 1>(al[mm], bl[j], acc[mm][j], scw, sbp);
                     }
             };
             auto wait_steps = [&](auto nc) {  // all but the copies of the last n steps issued have landed
@@ -620,44 +617,35 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
 #pragma unroll
                             for (int i = 0; i < 8; i++) rs += (float)v[i];
                         }
-                        if constexpr (LO8) {
+                        if constexpr (RES) {
+                            // the residual block sums of the step (bytes 24..27 of each 32-byte block)
                             const int q = tid & 3;
-                            const uint4 v = *(const uint4 *)(sp + PLANE + m * 64 + swz_b8(m, q) * 16);
-                            const int ex = sp[PLANE + Y::LO_BYTES + (q >> 1) * 128 + (m & 31) * 4 + (m >> 5)];
-                            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                            float t = 0.f;
-#pragma unroll
-                            for (int i = 0; i < 4; i++)
-                                t += (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 0) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1)) +
-                                     (__builtin_amdgcn_cvt_f32_fp8((int)w[i], 2) + __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3));
-                            rs += __builtin_ldexpf(t, ex - 127);
+                            if (q < 2) rs += *(const float *)(sp + PLANE + m * 64 + swz_b8(m, 2 * q + 1) * 16 + 8);
                         }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // substeps but the last: the MFMAs of substep s run interleaved with the fragment reads and
-                // the dequantisation of substep s + 1 (and the e4m3 conversion of substep s)
+                // the dequantisation of substep s + 1
 #pragma unroll
                 for (int ph = 0; ph < 3; ph++) {
                     rd_a(sp, ph + 1, (ph + 1) & 1);
-                    deq(ph + 1, (ph + 1) & 1);
-                    if constexpr (LO8) cvt(ph, ph & 1);
+                    deq(ph + 1, bqi(ph + 1));
                     mfmas(ph);
 #pragma unroll
                     for (int i = 0; i < 2 * MU; i++) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
                         if (i < MU) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                        __builtin_amdgcn_sched_group_barrier(0x002, LO8 ? 4 : 3, 0);  // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);            // VALU
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                if constexpr (LO8) {
-                    // substep 3 (with the reads of the residual fragments), then the residual product: its
-                    // e4m3 weights are complete once substep 3 is converted; step + 1 has landed everywhere
-                    // after the barrier, and its operands are read while the residual MFMAs run
+                if constexpr (RES) {
+                    // substep 3 (with the reads of the residual fragments and the e2m3 conversion of the
+                    // step's weights), then the residual product; step + 1 has landed everywhere after the
+                    // barrier, and its operands are read while the residual MFMAs run
                     rd_lo(sp);
-                    cvt(3, 1);
-                    swap_halves();
+                    pk6();
                     mfmas(3);
 #pragma unroll
                     for (int i = 0; i < 2 * MU; i++) {
@@ -730,51 +718,78 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 const int c = ocol[0];
                 // stored at the planes' position of channel c (int4 order within groups of 8)
                 const uint32_t hp = (uint32_t)(WBITS == 4 ? ((c & ~7) | pos8(c & 7)) : c);
-                const uint32_t o2 = c < nout ? 2 * hp : kOOB, o1 = c < nout ? hp : kOOB;
+                const uint32_t o2 = c < nout ? 2 * hp : kOOB;
                 const rsrc_t hhr = make_rsrc((shared ? G.hshi : G.hhi) + prow0 * I, (uint32_t)(rows * I * 2));
                 const rsrc_t hlr = make_rsrc((shared ? G.hslo : G.hlo) + prow0 * I, (uint32_t)(rows * I));
-                // the 32 channels of this wavefront form one residual block of K step nbase / 64 of the down
-                // pass (block (nbase / 32) % 2); lane lr = 0 of each half stores the exponents of its rows
+                // The 32 channels of this wavefront (positions nbase .. nbase + 31) form one residual block of K
+                // step nbase / 64 of the down pass (block (nbase / 32) % 2).  The residuals go through LDS, this
+                // wavefront's 128 rows x 32 fp32, so that one lane holds a row's block: position p sits in
+                // column 16 (p % 2) + p / 2 (the operand order of the paired conversion below), and the 16-byte
+                // chunks of a row are XOR-swizzled by the row so that the row reads spread over the banks.
                 const long scbase = ((long)rt * G.ksmax + (nbase >> 6)) * 256 + ((nbase >> 5) & 1) * 128;
                 const rsrc_t hsr = make_rsrc(G.hsc + scbase, 128);
-                const uint32_t os = (lr == 0 && nbase < nout) ? 0u : kOOB;
+                const bool blk_ok = nbase < nout;
                 const uint32_t mkI = (uint32_t)mk * (uint32_t)I;
+                float *tr = (float *)(gg_ring + wv * (GG_M * 128));
+                const int pc = (int)(hp & 31);
+                const int tcol = ((pc & 1) << 4) | (pc >> 1);
+                auto tix = [](int m, int col) { return m * 32 + ((((col >> 2) ^ m) & 7) << 2) + (col & 3); };
 #pragma unroll
                 for (int mm = 0; mm < MU; mm++) {
 #pragma unroll
-                    for (int r4 = 0; r4 < 16; r4 += 4) {  // four consecutive rows at a time
-                        _Float16 h_hi[4];
-                        float lo[4];
-                        uint32_t lb[4];
+                    for (int r = 0; r < 16; r++) {
+                        const int m = mrow(mm, r) + mk;
+                        const float xs = rsum[m];
+                        const float gv = sc[0] * (acc[mm][0][r] - zpe[0] * xs);
+                        const float uv = sc[1] * (acc[mm][1][r] - zpe[1] * xs);
+                        // silu through the hardware exp2 and reciprocal (relative error ~1e-6, below the
+                        // precision that h keeps)
+                        const float hv = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * gv)) * uv;
+                        const _Float16 hh = (_Float16)hv;
+                        const uint32_t mo = mkI + (uint32_t)mrow(mm, r) * (uint32_t)I;
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hh), hhr, (int)(2 * mo + o2), 0, 0);
+                        // rows past the tile and columns past the output give zeros (the block maximum ignores them)
+                        tr[tix(m, tcol)] = (c < nout && m < rows) ? hv - (float)hh : 0.f;
+                    }
+                }
+                __syncthreads();
+                // Lane L takes rows L and L + 64 (those of the MU blocks): the block exponent S puts the largest
+                // residual magnitude into [4, 7.75), the top binade of e2m3 (into [2, 4) where it would round
+                // past 7.5); the values, divided by 2^(S - 127), become e2m3 codes (nearest even).  32 bytes
+                // per row and block: the 24 of the codes, their sum in fp32, 4 unused.
+#pragma unroll
+                for (int rr = 0; rr < 2; rr++) {
+                    const int m = lane + 64 * rr;
+                    if (64 * rr < MU * 32 && m < MU * 32) {
+                        // (the maximum is taken from the loaded scalars: a bit cast of a vector element
+                        // compiles to a read of element 0 with this compiler)
+                        f16v_t b0, b1;
+                        uint32_t mx = 0;
+                        auto amax = [&](float f) { mx = max(mx, __builtin_bit_cast(uint32_t, f) & 0x7FFFFFFFu); };
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
-                            const int r = r4 + i, m = mrow(mm, r) + mk;
-                            const float xs = rsum[m];
-                            const float gv = sc[0] * (acc[mm][0][r] - zpe[0] * xs);
-                            const float uv = sc[1] * (acc[mm][1][r] - zpe[1] * xs);
-                            // silu through the hardware exp2 and reciprocal (relative error ~1e-6, below the
-                            // precision that h keeps)
-                            const float hv = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * gv)) * uv;
-                            h_hi[i] = (_Float16)hv;
-                            lo[i] = hv - (float)h_hi[i];
-                            // rows past the tile contribute zeros to the block maximum
-                            lb[i] = (c < nout && m < rows) ? (__builtin_bit_cast(uint32_t, lo[i]) & 0x7FFFFFFFu) : 0u;
+                            const float4 u = *(const float4 *)(tr + tix(m, 4 * i));
+                            const float4 v = *(const float4 *)(tr + tix(m, 16 + 4 * i));
+                            b0[4 * i] = u.x; b0[4 * i + 1] = u.y; b0[4 * i + 2] = u.z; b0[4 * i + 3] = u.w;
+                            b1[4 * i] = v.x; b1[4 * i + 1] = v.y; b1[4 * i + 2] = v.z; b1[4 * i + 3] = v.w;
+                            amax(u.x); amax(u.y); amax(u.z); amax(u.w);
+                            amax(v.x); amax(v.y); amax(v.z); amax(v.w);
                         }
-                        // block exponent (every lane of a half-wavefront holds the same row): the largest
-                        // residual of the block scaled into [128, 256), e4m3 values below 448; S is the
-                        // E8M0 byte of the inverse scaling
-                        max_half_wave4(lb);
+                        int S = (int)(mx >> 23) - 2 + ((mx & 0x7FFFFFu) >= 0x780000u ? 1 : 0);
+                        S = min(max(S, 1), 254);
+                        const float X = __builtin_bit_cast(float, (uint32_t)S << 23);
+                        const u6v_t q = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(b0, b1, X);
+                        // the sum of the stored (rounded) residuals, for the zero-point term of the down pass:
+                        // exact, as every value is a multiple of X / 8 below 7.5 X
+                        const f32x32v_t dq = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(q, X);
+                        float bs = 0.f;
 #pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            const int r = r4 + i, m = mrow(mm, r) + mk;
-                            const int S = max((int)(lb[i] >> 23) - 7, 0);
-                            const float mult = __builtin_bit_cast(float, (uint32_t)(254 - S) << 23);
-                            const int q8 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[i] * mult, 0.f, 0, false);
-                            const uint32_t mo = mkI + (uint32_t)mrow(mm, r) * (uint32_t)I;
-                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h_hi[i]), hhr, (int)(2 * mo + o2), 0, 0);
-                            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)q8, hlr, (int)(mo + o1), 0, 0);
-                            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)S, hsr, (int)((m & 31) * 4 + (m >> 5) + os), 0, 0);
-                        }
+                        for (int i = 0; i < 32; i++) bs += dq[i];
+                        const uint32_t ro = blk_ok ? (uint32_t)m * (uint32_t)I + (uint32_t)nbase : kOOB;
+                        typedef int i32x4 __attribute__((ext_vector_type(4)));
+                        __builtin_amdgcn_raw_buffer_store_b128((i32x4){(int)q[0], (int)q[1], (int)q[2], (int)q[3]}, hlr, (int)ro, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128((i32x4){(int)q[4], (int)q[5], __builtin_bit_cast(int, bs), 0}, hlr, (int)(ro + 16), 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)S, hsr, (int)((m & 31) * 4 + (m >> 5) + (blk_ok ? 0u : kOOB)), 0, 0);
                     }
                 }
             } else {
