@@ -189,6 +189,17 @@ def main():
     torch.cuda.synchronize()
     perm_us = e0.elapsed_time(e1) * 1e3 / n_fwd
 
+    # distribution of the step time: each step's graph replay between its own pair of events (a separate
+    # pass after the timed one, so the events do not enter the reported throughput)
+    n_dist = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    for j in range(n_dist):
+        evs[j][0].record(stream)
+        step_graphs[(args.warmup + j) % cycle].replay()
+        evs[j][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
     ebytes = spec.expert_bytes()
     sbytes = spec.expert_bytes(spec.I_shared) if spec.I_shared else 0
     bytes_per_fwd = float(np.mean(n_uniq)) * ebytes + sbytes
@@ -209,8 +220,10 @@ def main():
                 "avg_launch_us": round(fwd_us, 2)}
     else:
         achieved = flops_per_step / (fwd_s / n_fwd) / 1e12
+        traffic = measured_traffic(args.config, T, True)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "kernel": "moe_forward (gate/up + down expert-FFN kernels)",
                 "algorithmic_flops_per_launch": flops_per_step,
                 "avg_launch_us": round(fwd_us, 2)}
@@ -237,6 +250,7 @@ def main():
                    "assignments_per_unique_expert": round(T * spec.k / float(np.mean(n_uniq)), 2),
                    "permute_us_alone": round(perm_us, 2),
                    "timing": "HIP graph per step (the four ABI calls), replayed",
+                   "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
                    "path": args.path, "setup_s": round(setup_s, 1)},
         "roofline": roof,
     }

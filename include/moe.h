@@ -140,12 +140,26 @@ MOE_API int moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t
  * reading its weights once for all of them; results go to y_perm[p] (fp32,
  * [A][d]).  The shared expert (shared != NULL, shape->I_shared > 0) is
  * applied to every token; its output goes to y_shared [T][d] fp32.
- * Accumulation is fp32; the MFMA path rounds h to fp16 between the two
- * products.  `routed` describes E experts, `shared` one.
+ * Accumulation is fp32; between the two products the matrix-core path
+ * keeps h as fp16 plus its residual in fp6 (e2m3) under one power-of-two
+ * scale per row and 32 channels.  `routed` describes E experts, `shared` one.
+ *
+ * diag (optional, NULL = none; 4-byte alignment suffices): MOE_DIAG_COUNT
+ * uint32 device counters that the call adds to (the caller zeroes them;
+ * they never fail the call):
+ *   diag[MOE_DIAG_H_FP16_NONFINITE]  values of h, over every row and channel
+ *       of this call, that are not finite once rounded to fp16 on the
+ *       matrix-core path (|h| beyond the fp16 range, or a non-finite h);
+ *       such values make the outputs they enter non-finite.  The decode
+ *       path keeps h in fp32 and adds nothing.
+ * Near ties of the selection are reported by moe_route's gap output.
  */
+#define MOE_DIAG_H_FP16_NONFINITE 0
+#define MOE_DIAG_COUNT 1
+
 MOE_API int moe_forward(const moe_shape *shape, const void *x, const moe_qffn *routed, const moe_qffn *shared,
                 const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
-                float *y_perm, float *y_shared, void *ws, size_t ws_bytes, void *stream);
+                float *y_perm, float *y_shared, uint32_t *diag, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Weighted combine:

@@ -24,6 +24,10 @@ MOE_EDEVICE = -5
 MOE_ACT_F32 = 0
 MOE_ACT_BF16 = 1
 
+# moe_forward's diagnostic counters
+MOE_DIAG_H_FP16_NONFINITE = 0
+MOE_DIAG_COUNT = 1
+
 MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_GEMM = 2
@@ -68,7 +72,7 @@ def lib():
         L.moe_workspace_size.restype = C.c_size_t
         L.moe_route.argtypes = [S, P, P, P, P, P, P, P, C.c_size_t, P]
         L.moe_permute.argtypes = [S, P, P, P, P, P, P, P, P, C.c_size_t, P]
-        L.moe_forward.argtypes = [S, P, Q, Q, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_forward.argtypes = [S, P, Q, Q, P, P, P, P, P, P, P, P, C.c_size_t, P]
         L.moe_combine.argtypes = [S, P, P, P, P, P, P]
         for f in ("moe_route", "moe_permute", "moe_forward", "moe_combine", "moe_abi_version"):
             getattr(L, f).restype = C.c_int
@@ -133,12 +137,12 @@ def moe_permute(shape, topk_idx, counts, offsets, perm, inv, uniq, n_uniq, ws, w
 
 
 def moe_forward(shape, x, routed: moe_qffn, shared: Optional[moe_qffn], offsets, perm, uniq, n_uniq, y_perm,
-                y_shared, ws, ws_bytes=None, stream=None) -> None:
+                y_shared, diag, ws, ws_bytes=None, stream=None) -> None:
     ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib().moe_forward(C.byref(shape), _ptr(x), C.byref(routed),
                              C.byref(shared) if shared is not None else None, _ptr(offsets), _ptr(perm),
-                             _ptr(uniq), _ptr(n_uniq), _ptr(y_perm), _ptr(y_shared), _ptr(ws), ws_bytes,
-                             _stream(stream)))
+                             _ptr(uniq), _ptr(n_uniq), _ptr(y_perm), _ptr(y_shared), _ptr(diag), _ptr(ws),
+                             ws_bytes, _stream(stream)))
 
 
 def moe_combine(shape, y_perm, y_shared, inv, topk_w, y, stream=None) -> None:

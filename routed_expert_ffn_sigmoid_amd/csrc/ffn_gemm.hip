@@ -734,6 +734,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 const int pc = (int)(hp & 31);
                 const int tcol = ((pc & 1) << 4) | (pc >> 1);
                 auto tix = [](int m, int col) { return m * 32 + ((((col >> 2) ^ m) & 7) << 2) + (col & 3); };
+                uint32_t nonfinite = 0;  // h values of this lane that fp16 cannot hold
 #pragma unroll
                 for (int mm = 0; mm < MU; mm++) {
 #pragma unroll
@@ -749,9 +750,12 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                         const uint32_t mo = mkI + (uint32_t)mrow(mm, r) * (uint32_t)I;
                         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hh), hhr, (int)(2 * mo + o2), 0, 0);
                         // rows past the tile and columns past the output give zeros (the block maximum ignores them)
-                        tr[tix(m, tcol)] = (c < nout && m < rows) ? hv - (float)hh : 0.f;
+                        const bool valid = c < nout && m < rows;
+                        tr[tix(m, tcol)] = valid ? hv - (float)hh : 0.f;
+                        nonfinite += (valid && (__builtin_bit_cast(uint16_t, hh) & 0x7C00u) == 0x7C00u) ? 1u : 0u;
                     }
                 }
+                if (P.diag && nonfinite) atomicAdd(P.diag, nonfinite);
                 __syncthreads();
                 // Lane L takes rows L and L + 64 (those of the MU blocks): the block exponent S puts the largest
                 // residual magnitude into [4, 7.75), the top binade of e2m3 (into [2, 4) where it would round

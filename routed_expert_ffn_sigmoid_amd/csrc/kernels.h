@@ -24,6 +24,7 @@ struct FfnParams {
     const int32_t *offsets, *perm, *uniq, *n_uniq;
     int n_routed_slots;  // min(E, A): grid slots reserved for routed experts
     float *y_perm, *y_sh;
+    uint32_t *diag;      // optional counters (nullptr = none): [0] h values not finite in fp16
 };
 
 // router.hip

@@ -114,7 +114,7 @@ int launch_status(const char *fn, hipError_t err) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 const char *moe_last_error(void) { return g_err; }
 
@@ -166,7 +166,7 @@ int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, in
 
 int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
                 const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
-                float *y_perm, float *y_shared, void *ws, size_t ws_bytes, void *stream) {
+                float *y_perm, float *y_shared, uint32_t *diag, void *ws, size_t ws_bytes, void *stream) {
     const char *fn = "moe_forward";
     int rc = check_shape(fn, s);
     if (rc) return rc;
@@ -183,6 +183,7 @@ int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const
     REQUIRE_PTR(uniq, "uniq");
     REQUIRE_PTR(n_uniq, "n_uniq");
     REQUIRE_PTR(y_perm, "y_perm");
+    if (diag && !aligned(diag, 4)) return fail(MOE_EALIGN, "%s: diag is not 4-byte aligned", fn);
     rc = check_ws(fn, s, ws, ws_bytes);
     if (rc) return rc;
     moe::FfnParams P = ffn_params(s);
@@ -195,6 +196,7 @@ int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const
     P.n_uniq = n_uniq;
     P.y_perm = y_perm;
     P.y_sh = s->I_shared > 0 ? y_shared : nullptr;
+    P.diag = diag;
     const int path = forward_path(s);
     hipError_t err;
     if (path == MOE_PATH_GEMM) {

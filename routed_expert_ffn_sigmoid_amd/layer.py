@@ -110,6 +110,8 @@ class MoeRun:
         self.y_shared = torch.empty((T, d), dtype=torch.float32, device=device) if spec.I_shared > 0 else None
         self.y = torch.empty((T, d), dtype=torch.float32, device=device)
         self.ws = torch.empty(max(B.moe_workspace_size(self.shape), 256), dtype=torch.uint8, device=device)
+        # moe_forward's diagnostic counters (uint32 in the ABI), added to by every forward call
+        self.diag = torch.zeros(B.MOE_DIAG_COUNT, dtype=torch.int32, device=device)
 
     def route(self, x, W: DeviceLayerWeights, stream=None):
         B.moe_route(self.shape, x, W.W_r, W.bias, self.idx, self.w, self.gap, self.ws, stream=stream)
@@ -120,7 +122,7 @@ class MoeRun:
 
     def forward(self, x, W: DeviceLayerWeights, stream=None):
         B.moe_forward(self.shape, x, W.routed_q, W.shared_q, self.offsets, self.perm, self.uniq, self.n_uniq,
-                      self.y_perm, self.y_shared, self.ws, stream=stream)
+                      self.y_perm, self.y_shared, self.diag, self.ws, stream=stream)
 
     def combine(self, stream=None):
         B.moe_combine(self.shape, self.y_perm, self.y_shared, self.inv, self.w, self.y, stream=stream)

@@ -74,6 +74,10 @@ def test_null_and_misaligned_pointers():
     with pytest.raises(B.MoeError) as ei:
         B.moe_combine(s, FAKE, None, FAKE, FAKE, None, stream=0)
     assert ei.value.code == B.MOE_EINVAL
+    q = B.make_qffn(*([FAKE] * 9))
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward(s, FAKE, q, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 2, FAKE, 1 << 30, stream=0)
+    assert ei.value.code == B.MOE_EALIGN and "diag" in str(ei.value)
 
 
 def test_workspace_checks():
@@ -95,11 +99,11 @@ def test_forward_requires_shared_weights_when_configured():
     s = shape(I_shared=256)
     q = B.make_qffn(*([FAKE] * 9))
     with pytest.raises(B.MoeError) as ei:
-        B.moe_forward(s, FAKE, q, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
+        B.moe_forward(s, FAKE, q, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, stream=0)
     assert ei.value.code == B.MOE_EINVAL and "shared" in str(ei.value)
     bad = B.make_qffn(*([FAKE] * 8 + [None]))
     with pytest.raises(B.MoeError) as ei:
-        B.moe_forward(s, FAKE, bad, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
+        B.moe_forward(s, FAKE, bad, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, stream=0)
     assert ei.value.code == B.MOE_EINVAL and "z_down" in str(ei.value)
 
 

@@ -211,6 +211,63 @@ def test_repeat_is_bitwise_deterministic(dev):
         np.testing.assert_array_equal(o[1], outs[0][1])
 
 
+def _host_h(qm, sc, zp, x):
+    """h = silu(g) * u of int4 expert weights (per-row scale and zero point) for rows x, in fp64."""
+    def deq(q, s, z):
+        w = np.zeros((q.shape[0], q.shape[1] * 2))
+        w[:, 0::2] = q & 15
+        w[:, 1::2] = q >> 4
+        return (w - z[:, None]) * s[:, None]
+    g = x @ deq(qm[0], sc[0], zp[0]).T
+    u = x @ deq(qm[1], sc[1], zp[1]).T
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def test_diag_counts_h_beyond_fp16(dev):
+    """moe_forward's diag counter: scales of expert 0's gate and up rows raised 1000x put some h of its rows
+    beyond the fp16 range.  The matrix-core path counts exactly those values; repeated calls add to the counter;
+    the decode path (h in fp32) adds nothing; diag = NULL is accepted."""
+    kw, T = GEMM["gemm_int4_shared"]
+    spec = spec_of(**kw)
+
+    def tweak(inp):
+        inp.routed.s_gate[0] *= np.float32(1000.0)
+        inp.routed.s_up[0] *= np.float32(1000.0)
+
+    H = HostLayer(spec, T, dev, tweak=tweak)
+    x = (H.inp.x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    R = H.inp.routed
+    run = L.MoeRun(spec, T, dev, B.MOE_PATH_GEMM)
+    run.run(H.x, H.W)
+    torch.cuda.synchronize()
+    offsets = run.offsets.cpu().numpy()
+    perm = run.perm.cpu().numpy()
+    rows0 = perm[offsets[0]:offsets[1]] // spec.k
+    assert len(rows0) > 0, "expert 0 unused: the case no longer exercises the counter"
+    hs = [_host_h((R.q_gate[e], R.q_up[e]), (R.s_gate[e], R.s_up[e]), (R.z_gate[e], R.z_up[e]),
+                  x[perm[offsets[e]:offsets[e + 1]] // spec.k]) for e in range(spec.E) if offsets[e + 1] > offsets[e]]
+    S = H.inp.shared
+    hs.append(_host_h((S.q_gate[0], S.q_up[0]), (S.s_gate[0], S.s_up[0]), (S.z_gate[0], S.z_up[0]), x))
+    a = np.abs(np.concatenate([h.ravel() for h in hs]))
+    # fp16 rounds magnitudes from 65520 up to infinity; h itself is computed in fp32 on the GPU
+    lo, hi = int(np.sum(a > 65520 * 1.001)), int(np.sum(a >= 65520 * 0.999))
+    got = int(run.diag.cpu().numpy()[B.MOE_DIAG_H_FP16_NONFINITE])
+    say(f"   diag {got}, host count in [{lo}, {hi}] of {a.size} h values")
+    assert lo > 0 and lo <= got <= hi
+    run.forward(H.x, H.W)
+    torch.cuda.synchronize()
+    assert int(run.diag.cpu().numpy()[0]) == 2 * got
+    y_perm = run.y_perm.cpu().numpy().copy()
+    B.moe_forward(run.shape, H.x, H.W.routed_q, H.W.shared_q, run.offsets, run.perm, run.uniq, run.n_uniq,
+                  run.y_perm, run.y_shared, None, run.ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(run.y_perm.cpu().numpy(), y_perm)
+    gv = L.MoeRun(spec, T, dev, B.MOE_PATH_GEMV)
+    gv.run(H.x, H.W)
+    torch.cuda.synchronize()
+    assert int(gv.diag.cpu().numpy()[0]) == 0
+
+
 def test_permute_adversarial(orc, dev):
     """moe_permute on hand-made index arrays: skewed, single expert, all experts, large A."""
     rng = np.random.default_rng(7)
