@@ -293,9 +293,10 @@ __device__ __forceinline__ void wave_argmax(double &v, int &id) {
 }
 
 // One workgroup (1024 threads) per token.  Thread (e, g) sums the splits s = g, g+4, ... of expert e
-// (fixed order), the four groups are added in order; then the first wavefront takes sigmoid and bias
-// and picks the top k+1.  Each lane holds EJ experts (e = lane + 64 j), sorts them once, and exposes
-// its best unchosen one; each round is one wave-wide argmax and the winning lane moves to its next.
+// (fixed order); thread (e, 0) adds the four groups in order and takes sigmoid and bias (one expert per
+// thread, so the code holds one copy of exp and the sigmoids run in parallel); then the first wavefront
+// picks the top k+1.  Each lane holds EJ experts (e = lane + 64 j), sorts them once, and exposes its
+// best unchosen one; each round is one wave-wide argmax and the winning lane moves to its next.
 constexpr int RSEL_THREADS = 1024;
 constexpr int RSEL_LOADS = 8;
 
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
     const int tid = threadIdx.x, lane = tid & 63;
     const int ept = (E + 255) / 256;  // experts per thread column
     const rsrc_t psrc = make_rsrc(part, (uint32_t)((long)nsplit * T * E * 8));
+    const float bz = tid < E ? bias[tid] : 0.f;  // requested now, used after the sums (E <= RSEL_THREADS)
     for (int j = 0; j < ept; j++) {
         const int e = (tid & 255) + 256 * j;
         const int g = tid >> 8;
@@ -331,6 +333,15 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
         zs[g * E + e] = z;
     }
     __syncthreads();
+    // s and sel of expert e replace its first two partial sums (each thread touches only its own entries)
+    if (tid < E) {
+        const int e = tid;
+        const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
+        const double sv = 1.0 / (1.0 + exp(-z));
+        zs[e] = sv;
+        zs[E + e] = sv + (double)bz;
+    }
+    __syncthreads();
     if (tid >= 64) return;
     // this lane's candidates, sorted best first
     double cv[EJ], cs[EJ];
@@ -342,9 +353,8 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
         cs[j] = 0.0;
         ci[j] = 0x7fffffff;
         if (e < E) {
-            const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
-            cs[j] = 1.0 / (1.0 + exp(-z));
-            cv[j] = cs[j] + (double)bias[e];
+            cs[j] = zs[e];
+            cv[j] = zs[E + e];
             ci[j] = e;
         }
     }
