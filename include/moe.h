@@ -34,6 +34,10 @@
  *     every output untouched.  moe_last_error() gives a message for the
  *     calling thread's last failure.
  *   - Pointer arguments must be 16-byte aligned (MOE_EALIGN otherwise).
+ *   - T = 0 (an empty batch) is valid.  The calls check the rest of their
+ *     arguments and return MOE_OK; pointers to T-sized arrays may then be
+ *     NULL.  moe_permute still writes its E-sized outputs (zero counts and
+ *     offsets, uniq all -1, n_uniq 0); the other calls enqueue nothing.
  *
  * Shapes and layouts
  *   T tokens, d hidden size, E routed experts, k experts per token,

@@ -26,11 +26,16 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
         if (!(p)) return fail(MOE_EINVAL, "%s: %s is NULL", fn, name);           \
         if (!aligned((p), 16)) return fail(MOE_EALIGN, "%s: %s is not 16-byte aligned", fn, name); \
     } while (0)
+// a pointer to T-sized data: may be NULL when T = 0 (nothing is read or written through it then)
+#define REQUIRE_PTR_T(p, name)                                                   \
+    do {                                                                         \
+        if (s->T > 0 || (p)) REQUIRE_PTR(p, name);                               \
+    } while (0)
 
 int check_shape(const char *fn, const moe_shape *s) {
     if (!s) return fail(MOE_EINVAL, "%s: shape is NULL", fn);
-    if (s->T < 1 || s->d < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->I_shared < 0)
-        return fail(MOE_EINVAL, "%s: T, d, E, k, I must be >= 1 and I_shared >= 0", fn);
+    if (s->T < 0 || s->d < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->I_shared < 0)
+        return fail(MOE_EINVAL, "%s: d, E, k, I must be >= 1 and T, I_shared >= 0", fn);
     if (s->k > s->E || s->k > 32) return fail(MOE_EINVAL, "%s: k=%d must be <= min(E, 32)", fn, s->k);
     if (s->E > 1024) return fail(MOE_EINVAL, "%s: E=%d exceeds 1024", fn, s->E);
     if ((long)s->T * s->k >= (1L << 31)) return fail(MOE_EINVAL, "%s: T*k overflows int32", fn);
@@ -134,14 +139,15 @@ int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *
     const char *fn = "moe_route";
     int rc = check_shape(fn, s);
     if (rc) return rc;
-    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR_T(x, "x");
     REQUIRE_PTR(W_r, "W_r");
     REQUIRE_PTR(bias, "bias");
-    REQUIRE_PTR(topk_idx, "topk_idx");
-    REQUIRE_PTR(topk_w, "topk_w");
+    REQUIRE_PTR_T(topk_idx, "topk_idx");
+    REQUIRE_PTR_T(topk_w, "topk_w");
     if (gap && !aligned(gap, 16)) return fail(MOE_EALIGN, "%s: gap is not 16-byte aligned", fn);
     rc = check_ws(fn, s, ws, ws_bytes);
     if (rc) return rc;
+    if (s->T == 0) return MOE_OK;  // empty batch: nothing to route
     return launch_status(fn, moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
                                                 topk_idx, topk_w, gap, ws, (hipStream_t)stream));
 }
@@ -151,11 +157,11 @@ int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, in
     const char *fn = "moe_permute";
     int rc = check_shape(fn, s);
     if (rc) return rc;
-    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR_T(topk_idx, "topk_idx");
     REQUIRE_PTR(counts, "counts");
     REQUIRE_PTR(offsets, "offsets");
-    REQUIRE_PTR(perm, "perm");
-    REQUIRE_PTR(inv, "inv");
+    REQUIRE_PTR_T(perm, "perm");
+    REQUIRE_PTR_T(inv, "inv");
     REQUIRE_PTR(uniq, "uniq");
     REQUIRE_PTR(n_uniq, "n_uniq");
     rc = check_ws(fn, s, ws, ws_bytes);
@@ -170,22 +176,23 @@ int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const
     const char *fn = "moe_forward";
     int rc = check_shape(fn, s);
     if (rc) return rc;
-    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR_T(x, "x");
     rc = check_qffn(fn, routed, "routed");
     if (rc) return rc;
     if (s->I_shared > 0) {
         rc = check_qffn(fn, shared, "shared");
         if (rc) return rc;
-        REQUIRE_PTR(y_shared, "y_shared");
+        REQUIRE_PTR_T(y_shared, "y_shared");
     }
     REQUIRE_PTR(offsets, "offsets");
-    REQUIRE_PTR(perm, "perm");
+    REQUIRE_PTR_T(perm, "perm");
     REQUIRE_PTR(uniq, "uniq");
     REQUIRE_PTR(n_uniq, "n_uniq");
-    REQUIRE_PTR(y_perm, "y_perm");
+    REQUIRE_PTR_T(y_perm, "y_perm");
     if (diag && !aligned(diag, 4)) return fail(MOE_EALIGN, "%s: diag is not 4-byte aligned", fn);
     rc = check_ws(fn, s, ws, ws_bytes);
     if (rc) return rc;
+    if (s->T == 0) return MOE_OK;  // empty batch: no rows to transform
     moe::FfnParams P = ffn_params(s);
     P.x = x;
     P.routed = to_qw(routed);
@@ -214,11 +221,12 @@ int moe_combine(const moe_shape *s, const float *y_perm, const float *y_shared, 
     const char *fn = "moe_combine";
     int rc = check_shape(fn, s);
     if (rc) return rc;
-    REQUIRE_PTR(y_perm, "y_perm");
-    REQUIRE_PTR(inv, "inv");
-    REQUIRE_PTR(topk_w, "topk_w");
-    REQUIRE_PTR(y, "y");
+    REQUIRE_PTR_T(y_perm, "y_perm");
+    REQUIRE_PTR_T(inv, "inv");
+    REQUIRE_PTR_T(topk_w, "topk_w");
+    REQUIRE_PTR_T(y, "y");
     if (y_shared && !aligned(y_shared, 16)) return fail(MOE_EALIGN, "%s: y_shared is not 16-byte aligned", fn);
+    if (s->T == 0) return MOE_OK;  // empty batch
     return launch_status(fn, moe::launch_combine(y_perm, y_shared, inv, topk_w, s->T, s->d, s->k, y,
                                                  (hipStream_t)stream));
 }

@@ -448,6 +448,7 @@ int router_nsplit(int T, int d, int E) {
 }
 
 size_t router_workspace_bytes(int T, int d, int E) {
+    if (T <= 0) return 0;
     return (size_t)router_nsplit(T, d, E) * (size_t)T * (size_t)E * sizeof(double);
 }
 

@@ -43,7 +43,7 @@ def shape(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(k=9), B.MOE_EINVAL),           # k > E
     (dict(k=0), B.MOE_EINVAL),
-    (dict(T=0), B.MOE_EINVAL),
+    (dict(T=-1), B.MOE_EINVAL),
     (dict(E=2048, k=2), B.MOE_EINVAL),   # E > 1024
     (dict(E=64, k=33), B.MOE_EINVAL),    # k > 32
     (dict(wbits=4, d=48), B.MOE_EINVAL),  # int4 needs multiples of 32
@@ -105,6 +105,23 @@ def test_forward_requires_shared_weights_when_configured():
     with pytest.raises(B.MoeError) as ei:
         B.moe_forward(s, FAKE, bad, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, stream=0)
     assert ei.value.code == B.MOE_EINVAL and "z_down" in str(ei.value)
+
+
+def test_empty_batch_is_a_no_op():
+    """T = 0: the shape is valid, T-sized pointers may be NULL, and route, forward and combine return OK
+    without enqueueing anything (so this runs without a GPU).  Non-power-of-two E takes the router's
+    matrix-core sizing, which must not divide by the empty token count."""
+    for E in (16, 12):
+        s = shape(T=0, E=E)
+        need = B.moe_workspace_size(s)
+        assert need > 0
+        B.moe_route(s, None, FAKE, FAKE, None, None, None, FAKE, need, stream=0)
+        q = B.make_qffn(*([FAKE] * 9))
+        B.moe_forward(s, None, q, None, FAKE, None, FAKE, FAKE, None, None, None, FAKE, need, stream=0)
+        B.moe_combine(s, None, None, None, None, None, stream=0)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(shape(T=0), None, None, FAKE, None, None, None, FAKE, 1 << 20, stream=0)
+    assert ei.value.code == B.MOE_EINVAL and "W_r" in str(ei.value)
 
 
 def test_workspace_size_covers_every_call():

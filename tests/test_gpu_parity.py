@@ -269,6 +269,23 @@ def test_diag_counts_h_beyond_fp16(dev):
     assert int(gv.diag.cpu().numpy()[0]) == 0
 
 
+def test_empty_batch(dev):
+    """T = 0 through the whole layer: route, forward and combine do nothing, and moe_permute writes its
+    E-sized outputs for an empty assignment list."""
+    spec = spec_of(d=512, E=16, k=4, I=352, I_shared=96)
+    H = HostLayer(spec, 0, dev)
+    run = L.MoeRun(spec, 0, dev)
+    run.counts.fill_(7)
+    run.offsets.fill_(7)
+    run.uniq.fill_(7)
+    run.n_uniq.fill_(7)
+    run.run(H.x, H.W)
+    torch.cuda.synchronize()
+    assert not run.counts.cpu().numpy().any() and not run.offsets.cpu().numpy().any()
+    assert int(run.n_uniq.item()) == 0 and (run.uniq.cpu().numpy() == -1).all()
+    assert run.y.shape == (0, spec.d)
+
+
 def test_permute_adversarial(orc, dev):
     """moe_permute on hand-made index arrays: skewed, single expert, all experts, large A."""
     rng = np.random.default_rng(7)
