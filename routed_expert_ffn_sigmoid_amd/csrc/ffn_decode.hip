@@ -539,7 +539,9 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
 // [c*N/ncu, (c+1)*N/ncu).  The S wavefronts of a tile split its K range and TPW = DKP_WAVES / S
 // tiles share an item, so every wavefront of a CU works on the same item and the CU's items end
 // together.  Each wavefront's weight stream runs across items: while it consumes the last batch of
-// an item, the refills already fetch the first segments of the next item.
+// an item, the refills already fetch the first segments of the next item.  PF loads per matrix are in
+// flight (16 KB per wavefront); the host picks PF among two depths so that the item's segments fill
+// whole batches where they can.
 //
 // Start-up takes two memory round trips: the routing tables (unique list, offsets, permutation) go to
 // LDS in one round together with the first activation rows; the weight stream starts right after.
@@ -558,14 +560,13 @@ __host__ __device__ inline int dkp_tab_words(int mode, int n_routed_slots, int E
     return 1 + n_routed_slots + E + 1 + (mode == 0 ? A : 0);
 }
 
-template <int MODE, int WBITS, int SRC, int S>
+template <int MODE, int WBITS, int SRC, int S, int PF>
 __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(FfnParams P, float *__restrict__ h,
                                                                            float *__restrict__ h_sh, int kpad,
                                                                            int tiles_r, int tiles_s, int ncu) {
     constexpr int NW = DKP_WAVES;
     constexpr int TPW = NW / S;
     constexpr int NM = MODE == 0 ? 2 : 1;
-    constexpr int PF = MODE == 0 ? 8 : 16;  // 16 weight loads in flight per wavefront
     constexpr int SRCX = MODE == 0 ? SRC : 0;
     extern __shared__ __align__(16) uint8_t dk_lds[];
     __shared__ int wexpo[NW][DK_GMAX];
@@ -997,7 +998,16 @@ constexpr size_t DKP_LDS_BUDGET = 150 * 1024;  // routing table + digit planes (
 
 static size_t dkp_red_bytes(int mode) { return (size_t)DKP_WAVES * (mode == 0 ? 2 : 1) * 4 * 64 * 8; }
 
-static int dkp_pf(int mode) { return mode == 0 ? 8 : 16; }
+// Weight loads in flight per wavefront and matrix: 8 or 7 for gate/up (two matrices), 16 or 14 for down, 16
+// loads of 1 KB either way.  An item's segments are consumed in batches of PF, the last one padded with
+// loads that read nothing; a padded place carries no data, so fewer bytes are in flight while it waits.
+// The depth that pads least is taken (7 for the 7 segments of the large workload's gate/up wavefronts, 14
+// for the 28 of the mid workload's down wavefronts); ties go to the deeper one.
+static int dkp_pf(int mode, int nseg) {
+    const int a = mode == 0 ? 8 : 16, b = mode == 0 ? 7 : 14;
+    const int pad_a = (nseg + a - 1) / a * a - nseg, pad_b = (nseg + b - 1) / b * b - nseg;
+    return pad_b < pad_a ? b : a;
+}
 
 // K split of the persistent kernel: the S in {8, 4, 2, 1} (whole 16-byte chunks per wavefront).
 // Gate/up: the least work on the busiest CU at the largest possible slot count, counted as items x tiles
@@ -1009,7 +1019,6 @@ static int dkp_pf(int mode) { return mode == 0 ? 8 : 16; }
 static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, int wbits, int ncu) {
     const int chunk_inputs = wbits == 8 ? 16 : 32;
     const int nseg_full = (K * wbits / 8 + 63) / 64;
-    const int pf = dkp_pf(mode);
     int best = 1;
     double best_cost = -1;
     for (int i = 0; i < 4; i++) {
@@ -1017,6 +1026,7 @@ static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, in
         if (K % (S * chunk_inputs)) continue;
         const int tpw = DKP_WAVES / S;
         const int nseg = (nseg_full + S - 1) / S;
+        const int pf = dkp_pf(mode, nseg);
         const int nseg_pad = (nseg + pf - 1) / pf * pf;
         const long tiles = (nout + 16 * tpw - 1) / (16 * tpw);
         double cost;
@@ -1041,13 +1051,13 @@ static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad) {
     return tab + (size_t)S * 3 * P.T * (kpad + 16) + dkp_red_bytes(mode);
 }
 
-template <int MODE, int WBITS, int SRC, int S>
+template <int MODE, int WBITS, int SRC, int S, int PF>
 static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, hipStream_t stream) {
     const int rows_per_item = 16 * (DKP_WAVES / S);
     const int tiles_r = ((MODE == 0 ? P.I : P.d) + rows_per_item - 1) / rows_per_item;
     const int tiles_s = P.Is > 0 ? ((MODE == 0 ? P.Is : P.d) + rows_per_item - 1) / rows_per_item : 0;
     const size_t lds = dkp_lds_bytes(MODE, S, P, kpad);
-    auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S>;
+    auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S, PF>;
     hipError_t err = allow_lds(fn, lds);
     if (err != hipSuccess) return err;
     const int ncu = device_cus();
@@ -1078,11 +1088,17 @@ static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t
         dkp_lds_bytes(MODE, S, P, kpad) > DKP_LDS_BUDGET)
         return hipSuccess;
     *done = true;
+    constexpr int PFA = MODE == 0 ? 8 : 16, PFB = MODE == 0 ? 7 : 14;
+    const bool deep = dkp_pf(MODE, (K / S * WBITS / 8 + 63) / 64) == PFA;
     switch (S) {
-        case 8: return dkp_launch_s<MODE, WBITS, SRC, 8>(P, h, h_sh, kpad, stream);
-        case 4: return dkp_launch_s<MODE, WBITS, SRC, 4>(P, h, h_sh, kpad, stream);
-        case 2: return dkp_launch_s<MODE, WBITS, SRC, 2>(P, h, h_sh, kpad, stream);
-        default: return dkp_launch_s<MODE, WBITS, SRC, 1>(P, h, h_sh, kpad, stream);
+        case 8: return deep ? dkp_launch_s<MODE, WBITS, SRC, 8, PFA>(P, h, h_sh, kpad, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 8, PFB>(P, h, h_sh, kpad, stream);
+        case 4: return deep ? dkp_launch_s<MODE, WBITS, SRC, 4, PFA>(P, h, h_sh, kpad, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 4, PFB>(P, h, h_sh, kpad, stream);
+        case 2: return deep ? dkp_launch_s<MODE, WBITS, SRC, 2, PFA>(P, h, h_sh, kpad, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 2, PFB>(P, h, h_sh, kpad, stream);
+        default: return deep ? dkp_launch_s<MODE, WBITS, SRC, 1, PFA>(P, h, h_sh, kpad, stream)
+                             : dkp_launch_s<MODE, WBITS, SRC, 1, PFB>(P, h, h_sh, kpad, stream);
     }
 }
 
