@@ -62,8 +62,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                              "(python -m routed_expert_ffn_sigmoid_amd.build)")
+            raise ImportError(f"{LIB_PATH} is not built; run python -m routed_expert_ffn_sigmoid_amd.build")
         L = C.CDLL(LIB_PATH)
         P = C.c_void_p
         S = C.POINTER(moe_shape)

@@ -588,8 +588,8 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     int8_t *planes = (int8_t *)dk_lds + ((tab_words * 4 + 15) & ~15) + (long)kp * 3 * pb;
     double *red = (double *)(dk_lds + ((tab_words * 4 + 15) & ~15) + (long)S * 3 * pb);
 
-    // ---- round 1: routing table and (gate/up) this wavefront's first activation row, all requested
-    // before any of them is waited for
+    // ---- first memory round trip: routing table and (gate/up) this wavefront's first activation row, all
+    // requested before any of them is waited for
     const int kd = MODE == 0 ? P.d : 0;
     const rsrc_t xsrc0 = make_rsrc(P.x, (uint32_t)((long)T * P.d * (SRC == 0 ? 4 : 2)));
     StageRaw<SRCX> raw0;
