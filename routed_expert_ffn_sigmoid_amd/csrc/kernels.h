@@ -34,8 +34,9 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
 
 // permute.hip
 size_t permute_lds_bytes(int E);
+size_t permute_workspace_bytes(int A, int E);  // the multi-block path's histograms (0 below its threshold)
 hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
-                          int32_t *inv, int32_t *uniq, int32_t *n_uniq, hipStream_t stream);
+                          int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws, hipStream_t stream);
 
 // ffn_decode.hip: decode path, int8 MFMA with exact integer accumulation (h kept in fp32 in the workspace)
 size_t decode_workspace_bytes(const FfnParams &P);

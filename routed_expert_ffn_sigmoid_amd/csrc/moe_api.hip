@@ -131,6 +131,8 @@ size_t moe_workspace_size(const moe_shape *s) {
     size_t need = r > g ? r : g;
     size_t m = moe::gemm_workspace_bytes(P);
     if (m > need) need = m;
+    const size_t pm = moe::permute_workspace_bytes(s->T * s->k, s->E);
+    if (pm > need) need = pm;
     return (need + 255) & ~(size_t)255;
 }
 
@@ -167,7 +169,7 @@ int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, in
     rc = check_ws(fn, s, ws, ws_bytes);
     if (rc) return rc;
     return launch_status(fn, moe::launch_permute(topk_idx, s->T * s->k, s->E, counts, offsets, perm, inv, uniq,
-                                                 n_uniq, (hipStream_t)stream));
+                                                 n_uniq, ws, (hipStream_t)stream));
 }
 
 int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,

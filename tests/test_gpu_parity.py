@@ -294,6 +294,8 @@ def test_permute_adversarial(orc, dev):
         (np.stack([rng.permutation(256)[:8] for _ in range(4096)]).astype(np.int32), 256),
         (np.tile(np.arange(8, dtype=np.int32), (5, 1)), 8),
         (np.stack([rng.permutation(1024)[:32] for _ in range(70)]).astype(np.int32), 1024),
+        (np.full((10000, 2), 3, np.int32), 8),  # one expert takes all of a large A (multi-block path)
+        (np.stack([rng.permutation(1024)[:16] for _ in range(600)]).astype(np.int32), 1024),
     ]
     for idx, E in cases:
         T, k = idx.shape
@@ -307,6 +309,35 @@ def test_permute_adversarial(orc, dev):
         for name in ("counts", "offsets", "perm", "inv", "uniq"):
             np.testing.assert_array_equal(getattr(run, name).cpu().numpy(), getattr(p, name), err_msg=name)
         assert int(run.n_uniq.item()) == p.n_uniq
+
+
+def test_permute_invalid_ids(dev):
+    """Expert ids outside [0, E) in topk_idx: n_uniq = -1, those assignments get inv = -1 and no place in perm, and
+    the valid ones keep their stable order (single-workgroup and multi-block paths).  The expected arrays are a
+    numpy stable sort of the valid ids."""
+    rng = np.random.default_rng(11)
+    for T, k, E in ((150, 2, 8), (6000, 4, 64)):
+        idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+        bad = rng.random((T, k)) < 0.01
+        idx[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, E)
+        spec = spec_of(d=64, E=E, k=k, I=32)
+        run = L.MoeRun(spec, T, dev)
+        run.idx.copy_(torch.from_numpy(idx))
+        run.permute()
+        torch.cuda.synchronize()
+        flat = idx.ravel()
+        valid = (flat >= 0) & (flat < E)
+        a_valid = np.flatnonzero(valid)
+        order = a_valid[np.argsort(flat[a_valid], kind="stable")]
+        counts = np.bincount(flat[a_valid], minlength=E)
+        inv = np.full(T * k, -1, np.int64)
+        inv[order] = np.arange(order.size)
+        say(f"[permute-invalid] A={T * k} E={E} invalid={int((~valid).sum())}")
+        assert int(run.n_uniq.item()) == -1
+        np.testing.assert_array_equal(run.counts.cpu().numpy(), counts)
+        np.testing.assert_array_equal(run.offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(counts)]))
+        np.testing.assert_array_equal(run.perm.cpu().numpy()[:order.size], order)
+        np.testing.assert_array_equal(run.inv.cpu().numpy(), inv)
 
 
 # ---------------------------------------------------------------------------
