@@ -560,10 +560,14 @@ __host__ __device__ inline int dkp_tab_words(int mode, int n_routed_slots, int E
     return 1 + n_routed_slots + E + 1 + (mode == 0 ? A : 0);
 }
 
-template <int MODE, int WBITS, int SRC, int S, int PF>
+// PASSES (down only): the digit planes hold gcap < T token rows, so a slot with more rows is taken as
+// several virtual slots of at most gcap rows each, in row order, each streaming the expert's rows again
+// (the mid workload's down pass at T = 4: 3 x 14336 inputs of planes fit the LDS, 4 do not).
+template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES>
 __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(FfnParams P, float *__restrict__ h,
                                                                            float *__restrict__ h_sh, int kpad,
-                                                                           int tiles_r, int tiles_s, int ncu) {
+                                                                           int tiles_r, int tiles_s, int ncu,
+                                                                           int gcap) {
     constexpr int NW = DKP_WAVES;
     constexpr int TPW = NW / S;
     constexpr int NM = MODE == 0 ? 2 : 1;
@@ -584,9 +588,12 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     int *tab = (int *)dk_lds;
     const int *t_uniq = tab + 1, *t_off = tab + 1 + nrs, *t_perm = tab + 2 + nrs + P.E;
     const int stride = kpad + 16;
-    const long pb = (long)T * stride;  // bytes per digit plane of one K part
-    int8_t *planes = (int8_t *)dk_lds + ((tab_words * 4 + 15) & ~15) + (long)kp * 3 * pb;
-    double *red = (double *)(dk_lds + ((tab_words * 4 + 15) & ~15) + (long)S * 3 * pb);
+    const long pb = (long)(PASSES ? gcap : T) * stride;  // bytes per digit plane of one K part
+    const int vwords = PASSES ? nrs + 2 : 0;               // first virtual slot of each slot (PASSES)
+    int *vpre = tab + tab_words;
+    const long pl0 = ((long)(tab_words + vwords) * 4 + 15) & ~15L;
+    int8_t *planes = (int8_t *)dk_lds + pl0 + (long)kp * 3 * pb;
+    double *red = (double *)(dk_lds + pl0 + (long)S * 3 * pb);
 
     // ---- first memory round trip: routing table and (gate/up) this wavefront's first activation row, all
     // requested before any of them is waited for
@@ -628,8 +635,35 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
 
     int nu = __builtin_amdgcn_readfirstlane(tab[0]);
     nu = nu < 0 ? 0 : (nu > nrs ? nrs : nu);
+    int nvr = nu, nvs = P.Is > 0 ? 1 : 0;  // routed and shared (virtual) slots
+    if constexpr (PASSES) {
+        // vpre[s] = first virtual slot of routed slot s (exclusive prefix of its passes), vpre[nu] = their total
+        if (tid < 64) {
+            int carry = 0;
+            for (int b = 0; b < nu; b += 64) {
+                const int sl = b + lane;
+                int np = 0;
+                if (sl < nu) {
+                    const int e = t_uniq[sl];
+                    np = (t_off[e + 1] - t_off[e] + gcap - 1) / gcap;
+                }
+                int incl = np;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int t2 = __shfl_up(incl, o, 64);
+                    if (lane >= o) incl += t2;
+                }
+                if (sl < nu) vpre[sl] = carry + incl - np;
+                carry += __shfl(incl, 63, 64);
+            }
+            if (lane == 0) vpre[nu] = carry;
+        }
+        __syncthreads();
+        nvr = __builtin_amdgcn_readfirstlane(vpre[nu]);
+        nvs = P.Is > 0 ? (T + gcap - 1) / gcap : 0;
+    }
     // item counts stay far below 2^31 / ncu (at most 1025 slots x 2^16 tiles), so 32-bit index math
-    const int N = nu * tiles_r + (P.Is > 0 ? tiles_s : 0);
+    const int N = nvr * tiles_r + nvs * tiles_s;
     // With one tile per item (S = NW) the ranges are cut in half tiles (8 rows): every CU gets the same
     // number of rows to within 8, and a range may begin or end in the middle of a tile, whose rows
     // outside it read and store nothing.  Otherwise the ranges are cut in items.
@@ -663,7 +697,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             if (c >= G) return NU;
             const int p = (int)((long)c * NU / G);
             int st, len;
-            if (p < nu * ur) {
+            if (PASSES || p < nu * ur) {
                 st = p / ur * ur;
                 len = ur;
             } else {
@@ -682,7 +716,35 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
 
     auto decode = [&](int i) {
         DItem it;
-        if (i < nu * tiles_r) {
+        if (PASSES) {
+            const int vs = i / tiles_r;
+            it.slot = vs;
+            it.tile = i % tiles_r;
+            if (vs < nvr) {
+                // routed slot of virtual slot vs: the last s with vpre[s] <= vs
+                int lo = 0, hi = nu - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (vpre[mid] <= vs) lo = mid; else hi = mid - 1;
+                }
+                const int sl = __builtin_amdgcn_readfirstlane(lo);
+                const int q = vs - __builtin_amdgcn_readfirstlane(vpre[sl]);
+                it.e = __builtin_amdgcn_readfirstlane(t_uniq[sl]);
+                it.shared = false;
+                it.I = P.I;
+                const int o0 = __builtin_amdgcn_readfirstlane(t_off[it.e]);
+                const int c = __builtin_amdgcn_readfirstlane(t_off[it.e + 1]) - o0;
+                it.p0 = o0 + q * gcap;
+                it.ng = min(gcap, c - q * gcap);
+            } else {
+                const int q = vs - nvr;
+                it.e = 0;
+                it.shared = true;
+                it.I = P.Is;
+                it.p0 = q * gcap;
+                it.ng = min(gcap, T - q * gcap);
+            }
+        } else if (i < nu * tiles_r) {
             it.slot = i / tiles_r;
             it.tile = i % tiles_r;
             it.e = __builtin_amdgcn_readfirstlane(t_uniq[it.slot]);
@@ -768,7 +830,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         // stream starts.
         const rsrc_t src = h_src(cur);
         const int kpart = cur.I / S;
-        const long base = cur.shared ? 0 : cur.p0;
+        const long base = cur.p0;
         StageRaw<SRCX> raw1;
         const bool st1 = tile_w < cur.ng;
         const long ro1 = (base + tile_w) * cur.I + kp * kpart;
@@ -805,7 +867,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         if (MODE == 1 && cur.slot != staged_slot) {
             const rsrc_t src = h_src(cur);
             const int kpart = cur.I / S;
-            const long base = cur.shared ? 0 : cur.p0;
+            const long base = cur.p0;
             __syncthreads();  // every wavefront is done reading the previous planes
             for (int r = tile_w; r < cur.ng; r += TPW) {
                 const long ro = (base + r) * cur.I + kp * kpart;
@@ -919,7 +981,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
                     } else {
                         const float y = (float)((double)srow[0] * v[0][r]);
                         if (cur.shared)
-                            P.y_sh[(long)i2 * P.d + o] = y;
+                            P.y_sh[(long)(cur.p0 + i2) * P.d + o] = y;
                         else
                             P.y_perm[(long)(cur.p0 + i2) * P.d + o] = y;
                     }
@@ -1046,30 +1108,56 @@ static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, in
     return best;
 }
 
-static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad) {
-    const size_t tab = ((size_t)dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) * 4 + 15) & ~(size_t)15;
-    return tab + (size_t)S * 3 * P.T * (kpad + 16) + dkp_red_bytes(mode);
+// LDS of the persistent kernel with digit planes for g token rows (g < T: token passes, which add the
+// virtual-slot prefix after the routing table)
+static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad, int g) {
+    const int words = dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) + (g < P.T ? P.n_routed_slots + 2 : 0);
+    const size_t tab = ((size_t)words * 4 + 15) & ~(size_t)15;
+    return tab + (size_t)S * 3 * g * (kpad + 16) + dkp_red_bytes(mode);
 }
 
-template <int MODE, int WBITS, int SRC, int S, int PF>
-static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, hipStream_t stream) {
+template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES>
+static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, int gcap, hipStream_t stream) {
     const int rows_per_item = 16 * (DKP_WAVES / S);
     const int tiles_r = ((MODE == 0 ? P.I : P.d) + rows_per_item - 1) / rows_per_item;
     const int tiles_s = P.Is > 0 ? ((MODE == 0 ? P.Is : P.d) + rows_per_item - 1) / rows_per_item : 0;
-    const size_t lds = dkp_lds_bytes(MODE, S, P, kpad);
-    auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S, PF>;
+    const size_t lds = dkp_lds_bytes(MODE, S, P, kpad, gcap);
+    auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S, PF, PASSES>;
     hipError_t err = allow_lds(fn, lds);
     if (err != hipSuccess) return err;
     const int ncu = device_cus();
-    const long items = (long)P.n_routed_slots * tiles_r + tiles_s;
+    // at most: every routed assignment its own virtual slot when passes split the slots
+    const long vslots = PASSES ? (long)P.A + (P.Is > 0 ? (P.T + gcap - 1) / gcap : 0) : 0;
+    const long items = PASSES ? vslots * tiles_r : (long)P.n_routed_slots * tiles_r + tiles_s;
     long grid = ncu;
     if (grid > items) grid = items;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(DKP_WAVES * 64), lds, stream, P, h, h_sh, kpad, tiles_r,
-                       tiles_s, ncu);
+                       tiles_s, ncu, gcap);
     return hipGetLastError();
 }
 
-// Launches the persistent kernel if the digit planes of all T tokens fit; *done tells whether it did.
+// The down pass with token passes (instantiated for the down kernel only).
+template <int MODE, int WBITS, int SRC>
+static hipError_t dkp_launch_pass(const FfnParams &P, float *h, float *h_sh, int kpad, int gcap, int S, bool deep,
+                                  hipStream_t stream) {
+    if constexpr (MODE != 1) {
+        return hipErrorNotSupported;
+    } else {
+        switch (S) {
+            case 8: return deep ? dkp_launch_s<1, WBITS, SRC, 8, 16, true>(P, h, h_sh, kpad, gcap, stream)
+                                : dkp_launch_s<1, WBITS, SRC, 8, 14, true>(P, h, h_sh, kpad, gcap, stream);
+            case 4: return deep ? dkp_launch_s<1, WBITS, SRC, 4, 16, true>(P, h, h_sh, kpad, gcap, stream)
+                                : dkp_launch_s<1, WBITS, SRC, 4, 14, true>(P, h, h_sh, kpad, gcap, stream);
+            case 2: return deep ? dkp_launch_s<1, WBITS, SRC, 2, 16, true>(P, h, h_sh, kpad, gcap, stream)
+                                : dkp_launch_s<1, WBITS, SRC, 2, 14, true>(P, h, h_sh, kpad, gcap, stream);
+            default: return deep ? dkp_launch_s<1, WBITS, SRC, 1, 16, true>(P, h, h_sh, kpad, gcap, stream)
+                                 : dkp_launch_s<1, WBITS, SRC, 1, 14, true>(P, h, h_sh, kpad, gcap, stream);
+        }
+    }
+}
+
+// Launches the persistent kernel if the digit planes of all T tokens fit (for the down pass: of at least one
+// token, the slots then taken in passes); *done tells whether it did.
 template <int MODE, int WBITS, int SRC>
 static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t stream, bool *done) {
     *done = false;
@@ -1084,21 +1172,25 @@ static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t
     int S = dkp_pick_s(MODE, K, nout, slots, slots_exp, WBITS, device_cus());
     while (S > 1 && (Kmin % (S * (WBITS == 8 ? 16 : 32)))) S >>= 1;
     const int kpad = pad_k(K / S, WBITS);
-    if (P.T > DK_GMAX || dkp_tab_words(MODE, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64 ||
-        dkp_lds_bytes(MODE, S, P, kpad) > DKP_LDS_BUDGET)
+    if (P.T > DK_GMAX || dkp_tab_words(MODE, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64)
         return hipSuccess;
+    // token rows the planes hold: all T, or (down) fewer, with the slots taken in passes
+    int gcap = P.T;
+    while (gcap > 0 && dkp_lds_bytes(MODE, S, P, kpad, gcap) > DKP_LDS_BUDGET) gcap--;
+    if (gcap < 1 || (MODE == 0 && gcap < P.T)) return hipSuccess;
     *done = true;
     constexpr int PFA = MODE == 0 ? 8 : 16, PFB = MODE == 0 ? 7 : 14;
     const bool deep = dkp_pf(MODE, (K / S * WBITS / 8 + 63) / 64) == PFA;
+    if (MODE == 1 && gcap < P.T) return dkp_launch_pass<MODE, WBITS, SRC>(P, h, h_sh, kpad, gcap, S, deep, stream);
     switch (S) {
-        case 8: return deep ? dkp_launch_s<MODE, WBITS, SRC, 8, PFA>(P, h, h_sh, kpad, stream)
-                            : dkp_launch_s<MODE, WBITS, SRC, 8, PFB>(P, h, h_sh, kpad, stream);
-        case 4: return deep ? dkp_launch_s<MODE, WBITS, SRC, 4, PFA>(P, h, h_sh, kpad, stream)
-                            : dkp_launch_s<MODE, WBITS, SRC, 4, PFB>(P, h, h_sh, kpad, stream);
-        case 2: return deep ? dkp_launch_s<MODE, WBITS, SRC, 2, PFA>(P, h, h_sh, kpad, stream)
-                            : dkp_launch_s<MODE, WBITS, SRC, 2, PFB>(P, h, h_sh, kpad, stream);
-        default: return deep ? dkp_launch_s<MODE, WBITS, SRC, 1, PFA>(P, h, h_sh, kpad, stream)
-                             : dkp_launch_s<MODE, WBITS, SRC, 1, PFB>(P, h, h_sh, kpad, stream);
+        case 8: return deep ? dkp_launch_s<MODE, WBITS, SRC, 8, PFA, false>(P, h, h_sh, kpad, gcap, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 8, PFB, false>(P, h, h_sh, kpad, gcap, stream);
+        case 4: return deep ? dkp_launch_s<MODE, WBITS, SRC, 4, PFA, false>(P, h, h_sh, kpad, gcap, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 4, PFB, false>(P, h, h_sh, kpad, gcap, stream);
+        case 2: return deep ? dkp_launch_s<MODE, WBITS, SRC, 2, PFA, false>(P, h, h_sh, kpad, gcap, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 2, PFB, false>(P, h, h_sh, kpad, gcap, stream);
+        default: return deep ? dkp_launch_s<MODE, WBITS, SRC, 1, PFA, false>(P, h, h_sh, kpad, gcap, stream)
+                             : dkp_launch_s<MODE, WBITS, SRC, 1, PFB, false>(P, h, h_sh, kpad, gcap, stream);
     }
 }
 

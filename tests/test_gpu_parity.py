@@ -106,6 +106,8 @@ SMALL = {
     "E512_k16_router": (dict(d=256, E=512, k=16, I=64, routed_scale=2.5), 5),
     "E1000_k32_router": (dict(d=128, E=1000, k=32, I=32), 3),
     "E12_nonpow2": (dict(d=256, E=12, k=3, I=64, wbits=8, act=synth.ACT_F32), 8),
+    # down pass whose digit planes hold 3 of the 6 token rows: slots with more rows (and the shared expert) in passes
+    "down_token_passes": (dict(d=256, E=4, k=2, I=14336, I_shared=14336, wbits=8, act=synth.ACT_F32), 6),
     # 256 experts with a short hidden size: four experts per lane in the selection, few W_r rows per split
     "E256_d128_T4": (dict(d=128, E=256, k=8, I=64, I_shared=64, routed_scale=2.5), 4),
 }
