@@ -411,12 +411,13 @@ def test_full_workload_parity(orc, dev, name, T, nsample):
     say(f"   ok rel-L2 {rel:.2e} max-abs/RMS {mx:.2e}")
 
 
-def test_token_output_independent_of_batch(dev):
-    """Batch-shape invariance where the K split matches.  For the large layer the decode launches split K the
-    same way at T = 1 and T = 4, the router's per-token sums do not depend on T (T <= 4), and the expert
-    arithmetic is exact integer work in a fixed order, so each token's output inside a batch of 4 equals, bit for
-    bit, its output computed alone."""
-    spec = synth.CONFIGS["large"]
+@pytest.mark.parametrize("name", ["large", "mid"])
+def test_token_output_independent_of_batch(dev, name):
+    """Batch-shape invariance where the K split matches.  For the large and mid layers the decode launches split
+    K the same way at T = 1 and T = 4 (the mid layer's T = 4 down pass takes its slots in token passes), the
+    router's per-token sums do not depend on T (T <= 4), and the expert arithmetic is exact integer work in a
+    fixed order, so each token's output inside a batch of 4 equals, bit for bit, its output computed alone."""
+    spec = synth.CONFIGS[name]
     W = weights_for(spec, dev)
     x_np = synth.gen_x(spec, 4)
     run4 = L.MoeRun(spec, 4, dev)
