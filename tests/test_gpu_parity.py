@@ -363,7 +363,7 @@ def weights_for(spec, dev, layer=0):
     return W
 
 
-FULL = [("mid", 1, None), ("mid", 4, None), ("large", 1, None), ("large_zipf", 4, None),
+FULL = [("mid", 1, None), ("mid", 4, None), ("mid", 64, 8), ("large", 1, None), ("large_zipf", 4, None),
         ("large_zipf", 512, 24), ("prefill_int4_uniform", 8192, 8), ("prefill_int4_zipf", 8192, 8),
         ("prefill_int8_uniform", 8192, 8), ("prefill_int8_zipf", 8192, 8)]
 
@@ -401,7 +401,7 @@ def test_full_workload_parity(orc, dev, name, T, nsample):
     ro, Y, S, y = so.run(x_np, W_r, bias, tokens)
     y_gpu = run.y.cpu().numpy()[tokens]
     rel, mx = assert_layer_close(y_gpu, y, f"{name} T={T} y (sampled {tokens.size})")
-    if T > 16:  # these run on the matrix-core path
+    if T > 16 and spec.act != synth.ACT_F32:  # bf16 activations above T = 16 run on the matrix-core path
         assert rel <= GEMM_REL_L2, f"y rel-L2 {rel:.3e} above the matrix-core path's {GEMM_REL_L2}"
     inv = run.inv.cpu().numpy()
     yp = run.y_perm.cpu().numpy()
