@@ -53,7 +53,15 @@
  *   moe_qffn for n experts: q_gate, q_up [n][I][in_bytes],
  *   q_down [n][d][I*wbits/8], s_* fp32 and z_* as above, [n][out].
  *   Limits: 1 <= k <= min(E, 32), E <= 1024, T*k < 2^31;
- *   d and I (and I_shared) multiples of 32 for int4 and of 16 for int8.
+ *   d and I (and I_shared) multiples of 32 for int4 and of 16 for int8, and
+ *   below MOE_MAX_DIM (the decode kernels sum up to a whole row of int8
+ *   weight x 8-bit activation-digit products in int32: 2^17 x 2^14 < 2^31).
+ *   Every buffer a kernel reads or writes through a 32-bit offset stays below
+ *   2^31 bytes: x (T*d*4 or T*d*2), one expert matrix (I*d*wbits/8), the
+ *   router's partial sums, and the forward path's intermediate h (decode
+ *   path: T*k*I*4 and T*I_shared*4 bytes; matrix-core path: T*k*I*2).  A
+ *   shape past these limits is rejected with MOE_EUNSUPPORTED before anything
+ *   is enqueued, never computed with wrapped offsets.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -78,6 +86,8 @@ extern "C" {
 #define MOE_EALIGN (-4)       /* pointer not 16-byte (workspace: 256-byte) aligned */
 #define MOE_EDEVICE (-5)      /* kernel launch failed */
 
+#define MOE_MAX_DIM 131072 /* d, I and I_shared must be below this */
+
 #define MOE_ACT_F32 0
 #define MOE_ACT_BF16 1
 
@@ -100,7 +110,12 @@ typedef struct moe_qffn {
     const void *z_gate, *z_up, *z_down;
 } moe_qffn;
 
-/* Bytes of workspace that every call below needs for this shape (host only, no device work). */
+/*
+ * Bytes of workspace that every call below needs for this shape (host only, no device work); 0 for a shape
+ * that check fails.  The workspace is the per-request arena of the Colibri walk-through page
+ * ("企业官网建设流程全解析", section 3.2): sized once from the shape, carved by the calls, never freed between
+ * them, and owned by one request at a time (calls sharing it must be ordered on one stream).
+ */
 MOE_API size_t moe_workspace_size(const moe_shape *shape);
 
 /*
@@ -129,8 +144,13 @@ MOE_API int moe_route(const moe_shape *shape, const void *x, const float *W_r, c
  *   inv[a]         sorted position of assignment a              [A]
  *   uniq[0..n)     experts with counts > 0, ascending; -1 after [E]
  *   n_uniq[0]      number of unique experts                     [1]
- * Integer work, bit-exact and independent of scheduling.  topk_idx entries
- * outside [0, E) are not counted and set n_uniq to -1.
+ * Integer work, bit-exact and independent of scheduling.
+ * Invalid ids: topk_idx entries outside [0, E) are not counted, get no place
+ * in perm, have inv = -1, and set n_uniq to -1 (an error flag for the
+ * caller).  counts/offsets/uniq then describe the valid assignments only;
+ * moe_forward applies every expert listed in uniq (the non-negative prefix)
+ * and moe_combine leaves out the dropped choices, so y[t] is the shared term
+ * plus the token's valid choices.
  */
 MOE_API int moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t *counts, int32_t *offsets, int32_t *perm,
                 int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws, size_t ws_bytes, void *stream);
@@ -146,16 +166,24 @@ MOE_API int moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t
  * applied to every token; its output goes to y_shared [T][d] fp32.
  * Accumulation is fp32; between the two products the matrix-core path
  * keeps h as fp16 plus its residual in fp6 (e2m3) under one power-of-two
- * scale per row and 32 channels.  `routed` describes E experts, `shared` one.
+ * scale per row and 32 channels.  The matrix-core path takes x as fp16
+ * under one power-of-two scale per token (its largest magnitude put into
+ * [2^14, 2^15)), exact for every bf16 value above 2^-29 of the row's
+ * largest, so no range of activations overflows fp16.  The decode path
+ * takes each token's K part as 24-bit fixed point under one power-of-two
+ * scale.  `routed` describes E experts, `shared` one.
  *
  * diag (optional, NULL = none; 4-byte alignment suffices): MOE_DIAG_COUNT
  * uint32 device counters that the call adds to (the caller zeroes them;
  * they never fail the call):
  *   diag[MOE_DIAG_H_FP16_NONFINITE]  values of h, over every row and channel
- *       of this call, that are not finite once rounded to fp16 on the
- *       matrix-core path (|h| beyond the fp16 range, or a non-finite h);
- *       such values make the outputs they enter non-finite.  The decode
- *       path keeps h in fp32 and adds nothing.
+ *       of this call, that are not finite in the fp16 plane of the
+ *       matrix-core path; such values make the outputs they enter
+ *       non-finite.  That path stores h of each row under a power-of-two
+ *       scale taken from a bound on |h| (x's L1 norm times the expert's
+ *       largest |scale| x |q - zp| for gate and for up), so finite inputs
+ *       whose h is finite in fp32 never count here.  The decode path keeps h
+ *       in fp32 and adds nothing.
  * Near ties of the selection are reported by moe_route's gap output.
  */
 #define MOE_DIAG_H_FP16_NONFINITE 0
@@ -166,9 +194,13 @@ MOE_API int moe_forward(const moe_shape *shape, const void *x, const moe_qffn *r
                 float *y_perm, float *y_shared, uint32_t *diag, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Weighted combine:
+ * Weighted combine.  The layer output adds, to the always-on shared expert
+ * (dense part of the model: GLM-5.2 page, section 二), each routed expert's
+ * output scaled by its router weight (GLM-5.2 page, section 四.3: the
+ * routing's scaling semantics, lambda times the normalised selected scores):
  *   y[t] = y_shared[t] + sum_{j=0}^{k-1} topk_w[t][j] * y_perm[inv[t*k + j]]
- * summed in this order in fp32 (y_shared NULL = no shared term).
+ * summed in this order in fp32 (y_shared NULL = no shared term; choices with
+ * inv = -1, dropped by moe_permute for an invalid id, are left out).
  * Output y [T][d] fp32.
  */
 MOE_API int moe_combine(const moe_shape *shape, const float *y_perm, const float *y_shared, const int32_t *inv,

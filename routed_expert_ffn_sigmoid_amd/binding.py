@@ -24,6 +24,8 @@ MOE_EDEVICE = -5
 MOE_ACT_F32 = 0
 MOE_ACT_BF16 = 1
 
+MOE_MAX_DIM = 131072  # d, I and I_shared must be below this
+
 # moe_forward's diagnostic counters
 MOE_DIAG_H_FP16_NONFINITE = 0
 MOE_DIAG_COUNT = 1

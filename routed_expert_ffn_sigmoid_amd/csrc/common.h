@@ -56,6 +56,9 @@ __device__ __forceinline__ int32_t ld_const(const int32_t *p, long i) {
 // memory, so loads that may fall outside their row stay branch-free and keep many requests in flight.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOOB = 0x80000000u;  // offset that is always out of range
+// Every buffer a kernel addresses through a descriptor stays below kOOB bytes: the marker is then out of range
+// for every descriptor, and no valid offset reaches it.  The host rejects shapes that would pass this.
+constexpr long kMaxDescBytes = 1L << 31;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor, 32-bit data
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {

@@ -634,7 +634,13 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     __syncthreads();  // table in LDS (the compiler waits for the table loads before the stores)
 
     int nu = __builtin_amdgcn_readfirstlane(tab[0]);
-    nu = nu < 0 ? 0 : (nu > nrs ? nrs : nu);
+    if (nu < 0) {
+        // invalid expert ids in the routing (n_uniq = -1): the valid experts are the non-negative prefix of uniq
+        nu = 0;
+        while (nu < nrs && t_uniq[nu] >= 0) nu++;
+        nu = __builtin_amdgcn_readfirstlane(nu);
+    }
+    nu = nu > nrs ? nrs : nu;
     int nvr = nu, nvs = P.Is > 0 ? 1 : 0;  // routed and shared (virtual) slots
     if constexpr (PASSES) {
         // vpre[s] = first virtual slot of routed slot s (exclusive prefix of its passes), vpre[nu] = their total
@@ -1032,6 +1038,15 @@ static size_t dk_lds_bytes(int mode, int kpad, int gmax) {
     const size_t planes = (size_t)4 * 3 * gmax * (kpad + 16);
     const size_t red = dk_red_bytes(mode);
     return planes > red ? planes : red;
+}
+
+const char *decode_unsupported(const FfnParams &P) {
+    const long Imax = P.I > P.Is ? P.I : P.Is;
+    if ((long)P.T * P.d * (P.act == 0 ? 4 : 2) >= kMaxDescBytes) return "x exceeds 2^31 bytes";
+    if (Imax * ((long)P.d * P.wbits / 8) >= kMaxDescBytes) return "one expert weight matrix exceeds 2^31 bytes";
+    if ((long)P.A * P.I * 4 >= kMaxDescBytes) return "h of the routed rows (T*k*I fp32) exceeds 2^31 bytes";
+    if ((long)P.T * P.Is * 4 >= kMaxDescBytes) return "h of the shared expert (T*I_shared fp32) exceeds 2^31 bytes";
+    return nullptr;
 }
 
 size_t decode_workspace_bytes(const FfnParams &P) {

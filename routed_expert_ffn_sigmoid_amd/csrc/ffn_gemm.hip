@@ -10,8 +10,11 @@
 // Weights are the integers q of the per-channel quantisation (page "企业官网建设流程全解析", section
 // 3.4): w = s (q - z).  They enter the MFMA as fp16 values of q, exact for int8 and int4, dequantised in
 // registers from the packed bytes; the zero point is applied once per output through the row sum of the
-// activations, and the scale in the epilogue.  Activations: x is bf16 and is converted once to fp16
-// (exact save for magnitudes below 2^-14).  h enters the down GEMM as an fp16 plane plus the residual
+// activations, and the scale in the epilogue.  Activations: x is bf16 and is converted once to fp16 under
+// a power-of-two scale per token (exact for every value above 2^-29 of the row's largest; any range fits),
+// undone in the gate/up epilogue.  h is stored under a power-of-two scale per row, 2^-r, chosen from a bound
+// on |h| that x's L1 norm and the expert's scales give (see x16_kernel), so it never overflows fp16 either;
+// the down epilogue multiplies by 2^r.  h enters the down GEMM as an fp16 plane plus the residual
 // h - fp16(h) in fp6 e2m3 under one E8M0 exponent per row and 32 channels (the block form of the scaled
 // matrix-core product), about 15-16 significant bits for the larger values of a block: a single fp16
 // rounding of h would move the largest down outputs by up to 3e-3 of their RMS.  The residual product
@@ -138,29 +141,155 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff) {
 // s_waitcnt with only the vector-memory count (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
 #define GG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-// x (bf16 [T][d]) -> x16 (fp16 [T][d], int4 order within groups of 8).
+// x (bf16 [T][d]) -> x16 (fp16 [T][d], int4 order within groups of 8), one workgroup per row at a time.  Each
+// row is multiplied by the power of two 2^e that puts its largest magnitude into [2^14, 2^15), and xinv[t] =
+// 2^-e, which the gate/up epilogue applies (exactly).  bf16 carries 8 significant bits and fp16 11, so every
+// value of the row down to 2^-29 of its largest converts exactly, and no row overflows fp16 whatever its range.
+//
+// The same launch bounds h, so that it too is stored in fp16 without overflow whatever the range of x or of
+// the weights.  For channel c of an expert, |g_c| = |s_c sum_i (q_ci - z_c) x_i| <= |s_c| M_c ||x||_1 with
+// M_c = max |q - z| over the weight range, likewise |u_c|, and |silu(g)| <= |g|, so
+//     |h_c| = |silu(g_c) u_c| <= 2^(G_e + U_e + 2 L_t),
+// with 2^G_e >= max_c |s^g_c| M^g_c, 2^U_e likewise (hexp[e] = G_e + U_e; e = E for the shared expert) and
+// 2^L_t >= ||x_t||_1 (xl[t] = L_t).  The gate/up pass stores h of row t, expert e times 2^-r with
+// r = G_e + U_e + 2 L_t - 15 (below 2^15 in magnitude) and the down epilogue multiplies by 2^r.  The bound is
+// loose by about sqrt(d) max|q - z| / std(q) per factor (2^16 to 2^20 for h), which leaves typical values of h
+// far above fp16's subnormal range.  Workgroups [0, nrb) take rows, the next E (+1) experts.
+constexpr int XK_KEEP = 4;  // 16-byte chunks per thread held in registers between the two passes
+
+__device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t w, uint32_t m) {
+    // magnitude bit patterns of the two bf16 halves (they order as the magnitudes)
+    return max(m, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+}
+
+// exponent ex + 1 with v < 2^ex (v >= 0): a power of two at least twice v, so fp32 rounding of v cannot reach it
+__device__ __forceinline__ int exp_bound(float v) {
+    int ex = 0;
+    if (v > 0.f && v <= 3.0e38f) frexpf(v, &ex);
+    else if (v > 3.0e38f) ex = 128;
+    return ex + 1;
+}
+
 template <int WBITS>
-__global__ __launch_bounds__(256) void x16_kernel(const uint16_t *__restrict__ x, _Float16 *__restrict__ x16,
-                                                  long nchunks, int *__restrict__ tile_ctr) {
-    // the tile queues of the two GEMM launches that follow start empty
-    if (blockIdx.x == 0 && threadIdx.x < 2 * GG_XCDS) tile_ctr[threadIdx.x] = 0;
-    for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (long)gridDim.x * 256) {
-        const uint4 q = ((const uint4 *)x)[c];
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-        _Float16 v[8];
+__global__ __launch_bounds__(256) void x16_kernel(FfnParams P, _Float16 *__restrict__ x16, float *__restrict__ xinv,
+                                                  int *__restrict__ xl, int *__restrict__ hexp, int nrb,
+                                                  int *__restrict__ tile_ctr) {
+    __shared__ float wred[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    auto block_max2 = [&](float &a, float &b) {  // workgroup-wide maxima of two non-negative values
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            v[2 * i] = (_Float16)__uint_as_float(w[i] << 16);
-            v[2 * i + 1] = (_Float16)__uint_as_float(w[i] & 0xFFFF0000u);
+        for (int o = 32; o >= 1; o >>= 1) {
+            a = fmaxf(a, __shfl_xor(a, o, 64));
+            b = fmaxf(b, __shfl_xor(b, o, 64));
         }
-        h8_t o;
-        if (WBITS == 4)
-            o = (h8_t){v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};
-        else
-            o = (h8_t){v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
-        ((h8_t *)x16)[c] = o;
+        if (lane == 0) {
+            wred[0][wv] = a;
+            wred[1][wv] = b;
+        }
+        __syncthreads();
+        a = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+        b = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
+        __syncthreads();  // wred is rewritten next
+    };
+    if (blockIdx.x >= nrb) {
+        // ---- expert exponents: e < E routed, e == E the shared expert
+        const int e = blockIdx.x - nrb;
+        const bool sh = e == P.E;
+        const int I = sh ? P.Is : P.I;
+        const long base = sh ? 0 : (long)e * I;
+        const QW &W = sh ? P.shared : P.routed;
+        float mg = 0.f, mu = 0.f;
+        for (int c = tid; c < I; c += 256) {
+            float zg, zu;
+            if (WBITS == 8) {
+                zg = (float)((const int8_t *)W.zg)[base + c];
+                zu = (float)((const int8_t *)W.zu)[base + c];
+            } else {
+                zg = ((const float *)W.zg)[base + c];
+                zu = ((const float *)W.zu)[base + c];
+            }
+            const float Mg = WBITS == 4 ? fmaxf(fabsf(zg), fabsf(15.f - zg)) : 128.f + fabsf(zg);
+            const float Mu = WBITS == 4 ? fmaxf(fabsf(zu), fabsf(15.f - zu)) : 128.f + fabsf(zu);
+            mg = fmaxf(mg, fabsf(W.sg[base + c]) * Mg);
+            mu = fmaxf(mu, fabsf(W.su[base + c]) * Mu);
+        }
+        block_max2(mg, mu);
+        if (tid == 0) hexp[e] = exp_bound(mg) + exp_bound(mu);
+        return;
+    }
+    // the tile queues of the two GEMM launches that follow start empty
+    if (blockIdx.x == 0 && tid < 2 * GG_XCDS) tile_ctr[tid] = 0;
+    const int d = P.d, nch = d / 8;
+    const uint16_t *x = (const uint16_t *)P.x;
+    for (int t = blockIdx.x; t < P.T; t += nrb) {
+        const uint4 *row = (const uint4 *)(x + (long)t * d);
+        uint4 keep[XK_KEEP];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < XK_KEEP; i++) {
+            const int c = tid + 256 * i;
+            keep[i] = c < nch ? row[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < XK_KEEP; i++)
+            mx = bf16x2_absmax(keep[i].w, bf16x2_absmax(keep[i].z, bf16x2_absmax(keep[i].y, bf16x2_absmax(keep[i].x, mx))));
+        for (int c = tid + 256 * XK_KEEP; c < nch; c += 256) {
+            const uint4 q = row[c];
+            mx = bf16x2_absmax(q.w, bf16x2_absmax(q.z, bf16x2_absmax(q.y, bf16x2_absmax(q.x, mx))));
+        }
+        float m = __uint_as_float(mx << 16), unused = 0.f;
+        block_max2(m, unused);
+        // 2^e with the row maximum m in [2^(ex-1), 2^ex): e = 15 - ex; rows of zeros (and non-finite rows,
+        // whose outputs are not finite anyway) keep e = 0; e stays where 2^e and 2^-e are normal fp32
+        int e = 0;
+        if (m > 0.f && m <= 3.4e38f) {
+            int ex;
+            frexpf(m, &ex);
+            e = min(max(15 - ex, -120), 120);
+        }
+        const float sc = __builtin_ldexpf(1.f, e);
+        float l1 = 0.f;  // sum of the scaled magnitudes (each below 2^15: no overflow)
+        auto put = [&](int c, uint4 q) {
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            _Float16 v[8];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float a = __uint_as_float(w[i] << 16) * sc, b = __uint_as_float(w[i] & 0xFFFF0000u) * sc;
+                l1 += fabsf(a) + fabsf(b);
+                v[2 * i] = (_Float16)a;
+                v[2 * i + 1] = (_Float16)b;
+            }
+            h8_t o;
+            if (WBITS == 4)
+                o = (h8_t){v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};
+            else
+                o = (h8_t){v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+            ((h8_t *)(x16 + (long)t * d))[c] = o;
+        };
+#pragma unroll
+        for (int i = 0; i < XK_KEEP; i++) {
+            const int c = tid + 256 * i;
+            if (c < nch) put(c, keep[i]);
+        }
+        for (int c = tid + 256 * XK_KEEP; c < nch; c += 256) put(c, row[c]);
+        // the row's L1 norm only enters through its exponent (the sum's rounding is covered by exp_bound's
+        // factor 2), so a maximum-style reduction of partial sums would not do: sum them
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) l1 += __shfl_xor(l1, o, 64);
+        if (lane == 0) wred[0][wv] = l1;
+        __syncthreads();
+        if (tid == 0) {
+            xinv[t] = __builtin_ldexpf(1.f, -e);
+            xl[t] = exp_bound((wred[0][0] + wred[0][1]) + (wred[0][2] + wred[0][3])) - e;
+        }
+        __syncthreads();  // wred is rewritten by the next row
     }
 }
+
+// r for the h of a row: G_e + U_e + 2 L_t - 15, kept in [-126, 126] where 2^r and 2^-r are normal fp32.  At the
+// upper clamp any finite fp32 h times 2^-126 is below 4, so a finite h never overflows fp16; at the lower clamp
+// the bound is below 2^-111 and h times 2^126 stays below 2^15.
+__device__ __forceinline__ int h_row_exp(int he, int lt) { return min(max(he + 2 * lt - 15, -126), 126); }
 
 template <int V>
 struct GgInt {
@@ -168,7 +297,10 @@ struct GgInt {
 };
 
 struct GemmBufs {
-    const _Float16 *x16;       // [T][d]
+    const _Float16 *x16;       // [T][d], row t scaled by 1 / xinv[t]
+    float *xinv;               // [T] the power of two that undoes the scale of row t of x16
+    int *xl;                   // [T] L_t: 2^L_t >= ||x_t||_1
+    int *hexp;                 // [E + 1] G_e + U_e (e = E: the shared expert); see x16_kernel
     _Float16 *hhi;             // [A][I] h rounded to fp16
     uint8_t *hlo;              // [A][I] its residual h - hi: per 32 channels, 24 bytes of e2m3, their sum (fp32), 4 unused
     _Float16 *hshi;            // [T][I_shared], the same for the shared expert
@@ -238,6 +370,9 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
     extern __shared__ __align__(16) unsigned char gg_ring[];
     __shared__ int s_t0[GG_MAXSLOTS + 1];
     __shared__ float rsum[GG_M];
+    // per tile row: gate/up, the power of two that undoes the scale of x, and 2^-r that scales h; down, 2^r
+    __shared__ float rscale[GG_M];
+    __shared__ float hscale[GG_M];
     __shared__ int s_nslot;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -249,7 +384,15 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
     // ceil(c_s / 128) row tiles times tiles_n output tiles; s_t0 is the exclusive prefix
     if (wv == 0) {
         int nu = *P.n_uniq;
-        nu = nu < 0 ? 0 : (nu > P.n_routed_slots ? P.n_routed_slots : nu);
+        if (nu < 0) {
+            // invalid expert ids in the routing (n_uniq = -1): the valid experts are the non-negative prefix of uniq
+            nu = 0;
+            for (int b = 0; b < P.n_routed_slots; b += 64) {
+                const int s = b + lane;
+                nu += __popcll(__ballot(s < P.n_routed_slots && P.uniq[s] >= 0));
+            }
+        }
+        nu = nu > P.n_routed_slots ? P.n_routed_slots : nu;
         const int ns = nu + (P.Is > 0 ? 1 : 0);
         int carry = 0;
         for (int b = 0; b < ns; b += 64) {
@@ -375,6 +518,18 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                     if (MODE == 0) row = shared ? (r0 + m) : (P.perm[p0 + r0 + m] / P.k);
                     else row = (long)(shared ? 0 : p0) + r0 + m;
                     off = (uint32_t)(row * KK * 2) + 16 * alc;
+                    // one lane per row brings the row's scales (read in the epilogue, after the K loop's barriers;
+                    // the previous tile's epilogue is done with them since the barrier that ends it)
+                    if ((lane & 7) == 0) {
+                        const int he = G.hexp[shared ? P.E : e];
+                        if (MODE == 0) {
+                            rscale[m] = G.xinv[row];
+                            hscale[m] = __builtin_ldexpf(1.f, -h_row_exp(he, G.xl[row]));
+                        } else {
+                            const int tok = shared ? r0 + m : P.perm[p0 + r0 + m] / P.k;
+                            rscale[m] = __builtin_ldexpf(1.f, h_row_exp(he, G.xl[tok]));
+                        }
+                    }
                 }
                 asrc[i] = off;
             }
@@ -740,12 +895,14 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
                         const int m = mrow(mm, r) + mk;
-                        const float xs = rsum[m];
-                        const float gv = sc[0] * (acc[mm][0][r] - zpe[0] * xs);
-                        const float uv = sc[1] * (acc[mm][1][r] - zpe[1] * xs);
+                        const float xs = rsum[m], xr = rscale[m];
+                        // (x was scaled by 1 / xr, a power of two: these products are exact)
+                        const float gv = sc[0] * ((acc[mm][0][r] - zpe[0] * xs) * xr);
+                        const float uv = sc[1] * ((acc[mm][1][r] - zpe[1] * xs) * xr);
                         // silu through the hardware exp2 and reciprocal (relative error ~1e-6, below the
-                        // precision that h keeps)
-                        const float hv = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * gv)) * uv;
+                        // precision that h keeps); h is stored times 2^-r (exact: a power of two)
+                        const float hv = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * gv)) * uv *
+                                         hscale[m];
                         const _Float16 hh = (_Float16)hv;
                         const uint32_t mo = mkI + (uint32_t)mrow(mm, r) * (uint32_t)I;
                         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hh), hhr, (int)(2 * mo + o2), 0, 0);
@@ -806,11 +963,13 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                 for (int mm = 0; mm < MU; mm++) {
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
-                        const float xs = rsum[mrow(mm, r) + mk];
+                        const float xs = rsum[mrow(mm, r) + mk], hr = rscale[mrow(mm, r) + mk];
                         const uint32_t mo = mkd + (uint32_t)mrow(mm, r) * rowb;
 #pragma unroll
                         for (int j = 0; j < 2; j++) {
-                            const float y = sc[j] * (acc[mm][j][r] - zpe[j] * xs);
+                            // (h was stored times 2^-r: the product by 2^r is exact, and comes last so that
+                            // a large 2^r cannot overflow ahead of the scale)
+                            const float y = (sc[j] * (acc[mm][j][r] - zpe[j] * xs)) * hr;
                             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, y), yr, (int)(mo + yo[j]), 0, 0);
                         }
                     }
@@ -838,7 +997,8 @@ static long gg_ksmax(const FfnParams &P) { return (P.I > P.Is ? P.I : P.Is) / GG
 static size_t gg_hsc_bytes(const FfnParams &P) { return (size_t)gg_row_tiles(P) * gg_ksmax(P) * 256; }
 
 size_t gemm_workspace_bytes(const FfnParams &P) {
-    return al256((size_t)P.T * P.d * 2) + al256((size_t)P.A * P.I * 2) + al256((size_t)P.A * P.I) +
+    return al256((size_t)P.T * P.d * 2) + 2 * al256((size_t)P.T * 4) + al256((size_t)(P.E + 1) * 4) +
+           al256((size_t)P.A * P.I * 2) + al256((size_t)P.A * P.I) +
            al256((size_t)P.T * P.Is * 2) + al256((size_t)P.T * P.Is) + al256(gg_hsc_bytes(P)) +
            al256(2 * GG_XCDS * sizeof(int));
 }
@@ -880,11 +1040,11 @@ static hipError_t gg_launch_mode(const FfnParams &P, const GemmBufs &G, hipStrea
 
 template <int WBITS>
 static hipError_t gg_launch(const FfnParams &P, const GemmBufs &G, hipStream_t stream) {
-    const long nchunks = (long)P.T * P.d / 8;
-    long grid = (nchunks + 255) / 256;
-    if (grid > (long)gg_cus() * 8) grid = (long)gg_cus() * 8;
-    hipLaunchKernelGGL(x16_kernel<WBITS>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t *)P.x,
-                       (_Float16 *)G.x16, nchunks, G.tile_ctr);
+    long nrb = P.T;  // row workgroups, a row per workgroup at a time; then one per expert
+    if (nrb > (long)gg_cus() * 8) nrb = (long)gg_cus() * 8;
+    const long grid = nrb + P.E + (P.Is > 0 ? 1 : 0);
+    hipLaunchKernelGGL(x16_kernel<WBITS>, dim3((unsigned)grid), dim3(256), 0, stream, P, (_Float16 *)G.x16, G.xinv,
+                       G.xl, G.hexp, (int)nrb, G.tile_ctr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     err = gg_launch_mode<0, WBITS>(P, G, stream);
@@ -898,6 +1058,12 @@ hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream) {
     GemmBufs G;
     G.x16 = (const _Float16 *)p;
     p += al256((size_t)P.T * P.d * 2);
+    G.xinv = (float *)p;
+    p += al256((size_t)P.T * 4);
+    G.xl = (int *)p;
+    p += al256((size_t)P.T * 4);
+    G.hexp = (int *)p;
+    p += al256((size_t)(P.E + 1) * 4);
     G.hhi = (_Float16 *)p;
     p += al256((size_t)P.A * P.I * 2);
     G.hlo = (uint8_t *)p;

@@ -28,6 +28,8 @@ struct FfnParams {
 };
 
 // router.hip
+// nullptr when the router kernels take the shape, else why not (a buffer beyond 32-bit descriptor offsets)
+const char *router_unsupported(int T, int d, int E, int act);
 size_t router_workspace_bytes(int T, int d, int E);
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
                          float lambda, int32_t *idx, float *w, double *gap, void *ws, hipStream_t stream);
@@ -39,6 +41,7 @@ hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int
                           int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws, hipStream_t stream);
 
 // ffn_decode.hip: decode path, int8 MFMA with exact integer accumulation (h kept in fp32 in the workspace)
+const char *decode_unsupported(const FfnParams &P);  // nullptr when the decode kernels take the shape
 size_t decode_workspace_bytes(const FfnParams &P);
 hipError_t launch_ffn_decode(const FfnParams &P, void *ws, hipStream_t stream);
 

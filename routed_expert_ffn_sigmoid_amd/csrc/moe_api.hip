@@ -39,6 +39,9 @@ int check_shape(const char *fn, const moe_shape *s) {
     if (s->k > s->E || s->k > 32) return fail(MOE_EINVAL, "%s: k=%d must be <= min(E, 32)", fn, s->k);
     if (s->E > 1024) return fail(MOE_EINVAL, "%s: E=%d exceeds 1024", fn, s->E);
     if ((long)s->T * s->k >= (1L << 31)) return fail(MOE_EINVAL, "%s: T*k overflows int32", fn);
+    // the decode path sums a K part of up to a whole row of int8 weight x 8-bit digit products in int32
+    if (s->d >= MOE_MAX_DIM || s->I >= MOE_MAX_DIM || s->I_shared >= MOE_MAX_DIM)
+        return fail(MOE_EUNSUPPORTED, "%s: d, I and I_shared must be below %d", fn, MOE_MAX_DIM);
     if (s->act_dtype != MOE_ACT_F32 && s->act_dtype != MOE_ACT_BF16)
         return fail(MOE_EUNSUPPORTED, "%s: act_dtype %d not supported", fn, s->act_dtype);
     if (s->wbits != 8 && s->wbits != 4) return fail(MOE_EUNSUPPORTED, "%s: wbits %d not supported", fn, s->wbits);
@@ -150,6 +153,8 @@ int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *
     rc = check_ws(fn, s, ws, ws_bytes);
     if (rc) return rc;
     if (s->T == 0) return MOE_OK;  // empty batch: nothing to route
+    if (const char *why = moe::router_unsupported(s->T, s->d, s->E, s->act_dtype))
+        return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
     return launch_status(fn, moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
                                                 topk_idx, topk_w, gap, ws, (hipStream_t)stream));
 }
@@ -209,10 +214,13 @@ int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const
     const int path = forward_path(s);
     hipError_t err;
     if (path == MOE_PATH_GEMM) {
+        if (!moe::gemm_supported(P))
+            return fail(MOE_EUNSUPPORTED,
+                        "%s: the matrix-core path takes bf16 activations, d, I and I_shared multiples of 64 and "
+                        "buffers below 2^31 bytes", fn);
         err = moe::launch_ffn_gemm(P, ws, (hipStream_t)stream);
-        if (err == hipErrorNotSupported)
-            return fail(MOE_EUNSUPPORTED, "%s: the MFMA path does not support this shape", fn);
     } else {
+        if (const char *why = moe::decode_unsupported(P)) return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
         err = moe::launch_ffn_decode(P, ws, (hipStream_t)stream);
     }
     return launch_status(fn, err);

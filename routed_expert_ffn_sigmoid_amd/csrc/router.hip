@@ -447,6 +447,14 @@ int router_nsplit(int T, int d, int E) {
     return (d + chunk - 1) / chunk;
 }
 
+const char *router_unsupported(int T, int d, int E, int act) {
+    if ((long)T * d * (act == 0 ? 4 : 2) >= kMaxDescBytes) return "x exceeds 2^31 bytes";
+    if ((long)d * E * 4 >= kMaxDescBytes) return "W_r exceeds 2^31 bytes";
+    if (T > 0 && (long)router_nsplit(T, d, E) * T * E * 8 >= kMaxDescBytes)
+        return "the router's fp64 partial sums (splits x T x E) exceed 2^31 bytes";
+    return nullptr;
+}
+
 size_t router_workspace_bytes(int T, int d, int E) {
     if (T <= 0) return 0;
     return (size_t)router_nsplit(T, d, E) * (size_t)T * (size_t)E * sizeof(double);

@@ -129,3 +129,65 @@ def test_workspace_size_covers_every_call():
     s = shape(T=8192, d=7168, E=256, k=8, I=2048, I_shared=2048, wbits=4, act_dtype=B.MOE_ACT_BF16,
               routed_scale=2.5)
     assert B.moe_workspace_size(s) >= 8192 * 8 * 2048 * 4
+
+
+HUGE_WS = 1 << 62  # any workspace size passes; these calls fail on the shape before the workspace is used
+
+
+def test_dimension_limit_rejected():
+    """d, I, I_shared at or above MOE_MAX_DIM: the decode path's int32 sums of a K part could overflow."""
+    for kw in (dict(d=B.MOE_MAX_DIM), dict(I=B.MOE_MAX_DIM), dict(I_shared=B.MOE_MAX_DIM)):
+        s = shape(**kw)
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_route(s, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, HUGE_WS, stream=0)
+        assert ei.value.code == B.MOE_EUNSUPPORTED and f"below {B.MOE_MAX_DIM}" in str(ei.value)
+        assert B.moe_workspace_size(s) == 0
+    B.moe_workspace_size(shape(d=B.MOE_MAX_DIM - 16))  # just below: accepted
+
+
+def test_router_buffers_beyond_32_bit_offsets_rejected():
+    """x of T*d*4 bytes >= 2^31 (fp32): the router's descriptors would wrap; rejected, not computed."""
+    s = shape(T=65536, d=8192, E=8, k=2)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(s, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, HUGE_WS, stream=0)
+    assert ei.value.code == B.MOE_EUNSUPPORTED and "x exceeds" in str(ei.value)
+    s = shape(T=65536, d=8192, E=8, k=2, act_dtype=B.MOE_ACT_BF16)  # half the bytes: below the limit
+    assert B.moe_workspace_size(s) > 0
+
+
+def _forward(s):
+    q = B.make_qffn(*([FAKE] * 9))
+    sh = q if s.I_shared > 0 else None
+    B.moe_forward(s, FAKE, q, sh, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE if s.I_shared > 0 else None, None, FAKE,
+                  HUGE_WS, stream=0)
+
+
+def test_decode_h_beyond_32_bit_offsets_rejected():
+    """The mid layer with fp32 activations at T = 40000 goes to the decode kernels (no matrix-core path for fp32),
+    whose h of T*k*I*4 = 4.6 GB would wrap a 32-bit descriptor: rejected before anything is enqueued."""
+    s = shape(T=40000, d=4096, E=8, k=2, I=14336, wbits=8, act_dtype=B.MOE_ACT_F32)
+    with pytest.raises(B.MoeError) as ei:
+        _forward(s)
+    assert ei.value.code == B.MOE_EUNSUPPORTED and "h of the routed rows" in str(ei.value)
+    s = shape(T=40000, d=4096, E=8, k=2, I=14336, wbits=8, act_dtype=B.MOE_ACT_F32, path=B.MOE_PATH_GEMV)
+    with pytest.raises(B.MoeError) as ei:
+        _forward(s)
+    assert ei.value.code == B.MOE_EUNSUPPORTED
+
+
+def test_decode_expert_matrix_beyond_32_bit_offsets_rejected():
+    """One int8 expert matrix of I*d bytes >= 2^31 (d = 65536, I = 32768)."""
+    s = shape(T=2, d=65536, E=8, k=2, I=32768, wbits=8, act_dtype=B.MOE_ACT_F32)
+    with pytest.raises(B.MoeError) as ei:
+        _forward(s)
+    assert ei.value.code == B.MOE_EUNSUPPORTED and "weight matrix" in str(ei.value)
+
+
+def test_matrix_core_path_refuses_what_it_cannot_take():
+    """MOE_PATH_GEMM with fp32 activations, or with sizes that are not multiples of 64, is refused with a
+    message; MOE_PATH_AUTO sends such shapes to the decode kernels instead."""
+    for kw in (dict(act_dtype=B.MOE_ACT_F32), dict(act_dtype=B.MOE_ACT_BF16, d=272, wbits=8)):
+        s = shape(T=64, path=B.MOE_PATH_GEMM, **kw)
+        with pytest.raises(B.MoeError) as ei:
+            _forward(s)
+        assert ei.value.code == B.MOE_EUNSUPPORTED and "matrix-core path" in str(ei.value)
