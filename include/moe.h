@@ -20,7 +20,8 @@
  * Conventions shared by every call
  *   - Every array argument is a DEVICE pointer owned by the caller; only the
  *     moe_shape / moe_qffn structs are read on the host, during the call.
- *     The library allocates no memory and keeps no global mutable state.
+ *     The library allocates no memory and keeps no global mutable state,
+ *     except moe_forward_static's static scratch array (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without waiting for it.  Results are valid once
  *     the stream has reached that point.  Counts, offsets and the unique-
@@ -192,6 +193,31 @@ MOE_API int moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t
 MOE_API int moe_forward(const moe_shape *shape, const void *x, const moe_qffn *routed, const moe_qffn *shared,
                 const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
                 float *y_perm, float *y_shared, uint32_t *diag, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_forward for callers that cannot allocate memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same
+ * computation, arguments and results, with no workspace argument.  Its
+ * scratch memory is a static device array of MOE_STATIC_SCRATCH_BYTES that
+ * the library holds on every device it runs on until the process ends (the
+ * array's address on a device is looked up on the first call there).
+ *   - A shape whose forward needs more scratch than that (moe_forward's part
+ *     of moe_workspace_size: the decode path's h, or the matrix-core path's
+ *     fp16 x and h planes) fails with MOE_EWORKSPACE before anything is
+ *     enqueued.  Decode batches and prefill chunks of a few hundred tokens
+ *     fit; the 256-expert top-8 layer at T = 8192 does not.
+ *   - No call allocates or frees memory; nothing in the scratch needs to
+ *     start at zero (the kernels clear what they count with).
+ *   - Every call on one GPU shares that GPU's array and leaves the last call's
+ *     contents in it: calls that overlap on one GPU (different streams, or
+ *     different host threads) race and give wrong results.  Order them.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+
+MOE_API int moe_forward_static(const moe_shape *shape, const void *x, const moe_qffn *routed,
+                               const moe_qffn *shared, const int32_t *offsets, const int32_t *perm,
+                               const int32_t *uniq, const int32_t *n_uniq, float *y_perm, float *y_shared,
+                               uint32_t *diag, void *stream);
 
 /*
  * Weighted combine.  The layer output adds, to the always-on shared expert

@@ -35,8 +35,10 @@ MOE_PATH_GEMV = 1
 MOE_PATH_GEMM = 2
 
 # names declared in include/moe.h
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_combine",
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_static", "moe_combine",
            "moe_last_error", "moe_abi_version")
+
+MOE_STATIC_SCRATCH_BYTES = 64 << 20  # moe_forward_static's scratch
 
 
 class MoeError(RuntimeError):
@@ -74,8 +76,9 @@ def lib():
         L.moe_route.argtypes = [S, P, P, P, P, P, P, P, C.c_size_t, P]
         L.moe_permute.argtypes = [S, P, P, P, P, P, P, P, P, C.c_size_t, P]
         L.moe_forward.argtypes = [S, P, Q, Q, P, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_forward_static.argtypes = [S, P, Q, Q, P, P, P, P, P, P, P, P]
         L.moe_combine.argtypes = [S, P, P, P, P, P, P]
-        for f in ("moe_route", "moe_permute", "moe_forward", "moe_combine", "moe_abi_version"):
+        for f in ("moe_route", "moe_permute", "moe_forward", "moe_forward_static", "moe_combine", "moe_abi_version"):
             getattr(L, f).restype = C.c_int
         L.moe_last_error.restype = C.c_char_p
         _lib = L
@@ -144,6 +147,14 @@ def moe_forward(shape, x, routed: moe_qffn, shared: Optional[moe_qffn], offsets,
                              C.byref(shared) if shared is not None else None, _ptr(offsets), _ptr(perm),
                              _ptr(uniq), _ptr(n_uniq), _ptr(y_perm), _ptr(y_shared), _ptr(diag), _ptr(ws),
                              ws_bytes, _stream(stream)))
+
+
+def moe_forward_static(shape, x, routed: moe_qffn, shared: Optional[moe_qffn], offsets, perm, uniq, n_uniq, y_perm,
+                       y_shared, diag, stream=None) -> None:
+    _check(lib().moe_forward_static(C.byref(shape), _ptr(x), C.byref(routed),
+                                    C.byref(shared) if shared is not None else None, _ptr(offsets), _ptr(perm),
+                                    _ptr(uniq), _ptr(n_uniq), _ptr(y_perm), _ptr(y_shared), _ptr(diag),
+                                    _stream(stream)))
 
 
 def moe_combine(shape, y_perm, y_shared, inv, topk_w, y, stream=None) -> None:

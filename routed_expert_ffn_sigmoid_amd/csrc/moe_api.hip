@@ -4,8 +4,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
+
+// Scratch memory of moe_forward_static: one copy per device, at its own address on each, held until the process
+// ends.  Host code never passes this name to a kernel (on the host it is a stand-in, not a device address): it
+// uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -112,6 +119,34 @@ int forward_path(const moe_shape *s) {
     return MOE_PATH_GEMV;
 }
 
+// Workspace bytes of moe_forward alone for this shape (the path it takes).
+size_t forward_workspace_bytes(const moe_shape *s) {
+    const moe::FfnParams P = ffn_params(s);
+    return forward_path(s) == MOE_PATH_GEMM ? moe::gemm_workspace_bytes(P) : moe::decode_workspace_bytes(P);
+}
+
+// Device address of `scratch` on the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+int scratch_address(const char *fn, void **out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(MOE_EDEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(err));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EDEVICE, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !p)
+            return fail(MOE_EDEVICE, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(err));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
+
 int launch_status(const char *fn, hipError_t err) {
     if (err != hipSuccess) return fail(MOE_EDEVICE, "%s: launch failed: %s", fn, hipGetErrorString(err));
     g_err[0] = 0;
@@ -122,7 +157,7 @@ int launch_status(const char *fn, hipError_t err) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 2; }
+int moe_abi_version(void) { return 3; }
 
 const char *moe_last_error(void) { return g_err; }
 
@@ -177,10 +212,14 @@ int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, in
                                                  n_uniq, ws, (hipStream_t)stream));
 }
 
-int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
-                const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
-                float *y_perm, float *y_shared, uint32_t *diag, void *ws, size_t ws_bytes, void *stream) {
-    const char *fn = "moe_forward";
+}  // extern "C"
+
+namespace {
+
+// moe_forward's argument checks (all but the workspace); MOE_OK when the call may go ahead
+int check_forward(const char *fn, const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                  const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                  float *y_perm, float *y_shared, uint32_t *diag) {
     int rc = check_shape(fn, s);
     if (rc) return rc;
     REQUIRE_PTR_T(x, "x");
@@ -197,8 +236,23 @@ int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const
     REQUIRE_PTR(n_uniq, "n_uniq");
     REQUIRE_PTR_T(y_perm, "y_perm");
     if (diag && !aligned(diag, 4)) return fail(MOE_EALIGN, "%s: diag is not 4-byte aligned", fn);
-    rc = check_ws(fn, s, ws, ws_bytes);
-    if (rc) return rc;
+    if (s->T == 0) return MOE_OK;
+    const moe::FfnParams P = ffn_params(s);
+    if (forward_path(s) == MOE_PATH_GEMM) {
+        if (!moe::gemm_supported(P))
+            return fail(MOE_EUNSUPPORTED,
+                        "%s: the matrix-core path takes bf16 activations, d, I and I_shared multiples of 64 and "
+                        "buffers below 2^31 bytes", fn);
+    } else if (const char *why = moe::decode_unsupported(P)) {
+        return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
+    }
+    return MOE_OK;
+}
+
+// the forward kernels, after check_forward and a workspace check
+int run_forward(const char *fn, const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                float *y_perm, float *y_shared, uint32_t *diag, void *ws, void *stream) {
     if (s->T == 0) return MOE_OK;  // empty batch: no rows to transform
     moe::FfnParams P = ffn_params(s);
     P.x = x;
@@ -211,19 +265,41 @@ int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const
     P.y_perm = y_perm;
     P.y_sh = s->I_shared > 0 ? y_shared : nullptr;
     P.diag = diag;
-    const int path = forward_path(s);
-    hipError_t err;
-    if (path == MOE_PATH_GEMM) {
-        if (!moe::gemm_supported(P))
-            return fail(MOE_EUNSUPPORTED,
-                        "%s: the matrix-core path takes bf16 activations, d, I and I_shared multiples of 64 and "
-                        "buffers below 2^31 bytes", fn);
-        err = moe::launch_ffn_gemm(P, ws, (hipStream_t)stream);
-    } else {
-        if (const char *why = moe::decode_unsupported(P)) return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
-        err = moe::launch_ffn_decode(P, ws, (hipStream_t)stream);
-    }
+    const hipError_t err = forward_path(s) == MOE_PATH_GEMM ? moe::launch_ffn_gemm(P, ws, (hipStream_t)stream)
+                                                             : moe::launch_ffn_decode(P, ws, (hipStream_t)stream);
     return launch_status(fn, err);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                float *y_perm, float *y_shared, uint32_t *diag, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_forward";
+    int rc = check_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag);
+    if (rc) return rc;
+    rc = check_ws(fn, s, ws, ws_bytes);
+    if (rc) return rc;
+    return run_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag, ws, stream);
+}
+
+int moe_forward_static(const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                       const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                       float *y_perm, float *y_shared, uint32_t *diag, void *stream) {
+    const char *fn = "moe_forward_static";
+    int rc = check_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag);
+    if (rc) return rc;
+    const size_t need = forward_workspace_bytes(s);
+    if (need > (size_t)MOE_STATIC_SCRATCH_BYTES)
+        return fail(MOE_EWORKSPACE, "%s: this shape needs %zu bytes of scratch, above the static %u", fn, need,
+                    (unsigned)MOE_STATIC_SCRATCH_BYTES);
+    if (s->T == 0) return MOE_OK;
+    void *ws = nullptr;
+    rc = scratch_address(fn, &ws);
+    if (rc) return rc;
+    return run_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag, ws, stream);
 }
 
 int moe_combine(const moe_shape *s, const float *y_perm, const float *y_shared, const int32_t *inv,

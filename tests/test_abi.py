@@ -191,3 +191,19 @@ def test_matrix_core_path_refuses_what_it_cannot_take():
         with pytest.raises(B.MoeError) as ei:
             _forward(s)
         assert ei.value.code == B.MOE_EUNSUPPORTED and "matrix-core path" in str(ei.value)
+
+
+def test_static_forward_checks_before_anything_runs():
+    """moe_forward_static validates like moe_forward and refuses a shape whose scratch need passes its static
+    array (no GPU needed: the call fails before looking the array up)."""
+    s = shape(T=8192, d=7168, E=256, k=8, I=2048, I_shared=2048, wbits=4, act_dtype=B.MOE_ACT_BF16,
+              routed_scale=2.5)
+    q = B.make_qffn(*([FAKE] * 9))
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_static(s, FAKE, q, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.code == B.MOE_EWORKSPACE and "static" in str(ei.value)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_static(shape(), FAKE, q, None, FAKE, FAKE, FAKE, None, FAKE, None, None, stream=0)
+    assert ei.value.code == B.MOE_EINVAL and "n_uniq" in str(ei.value)
+    # an empty batch is a no-op here too
+    B.moe_forward_static(shape(T=0), None, q, None, FAKE, None, FAKE, FAKE, None, None, None, stream=0)
