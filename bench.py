@@ -9,11 +9,15 @@ Infinity Cache nor L2 holds the expert weights between steps.
 Each step of the rotation is captured once as a HIP graph (the four ABI
 calls) and replayed, so host launch overhead does not enter the timing.
 
-Prints ONE JSON line (the driver's contract).  `value` is MoE-layer tokens/s.
+Prints ONE JSON line (the driver's contract).  The top level is the headline
+workload (mid layer, T = 1 by default): `value` is MoE-layer tokens/s.
 `roofline` reports the expert-FFN stage (moe_forward) against HBM bandwidth
 (decode) or the bf16/fp16 MFMA peak (prefill), timed with HIP events on the
 stream the kernels run on around replays of a graph of moe_forward calls.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+With the default workload, `additional_workloads` holds the same figures for
+the 256-expert layer at T = 1 (HBM roof) and at T = 8192 with int4 weights
+(MFMA roof), each timed the same way in the same run.
 """
 from __future__ import annotations
 
@@ -33,8 +37,13 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2516.6  # dense bf16/fp16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
 
+# the workloads timed beside the headline one by default: (workload, T)
+ADDITIONAL = (("large", 1), ("prefill_int4_uniform", 8192))
+# workloads whose oracle is also timed on one thread (configs 0-2)
+ONE_THREAD = (("tiny", 16), ("mid", 1), ("large", 1))
 
-def parse():
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -44,12 +53,14 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="resident layers rotated per step")
     ap.add_argument("--pool", type=int, default=None, help="activation batches rotated per step (16 decode, 2 prefill)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--invariant", action="store_true", help="the batch-shape-invariant mode (MOE_FLAG_BATCH_INVARIANT)")
+    ap.add_argument("--only", action="store_true", help="the named workload alone (no additional workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of each oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three plain 1 GiB device-to-device copies (torch copy_), whose HBM counter "
                          "readings scale the counters read for the MoE kernels")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def measured_traffic(config, T, gemm=False):
@@ -75,60 +86,100 @@ def measured_traffic(config, T, gemm=False):
     return float(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(spec, T, target_s):
-    """The oracle, as it stands, on a bounded sample of the same workload (tokens of layer 0)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _sample_inputs(spec, T, n):
+    """The first n tokens of the workload's first batch, with router and bias, and a host expert set in which only
+    the experts those tokens hit (and the shared one) are generated: np.zeros leaves the other experts' pages
+    untouched, and the oracle reads only the experts it applies."""
     from oracle import oracle as orc
     from routed_expert_ffn_sigmoid_amd import synth
-    inp = synth.gen_layer(spec, T, 0, 0, 0)
+    x = synth.gen_x(spec, T, 0, 0)[:n]
+    W_r, bias = synth.gen_router(spec, 0, 0), synth.gen_bias(spec, 0, 0)
+    r = orc.router_select(orc.router_logits(orc.decode_act(x, spec.act), W_r), bias, spec.k, spec.routed_scale)
+    one = synth.stack_experts([synth.gen_expert(spec, 0)])
+    routed = synth.QExpertSet(*[np.zeros((spec.E,) + getattr(one, f).shape[1:], getattr(one, f).dtype)
+                                for f in ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down",
+                                          "z_gate", "z_up", "z_down")])
+    for e in sorted(set(int(v) for v in r.idx.ravel())):
+        ex = synth.stack_experts([synth.gen_expert(spec, e)])
+        for f in ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down"):
+            getattr(routed, f)[e] = getattr(ex, f)[0]
+    return x, W_r, bias, routed, synth.gen_shared_expert(spec)
+
+
+def cpu_baseline(spec, T, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload: whole oracle layers (route, batch union,
+    experts, shared expert, combine) over the first n tokens of its first batch.  Tokens are independent, so
+    tokens/s of a sample is that of the workload (the oracle gains nothing from weight reuse)."""
+    from oracle import oracle as orc
+    n = min(T, 16)
+    x, W_r, bias, routed, shared = _sample_inputs(spec, T, n)
     cores = orc.max_threads()
-    n, t0 = 0, time.perf_counter()
+    reps, t0 = 0, time.perf_counter()
     while True:
-        orc.moe_layer(spec, inp.x, inp.W_r, inp.bias, inp.routed, inp.shared)
-        n += 1
+        orc.moe_layer(spec, x, W_r, bias, routed, shared)
+        reps += 1
         el = time.perf_counter() - t0
-        if el >= target_s or n >= 1000:
+        if el >= target_s or reps >= 1000:
             break
-    return {"value": n * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} full {spec.name} layers at T={T} (layer 0, batch 0), {el:.1f} s, fp64 C with OpenMP"}
+    return {"value": round(reps * n / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{reps} oracle layers of the first {n} tokens of the {spec.name} T={T} batch (layer 0), "
+                      f"{el:.1f} s, fp64 C with OpenMP on {cores} threads"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
-              file=sys.stderr)
-        sys.exit(2)
+def one_thread_oracle():
+    """The oracle on one host thread, one whole layer each of configs 0-2 (tiny T=16, mid T=1, large T=1)."""
+    from oracle import oracle as orc
+    from routed_expert_ffn_sigmoid_amd import synth
+    out = {}
+    cores = orc.max_threads()
+    orc.set_threads(1)
+    try:
+        for name, T in ONE_THREAD:
+            spec = synth.CONFIGS[name]
+            x, W_r, bias, routed, shared = _sample_inputs(spec, T, T)
+            t0 = time.perf_counter()
+            orc.moe_layer(spec, x, W_r, bias, routed, shared)
+            el = time.perf_counter() - t0
+            out[f"{name}_T{T}"] = {"tokens_per_s": round(T / el, 3), "seconds": round(el, 3)}
+    finally:
+        orc.set_threads(cores)
+    return out
+
+
+def measure(spec, T, args, dev):
+    """Time one workload; returns the figures of its JSON object (without the top-level contract fields)."""
     import torch
     from routed_expert_ffn_sigmoid_amd import binding as B
     from routed_expert_ffn_sigmoid_amd import layer as L
     from routed_expert_ffn_sigmoid_amd import synth
 
-    spec = synth.CONFIGS[args.config]
-    T = args.T or synth.WORKLOAD_T[args.config][0]
     decode = T * spec.k <= 4 * spec.E or T <= 64
     n_layers = args.layers or (4 if decode else 1)
-    args.pool = args.pool or (16 if decode else 2)
+    pool_n = args.pool or (16 if decode else 2)
     path = {"auto": B.MOE_PATH_AUTO, "gemv": B.MOE_PATH_GEMV, "gemm": B.MOE_PATH_GEMM}[args.path]
-    dev = torch.device("cuda:0")
-    B.lib()
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    flags = B.MOE_FLAG_BATCH_INVARIANT if args.invariant else 0
 
     t_setup = time.perf_counter()
     layers = [L.DeviceLayerWeights(spec, 0, l, dev) for l in range(n_layers)]
-    pool = [L.upload_x(spec, synth.gen_x(spec, T, 0, b), dev) for b in range(args.pool)]
-    cycle = n_layers * args.pool // math.gcd(n_layers, args.pool)
+    pool = [L.upload_x(spec, synth.gen_x(spec, T, 0, b), dev) for b in range(pool_n)]
+    cycle = n_layers * pool_n // math.gcd(n_layers, pool_n)
     # one set of output/workspace buffers per step of the rotation, so each step can be a captured graph
-    runs = [L.MoeRun(spec, T, dev, path) for _ in range(cycle)]
+    runs = [L.MoeRun(spec, T, dev, path, flags) for _ in range(cycle)]
     setup_s = time.perf_counter() - t_setup
 
     def operands(i):
-        return pool[i % args.pool], layers[i % n_layers]
+        return pool[i % pool_n], layers[i % n_layers]
 
     # eager pass over the rotation: realized unique experts per step
     n_uniq = np.zeros(cycle, dtype=np.int64)
@@ -207,11 +258,11 @@ def main():
     # the roof that binds: HBM when the expert FFNs do fewer flops per expert-weight byte than the ridge
     # point of the two peaks (2516.6 TFLOP/s / 8 TB/s = 315 flop/B), the matrix cores otherwise
     ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    # the auto path runs the matrix-core GEMM for T > 16 with bf16 activations (outside the invariant mode)
+    gemm = args.path == "gemm" or (args.path == "auto" and not args.invariant and T > 16 and spec.act == synth.ACT_BF16)
+    traffic = None if args.invariant or args.path == "gemv" and T > 16 else measured_traffic(spec.name, T, gemm)
     if flops_per_step / bytes_per_fwd < ridge:
         achieved = bytes_per_fwd / (fwd_s / n_fwd) / 1e9
-        # the auto path runs the matrix-core GEMM for T > 16 with bf16 activations
-        gemm = args.path == "gemm" or (args.path == "auto" and T > 16 and spec.act == synth.ACT_BF16)
-        traffic = measured_traffic(args.config, T, gemm)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
@@ -220,42 +271,89 @@ def main():
                 "avg_launch_us": round(fwd_us, 2)}
     else:
         achieved = flops_per_step / (fwd_s / n_fwd) / 1e12
-        traffic = measured_traffic(args.config, T, True)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
                 "traffic": None if traffic is None else round(traffic),
-                "kernel": "moe_forward (gate/up + down expert-FFN kernels)",
+                "kernel": "moe_forward (x to fp16, gate/up and down grouped-GEMM kernels)",
                 "algorithmic_flops_per_launch": flops_per_step,
                 "avg_launch_us": round(fwd_us, 2)}
     steps_idx = range(args.warmup, args.warmup + args.steps)
-
-    ms_per_step = elapsed / args.steps * 1e3
-    out = {
-        "metric": "MoE-layer tokens/s",
+    res = {
         "value": round(T * args.steps / elapsed, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
         "dtype": ("bf16-act/" if spec.act == synth.ACT_BF16 else "f32-act/") + f"int{spec.wbits}-weights/f32-accum",
-        "data": "synthetic (seeded; random-init quantised weights)",
         "config": {"workload": f"{spec.name}: d={spec.d} E={spec.E} top-{spec.k} I={spec.I} "
                                f"shared={spec.I_shared} int{spec.wbits} T={T}",
-                   "T": T, "layers_resident": n_layers, "x_pool": args.pool,
+                   "T": T, "layers_resident": n_layers, "x_pool": pool_n,
                    "mean_unique_experts": round(float(np.mean([n_uniq[i % cycle] for i in steps_idx])), 2),
                    "assignments_per_unique_expert": round(T * spec.k / float(np.mean(n_uniq)), 2),
                    "permute_us_alone": round(perm_us, 2),
                    "timing": "HIP graph per step (the four ABI calls), replayed",
                    "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
-                   "path": args.path, "setup_s": round(setup_s, 1)},
+                   "path": args.path, "batch_invariant": bool(args.invariant), "setup_s": round(setup_s, 1)},
         "roofline": roof,
     }
+    del runs, step_graphs, fwd_graph, perm_graph, layers, pool
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from routed_expert_ffn_sigmoid_amd import binding as B
+    from routed_expert_ffn_sigmoid_amd import synth
+
+    spec = synth.CONFIGS[args.config]
+    T = args.T or synth.WORKLOAD_T[args.config][0]
+    dev = torch.device("cuda:0")
+    B.lib()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    head = measure(spec, T, args, dev)
+    out = {
+        "metric": "MoE-layer tokens/s",
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded; random-init quantised weights)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+    }
+    default_run = args.config == "mid" and args.T is None and not args.only and args.path == "auto" \
+        and not args.invariant and args.layers is None and args.pool is None
+    extra = []
+    if default_run:
+        for name, Tw in ADDITIONAL:
+            sub = measure(synth.CONFIGS[name], Tw, args, dev)
+            sub = {"metric": "MoE-layer tokens/s", "unit": "tokens/s", "steps": args.steps, "warmup": args.warmup,
+                   **sub}
+            extra.append((name, Tw, sub))
+        out["additional_workloads"] = [s for _, _, s in extra]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, T, args.cpu_seconds)
+        for name, Tw, sub in extra:
+            sub["cpu_baseline"] = cpu_baseline(synth.CONFIGS[name], Tw, args.cpu_seconds)
+        if default_run:
+            out["cpu_baseline"]["one_thread"] = one_thread_oracle()
     print(json.dumps(out), flush=True)
 
 

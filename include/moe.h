@@ -97,12 +97,33 @@ extern "C" {
 #define MOE_PATH_GEMV 1 /* bandwidth-bound dequant-GEMV (decode) */
 #define MOE_PATH_GEMM 2 /* MFMA grouped GEMM (prefill) */
 
+/*
+ * Batch-shape-invariant mode.  Quantised integer kernels may round differently
+ * for different batch shapes, so a token verified inside a batch (speculative
+ * drafts, batched prefill) need not match the single-token path byte for
+ * byte; strict reproducibility fixes the kernels and their paths ("25GB 内存跑
+ * 744B GLM-5.2 模型" page, section 六).  With this flag every result for a token
+ * (topk_idx, topk_w, gap, its y_perm rows, y_shared and y) is bit-identical
+ * whatever the batch it sits in and its position there:
+ *   - moe_route sums each token's logits in one order fixed by (d, E) alone;
+ *   - moe_forward with MOE_PATH_AUTO runs the decode kernels at every T, with
+ *     the K split of each pass fixed by (d, I, I_shared, E, k, wbits) alone
+ *     (MOE_PATH_GEMM stays on the matrix-core path, whose rows are
+ *     independent of each other too, and gives its own, different bits);
+ *   - moe_combine is per token already.
+ * Cost: the decode split is the one chosen for T = 1, so T <= 16 runs as fast
+ * or a little slower; above T = 16 the decode kernels stream every used expert
+ * again per 16 tokens, far slower than the matrix-core path.
+ */
+#define MOE_FLAG_BATCH_INVARIANT 1
+
 typedef struct moe_shape {
     int32_t T, d, E, k, I, I_shared;
     float routed_scale; /* lambda: the normalised combine weights are multiplied by it */
     int32_t act_dtype;  /* MOE_ACT_F32 | MOE_ACT_BF16 */
     int32_t wbits;      /* 8 | 4 */
     int32_t path;       /* MOE_PATH_* (moe_forward only) */
+    int32_t flags;      /* 0 or MOE_FLAG_BATCH_INVARIANT */
 } moe_shape;
 
 typedef struct moe_qffn {

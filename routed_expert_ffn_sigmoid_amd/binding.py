@@ -30,6 +30,8 @@ MOE_MAX_DIM = 131072  # d, I and I_shared must be below this
 MOE_DIAG_H_FP16_NONFINITE = 0
 MOE_DIAG_COUNT = 1
 
+MOE_FLAG_BATCH_INVARIANT = 1
+
 MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_GEMM = 2
@@ -50,7 +52,7 @@ class MoeError(RuntimeError):
 class moe_shape(C.Structure):
     _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("E", C.c_int32), ("k", C.c_int32), ("I", C.c_int32),
                 ("I_shared", C.c_int32), ("routed_scale", C.c_float), ("act_dtype", C.c_int32),
-                ("wbits", C.c_int32), ("path", C.c_int32)]
+                ("wbits", C.c_int32), ("path", C.c_int32), ("flags", C.c_int32)]
 
 
 class moe_qffn(C.Structure):
@@ -112,8 +114,8 @@ def _check(rc: int) -> None:
 
 
 def make_shape(T, d, E, k, I, I_shared=0, routed_scale=1.0, act_dtype=MOE_ACT_BF16, wbits=4,
-               path=MOE_PATH_AUTO) -> moe_shape:
-    return moe_shape(T, d, E, k, I, I_shared, routed_scale, act_dtype, wbits, path)
+               path=MOE_PATH_AUTO, flags=0) -> moe_shape:
+    return moe_shape(T, d, E, k, I, I_shared, routed_scale, act_dtype, wbits, path, flags)
 
 
 def make_qffn(q_gate, q_up, q_down, s_gate, s_up, s_down, z_gate, z_up, z_down) -> moe_qffn:

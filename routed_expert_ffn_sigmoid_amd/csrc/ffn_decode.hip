@@ -1093,14 +1093,14 @@ static int dkp_pf(int mode, int nseg) {
 // reads nothing), at the expected number of slots -- uniform routing hits E (1 - (1 - k/E)^T) experts, and
 // skewed routing fewer -- with items counted in half tiles when a tile is an item (its ranges are cut in
 // half tiles); ties go to the larger S.
-static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, int wbits, int ncu) {
+static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, int wbits, int ncu, int smax = DKP_WAVES) {
     const int chunk_inputs = wbits == 8 ? 16 : 32;
     const int nseg_full = (K * wbits / 8 + 63) / 64;
     int best = 1;
     double best_cost = -1;
     for (int i = 0; i < 4; i++) {
         const int S = mode == 0 ? 1 << i : DKP_WAVES >> i;
-        if (K % (S * chunk_inputs)) continue;
+        if (S > smax || K % (S * chunk_inputs)) continue;
         const int tpw = DKP_WAVES / S;
         const int nseg = (nseg_full + S - 1) / S;
         const int pf = dkp_pf(mode, nseg);
@@ -1121,6 +1121,21 @@ static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, in
         }
     }
     return best;
+}
+
+// K split of pass `mode` in the batch-invariant mode: the split the persistent kernel picks for one token, capped
+// at 4 (the token-group kernel's largest), and dividing both the routed and the shared K range.  It depends on the
+// layer's shape alone, so a token's staged fixed point and its order of sums are the same at every T.
+static int decode_pinned_s(int mode, const FfnParams &P) {
+    const int Imax = P.I > P.Is ? P.I : P.Is;
+    const int K = mode == 0 ? P.d : Imax;
+    const int Kmin = mode == 0 ? P.d : (P.Is > 0 && P.Is < P.I ? P.Is : P.I);
+    const int nout = mode == 0 ? Imax : P.d;
+    const int shared = P.Is > 0 ? 1 : 0;
+    const int rslots = P.E < P.k ? P.E : P.k;  // routed slots of one token
+    int S = dkp_pick_s(mode, K, nout, rslots + shared, (double)rslots + shared, P.wbits, device_cus(), 4);
+    while (S > 1 && (Kmin % (S * (P.wbits == 8 ? 16 : 32)) || K % (S * (P.wbits == 8 ? 16 : 32)))) S >>= 1;
+    return S;
 }
 
 // LDS of the persistent kernel with digit planes for g token rows (g < T: token passes, which add the
@@ -1184,7 +1199,7 @@ static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t
     const double uniq_exp = (double)P.E * (1.0 - std::pow(1.0 - (double)P.k / P.E, (double)P.T));
     const double slots_exp = std::min((double)P.n_routed_slots, uniq_exp) + (P.Is > 0 ? 1 : 0);
     // routed and shared expert split alike: the split must divide both K ranges
-    int S = dkp_pick_s(MODE, K, nout, slots, slots_exp, WBITS, device_cus());
+    int S = P.invariant ? decode_pinned_s(MODE, P) : dkp_pick_s(MODE, K, nout, slots, slots_exp, WBITS, device_cus());
     while (S > 1 && (Kmin % (S * (WBITS == 8 ? 16 : 32)))) S >>= 1;
     const int kpad = pad_k(K / S, WBITS);
     if (P.T > DK_GMAX || dkp_tab_words(MODE, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64)
@@ -1235,8 +1250,9 @@ static hipError_t dk_launch_mode(const FfnParams &P, float *h, float *h_sh, hipS
     const int K = MODE == 0 ? P.d : Imax;
     // both the routed and the shared expert must split the same way: use the smaller intermediate size
     const int Kmin = MODE == 0 ? P.d : (P.Is > 0 && P.Is < P.I ? P.Is : P.I);
-    const int S = pick_s(MODE, Kmin, WBITS) < pick_s(MODE, K, WBITS) ? pick_s(MODE, Kmin, WBITS)
-                                                                        : pick_s(MODE, K, WBITS);
+    const int S = P.invariant ? decode_pinned_s(MODE, P)
+                  : pick_s(MODE, Kmin, WBITS) < pick_s(MODE, K, WBITS) ? pick_s(MODE, Kmin, WBITS)
+                                                                      : pick_s(MODE, K, WBITS);
     const int kpad = pad_k(K / S, WBITS);  // the largest wavefront K part, padded to whole segments
     const int gmax = dk_gmax(P.T, kpad);
     if (S == 4) return dk_launch_s<MODE, WBITS, SRC, 4>(P, h, h_sh, kpad, gmax, stream);

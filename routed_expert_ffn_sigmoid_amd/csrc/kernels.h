@@ -23,16 +23,18 @@ struct FfnParams {
     QW routed, shared;
     const int32_t *offsets, *perm, *uniq, *n_uniq;
     int n_routed_slots;  // min(E, A): grid slots reserved for routed experts
+    bool invariant;      // batch-invariant mode: decode K split fixed by the layer's shape alone
     float *y_perm, *y_sh;
     uint32_t *diag;      // optional counters (nullptr = none): [0] h values not finite in fp16
 };
 
 // router.hip
 // nullptr when the router kernels take the shape, else why not (a buffer beyond 32-bit descriptor offsets)
-const char *router_unsupported(int T, int d, int E, int act);
-size_t router_workspace_bytes(int T, int d, int E);
+// inv: the batch-invariant mode (each token's sums in an order fixed by d and E alone)
+const char *router_unsupported(int T, int d, int E, int act, bool inv);
+size_t router_workspace_bytes(int T, int d, int E, bool inv);
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
-                         float lambda, int32_t *idx, float *w, double *gap, void *ws, hipStream_t stream);
+                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, hipStream_t stream);
 
 // permute.hip
 size_t permute_lds_bytes(int E);

@@ -57,6 +57,7 @@ int check_shape(const char *fn, const moe_shape *s) {
         return fail(MOE_EINVAL, "%s: d, I and I_shared must be multiples of %d for %d-bit weights", fn, m, s->wbits);
     if (s->path != MOE_PATH_AUTO && s->path != MOE_PATH_GEMV && s->path != MOE_PATH_GEMM)
         return fail(MOE_EINVAL, "%s: unknown path %d", fn, s->path);
+    if (s->flags & ~MOE_FLAG_BATCH_INVARIANT) return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, s->flags);
     return MOE_OK;
 }
 
@@ -107,13 +108,16 @@ moe::FfnParams ffn_params(const moe_shape *s) {
     P.wbits = s->wbits;
     P.act = s->act_dtype;
     P.n_routed_slots = s->E < P.A ? s->E : P.A;
+    P.invariant = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
     return P;
 }
 
 // Path the forward call takes for this shape: the matrix-core grouped GEMM once there are enough rows
-// per expert to reuse each weight (more than 16 tokens), the bandwidth-bound decode kernels otherwise.
+// per expert to reuse each weight (more than 16 tokens), the bandwidth-bound decode kernels otherwise; the
+// batch-invariant mode keeps every T on the decode kernels, so a token's bits never depend on the batch.
 int forward_path(const moe_shape *s) {
     if (s->path != MOE_PATH_AUTO) return s->path;
+    if (s->flags & MOE_FLAG_BATCH_INVARIANT) return MOE_PATH_GEMV;
     moe::FfnParams P = ffn_params(s);
     if (s->T > 16 && moe::gemm_supported(P)) return MOE_PATH_GEMM;
     return MOE_PATH_GEMV;
@@ -164,7 +168,8 @@ const char *moe_last_error(void) { return g_err; }
 size_t moe_workspace_size(const moe_shape *s) {
     if (check_shape("moe_workspace_size", s) != MOE_OK) return 0;
     moe::FfnParams P = ffn_params(s);
-    size_t r = moe::router_workspace_bytes(s->T, s->d, s->E);
+    const bool inv = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
+    size_t r = moe::router_workspace_bytes(s->T, s->d, s->E, inv);
     size_t g = moe::decode_workspace_bytes(P);
     size_t need = r > g ? r : g;
     size_t m = moe::gemm_workspace_bytes(P);
@@ -188,10 +193,11 @@ int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *
     rc = check_ws(fn, s, ws, ws_bytes);
     if (rc) return rc;
     if (s->T == 0) return MOE_OK;  // empty batch: nothing to route
-    if (const char *why = moe::router_unsupported(s->T, s->d, s->E, s->act_dtype))
+    const bool inv = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
+    if (const char *why = moe::router_unsupported(s->T, s->d, s->E, s->act_dtype, inv))
         return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
     return launch_status(fn, moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
-                                                topk_idx, topk_w, gap, ws, (hipStream_t)stream));
+                                                topk_idx, topk_w, gap, ws, inv, (hipStream_t)stream));
 }
 
 int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, int32_t *offsets, int32_t *perm,

@@ -186,6 +186,8 @@ __device__ __forceinline__ double sum_congruent(double a, int nq) {
     return a;
 }
 
+// grid: (row blocks, expert column blocks, token groups of RS_TMAX); each token's arithmetic depends only on
+// (d, E, rows), not on T or on the other tokens of its group.
 template <int ACT>
 __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const void *__restrict__ x,
                                                                            const float *__restrict__ Wr, int T,
@@ -194,6 +196,7 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
     __shared__ double red[RSK_THREADS / 64][256];
     __shared__ float xs[RS_TMAX * RSK_MAX_ROWS];  // [t][row in block], row pitch = rows
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tg = blockIdx.z * RS_TMAX, ng = min(RS_TMAX, T - tg);  // this workgroup's tokens tg .. tg + ng
     const int EB = E < RSK_EB ? E : RSK_EB, e0 = blockIdx.y * EB;  // this workgroup's experts
     const int nq = EB >> 2;            // expert quads: a power of two <= 8
     const int R = RSK_THREADS / nq;    // row groups (>= 16: every wave holds at least one)
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
     for (int c = 0; c < XPT; c++) {
         const int o = tid + c * RSK_THREADS;
         const int t = o / rows, i = i0 + o % rows;
-        const uint32_t xo = (t < T && i < i1) ? (uint32_t)(((long)t * d + i) * (ACT == 0 ? 4 : 2)) : kOOB;
+        const uint32_t xo = (t < ng && i < i1) ? (uint32_t)(((long)(tg + t) * d + i) * (ACT == 0 ? 4 : 2)) : kOOB;
         xr[c] = ACT == 0 ? buf_load4(xsrc, xo) : (uint32_t)buf_load2(xsrc, xo);
     }
     uint4 w[RSK_MAXR];
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
     }
     // fixed-order reduction over row groups: the lanes holding the same quad inside a wave, then the 16
     // waves in order, one token at a time
-    for (int t = 0; t < T; t++) {
+    for (int t = 0; t < ng; t++) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const double a = sum_congruent(acc[t][v], nq);
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
         if (tid < EB) {
             double z = 0.0;
             for (int w2 = 0; w2 < RSK_THREADS / 64; w2++) z += red[w2][tid];
-            part[((long)blockIdx.x * T + t) * E + e0 + tid] = z;
+            part[((long)blockIdx.x * T + tg + t) * E + e0 + tid] = z;
         }
         __syncthreads();
     }
@@ -413,7 +416,11 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
     }
 }
 
-static bool use_skinny(int T, int E) { return T <= RS_TMAX && E >= 4 && E <= 256 && (E & (E - 1)) == 0; }
+static bool skinny_fits(int E) { return E >= 4 && E <= 256 && (E & (E - 1)) == 0; }
+
+// The skinny kernel takes T <= RS_TMAX; in the batch-invariant mode it takes every T (in groups of RS_TMAX tokens,
+// each group reading W_r again, mostly from the caches), so that a token's sums never depend on T.
+static bool use_skinny(int T, int E, bool inv) { return (inv || T <= RS_TMAX) && skinny_fits(E); }
 
 static int skinny_eb(int E) { return E < RSK_EB ? E : RSK_EB; }
 
@@ -431,13 +438,14 @@ static int skinny_rows(int d, int E) {
     return (int)rows;
 }
 
-int router_nsplit(int T, int d, int E) {
-    if (use_skinny(T, E)) {
+int router_nsplit(int T, int d, int E, bool inv) {
+    if (use_skinny(T, E, inv)) {
         const int rows = skinny_rows(d, E);
         return (d + rows - 1) / rows;
     }
-    // about two workgroups per CU, at least 4 stages of rows per split
-    const int gx = (E + RM_TE - 1) / RM_TE, gy = (T + RM_TT - 1) / RM_TT;
+    // about two workgroups per CU, at least 4 stages of rows per split; the batch-invariant mode counts one
+    // token tile whatever T is, so the split (and each token's order of sums) depends on (d, E) alone
+    const int gx = (E + RM_TE - 1) / RM_TE, gy = inv ? 1 : (T + RM_TT - 1) / RM_TT;
     const int ksteps = (d + RM_KS - 1) / RM_KS;
     int want = (512 + gx * gy - 1) / (gx * gy);
     if (want > ksteps / 4) want = ksteps / 4;
@@ -447,36 +455,35 @@ int router_nsplit(int T, int d, int E) {
     return (d + chunk - 1) / chunk;
 }
 
-const char *router_unsupported(int T, int d, int E, int act) {
+const char *router_unsupported(int T, int d, int E, int act, bool inv) {
     if ((long)T * d * (act == 0 ? 4 : 2) >= kMaxDescBytes) return "x exceeds 2^31 bytes";
     if ((long)d * E * 4 >= kMaxDescBytes) return "W_r exceeds 2^31 bytes";
-    if (T > 0 && (long)router_nsplit(T, d, E) * T * E * 8 >= kMaxDescBytes)
+    if (T > 0 && (long)router_nsplit(T, d, E, inv) * T * E * 8 >= kMaxDescBytes)
         return "the router's fp64 partial sums (splits x T x E) exceed 2^31 bytes";
     return nullptr;
 }
 
-size_t router_workspace_bytes(int T, int d, int E) {
+size_t router_workspace_bytes(int T, int d, int E, bool inv) {
     if (T <= 0) return 0;
-    return (size_t)router_nsplit(T, d, E) * (size_t)T * (size_t)E * sizeof(double);
+    return (size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double);
 }
 
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
-                         float lambda, int32_t *idx, float *w, double *gap, void *ws, hipStream_t stream) {
+                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, hipStream_t stream) {
     double *part = (double *)ws;
     int nsplit;
-    if (use_skinny(T, E)) {
+    if (use_skinny(T, E, inv)) {
         const int rows = skinny_rows(d, E);
         nsplit = (d + rows - 1) / rows;
+        const dim3 grid(nsplit, E / skinny_eb(E), (T + RS_TMAX - 1) / RS_TMAX);
         if (act == 0)
-            hipLaunchKernelGGL(router_logits_skinny_kernel<0>, dim3(nsplit, E / skinny_eb(E)), dim3(RSK_THREADS), 0,
-                               stream, x, Wr, T,
-                               d, E, rows, part);
+            hipLaunchKernelGGL(router_logits_skinny_kernel<0>, grid, dim3(RSK_THREADS), 0, stream, x, Wr, T, d, E,
+                               rows, part);
         else
-            hipLaunchKernelGGL(router_logits_skinny_kernel<1>, dim3(nsplit, E / skinny_eb(E)), dim3(RSK_THREADS), 0,
-                               stream, x, Wr, T,
-                               d, E, rows, part);
+            hipLaunchKernelGGL(router_logits_skinny_kernel<1>, grid, dim3(RSK_THREADS), 0, stream, x, Wr, T, d, E,
+                               rows, part);
     } else {
-        nsplit = router_nsplit(T, d, E);
+        nsplit = router_nsplit(T, d, E, inv);
         const int chunk = (((d + RM_KS - 1) / RM_KS + nsplit - 1) / nsplit) * RM_KS;
         dim3 grid((E + RM_TE - 1) / RM_TE, (T + RM_TT - 1) / RM_TT, nsplit);
         if (act == 0)

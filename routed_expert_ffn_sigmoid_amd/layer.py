@@ -91,11 +91,12 @@ class DeviceLayerWeights:
 class MoeRun:
     """Output and workspace buffers for one (spec, T) and the four calls that fill them."""
 
-    def __init__(self, spec: synth.LayerSpec, T: int, device="cuda", path: int = B.MOE_PATH_AUTO):
+    def __init__(self, spec: synth.LayerSpec, T: int, device="cuda", path: int = B.MOE_PATH_AUTO, flags: int = 0):
         self.spec, self.T = spec, T
         k, E, d = spec.k, spec.E, spec.d
         A = T * k
-        self.shape = B.make_shape(T, d, E, k, spec.I, spec.I_shared, spec.routed_scale, spec.act, spec.wbits, path)
+        self.shape = B.make_shape(T, d, E, k, spec.I, spec.I_shared, spec.routed_scale, spec.act, spec.wbits, path,
+                                  flags)
         i32 = dict(dtype=torch.int32, device=device)
         self.idx = torch.empty((T, k), **i32)
         self.w = torch.empty((T, k), dtype=torch.float32, device=device)

@@ -207,3 +207,13 @@ def test_static_forward_checks_before_anything_runs():
     assert ei.value.code == B.MOE_EINVAL and "n_uniq" in str(ei.value)
     # an empty batch is a no-op here too
     B.moe_forward_static(shape(T=0), None, q, None, FAKE, None, FAKE, FAKE, None, None, None, stream=0)
+
+
+def test_flags_checked():
+    """Unknown flag bits are refused; the batch-invariant flag is accepted and sizes the router's fixed split."""
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(shape(flags=2), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, HUGE_WS, stream=0)
+    assert ei.value.code == B.MOE_EINVAL and "flags" in str(ei.value)
+    big = dict(T=4096, d=7168, E=256, k=8, I=2048, I_shared=2048, wbits=4, act_dtype=B.MOE_ACT_BF16)
+    assert B.moe_workspace_size(shape(flags=B.MOE_FLAG_BATCH_INVARIANT, **big)) > 0
+    assert B.moe_workspace_size(shape(flags=B.MOE_FLAG_BATCH_INVARIANT)) > 0

@@ -621,23 +621,65 @@ def tile_end_rows(p0, p1, block):
     return np.asarray(rows, dtype=np.int64)
 
 
+INV = B.MOE_FLAG_BATCH_INVARIANT
+
+
+def _results(run, t):
+    """Everything the layer gives token t of a run: routing, its expert rows in choice order, shared and y."""
+    k = run.spec.k
+    inv = run.inv.cpu().numpy()
+    rows = run.y_perm.cpu().numpy()[inv[t * k:(t + 1) * k]]
+    out = dict(idx=run.idx.cpu().numpy()[t], w=run.w.cpu().numpy()[t], gap=run.gap.cpu().numpy()[t:t + 1],
+               y_perm=rows, y=run.y.cpu().numpy()[t])
+    if run.y_shared is not None:
+        out["y_shared"] = run.y_shared.cpu().numpy()[t]
+    return out
+
+
 @pytest.mark.parametrize("name", ["large", "mid"])
-def test_token_output_independent_of_batch(dev, name):
-    """Batch-shape invariance where the K split matches.  For the large and mid layers the decode launches split
-    K the same way at T = 1 and T = 4 (the mid layer's T = 4 down pass takes its slots in token passes), the
-    router's per-token sums do not depend on T (T <= 4), and the expert arithmetic is exact integer work in a
-    fixed order, so each token's output inside a batch of 4 equals, bit for bit, its output computed alone."""
+def test_batch_invariant_mode(orc, dev, name):
+    """MOE_FLAG_BATCH_INVARIANT on the full-size large and mid layers: every result of a token (indices, weights,
+    gap, its y_perm rows, y_shared, y) is bit-identical whether the token runs alone or inside a batch of 2, 4, 8,
+    16 or 20 tokens (20: past the persistent decode kernel, on the token-group kernel), or at another position of a
+    batch (16 tokens in reverse order).  The batch of 16 also matches the oracle."""
     spec = synth.CONFIGS[name]
     W = weights_for(spec, dev)
-    x_np = synth.gen_x(spec, 4)
-    run4 = L.MoeRun(spec, 4, dev)
-    run4.run(L.upload_x(spec, x_np, dev), W)
-    torch.cuda.synchronize()
-    y4 = run4.y.cpu().numpy()
-    run1 = L.MoeRun(spec, 1, dev)
-    for t in range(4):
+    x_np = synth.gen_x(spec, 20, batch=3)
+    alone = []
+    run1 = L.MoeRun(spec, 1, dev, flags=INV)
+    for t in range(20):
         run1.run(L.upload_x(spec, x_np[t:t + 1], dev), W)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(run1.idx.cpu().numpy()[0], run4.idx.cpu().numpy()[t])
-        np.testing.assert_array_equal(run1.y.cpu().numpy()[0], y4[t], err_msg=f"token {t}")
-    say("   T=1 and T=4 outputs identical bit for bit")
+        alone.append(_results(run1, 0))
+    batches = [(T, np.arange(T)) for T in (2, 4, 8, 16, 20)] + [(16, np.arange(16)[::-1])]
+    for T, order in batches:
+        say(f"[invariant] {name} T={T} order={'reversed' if order[0] else 'ascending'}")
+        run = L.MoeRun(spec, T, dev, flags=INV)
+        run.run(L.upload_x(spec, np.ascontiguousarray(x_np[order]), dev), W)
+        torch.cuda.synchronize()
+        for pos, t in enumerate(order):
+            got = _results(run, pos)
+            for key, ref in alone[t].items():
+                np.testing.assert_array_equal(got[key], ref, err_msg=f"T={T} token {t} at {pos}: {key}")
+        if T == 16 and not order[0]:
+            so = sampled_oracle(orc, spec)
+            ro, Y, S, y = so.run(x_np[:16], synth.gen_router(spec), synth.gen_bias(spec), np.arange(16))
+            np.testing.assert_array_equal(run.idx.cpu().numpy(), ro.idx)
+            assert_layer_close(run.y.cpu().numpy(), y, f"{name} invariant mode T=16 y")
+    say("   every token bit-identical alone and in every batch")
+
+
+def test_batch_invariant_mode_matrix_core(dev):
+    """With the flag and MOE_PATH_GEMM the matrix-core path stays in use; its rows are independent of each other
+    as well, so a token alone and the same token inside a batch of 40 (at another position) agree bit for bit."""
+    spec = spec_of(d=512, E=16, k=4, I=384, I_shared=192, routed_scale=2.5)
+    H = HostLayer(spec, 40, dev)
+    run = L.MoeRun(spec, 40, dev, B.MOE_PATH_GEMM, flags=INV)
+    run.run(H.x, H.W)
+    run1 = L.MoeRun(spec, 1, dev, B.MOE_PATH_GEMM, flags=INV)
+    for t in (0, 17, 39):
+        run1.run(H.x[t:t + 1], H.W)
+        torch.cuda.synchronize()
+        got, ref = _results(run, t), _results(run1, 0)
+        for key in ref:
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=f"token {t}: {key}")
