@@ -26,6 +26,20 @@
  *  - the shared expert is part of the dense, always-resident weights (GLM-5.2
  *    page, section 二) and is added to every token with weight 1.
  *  - combine: y[t] = S[t] + sum_j w[t][j] * Y[sorted position of (t, j)].
+ *  - router variants.  The deep-dive page (lshu.cn, untitled Colibri deep dive) gates 8 experts with a
+ *    softmax over the logits, computed against the maximum logit so exp cannot overflow, and keeps the
+ *    top 2 (its section 3.2); a Mixtral-style gate keeps the top 2 under a capacity factor of 1.2 (its
+ *    section 6.2); the walk-through page names expert-choice and soft routing as other router logics that
+ *    reuse the rest of the engine (its section 6).  Readings where the pages are silent:
+ *      softmax top-k: the k largest logits (softmax keeps their order), ties to the lower id; weights
+ *        lambda * p_j / sum of the selected p, i.e. lambda * exp(z_j - z_max) / sum exp(z_j' - z_max);
+ *        soft routing is the same gate with k = E (every expert, weighted by its softmax probability);
+ *      capacity: every expert keeps at most C = ceil(cf * T * k / E) assignments, claimed in the order
+ *        all tokens' first choices, then all second choices, ... (token order within a choice); the
+ *        others become empty slots (id -1) and add nothing, the kept weights are not renormalised;
+ *      expert choice: p = softmax over the experts of each token; every expert takes the C =
+ *        min(T, ceil(cf * T / E)) tokens of largest p (ties to the lower token), weight lambda * p.
+ *    An empty slot (id -1) is skipped by the permutation and the combine.
  *
  * All sums run in index order in fp64.  The OpenMP loops split work only over
  * independent output elements, so results do not depend on the thread count.
@@ -152,12 +166,17 @@ void oracle_permute(int T, int k, int E, const int32_t *idx, int32_t *counts, in
                     int32_t *perm, int32_t *inv, int32_t *uniq, int32_t *n_uniq) {
     long A = (long)T * k;
     for (int e = 0; e < E; e++) counts[e] = 0;
-    for (long a = 0; a < A; a++) counts[idx[a]]++;
+    for (long a = 0; a < A; a++)
+        if (idx[a] >= 0) counts[idx[a]]++;  /* -1: an empty slot */
     offsets[0] = 0;
     for (int e = 0; e < E; e++) offsets[e + 1] = offsets[e] + counts[e];
     int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
     for (int e = 0; e < E; e++) cursor[e] = offsets[e];
     for (long a = 0; a < A; a++) {
+        if (idx[a] < 0) {
+            inv[a] = -1;
+            continue;
+        }
         int32_t p = cursor[idx[a]]++;
         perm[p] = (int32_t)a;
         inv[a] = p;
@@ -234,10 +253,116 @@ void oracle_combine(int T, int k, int d, const double *Y, const double *S, const
         for (int o = 0; o < d; o++) {
             double acc = S ? S[(long)t * d + o] : 0.0;
             for (int j = 0; j < k; j++)
-                acc += (double)w[(long)t * k + j] * Y[(long)inv[(long)t * k + j] * d + o];
+                if (inv[(long)t * k + j] >= 0)  /* an empty slot adds nothing */
+                    acc += (double)w[(long)t * k + j] * Y[(long)inv[(long)t * k + j] * d + o];
             y[(long)t * d + o] = acc;
         }
     }
+}
+
+/*
+ * Softmax top-k, one token at a time (reading in the header): idx[t][0..k) = the k largest z (desc, equal
+ * z by lower id); with m = z of idx[t][0], u_j = exp(z_j - m) and w[t][j] = lambda * u_j / sum_j' u_j' (fp64,
+ * stored fp32); gap[t] = z of the k-th minus z of the (k+1)-th (INFINITY when k == E).
+ */
+void oracle_router_select_softmax(int T, int E, int k, const double *z, double lambda, int32_t *idx, float *w,
+                                  double *gap) {
+#pragma omp parallel
+    {
+        oracle_kv *kv = (oracle_kv *)malloc(sizeof(oracle_kv) * (size_t)E);
+        double *u = (double *)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; t++) {
+            for (int e = 0; e < E; e++) {
+                kv[e].v = z[(long)t * E + e];
+                kv[e].id = e;
+            }
+            qsort(kv, (size_t)E, sizeof(oracle_kv), kv_cmp);
+            double sum = 0.0;
+            for (int j = 0; j < k; j++) {
+                idx[(long)t * k + j] = kv[j].id;
+                u[j] = exp(kv[j].v - kv[0].v);
+                sum += u[j];
+            }
+            for (int j = 0; j < k; j++) w[(long)t * k + j] = (float)(lambda * u[j] / sum);
+            if (gap) gap[t] = (k < E) ? kv[k - 1].v - kv[k].v : INFINITY;
+        }
+        free(kv);
+        free(u);
+    }
+}
+
+/*
+ * Capacity: every expert keeps at most C of the assignments idx [T][k] (in place), claimed choice by choice
+ * (j = 0 for every token, then j = 1, ...) and token by token within a choice; the rest become -1.  Slots
+ * that are already -1 stay so.
+ */
+void oracle_capacity(int T, int k, int E, int C, int32_t *idx) {
+    int32_t *used = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    for (int j = 0; j < k; j++)
+        for (int t = 0; t < T; t++) {
+            int32_t *a = idx + (long)t * k + j;
+            if (*a < 0) continue;
+            if (used[*a] < C)
+                used[*a]++;
+            else
+                *a = -1;
+        }
+    free(used);
+}
+
+/* order of tokens for one expert: larger probability first, equal ones by lower token */
+typedef struct {
+    double p;
+    int t;
+} oracle_tp;
+
+static int tp_cmp(const void *a, const void *b) {
+    const oracle_tp *x = (const oracle_tp *)a, *y = (const oracle_tp *)b;
+    if (x->p > y->p) return -1;
+    if (x->p < y->p) return 1;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+/*
+ * Expert choice: p[t][e] = exp(z[t][e] - m_t) / sum_e' exp(z[t][e'] - m_t), m_t = max_e z[t][e], the sum taken
+ * over e ascending; expert e takes the C tokens of largest p[.][e] (equal p by lower token).  Outputs, with one
+ * slot per expert (k = E): idx[t][e] = e and w[t][e] = lambda * p[t][e] (fp32) when e took t, else -1 and 0.
+ * gap_e (optional, [E]): p of the C-th chosen token minus p of the (C+1)-th (INFINITY when C == T).
+ */
+void oracle_expert_choice(int T, int E, int C, const double *z, double lambda, int32_t *idx, float *w,
+                          double *gap_e) {
+    double *p = (double *)malloc(sizeof(double) * (size_t)T * (size_t)E);
+    for (int t = 0; t < T; t++) {
+        const double *zt = z + (long)t * E;
+        double m = zt[0], s = 0.0;
+        for (int e = 1; e < E; e++) m = zt[e] > m ? zt[e] : m;
+        for (int e = 0; e < E; e++) s += exp(zt[e] - m);
+        for (int e = 0; e < E; e++) p[(long)t * E + e] = exp(zt[e] - m) / s;
+        for (int e = 0; e < E; e++) {
+            idx[(long)t * E + e] = -1;
+            w[(long)t * E + e] = 0.0f;
+        }
+    }
+#pragma omp parallel
+    {
+        oracle_tp *tp = (oracle_tp *)malloc(sizeof(oracle_tp) * (size_t)T);
+#pragma omp for schedule(static)
+        for (int e = 0; e < E; e++) {
+            for (int t = 0; t < T; t++) {
+                tp[t].p = p[(long)t * E + e];
+                tp[t].t = t;
+            }
+            qsort(tp, (size_t)T, sizeof(oracle_tp), tp_cmp);
+            for (int c = 0; c < C; c++) {
+                idx[(long)tp[c].t * E + e] = e;
+                w[(long)tp[c].t * E + e] = (float)(lambda * tp[c].p);
+            }
+            if (gap_e) gap_e[e] = C < T ? tp[C - 1].p - tp[C].p : INFINITY;
+        }
+        free(tp);
+    }
+    free(p);
 }
 
 /* Pointers to expert e inside stacked [n][rows][row_bytes] weight arrays. */

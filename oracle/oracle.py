@@ -33,6 +33,9 @@ def lib():
         _lib.oracle_combine.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P]
         _lib.oracle_moe_layer.argtypes = ([C.c_int] * 7 + [C.c_double, C.c_int] + [P] * 5 + [P] * 12)
         _lib.oracle_moe_tokens.argtypes = ([C.c_int, P] + [C.c_int] * 6 + [C.c_double, C.c_int] + [P] * 5 + [P] * 4)
+        _lib.oracle_router_select_softmax.argtypes = [C.c_int, C.c_int, C.c_int, P, C.c_double, P, P, P]
+        _lib.oracle_capacity.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P]
+        _lib.oracle_expert_choice.argtypes = [C.c_int, C.c_int, C.c_int, P, C.c_double, P, P, P]
     return _lib
 
 
@@ -214,3 +217,89 @@ def moe_tokens(spec, tokens, x, W_r, bias, routed, shared) -> TokenResult:
                             C.byref(r), C.byref(s) if s is not None else None,
                             _p(idx), _p(w), _p(gap), _p(y))
     return TokenResult(tokens, idx, w, gap, y)
+
+
+# ----------------------------------------------------------------------------
+# router variants (softmax top-k, capacity, expert choice)
+# ----------------------------------------------------------------------------
+
+ROUTER_SIGMOID_BIAS = 0
+ROUTER_SOFTMAX = 1
+ROUTER_EXPERT_CHOICE = 2
+
+
+def router_select_softmax(z: np.ndarray, k: int, lam: float) -> Routing:
+    """Softmax top-k: the k largest logits (ties to the lower id), weights lambda * softmax renormalised over them;
+    gap in logit units.  s and sel are not produced (None)."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    T, E = z.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    gap = np.empty(T, dtype=np.float64)
+    lib().oracle_router_select_softmax(T, E, k, _p(z), float(lam), _p(idx), _p(w), _p(gap))
+    return Routing(idx, w, gap, None, None)
+
+
+def capacity_of(T: int, k: int, E: int, cf: float) -> int:
+    """C = ceil(cf * T * k / E) with cf as the fp32 value the ABI carries."""
+    return int(np.ceil(float(np.float32(cf)) * T * k / E))
+
+
+def capacity(idx: np.ndarray, E: int, C: int) -> np.ndarray:
+    """A copy of idx [T][k] in which every expert keeps at most C assignments (choice-major, then token order)."""
+    out = np.ascontiguousarray(idx, dtype=np.int32).copy()
+    T, k = out.shape
+    lib().oracle_capacity(T, k, E, int(C), _p(out))
+    return out
+
+
+def expert_choice_capacity(T: int, E: int, cf: float) -> int:
+    """C = min(T, ceil(cf * T / E)) with cf as the fp32 value the ABI carries."""
+    return min(T, int(np.ceil(float(np.float32(cf)) * T / E)))
+
+
+def expert_choice(z: np.ndarray, C: int, lam: float):
+    """Expert choice: per expert the C tokens of largest softmax probability.  Returns (idx [T][E], w [T][E],
+    gap_e [E])."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    T, E = z.shape
+    idx = np.empty((T, E), dtype=np.int32)
+    w = np.empty((T, E), dtype=np.float32)
+    gap = np.empty(E, dtype=np.float64)
+    lib().oracle_expert_choice(T, E, int(C), _p(z), float(lam), _p(idx), _p(w), _p(gap))
+    return idx, w, gap
+
+
+def route_variant(spec, x, W_r, bias, router: int, capacity_factor: float = 0.0):
+    """Routing of a layer under one of the router variants: (idx, w, gap).  gap is per token for the top-k routers
+    and per expert for expert choice."""
+    z = router_logits(decode_act(x, spec.act), W_r)
+    T = z.shape[0]
+    if router == ROUTER_EXPERT_CHOICE:
+        return expert_choice(z, expert_choice_capacity(T, spec.E, capacity_factor), spec.routed_scale)
+    if router == ROUTER_SOFTMAX:
+        r = router_select_softmax(z, spec.k, spec.routed_scale)
+    else:
+        r = router_select(z, bias, spec.k, spec.routed_scale)
+    idx = r.idx
+    if capacity_factor > 0:
+        idx = capacity(idx, spec.E, capacity_of(T, spec.k, spec.E, capacity_factor))
+    return idx, r.w, r.gap
+
+
+def moe_layer_routed(spec, x, idx, w, routed, shared, k=None):
+    """The rest of the layer for a given routing idx/w [T][k] (empty slots -1): batch union, experts, shared expert,
+    combine, each by the oracle functions above.  k defaults to spec.k (expert choice passes E)."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T = idx.shape[0]
+    k = idx.shape[1] if k is None else k
+    xd = decode_act(x, spec.act)
+    p = permute(idx, spec.E)
+    Yperm = np.zeros((T * k, spec.d))
+    for u in range(p.n_uniq):
+        e = int(p.uniq[u])
+        rows = p.perm[p.offsets[e]:p.offsets[e + 1]]
+        Yperm[p.offsets[e]:p.offsets[e + 1]] = expert_apply(xd[rows // k], spec.d, spec.I, spec.wbits, routed, e)
+    S = expert_apply(xd, spec.d, spec.I_shared, spec.wbits, shared, 0) if spec.I_shared else None
+    y = combine(Yperm, S, p.inv, w)
+    return p, Yperm, S, y

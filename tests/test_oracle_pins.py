@@ -313,3 +313,126 @@ def test_thread_count_and_seed_determinism(orc):
         orc.set_threads(n0)
     np.testing.assert_array_equal(a.y, b.y)
     np.testing.assert_array_equal(a.Yperm, b.Yperm)
+
+
+# ----------------------------------------------------------------------------
+# router variants: softmax top-k (soft routing = k = E), capacity, expert choice
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("E,k,ties", [(8, 2, False), (16, 4, False), (8, 2, True), (12, 5, True)])
+def test_softmax_topk_equals_full_sort_of_scipy_softmax(orc, E, k, ties):
+    """The deep-dive page's gate: softmax over the logits, keep the top k.  Selection equals a brute-force full sort
+    of scipy's softmax probabilities (larger first, equal ones by lower id); weights equal those probabilities
+    renormalised over the selected and scaled by lambda; gap is the logit margin of the k-th over the (k+1)-th."""
+    rng = np.random.default_rng(E * 7 + k)
+    z = rng.standard_normal((300, E)) * 3
+    if ties:
+        z = np.round(z)
+    lam = 1.7
+    r = orc.router_select_softmax(z, k, lam)
+    p = scipy.special.softmax(z, axis=1)
+    for t in range(z.shape[0]):
+        top, order = brute_topk(z[t], k)  # softmax keeps the order of the logits, so this is the order of p
+        assert list(r.idx[t]) == top
+        assert list(r.idx[t]) == sorted(top, key=lambda e: (-p[t][e], e))
+        ref = lam * p[t][top] / p[t][top].sum()
+        np.testing.assert_allclose(r.w[t], ref, rtol=2e-7, atol=0)
+        assert r.gap[t] == z[t][order[k - 1]] - z[t][order[k]]
+
+
+def test_soft_routing_is_softmax_with_k_equal_e(orc):
+    """Soft routing: every expert with its softmax probability (times lambda), in descending order."""
+    rng = np.random.default_rng(31)
+    z = rng.standard_normal((50, 8)) * 2
+    r = orc.router_select_softmax(z, 8, 1.0)
+    p = scipy.special.softmax(z, axis=1)
+    for t in range(z.shape[0]):
+        np.testing.assert_allclose(r.w[t], p[t][r.idx[t]], rtol=2e-7, atol=0)
+        assert sorted(r.idx[t]) == list(range(8)) and np.isinf(r.gap[t])
+    # large logits: the maximum is subtracted first, so nothing overflows
+    r = orc.router_select_softmax(z * 1000, 2, 1.0)
+    assert np.all(np.isfinite(r.w)) and np.allclose(r.w.sum(1), 1.0)
+
+
+def test_softmax_all_tie(orc):
+    r = orc.router_select_softmax(np.zeros((4, 8)), 3, 2.5)
+    assert np.all(r.idx == np.arange(3)) and np.all(r.w == np.float32(2.5 / 3)) and np.all(r.gap == 0)
+
+
+def _capacity_by_grouping(idx, E, C):
+    """Per expert, its assignments listed by (choice, token) and the first C kept: built by grouping, not by
+    walking the assignments in order as the oracle does."""
+    T, k = idx.shape
+    out = np.full_like(idx, -1)
+    for e in range(E):
+        ts, js = np.nonzero(idx == e)
+        order = np.lexsort((ts, js))[:C]  # sort by choice, then token
+        out[ts[order], js[order]] = e
+    return out
+
+
+@pytest.mark.parametrize("T,k,E,cf", [(64, 2, 8, 1.2), (200, 2, 8, 1.0), (37, 4, 16, 1.25), (500, 8, 256, 1.2),
+                                      (20, 2, 4, 100.0)])
+def test_capacity_keeps_the_first_c_of_each_expert(orc, T, k, E, cf):
+    """Top-k with a capacity factor (the deep-dive page's Mixtral-style gate, capacity factor 1.2): every expert
+    keeps at most C = ceil(cf T k / E) assignments, the earliest by (choice, token); a huge factor drops nothing."""
+    rng = np.random.default_rng(T + k)
+    # skewed routing so that popular experts overflow
+    pop = rng.zipf(1.5, size=(T, k * 4)) % E
+    idx = np.array([list(dict.fromkeys(row))[:k] + [-1] * (k - len(set(row[:k * 4])))
+                    for row in pop])[:, :k].astype(np.int32)
+    C = orc.capacity_of(T, k, E, cf)
+    assert C == int(np.ceil(float(np.float32(cf)) * T * k / E))
+    out = orc.capacity(idx, E, C)
+    np.testing.assert_array_equal(out, _capacity_by_grouping(idx, E, C))
+    counts = np.bincount(out[out >= 0], minlength=E)
+    assert counts.max() <= C
+    kept_or_empty = (out == idx) | (out == -1)
+    assert kept_or_empty.all()
+    if cf >= 100:
+        np.testing.assert_array_equal(out, idx)
+
+
+@pytest.mark.parametrize("T,E,cf", [(64, 8, 2.0), (33, 4, 1.0), (300, 16, 2.5), (10, 8, 20.0)])
+def test_expert_choice_takes_top_tokens_per_expert(orc, T, E, cf):
+    """Expert choice (the walk-through page's other router logic): each expert takes the C tokens of largest
+    softmax probability; checked against scipy's softmax and a stable argsort per expert."""
+    rng = np.random.default_rng(T * E)
+    z = rng.standard_normal((T, E)) * 2
+    C = orc.expert_choice_capacity(T, E, cf)
+    assert C == min(T, int(np.ceil(float(np.float32(cf)) * T / E)))
+    idx, w, gap = orc.expert_choice(z, C, 2.5)
+    p = scipy.special.softmax(z, axis=1)
+    for e in range(E):
+        order = np.argsort(-p[:, e], kind="stable")[:C]
+        chosen = np.flatnonzero(idx[:, e] == e)
+        assert sorted(chosen.tolist()) == sorted(order.tolist())
+        assert np.all(idx[:, e][~np.isin(np.arange(T), chosen)] == -1)
+        np.testing.assert_allclose(w[chosen, e], 2.5 * p[chosen, e], rtol=2e-7, atol=0)
+        assert np.all(w[idx[:, e] < 0, e] == 0)
+    assert np.all((idx >= 0).sum(0) == C)
+
+
+def test_permute_and_combine_skip_empty_slots(orc):
+    """Empty slots (-1, from capacity or expert choice) take no place in the permutation (inv = -1) and add nothing
+    in the combine: the layer equals the sum over the kept slots, computed by hand."""
+    rng = np.random.default_rng(9)
+    spec = tiny_spec(E=8, k=3, I=32, I_shared=32)
+    inp = synth.gen_layer(spec, 12)
+    idx, w, _ = orc.route_variant(spec, inp.x, inp.W_r, inp.bias, orc.ROUTER_SOFTMAX, 0.7)
+    assert (idx < 0).any()
+    p, Yperm, S, y = orc.moe_layer_routed(spec, inp.x, idx, w, inp.routed, inp.shared)
+    flat = idx.ravel()
+    assert np.all(p.inv[flat < 0] == -1) and p.counts.sum() == (flat >= 0).sum() and p.n_uniq >= 0
+    valid = np.flatnonzero(flat >= 0)
+    np.testing.assert_array_equal(p.perm[:valid.size], valid[np.argsort(flat[valid], kind="stable")])
+    xd = orc.decode_act(inp.x, spec.act)
+    ref = S.copy()
+    for t in range(12):
+        for j in range(3):
+            e = idx[t, j]
+            if e >= 0:
+                ref[t] += np.float64(w[t, j]) * orc.expert_apply(xd[t:t + 1], spec.d, spec.I, 8, inp.routed, e)[0]
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    del rng
