@@ -54,6 +54,9 @@ def parse(argv=None):
     ap.add_argument("--pool", type=int, default=None, help="activation batches rotated per step (16 decode, 2 prefill)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--invariant", action="store_true", help="the batch-shape-invariant mode (MOE_FLAG_BATCH_INVARIANT)")
+    ap.add_argument("--router", default="sigmoid", choices=["sigmoid", "softmax", "expert-choice"],
+                    help="router variant (expert choice runs the layer with one slot per expert, k = E)")
+    ap.add_argument("--capacity-factor", type=float, default=0.0)
     ap.add_argument("--only", action="store_true", help="the named workload alone (no additional workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of each oracle sample")
@@ -169,13 +172,17 @@ def measure(spec, T, args, dev):
     pool_n = args.pool or (16 if decode else 2)
     path = {"auto": B.MOE_PATH_AUTO, "gemv": B.MOE_PATH_GEMV, "gemm": B.MOE_PATH_GEMM}[args.path]
     flags = B.MOE_FLAG_BATCH_INVARIANT if args.invariant else 0
+    router = {"sigmoid": B.MOE_ROUTER_SIGMOID_BIAS, "softmax": B.MOE_ROUTER_SOFTMAX,
+              "expert-choice": B.MOE_ROUTER_EXPERT_CHOICE}[args.router]
+    if router == B.MOE_ROUTER_EXPERT_CHOICE:
+        spec = synth.small_spec(spec, k=spec.E)
 
     t_setup = time.perf_counter()
     layers = [L.DeviceLayerWeights(spec, 0, l, dev) for l in range(n_layers)]
     pool = [L.upload_x(spec, synth.gen_x(spec, T, 0, b), dev) for b in range(pool_n)]
     cycle = n_layers * pool_n // math.gcd(n_layers, pool_n)
     # one set of output/workspace buffers per step of the rotation, so each step can be a captured graph
-    runs = [L.MoeRun(spec, T, dev, path, flags) for _ in range(cycle)]
+    runs = [L.MoeRun(spec, T, dev, path, flags, router, args.capacity_factor) for _ in range(cycle)]
     setup_s = time.perf_counter() - t_setup
 
     def operands(i):
@@ -208,6 +215,11 @@ def measure(spec, T, args, dev):
     with torch.cuda.graph(perm_graph, stream=side):
         for i in range(cycle):
             runs[i].permute()
+    route_graph = torch.cuda.CUDAGraph()  # the router alone
+    with torch.cuda.graph(route_graph, stream=side):
+        for i in range(cycle):
+            x, W = operands(i)
+            runs[i].route(x, W)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -239,6 +251,13 @@ def measure(spec, T, args, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     perm_us = e0.elapsed_time(e1) * 1e3 / n_fwd
+    route_graph.replay()
+    e0.record(stream)
+    for _ in range(fwd_reps):
+        route_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    route_us = e0.elapsed_time(e1) * 1e3 / n_fwd
 
     # distribution of the step time: each step's graph replay between its own pair of events (a separate
     # pass after the timed one, so the events do not enter the reported throughput)
@@ -287,13 +306,14 @@ def measure(spec, T, args, dev):
                    "T": T, "layers_resident": n_layers, "x_pool": pool_n,
                    "mean_unique_experts": round(float(np.mean([n_uniq[i % cycle] for i in steps_idx])), 2),
                    "assignments_per_unique_expert": round(T * spec.k / float(np.mean(n_uniq)), 2),
-                   "permute_us_alone": round(perm_us, 2),
+                   "permute_us_alone": round(perm_us, 2), "route_us_alone": round(route_us, 2),
+                   "router": args.router, "capacity_factor": args.capacity_factor,
                    "timing": "HIP graph per step (the four ABI calls), replayed",
                    "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
                    "path": args.path, "batch_invariant": bool(args.invariant), "setup_s": round(setup_s, 1)},
         "roofline": roof,
     }
-    del runs, step_graphs, fwd_graph, perm_graph, layers, pool
+    del runs, step_graphs, fwd_graph, perm_graph, route_graph, layers, pool
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
@@ -339,7 +359,8 @@ def main(argv=None):
         "roofline": head["roofline"],
     }
     default_run = args.config == "mid" and args.T is None and not args.only and args.path == "auto" \
-        and not args.invariant and args.layers is None and args.pool is None
+        and not args.invariant and args.layers is None and args.pool is None and args.router == "sigmoid" \
+        and args.capacity_factor == 0
     extra = []
     if default_run:
         for name, Tw in ADDITIONAL:

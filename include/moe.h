@@ -117,13 +117,45 @@ extern "C" {
  */
 #define MOE_FLAG_BATCH_INVARIANT 1
 
+/*
+ * Router variants (moe_route).  The default is the sigmoid router above.  The
+ * untitled Colibri deep-dive page (lshu.cn) gates 8 experts with a softmax over
+ * the logits, taken against the largest logit, and keeps the top 2 (its section
+ * 3.2), and gives a Mixtral-style gate a capacity factor of 1.2 (its section
+ * 6.2); the walk-through page names expert choice and soft routing as router
+ * logics that reuse the rest of the engine (its section 6).  As read here:
+ *   MOE_ROUTER_SIGMOID_BIAS  sigmoid scores, bias for selection (see moe_route).
+ *   MOE_ROUTER_SOFTMAX       the k largest logits z (softmax keeps their order),
+ *       equal ones by lower id; topk_w[t][j] = lambda * exp(z_j - z_max) /
+ *       sum over the selected of exp(z_j' - z_max), i.e. the softmax probability
+ *       renormalised over the selected; gap in logit units; bias is not used
+ *       (may be NULL).  Soft routing is this gate with k = E.
+ *   MOE_ROUTER_EXPERT_CHOICE  p[t][e] = softmax over the experts of token t;
+ *       every expert takes the C = min(T, ceil(capacity_factor * T / E)) tokens
+ *       of largest p (equal p by lower token).  Requires k = E (one slot per
+ *       expert): topk_idx[t][e] = e and topk_w[t][e] = lambda * p[t][e] when
+ *       expert e took token t, else -1 and 0; gap (optional) then has E entries:
+ *       p of expert e's C-th token minus p of its (C+1)-th (+inf when C = T).
+ * capacity_factor (top-k routers; 0 = none): every expert keeps at most
+ *   C = ceil(capacity_factor * T * k / E) of its assignments, all tokens' first
+ *   choices before any second choice and tokens in order within a choice; the
+ *   others become empty slots (id -1; their weights are kept, not
+ *   renormalised).  Empty slots take no place in moe_permute and add nothing in
+ *   moe_combine.
+ */
+#define MOE_ROUTER_SIGMOID_BIAS 0
+#define MOE_ROUTER_SOFTMAX 1
+#define MOE_ROUTER_EXPERT_CHOICE 2
+
 typedef struct moe_shape {
     int32_t T, d, E, k, I, I_shared;
-    float routed_scale; /* lambda: the normalised combine weights are multiplied by it */
-    int32_t act_dtype;  /* MOE_ACT_F32 | MOE_ACT_BF16 */
-    int32_t wbits;      /* 8 | 4 */
-    int32_t path;       /* MOE_PATH_* (moe_forward only) */
-    int32_t flags;      /* 0 or MOE_FLAG_BATCH_INVARIANT */
+    float routed_scale;    /* lambda: the normalised combine weights are multiplied by it */
+    int32_t act_dtype;     /* MOE_ACT_F32 | MOE_ACT_BF16 */
+    int32_t wbits;         /* 8 | 4 */
+    int32_t path;          /* MOE_PATH_* (moe_forward only) */
+    int32_t flags;         /* 0 or MOE_FLAG_BATCH_INVARIANT */
+    int32_t router;        /* MOE_ROUTER_* (moe_route only) */
+    float capacity_factor; /* see MOE_ROUTER_*; 0 = no capacity limit for the top-k routers */
 } moe_shape;
 
 typedef struct moe_qffn {
@@ -167,9 +199,10 @@ MOE_API int moe_route(const moe_shape *shape, const void *x, const float *W_r, c
  *   uniq[0..n)     experts with counts > 0, ascending; -1 after [E]
  *   n_uniq[0]      number of unique experts                     [1]
  * Integer work, bit-exact and independent of scheduling.
- * Invalid ids: topk_idx entries outside [0, E) are not counted, get no place
- * in perm, have inv = -1, and set n_uniq to -1 (an error flag for the
- * caller).  counts/offsets/uniq then describe the valid assignments only;
+ * Empty slots: entries equal to -1 (capacity drops, expert choice) are not
+ * counted, get no place in perm and have inv = -1.
+ * Invalid ids: other entries outside [0, E) are treated the same way and
+ * also set n_uniq to -1 (an error flag for the caller).  counts/offsets/uniq then describe the valid assignments only;
  * moe_forward applies every expert listed in uniq (the non-negative prefix)
  * and moe_combine leaves out the dropped choices, so y[t] is the shared term
  * plus the token's valid choices.

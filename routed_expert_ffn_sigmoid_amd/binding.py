@@ -32,6 +32,10 @@ MOE_DIAG_COUNT = 1
 
 MOE_FLAG_BATCH_INVARIANT = 1
 
+MOE_ROUTER_SIGMOID_BIAS = 0
+MOE_ROUTER_SOFTMAX = 1
+MOE_ROUTER_EXPERT_CHOICE = 2
+
 MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_GEMM = 2
@@ -52,7 +56,8 @@ class MoeError(RuntimeError):
 class moe_shape(C.Structure):
     _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("E", C.c_int32), ("k", C.c_int32), ("I", C.c_int32),
                 ("I_shared", C.c_int32), ("routed_scale", C.c_float), ("act_dtype", C.c_int32),
-                ("wbits", C.c_int32), ("path", C.c_int32), ("flags", C.c_int32)]
+                ("wbits", C.c_int32), ("path", C.c_int32), ("flags", C.c_int32), ("router", C.c_int32),
+                ("capacity_factor", C.c_float)]
 
 
 class moe_qffn(C.Structure):
@@ -114,8 +119,8 @@ def _check(rc: int) -> None:
 
 
 def make_shape(T, d, E, k, I, I_shared=0, routed_scale=1.0, act_dtype=MOE_ACT_BF16, wbits=4,
-               path=MOE_PATH_AUTO, flags=0) -> moe_shape:
-    return moe_shape(T, d, E, k, I, I_shared, routed_scale, act_dtype, wbits, path, flags)
+               path=MOE_PATH_AUTO, flags=0, router=0, capacity_factor=0.0) -> moe_shape:
+    return moe_shape(T, d, E, k, I, I_shared, routed_scale, act_dtype, wbits, path, flags, router, capacity_factor)
 
 
 def make_qffn(q_gate, q_up, q_down, s_gate, s_up, s_down, z_gate, z_up, z_down) -> moe_qffn:

@@ -31,10 +31,13 @@ struct FfnParams {
 // router.hip
 // nullptr when the router kernels take the shape, else why not (a buffer beyond 32-bit descriptor offsets)
 // inv: the batch-invariant mode (each token's sums in an order fixed by d and E alone)
+// router: 0 sigmoid + bias, 1 softmax gate, 2 expert choice; C: capacity (0 = none for the top-k routers; the
+// tokens per expert for expert choice)
 const char *router_unsupported(int T, int d, int E, int act, bool inv);
-size_t router_workspace_bytes(int T, int d, int E, bool inv);
+size_t router_workspace_bytes(int T, int d, int E, bool inv, int k, int router, bool capacity);
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
-                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, hipStream_t stream);
+                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
+                         hipStream_t stream);
 
 // permute.hip
 size_t permute_lds_bytes(int E);

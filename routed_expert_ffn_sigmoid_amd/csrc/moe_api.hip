@@ -1,5 +1,6 @@
 // C ABI of the MoE-layer forward: argument validation, workspace layout and kernel launches.
 // Nothing here allocates device memory or waits on the device.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -58,6 +59,12 @@ int check_shape(const char *fn, const moe_shape *s) {
     if (s->path != MOE_PATH_AUTO && s->path != MOE_PATH_GEMV && s->path != MOE_PATH_GEMM)
         return fail(MOE_EINVAL, "%s: unknown path %d", fn, s->path);
     if (s->flags & ~MOE_FLAG_BATCH_INVARIANT) return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, s->flags);
+    if (s->router != MOE_ROUTER_SIGMOID_BIAS && s->router != MOE_ROUTER_SOFTMAX && s->router != MOE_ROUTER_EXPERT_CHOICE)
+        return fail(MOE_EINVAL, "%s: unknown router %d", fn, s->router);
+    if (!(s->capacity_factor >= 0.f && s->capacity_factor <= 1e6f))
+        return fail(MOE_EINVAL, "%s: capacity_factor must be in [0, 1e6]", fn);
+    if (s->router == MOE_ROUTER_EXPERT_CHOICE && (s->k != s->E || !(s->capacity_factor > 0.f)))
+        return fail(MOE_EINVAL, "%s: expert choice needs k = E (one slot per expert) and capacity_factor > 0", fn);
     return MOE_OK;
 }
 
@@ -123,6 +130,19 @@ int forward_path(const moe_shape *s) {
     return MOE_PATH_GEMV;
 }
 
+// Capacity the router applies: top-k routers, ceil(cf T k / E) (0 = none); expert choice, the tokens each expert
+// takes, min(T, ceil(cf T / E)).
+int router_capacity(const moe_shape *s) {
+    if (s->capacity_factor <= 0.f || s->T == 0) return 0;
+    const double cf = (double)s->capacity_factor;
+    if (s->router == MOE_ROUTER_EXPERT_CHOICE) {
+        const double c = ceil(cf * s->T / s->E);
+        return c >= s->T ? s->T : (int)c;
+    }
+    const double c = ceil(cf * s->T * s->k / s->E);
+    return c >= (double)s->T * s->k ? s->T * s->k : (int)c;
+}
+
 // Workspace bytes of moe_forward alone for this shape (the path it takes).
 size_t forward_workspace_bytes(const moe_shape *s) {
     const moe::FfnParams P = ffn_params(s);
@@ -169,7 +189,7 @@ size_t moe_workspace_size(const moe_shape *s) {
     if (check_shape("moe_workspace_size", s) != MOE_OK) return 0;
     moe::FfnParams P = ffn_params(s);
     const bool inv = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
-    size_t r = moe::router_workspace_bytes(s->T, s->d, s->E, inv);
+    size_t r = moe::router_workspace_bytes(s->T, s->d, s->E, inv, s->k, s->router, router_capacity(s) > 0);
     size_t g = moe::decode_workspace_bytes(P);
     size_t need = r > g ? r : g;
     size_t m = moe::gemm_workspace_bytes(P);
@@ -186,7 +206,7 @@ int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *
     if (rc) return rc;
     REQUIRE_PTR_T(x, "x");
     REQUIRE_PTR(W_r, "W_r");
-    REQUIRE_PTR(bias, "bias");
+    if (s->router == MOE_ROUTER_SIGMOID_BIAS || bias) REQUIRE_PTR(bias, "bias");  // the other routers take no bias
     REQUIRE_PTR_T(topk_idx, "topk_idx");
     REQUIRE_PTR_T(topk_w, "topk_w");
     if (gap && !aligned(gap, 16)) return fail(MOE_EALIGN, "%s: gap is not 16-byte aligned", fn);
@@ -197,7 +217,8 @@ int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *
     if (const char *why = moe::router_unsupported(s->T, s->d, s->E, s->act_dtype, inv))
         return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
     return launch_status(fn, moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
-                                                topk_idx, topk_w, gap, ws, inv, (hipStream_t)stream));
+                                                topk_idx, topk_w, gap, ws, inv, s->router, router_capacity(s),
+                                                (hipStream_t)stream));
 }
 
 int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, int32_t *offsets, int32_t *perm,

@@ -10,7 +10,8 @@
 //      same expert find each other with one ballot per key bit, take their
 //      rank among lower lanes, and the highest lane of each group advances
 //      the wave's running count.
-// Every output is a function of topk_idx alone, independent of scheduling.
+// Every output is a function of topk_idx alone, independent of scheduling.  An id of -1 is an empty slot
+// (a capacity drop, or no expert in expert choice): skipped like an invalid id, without the error flag.
 //
 // Above PMB_MIN_A assignments one workgroup would take the whole sort in series (84 us at A = 65536), so
 // the work is cut into nb contiguous blocks of about PMB_PER_BLOCK assignments, in three launches:
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(PM_THREADS) void permute_kernel(const int32_t *__re
         int key = keys[a];
         if (key >= 0 && key < E)
             atomicAdd(&cnt[wv * E + key], 1);
-        else
+        else if (key != -1)  // -1: an empty slot, skipped; any other id out of range is an error
             atomicOr(&bad, 1);
     }
     __syncthreads();
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(PMB_WAVES * 64) void permute_hist_kernel(const int3
         const int key = keys[a];
         if (key >= 0 && key < E)
             atomicAdd(&h[key], 1);
-        else
+        else if (key != -1)  // -1: an empty slot, skipped; any other id out of range is an error
             atomicOr(&bad, 1);
     }
     __syncthreads();

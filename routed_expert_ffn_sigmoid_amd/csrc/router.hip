@@ -16,6 +16,9 @@
 // unless two selection scores agree to ~1e-16.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -303,7 +306,9 @@ __device__ __forceinline__ void wave_argmax(double &v, int &id) {
 constexpr int RSEL_THREADS = 1024;
 constexpr int RSEL_LOADS = 8;
 
-template <int EJ>
+// MODE 0: sigmoid scores, selection by s + bias.  MODE 1: softmax gate, selection by the logits and weights
+// lambda * exp(z_j - z_max) / sum over the selected (the max-subtracted softmax renormalised over them).
+template <int EJ, int MODE>
 __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const double *__restrict__ part, int nsplit,
                                                                      int T, int E, int k,
                                                                      const float *__restrict__ bias, float lambda,
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
     const int tid = threadIdx.x, lane = tid & 63;
     const int ept = (E + 255) / 256;  // experts per thread column
     const rsrc_t psrc = make_rsrc(part, (uint32_t)((long)nsplit * T * E * 8));
-    const float bz = tid < E ? bias[tid] : 0.f;  // requested now, used after the sums (E <= RSEL_THREADS)
+    const float bz = (MODE == 0 && tid < E) ? bias[tid] : 0.f;  // requested now, used after the sums (E <= RSEL_THREADS)
     for (int j = 0; j < ept; j++) {
         const int e = (tid & 255) + 256 * j;
         const int g = tid >> 8;
@@ -340,9 +345,14 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
     if (tid < E) {
         const int e = tid;
         const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
-        const double sv = 1.0 / (1.0 + exp(-z));
-        zs[e] = sv;
-        zs[E + e] = sv + (double)bz;
+        if (MODE == 0) {
+            const double sv = 1.0 / (1.0 + exp(-z));
+            zs[e] = sv;
+            zs[E + e] = sv + (double)bz;
+        } else {
+            zs[e] = z;
+            zs[E + e] = z;
+        }
     }
     __syncthreads();
     if (tid >= 64) return;
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
                 ci[b2 - 1] = ti;
             }
     int head = 0;  // next unchosen candidate of this lane
-    double sum_s = 0.0, prev_v = 0.0;
+    double sum_s = 0.0, prev_v = 0.0, top_z = 0.0;
     double my_s = 0.0;  // lane r < k keeps the score of choice r
     int my_id = 0;
     const int rounds = (k < E) ? k + 1 : k;
@@ -399,9 +409,12 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
             double, make_int2(__builtin_amdgcn_readlane(sb.x, wl), __builtin_amdgcn_readlane(sb.y, wl)));
         if (r < k) {
             if (lane == wl) head++;
-            sum_s += bs;
+            // the weight's numerator: the sigmoid score, or exp(z - z_max) of the softmax gate
+            if (MODE == 1 && r == 0) top_z = bs;
+            const double u = MODE == 0 ? bs : exp(bs - top_z);
+            sum_s += u;
             if (lane == r) {
-                my_s = bs;
+                my_s = u;
                 my_id = bid;
             }
             prev_v = bv;
@@ -414,6 +427,91 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
         idx[(long)t * k + lane] = my_id;
         w[(long)t * k + lane] = (float)((double)lambda * my_s / sum_s);
     }
+}
+
+// ---------------------------------------------------------------------------- router variants
+
+// Logit of (t, e) from the split partials, in the order the select kernel adds them: splits g, g + 4, g + 8, ...
+// summed for each g in 0..3, then the four sums left to right.
+__device__ __forceinline__ double logit_of(const double *part, int nsplit, int T, int E, int t, int e) {
+    double zg[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+        for (int sp = g; sp < nsplit; sp += 4) zg[g] += part[((long)sp * T + t) * E + e];
+    return ((zg[0] + zg[1]) + zg[2]) + zg[3];
+}
+
+// Expert choice, step 1: pT[e][t] = softmax over the experts of token t (E <= 32), the maximum subtracted and the
+// sum taken over e ascending.  One thread per token.
+__global__ __launch_bounds__(256) void ec_softmax_kernel(const double *__restrict__ part, int nsplit, int T, int E,
+                                                         double *__restrict__ pT) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    double z[32];
+    double m = -INFINITY;
+    for (int e = 0; e < E; e++) {
+        z[e] = logit_of(part, nsplit, T, E, t, e);
+        m = fmax(m, z[e]);
+    }
+    double sum = 0.0;
+    for (int e = 0; e < E; e++) sum += exp(z[e] - m);
+    for (int e = 0; e < E; e++) pT[(long)e * T + t] = exp(z[e] - m) / sum;
+}
+
+// Expert choice, step 2: one workgroup per expert takes the C tokens of largest p (equal p by lower token) by an
+// exact radix selection over the bit patterns of the fp64 probabilities (non-negative: they order as the values).
+// Writes column e of idx [T][E] (e or -1) and w (lambda p or 0), and gap[e] (p of the C-th minus the (C+1)-th).
+constexpr int EC_THREADS = 1024;
+
+__global__ __launch_bounds__(EC_THREADS) void ec_select_kernel(const double *__restrict__ pT, int T, int E, int C,
+                                                               float lambda, int32_t *__restrict__ idx,
+                                                               float *__restrict__ w, double *__restrict__ gap) {
+    __shared__ int hist[256];
+    __shared__ int scan[EC_THREADS / 64 + 1];
+    __shared__ TopkState st;
+    __shared__ unsigned long long below;  // largest key not chosen
+    const int e = blockIdx.x;
+    const double *p = pT + (long)e * T;
+    auto key = [&](int i) { return (uint64_t)__double_as_longlong(p[i]); };
+    if (threadIdx.x == 0) below = 0ull;
+    const TopkState s = radix_kth_largest<EC_THREADS, 64>(key, T, C, hist, &st);
+    visit_topk<EC_THREADS>(
+        key, T, s, scan,
+        [&](int i, int) {
+            idx[(long)i * E + e] = e;
+            w[(long)i * E + e] = (float)((double)lambda * p[i]);
+        },
+        [&](int i) {
+            idx[(long)i * E + e] = -1;
+            w[(long)i * E + e] = 0.f;
+            atomicMax(&below, (unsigned long long)key(i));
+        });
+    __syncthreads();
+    if (threadIdx.x == 0 && gap)
+        gap[e] = C >= T ? INFINITY : (s.eq > s.need ? 0.0 : __longlong_as_double((long long)s.v) -
+                                                              __longlong_as_double((long long)below));
+}
+
+// Capacity, step 1: the assignments in (choice, token) order, idxT[j * T + t] = idx[t * k + j].
+__global__ __launch_bounds__(256) void cap_transpose_kernel(const int32_t *__restrict__ idx, int T, int k,
+                                                            int32_t *__restrict__ idxT) {
+    const long a = (long)blockIdx.x * 256 + threadIdx.x;
+    if (a >= (long)T * k) return;
+    const int t = (int)(a / k), j = (int)(a % k);
+    idxT[(long)j * T + t] = idx[a];
+}
+
+// Capacity, step 3: after the stable counting sort of idxT, an assignment's place within its expert is its rank in
+// (choice, token) order; places C and beyond become empty slots.
+__global__ __launch_bounds__(256) void cap_drop_kernel(int32_t *__restrict__ idx, int T, int k, int C,
+                                                       const int32_t *__restrict__ invT,
+                                                       const int32_t *__restrict__ offT) {
+    const long a = (long)blockIdx.x * 256 + threadIdx.x;
+    if (a >= (long)T * k) return;
+    const int e = idx[a];
+    if (e < 0) return;
+    const int t = (int)(a / k), j = (int)(a % k);
+    if (invT[(long)j * T + t] - offT[e] >= C) idx[a] = -1;
 }
 
 static bool skinny_fits(int E) { return E >= 4 && E <= 256 && (E & (E - 1)) == 0; }
@@ -463,14 +561,29 @@ const char *router_unsupported(int T, int d, int E, int act, bool inv) {
     return nullptr;
 }
 
-size_t router_workspace_bytes(int T, int d, int E, bool inv) {
+static size_t r_al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace after the partials: the capacity step's transposed assignments, its counting sort (counts, offsets,
+// perm, inv, uniq, n_uniq) and that sort's own workspace; or expert choice's probabilities pT [E][T].
+static size_t variant_bytes(int T, int E, int k, int router, bool capacity) {
+    const size_t A = (size_t)T * k;
+    if (router == 2) return r_al256((size_t)E * T * sizeof(double));
+    if (!capacity) return 0;
+    return r_al256(A * 4) * 3 + r_al256((size_t)E * 4) * 2 + r_al256((size_t)(E + 1) * 4) + r_al256(4) +
+           r_al256(permute_workspace_bytes((int)A, E));
+}
+
+size_t router_workspace_bytes(int T, int d, int E, bool inv, int k, int router, bool capacity) {
     if (T <= 0) return 0;
-    return (size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double);
+    return r_al256((size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double)) +
+           variant_bytes(T, E, k, router, capacity);
 }
 
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
-                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, hipStream_t stream) {
+                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
+                         hipStream_t stream) {
     double *part = (double *)ws;
+    char *vws = (char *)ws + r_al256((size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double));
     int nsplit;
     if (use_skinny(T, E, inv)) {
         const int rows = skinny_rows(d, E);
@@ -493,16 +606,52 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (router == 2) {
+        // expert choice: per-token softmax, then per expert the C tokens of largest probability
+        double *pT = (double *)vws;
+        hipLaunchKernelGGL(ec_softmax_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, part, nsplit, T, E, pT);
+        hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(EC_THREADS), 0, stream, pT, T, E, C, lambda, idx, w, gap);
+        return hipGetLastError();
+    }
     const size_t lds = 4 * E * sizeof(double);
-    if (E <= 64)
-        hipLaunchKernelGGL(router_select_kernel<1>, dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T, E, k,
-                           bias, lambda, idx, w, gap);
-    else if (E <= 256)
-        hipLaunchKernelGGL(router_select_kernel<4>, dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T, E, k,
-                           bias, lambda, idx, w, gap);
+    auto select = [&](auto mode) {
+        constexpr int M = decltype(mode)::value;
+        if (E <= 64)
+            hipLaunchKernelGGL((router_select_kernel<1, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
+                               E, k, bias, lambda, idx, w, gap);
+        else if (E <= 256)
+            hipLaunchKernelGGL((router_select_kernel<4, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
+                               E, k, bias, lambda, idx, w, gap);
+        else
+            hipLaunchKernelGGL((router_select_kernel<16, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit,
+                               T, E, k, bias, lambda, idx, w, gap);
+    };
+    if (router == 1)
+        select(std::integral_constant<int, 1>{});
     else
-        hipLaunchKernelGGL(router_select_kernel<16>, dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T, E,
-                           k, bias, lambda, idx, w, gap);
+        select(std::integral_constant<int, 0>{});
+    err = hipGetLastError();
+    if (err != hipSuccess || C <= 0) return err;
+    // capacity: rank every assignment within its expert in (choice, token) order by the stable counting sort of
+    // the transposed assignments, then empty the slots ranked C and beyond
+    const long A = (long)T * k;
+    char *p = vws;
+    auto take = [&](size_t b) {
+        char *q = p;
+        p += r_al256(b);
+        return q;
+    };
+    int32_t *idxT = (int32_t *)take(A * 4), *permT = (int32_t *)take(A * 4), *invT = (int32_t *)take(A * 4);
+    int32_t *cntT = (int32_t *)take((size_t)E * 4), *uniqT = (int32_t *)take((size_t)E * 4);
+    int32_t *offT = (int32_t *)take((size_t)(E + 1) * 4), *nuT = (int32_t *)take(4);
+    void *pws = take(permute_workspace_bytes((int)A, E));
+    const unsigned g = (unsigned)((A + 255) / 256);
+    hipLaunchKernelGGL(cap_transpose_kernel, dim3(g), dim3(256), 0, stream, idx, T, k, idxT);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = launch_permute(idxT, (int)A, E, cntT, offT, permT, invT, uniqT, nuT, pws, stream);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(cap_drop_kernel, dim3(g), dim3(256), 0, stream, idx, T, k, C, invT, offT);
     return hipGetLastError();
 }
 

@@ -91,16 +91,18 @@ class DeviceLayerWeights:
 class MoeRun:
     """Output and workspace buffers for one (spec, T) and the four calls that fill them."""
 
-    def __init__(self, spec: synth.LayerSpec, T: int, device="cuda", path: int = B.MOE_PATH_AUTO, flags: int = 0):
+    def __init__(self, spec: synth.LayerSpec, T: int, device="cuda", path: int = B.MOE_PATH_AUTO, flags: int = 0,
+                 router: int = B.MOE_ROUTER_SIGMOID_BIAS, capacity_factor: float = 0.0):
         self.spec, self.T = spec, T
         k, E, d = spec.k, spec.E, spec.d
         A = T * k
         self.shape = B.make_shape(T, d, E, k, spec.I, spec.I_shared, spec.routed_scale, spec.act, spec.wbits, path,
-                                  flags)
+                                  flags, router, capacity_factor)
         i32 = dict(dtype=torch.int32, device=device)
         self.idx = torch.empty((T, k), **i32)
         self.w = torch.empty((T, k), dtype=torch.float32, device=device)
-        self.gap = torch.empty(T, dtype=torch.float64, device=device)
+        # the selection margin per token, or per expert under expert choice
+        self.gap = torch.empty(E if router == B.MOE_ROUTER_EXPERT_CHOICE else T, dtype=torch.float64, device=device)
         self.counts = torch.empty(E, **i32)
         self.offsets = torch.empty(E + 1, **i32)
         self.perm = torch.empty(A, **i32)

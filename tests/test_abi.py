@@ -217,3 +217,25 @@ def test_flags_checked():
     big = dict(T=4096, d=7168, E=256, k=8, I=2048, I_shared=2048, wbits=4, act_dtype=B.MOE_ACT_BF16)
     assert B.moe_workspace_size(shape(flags=B.MOE_FLAG_BATCH_INVARIANT, **big)) > 0
     assert B.moe_workspace_size(shape(flags=B.MOE_FLAG_BATCH_INVARIANT)) > 0
+
+
+def test_router_fields_checked():
+    """Unknown routers and capacity factors out of range are refused; expert choice needs k = E and a factor;
+    the softmax and expert-choice routers take no bias (NULL accepted), the sigmoid router needs it."""
+    for kw, msg in ((dict(router=3), "router"), (dict(capacity_factor=-1.0), "capacity"),
+                    (dict(capacity_factor=float("nan")), "capacity"),
+                    (dict(router=B.MOE_ROUTER_EXPERT_CHOICE, capacity_factor=2.0), "expert choice"),
+                    (dict(router=B.MOE_ROUTER_EXPERT_CHOICE, k=8, capacity_factor=0.0), "expert choice")):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_route(shape(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, HUGE_WS, stream=0)
+        assert ei.value.code == B.MOE_EINVAL and msg in str(ei.value), str(ei.value)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(shape(), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, HUGE_WS, stream=0)
+    assert "bias" in str(ei.value)
+    # T = 0 returns before anything runs: no bias needed for the softmax and expert-choice routers
+    B.moe_route(shape(T=0, router=B.MOE_ROUTER_SOFTMAX), None, FAKE, None, None, None, None, FAKE, HUGE_WS, stream=0)
+    B.moe_route(shape(T=0, k=8, router=B.MOE_ROUTER_EXPERT_CHOICE, capacity_factor=2.0), None, FAKE, None, None, None,
+                None, FAKE, HUGE_WS, stream=0)
+    # the capacity step needs workspace beyond the partial sums
+    base = B.moe_workspace_size(shape(T=5000))
+    assert B.moe_workspace_size(shape(T=5000, capacity_factor=1.2)) >= base

@@ -683,3 +683,79 @@ def test_batch_invariant_mode_matrix_core(dev):
         got, ref = _results(run, t), _results(run1, 0)
         for key in ref:
             np.testing.assert_array_equal(got[key], ref[key], err_msg=f"token {t}: {key}")
+
+
+# ---------------------------------------------------------------------------
+# router variants: softmax top-k (soft routing = k = E), capacity factor, expert choice
+# ---------------------------------------------------------------------------
+
+SM, EC, SG = B.MOE_ROUTER_SOFTMAX, B.MOE_ROUTER_EXPERT_CHOICE, B.MOE_ROUTER_SIGMOID_BIAS
+VARIANTS = {
+    # (layer, T, router, capacity factor, forward path)
+    "softmax_top2_decode": (dict(d=512, E=8, k=2, I=256, wbits=8, act=synth.ACT_F32, bias="uniform0.01"), 12, SM, 0.0,
+                            B.MOE_PATH_AUTO),
+    "softmax_top4_matrix_core": (dict(d=512, E=16, k=4, I=384, I_shared=192, routed_scale=2.5), 70, SM, 0.0,
+                                 B.MOE_PATH_GEMM),
+    "soft_routing_k_eq_e": (dict(d=256, E=8, k=8, I=64, I_shared=64), 9, SM, 0.0, B.MOE_PATH_AUTO),
+    "softmax_top2_capacity_1.2": (dict(d=256, E=8, k=2, I=64, bias="zipf"), 200, SM, 1.2, B.MOE_PATH_AUTO),
+    "sigmoid_capacity_multiblock": (dict(d=256, E=8, k=2, I=64, I_shared=64), 5000, SG, 1.0, B.MOE_PATH_AUTO),
+    "expert_choice": (dict(d=256, E=8, k=8, I=64, I_shared=64, routed_scale=1.0), 100, EC, 2.0, B.MOE_PATH_AUTO),
+    "expert_choice_decode": (dict(d=512, E=8, k=8, I=128, wbits=8, act=synth.ACT_F32), 6, EC, 3.0, B.MOE_PATH_AUTO),
+    "expert_choice_e32_t3000": (dict(d=128, E=32, k=32, I=32), 3000, EC, 1.0, B.MOE_PATH_AUTO),
+}
+
+
+def _variant_spec(kw):
+    kw = dict(kw)
+    skew = kw.get("bias") == "zipf"
+    if skew:
+        kw["bias"] = "normal0.05"
+    return spec_of(**kw), skew
+
+
+@pytest.mark.parametrize("case", list(VARIANTS))
+def test_router_variant_parity(orc, dev, case):
+    """A router variant through the whole layer against the oracle: indices (empty slots included) and the
+    permutation bit-exact, weights within 1e-6, margins within 1e-12 with the same near ties, the layer within the
+    bound."""
+    kw, T, router, cf, path = VARIANTS[case]
+    spec, skew = _variant_spec(kw)
+    say(f"[variant] {case} T={T} E={spec.E} k={spec.k} router={router} cf={cf}")
+
+    def tweak(inp):
+        if skew:  # a few popular experts, so that capacities overflow
+            inp.W_r[:, :2] *= np.float32(4.0)
+    H = HostLayer(spec, T, dev, tweak=tweak)
+    run = L.MoeRun(spec, T, dev, path, router=router, capacity_factor=cf)
+    for buf in (run.y_perm, run.y):
+        buf.fill_(float("nan"))
+    run.run(H.x, H.W)
+    torch.cuda.synchronize()
+    idx, w, gap = orc.route_variant(spec, H.inp.x, H.inp.W_r, H.inp.bias, router, cf)
+    np.testing.assert_array_equal(run.idx.cpu().numpy(), idx, err_msg="topk_idx")
+    keep = idx >= 0
+    np.testing.assert_allclose(run.w.cpu().numpy()[keep], w[keep], rtol=1e-6, atol=0, err_msg="topk_w")
+    if router == EC:
+        assert np.all(run.w.cpu().numpy()[~keep] == 0)
+    g = run.gap.cpu().numpy()[:gap.size]
+    fin = np.isfinite(gap)
+    np.testing.assert_allclose(g[fin], gap[fin], rtol=0, atol=1e-12, err_msg="gap")
+    assert np.all(np.isinf(g[~fin]))
+    assert list(np.flatnonzero(g < NEAR_TIE)) == list(np.flatnonzero(gap < NEAR_TIE))
+    dropped = int((~keep).sum())
+    p, Yperm, S, y = orc.moe_layer_routed(spec, H.inp.x, idx, w, H.inp.routed, H.inp.shared)
+    for nm in ("counts", "offsets", "perm", "inv", "uniq"):
+        got = getattr(run, nm).cpu().numpy()
+        ref = getattr(p, nm)
+        if nm == "perm":
+            got, ref = got[:p.counts.sum()], ref[:p.counts.sum()]
+        np.testing.assert_array_equal(got, ref, err_msg=nm)
+    assert int(run.n_uniq.item()) == p.n_uniq >= 0
+    rows = p.counts.sum()
+    assert_layer_close(run.y_perm.cpu().numpy()[:rows], Yperm[:rows], "y_perm")
+    if spec.I_shared:
+        assert_layer_close(run.y_shared.cpu().numpy(), S, "y_shared")
+    rel, mx = assert_layer_close(run.y.cpu().numpy(), y, "y")
+    say(f"   ok: {dropped} empty slots of {idx.size}, n_uniq {p.n_uniq}, rel-L2 {rel:.2e} max-abs/RMS {mx:.2e}")
+    if cf > 0 and router != EC:
+        assert dropped > 0, "the capacity dropped nothing: the case no longer exercises it"
