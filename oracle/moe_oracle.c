@@ -465,3 +465,65 @@ void oracle_moe_tokens(int n, const int32_t *tokens, int d, int E, int k, int I,
     free(z);
     free(Y);
 }
+
+/*
+ * Sparse-attention indexer and its top-K selection.  The GLM-5.2 page has the engine run the model's lightning
+ * indexer and keep, per layer, the top 2048 causal keys for attention (its section 三.3); a light indexer first
+ * scores the history's keys, then the top-k entries go to the real attention (its section 四.4, on DeepSeek
+ * Sparse Attention).  The pages give no formula; the reading taken is the DSA indexer's published form with
+ * integer operands so that both implementations compute the same bits:
+ *   dot[t][h][s] = sum_i q[t][h][i] * k[s][i]          (int8 operands, exact integer sum)
+ *   I[t][s]      = kscale[s] * sum_{h=0}^{H-1} w[t][h] * max(0, dot[t][h][s])
+ * the head sum a chain of fused multiply-adds acc = fma(w, relu, acc) in head order from 0, then one product by
+ * kscale[s], all in fp64.  Query t sits at position pos0 + t and sees the keys s <= pos0 + t.  Its output is the
+ * set of the K largest scores among them (equal scores by lower position), listed by ascending position, padded
+ * with -1 when fewer than K keys are visible; gap[t] = score of the K-th minus score of the (K+1)-th of that order
+ * (INFINITY when all visible keys are taken).  scores (optional, [T][S]) returns I (0 where s is not visible).
+ */
+static int ix_cmp(const void *a, const void *b) {  /* larger score first, equal scores by lower position */
+    const oracle_kv *x = (const oracle_kv *)a, *y = (const oracle_kv *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+static int int_cmp(const void *a, const void *b) {
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+void oracle_index_topk(int T, int S, int H, int D, int K, int pos0, const int8_t *q, const float *w,
+                       const int8_t *k, const float *kscale, int32_t *top, double *gap, double *scores) {
+#pragma omp parallel
+    {
+        oracle_kv *kv = (oracle_kv *)malloc(sizeof(oracle_kv) * (size_t)(S > 0 ? S : 1));
+#pragma omp for schedule(dynamic)
+        for (int t = 0; t < T; t++) {
+            int n = pos0 + t + 1;
+            if (n > S) n = S;
+            if (n < 0) n = 0;
+            for (int s = 0; s < n; s++) {
+                double acc = 0.0;
+                for (int h = 0; h < H; h++) {
+                    long dot = 0;
+                    const int8_t *qr = q + ((long)t * H + h) * D, *kr = k + (long)s * D;
+                    for (int i = 0; i < D; i++) dot += (long)qr[i] * (long)kr[i];
+                    acc = fma((double)w[(long)t * H + h], (double)(dot > 0 ? dot : 0), acc);
+                }
+                kv[s].v = (double)kscale[s] * acc;
+                kv[s].id = s;
+                if (scores) scores[(long)t * S + s] = kv[s].v;
+            }
+            if (scores)
+                for (int s = n; s < S; s++) scores[(long)t * S + s] = 0.0;
+            qsort(kv, (size_t)n, sizeof(oracle_kv), ix_cmp);
+            const int m = n < K ? n : K;
+            int32_t *out = top + (long)t * K;
+            for (int j = 0; j < m; j++) out[j] = kv[j].id;
+            qsort(out, (size_t)m, sizeof(int32_t), int_cmp);
+            for (int j = m; j < K; j++) out[j] = -1;
+            if (gap) gap[t] = n > K ? kv[K - 1].v - kv[K].v : INFINITY;
+        }
+        free(kv);
+    }
+}

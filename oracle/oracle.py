@@ -36,6 +36,7 @@ def lib():
         _lib.oracle_router_select_softmax.argtypes = [C.c_int, C.c_int, C.c_int, P, C.c_double, P, P, P]
         _lib.oracle_capacity.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P]
         _lib.oracle_expert_choice.argtypes = [C.c_int, C.c_int, C.c_int, P, C.c_double, P, P, P]
+        _lib.oracle_index_topk.argtypes = [C.c_int] * 6 + [P] * 7
     return _lib
 
 
@@ -303,3 +304,31 @@ def moe_layer_routed(spec, x, idx, w, routed, shared, k=None):
     S = expert_apply(xd, spec.d, spec.I_shared, spec.wbits, shared, 0) if spec.I_shared else None
     y = combine(Yperm, S, p.inv, w)
     return p, Yperm, S, y
+
+
+# ----------------------------------------------------------------------------
+# sparse-attention indexer: scores and top-K causal keys
+# ----------------------------------------------------------------------------
+
+
+@dataclass
+class IndexTopk:
+    top: np.ndarray     # [T][K] int32, ascending positions, -1 padded
+    gap: np.ndarray     # [T] fp64
+    scores: Optional[np.ndarray]  # [T][S] fp64 (0 where not visible)
+
+
+def index_topk(q: np.ndarray, w: np.ndarray, k: np.ndarray, kscale: np.ndarray, K: int, pos0: int,
+               want_scores: bool = False) -> IndexTopk:
+    """q [T][H][D] int8, w [T][H] fp32, k [S][D] int8, kscale [S] fp32; query t sees keys s <= pos0 + t."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.int8)
+    kscale = np.ascontiguousarray(kscale, dtype=np.float32)
+    T, H, D = q.shape
+    S = k.shape[0]
+    top = np.empty((T, K), np.int32)
+    gap = np.empty(T, np.float64)
+    sc = np.empty((T, S), np.float64) if want_scores else None
+    lib().oracle_index_topk(T, S, H, D, K, pos0, _p(q), _p(w), _p(k), _p(kscale), _p(top), _p(gap), _p(sc))
+    return IndexTopk(top, gap, sc)

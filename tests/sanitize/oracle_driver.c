@@ -102,6 +102,38 @@ static int run(int T, int d, int E, int k, int I, int Is, int wbits, int act) {
     return bad;
 }
 
+void oracle_router_select_softmax(int T, int E, int k, const double *z, double lambda, int32_t *idx, float *w,
+                                  double *gap);
+void oracle_capacity(int T, int k, int E, int C, int32_t *idx);
+void oracle_expert_choice(int T, int E, int C, const double *z, double lambda, int32_t *idx, float *w,
+                          double *gap_e);
+void oracle_index_topk(int T, int S, int H, int D, int K, int pos0, const int8_t *q, const float *w,
+                       const int8_t *k, const float *kscale, int32_t *top, double *gap, double *scores);
+
+static void run_variants(void) {
+    const int T = 40, E = 8, k = 3;
+    double *z = alloc(sizeof(double) * T * E), *gap = alloc(sizeof(double) * (T > E ? T : E));
+    int32_t *idx = alloc(4 * T * E);
+    float *w = alloc(4 * T * E);
+    for (int i = 0; i < T * E; i++) z[i] = 3.0 * frnd();
+    oracle_router_select_softmax(T, E, k, z, 2.5, idx, w, gap);
+    oracle_capacity(T, k, E, 12, idx);
+    oracle_expert_choice(T, E, 10, z, 1.0, idx, w, gap);
+    free(z), free(gap), free(idx), free(w);
+    const int S = 300, H = 8, D = 64, K = 32;
+    int8_t *q = alloc((size_t)4 * H * D), *kk = alloc((size_t)S * D);
+    float *wh = alloc(4 * 4 * H), *ks = alloc(4 * S);
+    for (int i = 0; i < 4 * H * D; i++) q[i] = (int8_t)(rnd() % 255 - 127);
+    for (int i = 0; i < S * D; i++) kk[i] = (int8_t)(rnd() % 255 - 127);
+    for (int i = 0; i < 4 * H; i++) wh[i] = frnd();
+    for (int i = 0; i < S; i++) ks[i] = 1.0f + 0.5f * frnd();
+    int32_t *top = alloc(4 * 4 * K);
+    double *g2 = alloc(8 * 4), *sc = alloc(8 * 4 * S);
+    oracle_index_topk(4, S, H, D, K, 10, q, wh, kk, ks, top, g2, sc);
+    oracle_index_topk(4, S, H, D, K, S - 4, q, wh, kk, ks, top, g2, NULL);
+    free(q), free(kk), free(wh), free(ks), free(top), free(g2), free(sc);
+}
+
 int main(void) {
     int bad = 0;
     oracle_set_threads(2);
@@ -109,6 +141,7 @@ int main(void) {
     bad |= run(4, 64, 8, 2, 64, 0, 4, 1);
     bad |= run(3, 32, 4, 4, 32, 64, 4, 0);  /* k == E: gap is +inf */
     bad |= run(1, 128, 16, 1, 32, 32, 8, 1);
+    run_variants();
     printf(bad ? "batch union and per-token loop differ\n" : "oracle driver ok\n");
     return bad;
 }

@@ -436,3 +436,75 @@ def test_permute_and_combine_skip_empty_slots(orc):
                 ref[t] += np.float64(w[t, j]) * orc.expert_apply(xd[t:t + 1], spec.d, spec.I, 8, inp.routed, e)[0]
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
     del rng
+
+
+# ----------------------------------------------------------------------------
+# sparse-attention indexer: scores and top-K causal keys
+# ----------------------------------------------------------------------------
+
+
+def _index_inputs(T, S, H, D, seed, dup=False):
+    rng = np.random.default_rng(seed)
+    q = np.clip(np.rint(rng.standard_normal((T, H, D)) * 40), -127, 127).astype(np.int8)
+    k = np.clip(np.rint(rng.standard_normal((S, D)) * 40), -127, 127).astype(np.int8)
+    if dup:  # repeated keys: exactly equal scores, decided by position
+        k[S // 2:] = k[:S - S // 2]
+    w = (rng.standard_normal((T, H)) / np.sqrt(H)).astype(np.float32)
+    ks = rng.uniform(0.5, 1.5, S).astype(np.float32) if not dup else np.full(S, 0.75, np.float32)
+    return q, w, k, ks
+
+
+@pytest.mark.parametrize("T,S,H,D,K,pos0", [(4, 300, 8, 64, 32, 296), (6, 200, 16, 128, 64, 20), (3, 50, 4, 64, 8, 0)])
+def test_index_scores_match_numpy(orc, T, S, H, D, K, pos0):
+    """The score, evaluated by numpy in a different order (int64 matrix products per head, a float64 sum over
+    heads): within 1e-12 of the largest term; zero where a key is not visible to the query."""
+    q, w, k, ks = _index_inputs(T, S, H, D, T + S)
+    r = orc.index_topk(q, w, k, ks, K, pos0, want_scores=True)
+    dots = np.einsum("thi,si->ths", q.astype(np.int64), k.astype(np.int64))
+    terms = w.astype(np.float64)[:, :, None] * np.maximum(dots, 0)
+    ref = ks.astype(np.float64)[None, :] * terms.sum(1)
+    scale = ks.astype(np.float64)[None, :] * np.abs(terms).sum(1)
+    for t in range(T):
+        n = min(S, pos0 + t + 1)
+        assert np.all(np.abs(r.scores[t, :n] - ref[t, :n]) <= 1e-12 * scale[t, :n] + 1e-300)
+        assert np.all(r.scores[t, n:] == 0)
+
+
+@pytest.mark.parametrize("dup,pos0", [(False, 20), (False, 392), (True, 392)])
+def test_index_topk_equals_brute_force(orc, dup, pos0):
+    """Top-K of the visible keys by (score desc, position asc), listed by ascending position: equals a lexsort of
+    the scores; no position beyond the query's own; queries that see K keys or fewer take all of them."""
+    T, S, H, D, K = 8, 400, 8, 64, 40
+    q, w, k, ks = _index_inputs(T, S, H, D, 77, dup)
+    r = orc.index_topk(q, w, k, ks, K, pos0, want_scores=True)
+    for t in range(T):
+        n = min(S, pos0 + t + 1)
+        sc = r.scores[t, :n]
+        order = np.lexsort((np.arange(n), -sc))  # score desc, then position asc
+        want = np.sort(order[:K])
+        m = min(n, K)
+        np.testing.assert_array_equal(r.top[t, :m], want)
+        assert np.all(r.top[t, m:] == -1) and np.all(r.top[t, :m] <= pos0 + t)
+        if n > K:
+            assert r.gap[t] == sc[order[K - 1]] - sc[order[K]]
+        else:
+            assert np.isinf(r.gap[t])
+    if dup:
+        assert np.any(r.gap == 0), "the duplicated keys no longer give equal scores"
+
+
+def test_index_topk_invariances(orc):
+    """Doubling every key scale doubles the scores exactly and keeps the selection; a single head with weight 1
+    selects by kscale * relu(q_h . k)."""
+    T, S, H, D, K = 3, 500, 4, 64, 50
+    q, w, k, ks = _index_inputs(T, S, H, D, 5)
+    a = orc.index_topk(q, w, k, ks, K, S - T, want_scores=True)
+    b = orc.index_topk(q, w, k, ks * np.float32(2), K, S - T, want_scores=True)
+    np.testing.assert_array_equal(a.top, b.top)
+    np.testing.assert_array_equal(b.scores, 2 * a.scores)
+    w1 = np.zeros_like(w)
+    w1[:, 2] = 1
+    c = orc.index_topk(q, w1, k, ks, K, S - T, want_scores=True)
+    dots = np.maximum(q[:, 2, :].astype(np.int64) @ k.astype(np.int64).T, 0)
+    visible = np.arange(S)[None, :] <= (S - T + np.arange(T))[:, None]
+    np.testing.assert_array_equal(c.scores, np.where(visible, ks.astype(np.float64)[None, :] * dots, 0.0))
