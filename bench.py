@@ -58,6 +58,9 @@ def parse(argv=None):
                     help="router variant (expert choice runs the layer with one slot per expert, k = E)")
     ap.add_argument("--capacity-factor", type=float, default=0.0)
     ap.add_argument("--only", action="store_true", help="the named workload alone (no additional workloads)")
+    ap.add_argument("--index", default=None, metavar="T,S",
+                    help="time the sparse-attention indexer's top-2048 (dsa_index_topk) for T queries at the end of "
+                         "an S-key cache (64 heads of 128) instead of the MoE layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of each oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -319,12 +322,71 @@ def measure(spec, T, args, dev):
     return res
 
 
+PEAK_MFMA_INT8_TOPS = 5033.2  # dense int8 MFMA, 256 CU x 8192 op/clk x 2.4 GHz
+
+
+def measure_index(args, dev):
+    """The indexer's scores and top-2048 for T queries at the end of an S-key cache: one call = both kernels."""
+    import torch
+    from routed_expert_ffn_sigmoid_amd import binding as B
+    from routed_expert_ffn_sigmoid_amd import synth
+    T, S = (int(v) for v in args.index.split(","))
+    H, D, K = 64, 128, 2048
+    pos0 = S - T
+    pool = max(1, min(8, (1 << 30) // (S * D)))  # key caches rotated so the 256 MB Infinity Cache holds none
+    inps = [synth.gen_index(T, S, H, D, seed=b) for b in range(pool)]
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    bufs = [(up(i.q), up(i.w), up(i.k), up(i.kscale)) for i in inps]
+    shape = B.dsa_index_shape(T, S, H, D, K, pos0)
+    ws = torch.empty(B.dsa_index_workspace_size(shape), dtype=torch.uint8, device=dev)
+    top = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gap = torch.empty(T, dtype=torch.float64, device=dev)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for q, w, k, ks in bufs:
+            B.dsa_index_topk(shape, q, w, k, ks, top, gap, ws)
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup // pool)):
+        g.replay()
+    reps = max(1, args.steps // pool)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * pool)
+    visible = sum(min(S, pos0 + t + 1) for t in range(T))
+    ops = 2.0 * visible * H * D
+    nbytes = S * D + S * 4 + T * H * D + T * H * 4 + T * K * 4
+    if ops / nbytes < PEAK_MFMA_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ops / us / 1e6, 1), "peak": PEAK_MFMA_INT8_TOPS, "unit": "TOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof.update({"kernel": "dsa_index_topk (int8 scores, then the top 2048 by radix selection)",
+                 "algorithmic_bytes_per_call": nbytes, "algorithmic_int8_ops_per_call": ops, "avg_call_us": round(us, 2)})
+    return {"metric": "indexer queries/s", "value": round(T / us * 1e6, 2), "unit": "queries/s", "n_gpus": 1,
+            "steps": reps * pool, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8-qk/f64-score", "data": "synthetic (seeded)",
+            "config": {"workload": f"indexer top-{K}: T={T} queries at the end of S={S} keys, H={H}, D={D}",
+                       "key_caches_rotated": pool}, "roofline": roof}
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.index:
+        import torch
+        from routed_expert_ffn_sigmoid_amd import binding as B
+        B.lib()
+        print(json.dumps(measure_index(args, torch.device("cuda:0"))), flush=True)
+        return
     import torch
     from routed_expert_ffn_sigmoid_amd import binding as B
     from routed_expert_ffn_sigmoid_amd import synth

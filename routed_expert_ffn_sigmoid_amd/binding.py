@@ -42,7 +42,7 @@ MOE_PATH_GEMM = 2
 
 # names declared in include/moe.h
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_static", "moe_combine",
-           "moe_last_error", "moe_abi_version")
+           "moe_last_error", "moe_abi_version", "dsa_index_workspace_size", "dsa_index_topk")
 
 MOE_STATIC_SCRATCH_BYTES = 64 << 20  # moe_forward_static's scratch
 
@@ -58,6 +58,10 @@ class moe_shape(C.Structure):
                 ("I_shared", C.c_int32), ("routed_scale", C.c_float), ("act_dtype", C.c_int32),
                 ("wbits", C.c_int32), ("path", C.c_int32), ("flags", C.c_int32), ("router", C.c_int32),
                 ("capacity_factor", C.c_float)]
+
+
+class dsa_index_shape(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("T", "S", "H", "D", "K", "pos0")]
 
 
 class moe_qffn(C.Structure):
@@ -88,6 +92,11 @@ def lib():
         for f in ("moe_route", "moe_permute", "moe_forward", "moe_forward_static", "moe_combine", "moe_abi_version"):
             getattr(L, f).restype = C.c_int
         L.moe_last_error.restype = C.c_char_p
+        X = C.POINTER(dsa_index_shape)
+        L.dsa_index_workspace_size.argtypes = [X]
+        L.dsa_index_workspace_size.restype = C.c_size_t
+        L.dsa_index_topk.argtypes = [X, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.dsa_index_topk.restype = C.c_int
         _lib = L
     return _lib
 
@@ -167,3 +176,13 @@ def moe_forward_static(shape, x, routed: moe_qffn, shared: Optional[moe_qffn], o
 def moe_combine(shape, y_perm, y_shared, inv, topk_w, y, stream=None) -> None:
     _check(lib().moe_combine(C.byref(shape), _ptr(y_perm), _ptr(y_shared), _ptr(inv), _ptr(topk_w), _ptr(y),
                              _stream(stream)))
+
+
+def dsa_index_workspace_size(shape: dsa_index_shape) -> int:
+    return int(lib().dsa_index_workspace_size(C.byref(shape)))
+
+
+def dsa_index_topk(shape, q, w, k, kscale, top, gap, ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().dsa_index_topk(C.byref(shape), _ptr(q), _ptr(w), _ptr(k), _ptr(kscale), _ptr(top), _ptr(gap),
+                                _ptr(ws), ws_bytes, _stream(stream)))

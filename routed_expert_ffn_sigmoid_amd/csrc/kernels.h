@@ -55,6 +55,12 @@ bool gemm_supported(const FfnParams &P);
 size_t gemm_workspace_bytes(const FfnParams &P);
 hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream);
 
+// dsa_index.hip: sparse-attention indexer scores and top-K causal keys
+size_t index_workspace_bytes(int T, int S);
+const char *index_unsupported(int T, int S, int H, int D);
+hipError_t launch_index_topk(const int8_t *q, const float *w, const int8_t *k, const float *kscale, int T, int S,
+                             int H, int D, int K, int pos0, int32_t *top, double *gap, void *ws, hipStream_t stream);
+
 // combine.hip
 hipError_t launch_combine(const float *y_perm, const float *y_shared, const int32_t *inv, const float *w, int T,
                           int d, int k, float *y, hipStream_t stream);

@@ -7,6 +7,7 @@
 
 #include <mutex>
 
+#include "../../include/dsa_index.h"
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -327,6 +328,50 @@ int moe_forward_static(const moe_shape *s, const void *x, const moe_qffn *routed
     rc = scratch_address(fn, &ws);
     if (rc) return rc;
     return run_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_index_shape(const char *fn, const dsa_index_shape *s) {
+    if (!s) return fail(MOE_EINVAL, "%s: shape is NULL", fn);
+    if (s->T < 0 || s->S < 0 || s->K < 1 || s->pos0 < 0) return fail(MOE_EINVAL, "%s: T, S, pos0 >= 0 and K >= 1", fn);
+    if (s->H < 16 || s->H > 64 || s->H % 16) return fail(MOE_EUNSUPPORTED, "%s: H must be 16, 32, 48 or 64", fn);
+    if (s->D < 64 || s->D > 256 || s->D % 64) return fail(MOE_EUNSUPPORTED, "%s: D must be 64, 128, 192 or 256", fn);
+    if (const char *why = moe::index_unsupported(s->T, s->S, s->H, s->D)) return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_index_workspace_size(const dsa_index_shape *s) {
+    if (check_index_shape("dsa_index_workspace_size", s) != MOE_OK) return 0;
+    return (moe::index_workspace_bytes(s->T, s->S) + 255) & ~(size_t)255;
+}
+
+int dsa_index_topk(const dsa_index_shape *s, const int8_t *q, const float *w, const int8_t *k, const float *kscale,
+                   int32_t *top, double *gap, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "dsa_index_topk";
+    int rc = check_index_shape(fn, s);
+    if (rc) return rc;
+    REQUIRE_PTR_T(q, "q");
+    REQUIRE_PTR_T(w, "w");
+    REQUIRE_PTR_T(top, "top");
+    if (s->S > 0 || k) REQUIRE_PTR(k, "k");
+    if (s->S > 0 || kscale) REQUIRE_PTR(kscale, "kscale");
+    if (gap && !aligned(gap, 16)) return fail(MOE_EALIGN, "%s: gap is not 16-byte aligned", fn);
+    const size_t need = dsa_index_workspace_size(s);
+    if (need > 0) {
+        if (!ws) return fail(MOE_EWORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+        if (!aligned(ws, 256)) return fail(MOE_EALIGN, "%s: workspace is not 256-byte aligned", fn);
+        if (ws_bytes < need) return fail(MOE_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    }
+    if (s->T == 0) return MOE_OK;
+    return launch_status(fn, moe::launch_index_topk(q, w, k, kscale, s->T, s->S, s->H, s->D, s->K, s->pos0, top, gap,
+                                                    ws, (hipStream_t)stream));
 }
 
 int moe_combine(const moe_shape *s, const float *y_perm, const float *y_shared, const int32_t *inv,

@@ -469,23 +469,27 @@ __global__ __launch_bounds__(EC_THREADS) void ec_select_kernel(const double *__r
     __shared__ int hist[256];
     __shared__ int scan[EC_THREADS / 64 + 1];
     __shared__ TopkState st;
+    __shared__ uint64_t cand[TOPK_CAND];
+    __shared__ int ncand;
     __shared__ unsigned long long below;  // largest key not chosen
     const int e = blockIdx.x;
     const double *p = pT + (long)e * T;
     auto key = [&](int i) { return (uint64_t)__double_as_longlong(p[i]); };
     if (threadIdx.x == 0) below = 0ull;
-    const TopkState s = radix_kth_largest<EC_THREADS, 64>(key, T, C, hist, &st);
+    const TopkState s = radix_kth_largest<EC_THREADS, 64>(key, T, C, hist, &st, cand, &ncand);
+    uint64_t mine = 0;  // this thread's largest key not taken
     visit_topk<EC_THREADS>(
         key, T, s, scan,
         [&](int i, int) {
             idx[(long)i * E + e] = e;
             w[(long)i * E + e] = (float)((double)lambda * p[i]);
         },
-        [&](int i) {
+        [&](int i, uint64_t ki) {
             idx[(long)i * E + e] = -1;
             w[(long)i * E + e] = 0.f;
-            atomicMax(&below, (unsigned long long)key(i));
+            mine = ki > mine ? ki : mine;
         });
+    block_max_u64(mine, &below);
     __syncthreads();
     if (threadIdx.x == 0 && gap)
         gap[e] = C >= T ? INFINITY : (s.eq > s.need ? 0.0 : __longlong_as_double((long long)s.v) -

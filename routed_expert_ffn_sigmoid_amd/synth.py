@@ -340,3 +340,35 @@ def sha256_of(*arrays: np.ndarray) -> str:
     for a in arrays:
         h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()
+
+
+# ----------------------------------------------------------------------------
+# sparse-attention indexer inputs
+# ----------------------------------------------------------------------------
+
+_T_IQ, _T_IW, _T_IK, _T_IKS = 20, 21, 22, 23
+_INDEX_FAMILY = 50
+
+
+@dataclasses.dataclass
+class IndexInputs:
+    q: np.ndarray       # [T][H][D] int8
+    w: np.ndarray       # [T][H] fp32
+    k: np.ndarray       # [S][D] int8
+    kscale: np.ndarray  # [S] fp32
+
+
+def gen_index(T: int, S: int, H: int, D: int, seed: int = 0, dup_keys: bool = False) -> IndexInputs:
+    """Indexer queries and keys as int8 (N(0,1) samples times 40, rounded and clipped to [-127, 127]), head weights
+    N(0, 1/H) and key scales U(0.5, 1.5) / 40.  dup_keys: the second half of the keys repeats the first with one
+    common scale, so that exactly equal scores occur."""
+    def rng(tid):
+        return _rng(seed, _INDEX_FAMILY, 0, tid)
+    q = np.clip(np.rint(rng(_T_IQ).standard_normal((T, H, D), dtype=np.float32) * 40), -127, 127).astype(np.int8)
+    k = np.clip(np.rint(rng(_T_IK).standard_normal((S, D), dtype=np.float32) * 40), -127, 127).astype(np.int8)
+    w = (rng(_T_IW).standard_normal((T, H)) / math.sqrt(H)).astype(np.float32)
+    ks = (rng(_T_IKS).uniform(0.5, 1.5, S) / 40).astype(np.float32)
+    if dup_keys:
+        k[S // 2:] = k[:S - S // 2]
+        ks[:] = np.float32(1 / 40)
+    return IndexInputs(q, w, k, ks)

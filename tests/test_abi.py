@@ -14,8 +14,11 @@ FAKE = 0x10000  # a 256-byte aligned, never dereferenced address
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"MOE_API\s+[\w\s\*]+?\b((?:moe|dsa)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_abi():
@@ -239,3 +242,24 @@ def test_router_fields_checked():
     # the capacity step needs workspace beyond the partial sums
     base = B.moe_workspace_size(shape(T=5000))
     assert B.moe_workspace_size(shape(T=5000, capacity_factor=1.2)) >= base
+
+
+
+def test_index_shape_checked():
+    """The indexer's shape checks: heads and head dimension the kernels take, non-negative sizes, K >= 1."""
+    for kw, code in ((dict(H=8), B.MOE_EUNSUPPORTED), (dict(D=96), B.MOE_EUNSUPPORTED), (dict(K=0), B.MOE_EINVAL),
+                     (dict(T=-1), B.MOE_EINVAL), (dict(pos0=-1), B.MOE_EINVAL)):
+        d = dict(T=2, S=100, H=64, D=128, K=16, pos0=98)
+        d.update(kw)
+        s = B.dsa_index_shape(**d)
+        assert B.dsa_index_workspace_size(s) == 0
+        with pytest.raises(B.MoeError) as ei:
+            B.dsa_index_topk(s, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, HUGE_WS, stream=0)
+        assert ei.value.code == code
+    s = B.dsa_index_shape(T=2, S=100, H=64, D=128, K=16, pos0=98)
+    assert B.dsa_index_workspace_size(s) == 2 * 100 * 8 + 256 - (2 * 100 * 8) % 256
+    with pytest.raises(B.MoeError) as ei:
+        B.dsa_index_topk(s, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, HUGE_WS, stream=0)
+    assert "k is NULL" in str(ei.value)
+    B.dsa_index_topk(B.dsa_index_shape(T=0, S=100, H=64, D=128, K=16, pos0=0), None, None, FAKE, FAKE, None, None,
+                     FAKE, HUGE_WS, stream=0)
