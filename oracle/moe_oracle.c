@@ -41,10 +41,27 @@
  *        min(T, ceil(cf * T / E)) tokens of largest p (ties to the lower token), weight lambda * p.
  *    An empty slot (id -1) is skipped by the permutation and the combine.
  *
+ *  - expert residency tiers.  The deep-dive page (pwwt.cn Colibri write-up) keeps an expert cache of slots,
+ *    each holding one expert's complete weights, by default 4 times the experts a token activates (its
+ *    section 3.1); eviction is a weighted LRU whose weight is how often the expert was activated lately: each
+ *    slot keeps a last-used time and a hit count and the slot with few hits and an old last use goes first
+ *    (same section).  The GLM-5.2 page keeps one LRU cache per layer, reads the next experts ahead while the
+ *    current ones compute (its section 三.5), merges a batch's requests so each distinct expert is read once
+ *    (三.4) and can pin hot experts in the faster tier (五).  Readings where the pages are silent:
+ *      a step is one layer call; its requests are the batch union U of the experts its tokens chose;
+ *      a resident expert of U is a hit: its slot's hit count += 1 and last use = the step number (steps count
+ *        from 1);
+ *      the missing experts of U, in ascending id, each take the first evictable slot in the order: empty
+ *        slots (lower slot first), then fewest hits, then oldest last use, then lower expert id (pure LRU,
+ *        kept for comparison: empty, then oldest last use, then lower id); a slot holding an expert of U, or
+ *        a pinned slot, is not evictable; a loaded slot starts with hit count 1 and last use = the step;
+ *      pinned experts fill slots 0 .. P-1 from the start and never leave;
+ *      the counts are per residence: an evicted expert that comes back starts again from 1.
+ *
  * All sums run in index order in fp64.  The OpenMP loops split work only over
  * independent output elements, so results do not depend on the thread count.
  *
- * Parity pins live in tests/test_oracle_pins.py.
+ * Parity pins live in tests/test_oracle_pins.py and tests/test_oracle_cache_pins.py.
  */
 #include <math.h>
 #include <stdint.h>
@@ -526,4 +543,80 @@ void oracle_index_topk(int T, int S, int H, int D, int K, int pos0, const int8_t
         }
         free(kv);
     }
+}
+
+/* ---------------------------------------------------------------------------------------------------------
+ * Expert residency (cache of HBM slots over the host tier); readings in the header.
+ * State: slot_expert[S] (-1 empty), expert_slot[E] (-1 not resident), last_used[S], hits[S].
+ */
+void oracle_cache_init(int E, int S, int P, const int32_t *pinned, int32_t *slot_expert, int32_t *expert_slot,
+                       int64_t *last_used, int64_t *hits) {
+    for (int e = 0; e < E; e++) expert_slot[e] = -1;
+    for (int s = 0; s < S; s++) {
+        slot_expert[s] = -1;
+        last_used[s] = 0;
+        hits[s] = 0;
+    }
+    for (int i = 0; i < P; i++) {
+        slot_expert[i] = pinned[i];
+        expert_slot[pinned[i]] = i;
+    }
+}
+
+/* Is slot a a better victim than slot b (policy 0 weighted LRU, 1 LRU)? */
+static int victim_before(int policy, int a, int b, const int32_t *slot_expert, const int64_t *last_used,
+                         const int64_t *hits) {
+    const int ea = slot_expert[a] >= 0, eb = slot_expert[b] >= 0;
+    if (!ea || !eb) {
+        if (ea != eb) return !ea;  /* an empty slot first */
+        return a < b;
+    }
+    if (policy == 0 && hits[a] != hits[b]) return hits[a] < hits[b];
+    if (last_used[a] != last_used[b]) return last_used[a] < last_used[b];
+    return slot_expert[a] < slot_expert[b];
+}
+
+/* One step at time `now`: U = the nu distinct experts of uniq (any order).  Writes the hits and the misses in
+ * ascending expert id and, per miss, the expert its slot held before (-1: the slot was empty).  Returns 0, or -1
+ * when a miss finds no evictable slot (the state is then partly updated). */
+int oracle_cache_step(int E, int S, int P, int policy, int64_t now, int32_t *slot_expert, int32_t *expert_slot,
+                      int64_t *last_used, int64_t *hits, int nu, const int32_t *uniq, int32_t *hit_list,
+                      int32_t *n_hit, int32_t *miss_list, int32_t *n_miss, int32_t *evicted) {
+    unsigned char *inU = (unsigned char *)calloc((size_t)E, 1);
+    for (int i = 0; i < nu; i++) inU[uniq[i]] = 1;
+    int nh = 0, nm = 0;
+    for (int e = 0; e < E; e++) {
+        if (!inU[e]) continue;
+        const int s = expert_slot[e];
+        if (s >= 0) {
+            hits[s] += 1;
+            last_used[s] = now;
+            hit_list[nh++] = e;
+        } else {
+            miss_list[nm++] = e;
+        }
+    }
+    int rc = 0;
+    for (int i = 0; i < nm; i++) {
+        const int e = miss_list[i];
+        int best = -1;
+        for (int s = P; s < S; s++) {
+            if (slot_expert[s] >= 0 && inU[slot_expert[s]]) continue;
+            if (best < 0 || victim_before(policy, s, best, slot_expert, last_used, hits)) best = s;
+        }
+        if (best < 0) {
+            rc = -1;
+            break;
+        }
+        evicted[i] = slot_expert[best];
+        if (slot_expert[best] >= 0) expert_slot[slot_expert[best]] = -1;
+        slot_expert[best] = e;
+        expert_slot[e] = best;
+        hits[best] = 1;
+        last_used[best] = now;
+    }
+    *n_hit = nh;
+    *n_miss = nm;
+    free(inU);
+    return rc;
 }

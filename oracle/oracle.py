@@ -37,6 +37,9 @@ def lib():
         _lib.oracle_capacity.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P]
         _lib.oracle_expert_choice.argtypes = [C.c_int, C.c_int, C.c_int, P, C.c_double, P, P, P]
         _lib.oracle_index_topk.argtypes = [C.c_int] * 6 + [P] * 7
+        _lib.oracle_cache_init.argtypes = [C.c_int] * 3 + [P] * 5
+        _lib.oracle_cache_step.argtypes = [C.c_int] * 4 + [C.c_int64] + [P] * 4 + [C.c_int] + [P] * 6
+        _lib.oracle_cache_step.restype = C.c_int
     return _lib
 
 
@@ -332,3 +335,58 @@ def index_topk(q: np.ndarray, w: np.ndarray, k: np.ndarray, kscale: np.ndarray, 
     sc = np.empty((T, S), np.float64) if want_scores else None
     lib().oracle_index_topk(T, S, H, D, K, pos0, _p(q), _p(w), _p(k), _p(kscale), _p(top), _p(gap), _p(sc))
     return IndexTopk(top, gap, sc)
+
+
+# ----------------------------------------------------------------------------
+# expert residency: weighted-LRU cache of HBM slots
+# ----------------------------------------------------------------------------
+
+CACHE_WEIGHTED_LRU = 0
+CACHE_LRU = 1
+
+
+@dataclass
+class CacheStep:
+    hits: np.ndarray     # experts of the step already resident, ascending
+    misses: np.ndarray   # experts copied in this step, ascending
+    evicted: np.ndarray  # per miss: the expert its slot held before (-1: the slot was empty)
+
+
+class ExpertCache:
+    """State of one layer's slots: slot_expert [S], expert_slot [E], last_used [S], hits [S], and the step count."""
+
+    def __init__(self, E: int, S: int, pinned=(), policy: int = CACHE_WEIGHTED_LRU):
+        pinned = np.ascontiguousarray(pinned, dtype=np.int32)
+        if not 0 < S <= E or pinned.size > S or len(set(pinned.tolist())) != pinned.size:
+            raise ValueError("bad cache shape")
+        if pinned.size and (pinned.min() < 0 or pinned.max() >= E):
+            raise ValueError("pinned expert out of range")
+        self.E, self.S, self.P, self.policy = E, S, int(pinned.size), policy
+        self.slot_expert = np.empty(S, np.int32)
+        self.expert_slot = np.empty(E, np.int32)
+        self.last_used = np.empty(S, np.int64)
+        self.hits = np.empty(S, np.int64)
+        self.now = 0
+        self.n_hits = self.n_misses = self.n_evictions = 0
+        lib().oracle_cache_init(E, S, self.P, _p(pinned), _p(self.slot_expert), _p(self.expert_slot),
+                                _p(self.last_used), _p(self.hits))
+
+    def step(self, uniq) -> CacheStep:
+        """One layer call whose tokens chose the experts in uniq (the batch union, any order)."""
+        u = np.unique(np.ascontiguousarray(uniq, dtype=np.int32))
+        hit = np.empty(max(u.size, 1), np.int32)
+        miss = np.empty(max(u.size, 1), np.int32)
+        ev = np.empty(max(u.size, 1), np.int32)
+        nh = np.zeros(1, np.int32)
+        nm = np.zeros(1, np.int32)
+        self.now += 1
+        rc = lib().oracle_cache_step(self.E, self.S, self.P, self.policy, self.now, _p(self.slot_expert),
+                                     _p(self.expert_slot), _p(self.last_used), _p(self.hits), int(u.size), _p(u),
+                                     _p(hit), _p(nh), _p(miss), _p(nm), _p(ev))
+        if rc != 0:
+            raise RuntimeError("a step's misses exceed the evictable slots")
+        r = CacheStep(hit[:nh[0]].copy(), miss[:nm[0]].copy(), ev[:nm[0]].copy())
+        self.n_hits += r.hits.size
+        self.n_misses += r.misses.size
+        self.n_evictions += int((r.evicted >= 0).sum())
+        return r
