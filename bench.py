@@ -61,6 +61,11 @@ def parse(argv=None):
     ap.add_argument("--index", default=None, metavar="T,S",
                     help="time the sparse-attention indexer's top-2048 (dsa_index_topk) for T queries at the end of "
                          "an S-key cache (64 heads of 128) instead of the MoE layer")
+    ap.add_argument("--tiered", action="store_true",
+                    help="decode with the routed experts in pinned host memory behind a per-layer HBM cache")
+    ap.add_argument("--slots", type=int, default=None,
+                    help="HBM slots per layer (--tiered; default 4 k, at least a step's experts + the pinned ones)")
+    ap.add_argument("--pinned", type=int, default=None, help="pinned hot experts per layer (--tiered; default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of each oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -375,12 +380,151 @@ def measure_index(args, dev):
                        "key_caches_rotated": pool}, "roofline": roof}
 
 
+PEAK_PCIE_GBS = 64.0  # the host link, PCIe 5.0 x16, one direction
+
+
+def cache_hit_rates(spec, W, T, dev, xs, slot_counts, pinned, warm):
+    """Hit rates of the device planner for each (policy, slots) over one token stream: the layer's router and
+    permutation per step, then one plan per cache (no copies: the rates do not depend on them).  xs: [n*T][d];
+    the first `warm` steps fill the caches and are not counted."""
+    import torch
+    from routed_expert_ffn_sigmoid_amd import binding as B
+    from routed_expert_ffn_sigmoid_amd import layer as L
+    run = L.MoeRun(spec, T, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    caches = []
+    for policy in (B.MOE_CACHE_WEIGHTED_LRU, B.MOE_CACHE_LRU):
+        for S in slot_counts:
+            c = B.make_cache_shape(spec.E, S, len(pinned), policy)
+            st = torch.empty(B.moe_cache_state_size(c), dtype=torch.uint8, device=dev)
+            lists = [torch.empty(spec.E, **i32), torch.empty(1, **i32), torch.empty(spec.E, **i32),
+                     torch.empty(1, **i32)]
+            B.moe_cache_init(c, pinned, st, lists[2], lists[3])
+            caches.append((policy, S, c, st, lists))
+    n = xs.shape[0] // T
+    base = {}
+    for i in range(n):
+        if i == warm:
+            torch.cuda.synchronize()
+            base = {(p, S): B.moe_cache_stats(c, st) for p, S, c, st, _ in caches}
+        run.route(xs[i * T:(i + 1) * T], W)
+        run.permute()
+        for _, _, c, st, (h, nh, m, nm) in caches:
+            B.moe_cache_plan(c, T, spec.k, run.uniq, run.n_uniq, st, h, nh, m, nm)
+    torch.cuda.synchronize()
+    out = {}
+    for p, S, c, st, _ in caches:
+        s1 = B.moe_cache_stats(c, st)
+        s0 = base[(p, S)]
+        hits, misses = s1[1] - s0[1], s1[2] - s0[2]
+        out[f"{'weighted_lru' if p == B.MOE_CACHE_WEIGHTED_LRU else 'lru'}_slots{S}"] = round(hits / (hits + misses), 4)
+    return out
+
+
+def measure_tiered(args, dev):
+    """Decode through the residency tier: every routed expert of each layer in pinned host memory, a weighted-LRU
+    cache of HBM slots per layer in front of it.  One step = one layer call (route, permute, plan, the missed
+    experts copied from host memory on a second stream while the resident ones compute, the missed ones, combine)
+    for T fresh tokens, layers rotated."""
+    import torch
+    from routed_expert_ffn_sigmoid_amd import binding as B
+    from routed_expert_ffn_sigmoid_amd import layer as L
+    from routed_expert_ffn_sigmoid_amd import synth
+    spec = synth.CONFIGS["large_zipf"]
+    T = args.T or 1
+    nl = args.layers or 2
+    npin = 4 if args.pinned is None else args.pinned
+    # four times the experts a token activates, and room for a whole step's misses
+    slots = args.slots or max(4 * spec.k, min(spec.E, T * spec.k) + npin)
+    t0 = time.time()
+    copy_stream = torch.cuda.Stream()
+    tiers, Ws, runs, tq = [], [], [], []
+    for l in range(nl):
+        tiers.append(L.HostTier(spec, layer=l))
+        tq.append(tiers[-1].qffn())
+        Ws.append(L.DeviceLayerWeights(spec, layer=l, device=dev, routed=False))
+        pinned = synth.popularity_order(spec, layer=l)[:npin].tolist()
+        runs.append(L.CachedMoeRun(spec, T, slots, pinned, device=dev, copy_stream=copy_stream))
+        runs[-1].init(tiers[-1])
+    setup_s = time.time() - t0
+    steps, warm = args.steps, max(args.warmup, 8 * nl)
+    xs = L.upload_x(spec, synth.gen_x(spec, (steps + warm) * T, 0, 1000), dev)  # a fresh token every step
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def one(i, ev=None):
+        l = i % nl
+        runs[l].step(xs[i * T:(i + 1) * T], Ws[l], tiers[l], tq[l], ev)
+
+    for i in range(warm):
+        one(i)
+    torch.cuda.synchronize()
+    s0 = [r.stats() for r in runs]
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        one(warm + i, fev[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    s1 = [r.stats() for r in runs]
+    hits = sum(b[1] - a[1] for a, b in zip(s0, s1))
+    misses = sum(b[2] - a[2] for a, b in zip(s0, s1))
+    eb = spec.expert_bytes()
+    fetch_ms = sum(a.elapsed_time(b) for a, b in fev)
+    fetched = misses * eb
+    # the host link through the DMA engines (hipMemcpyAsync from the same pinned tier), for comparison
+    dst = L.DeviceExperts(spec, 1, spec.I, dev)
+    names = ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down")
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 8
+    c0.record(stream)
+    for r in range(reps):
+        for n in names:
+            getattr(dst, n)[0].copy_(getattr(tiers[0], n)[5 + r], non_blocking=True)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    dma_gbs = reps * eb / (c0.elapsed_time(c1) * 1e6)
+    # hit rates by policy and slot count on one stream of independent tokens and one of correlated tokens
+    nrate, wrate = 2048, 512
+    pin0 = synth.popularity_order(spec, layer=0)[:npin].tolist()
+    sc = sorted({16, 2 * spec.k * T + npin, slots, 64, 128})
+    sc = [S for S in sc if S - npin >= min(spec.E, T * spec.k)]
+    x_iid = L.upload_x(spec, synth.gen_x(spec, nrate * T, 0, 2000), dev)
+    x_ar = L.upload_x(spec, synth.gen_x_correlated(spec, nrate * T, 0.9, 0, 0), dev)
+    rates = {"independent_tokens": cache_hit_rates(spec, Ws[0], T, dev, x_iid, sc, pin0, wrate),
+             "correlated_tokens_rho0.9": cache_hit_rates(spec, Ws[0], T, dev, x_ar, sc, pin0, wrate)}
+    achieved = fetched / (fetch_ms * 1e6) if fetch_ms > 0 else 0.0
+    return {"metric": "MoE-layer tokens/s, routed experts in a host tier behind an HBM cache",
+            "value": round(T / ms * 1e3, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int4-weights/bf16-act/f32-out", "data": "synthetic (seeded; random-init quantised weights)",
+            "config": {"workload": f"256-expert top-8 int4 layer (d=7168, I=2048, shared 2048), Zipf(1.1) bias, "
+                                   f"T={T} per step, {nl} layers rotated, every routed expert in pinned host memory",
+                       "slots_per_layer": slots, "pinned_per_layer": npin, "policy": "weighted LRU",
+                       "setup_s": round(setup_s, 1)},
+            "hit_rate": round(hits / max(1, hits + misses), 4),
+            "experts_fetched_per_step": round(misses / steps, 3),
+            "roofline": {"bound": "pcie", "achieved": round(achieved, 2), "peak": PEAK_PCIE_GBS, "unit": "GB/s",
+                         "frac": round(achieved / PEAK_PCIE_GBS, 4), "traffic": None,
+                         "kernel": "cache_fetch_kernel (missed experts, host tier -> HBM slots)",
+                         "algorithmic_bytes_per_expert": eb, "fetch_ms_per_step": round(fetch_ms / steps, 4),
+                         "dma_engine_gbs": round(dma_gbs, 2)},
+            "hit_rates_by_policy": rates}
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.tiered:
+        import torch
+        from routed_expert_ffn_sigmoid_amd import binding as B
+        B.lib()
+        print(json.dumps(measure_tiered(args, torch.device("cuda:0"))), flush=True)
+        return
     if args.index:
         import torch
         from routed_expert_ffn_sigmoid_amd import binding as B

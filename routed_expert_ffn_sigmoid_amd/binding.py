@@ -40,9 +40,14 @@ MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_GEMM = 2
 
-# names declared in include/moe.h
+MOE_CACHE_WEIGHTED_LRU = 0
+MOE_CACHE_LRU = 1
+
+# names declared in include/*.h
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_static", "moe_combine",
-           "moe_last_error", "moe_abi_version", "dsa_index_workspace_size", "dsa_index_topk")
+           "moe_last_error", "moe_abi_version", "dsa_index_workspace_size", "dsa_index_topk",
+           "moe_cache_state_size", "moe_cache_init", "moe_cache_plan", "moe_cache_fetch", "moe_forward_cached",
+           "moe_cache_stats")
 
 MOE_STATIC_SCRATCH_BYTES = 64 << 20  # moe_forward_static's scratch
 
@@ -62,6 +67,10 @@ class moe_shape(C.Structure):
 
 class dsa_index_shape(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("T", "S", "H", "D", "K", "pos0")]
+
+
+class moe_cache_shape(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("E", "slots", "pinned", "policy")]
 
 
 class moe_qffn(C.Structure):
@@ -97,6 +106,17 @@ def lib():
         L.dsa_index_workspace_size.restype = C.c_size_t
         L.dsa_index_topk.argtypes = [X, P, P, P, P, P, P, P, C.c_size_t, P]
         L.dsa_index_topk.restype = C.c_int
+        K = C.POINTER(moe_cache_shape)
+        I32 = C.c_int32
+        L.moe_cache_state_size.argtypes = [K]
+        L.moe_cache_state_size.restype = C.c_size_t
+        L.moe_cache_init.argtypes = [K, P, P, P, P, P]
+        L.moe_cache_plan.argtypes = [K, I32, I32, P, P, P, P, P, P, P, P]
+        L.moe_cache_fetch.argtypes = [S, K, Q, Q, P, P, P, P]
+        L.moe_forward_cached.argtypes = [S, K, P, Q, P, Q, P, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_cache_stats.argtypes = [K, P, P, P, P]
+        for f in ("moe_cache_init", "moe_cache_plan", "moe_cache_fetch", "moe_forward_cached", "moe_cache_stats"):
+            getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
 
@@ -186,3 +206,49 @@ def dsa_index_topk(shape, q, w, k, kscale, top, gap, ws, ws_bytes=None, stream=N
     ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib().dsa_index_topk(C.byref(shape), _ptr(q), _ptr(w), _ptr(k), _ptr(kscale), _ptr(top), _ptr(gap),
                                 _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def make_cache_shape(E, slots, pinned=0, policy=MOE_CACHE_WEIGHTED_LRU) -> moe_cache_shape:
+    return moe_cache_shape(E, slots, pinned, policy)
+
+
+def moe_cache_state_size(cache: moe_cache_shape) -> int:
+    return int(lib().moe_cache_state_size(C.byref(cache)))
+
+
+def moe_cache_init(cache, pinned_ids, state, miss, n_miss, stream=None) -> None:
+    """pinned_ids: a sequence of ints (host), or None when cache.pinned == 0."""
+    arr = None
+    if pinned_ids is not None and len(pinned_ids):
+        arr = (C.c_int32 * len(pinned_ids))(*[int(v) for v in pinned_ids])
+    _check(lib().moe_cache_init(C.byref(cache), C.cast(arr, C.c_void_p) if arr is not None else None, _ptr(state),
+                                _ptr(miss), _ptr(n_miss), _stream(stream)))
+
+
+def moe_cache_plan(cache, T, k, uniq, n_uniq, state, hit, n_hit, miss, n_miss, stream=None) -> None:
+    _check(lib().moe_cache_plan(C.byref(cache), int(T), int(k), _ptr(uniq), _ptr(n_uniq), _ptr(state), _ptr(hit),
+                                _ptr(n_hit), _ptr(miss), _ptr(n_miss), _stream(stream)))
+
+
+def moe_cache_fetch(shape, cache, host_tier: moe_qffn, slots: moe_qffn, state, miss, n_miss, stream=None) -> None:
+    _check(lib().moe_cache_fetch(C.byref(shape), C.byref(cache), C.byref(host_tier), C.byref(slots), _ptr(state),
+                                 _ptr(miss), _ptr(n_miss), _stream(stream)))
+
+
+def moe_forward_cached(shape, cache, x, slots: moe_qffn, state, shared: Optional[moe_qffn], offsets, perm, lst,
+                       n_list, y_perm, y_shared, diag, ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().moe_forward_cached(C.byref(shape), C.byref(cache), _ptr(x), C.byref(slots), _ptr(state),
+                                    C.byref(shared) if shared is not None else None, _ptr(offsets), _ptr(perm),
+                                    _ptr(lst), _ptr(n_list), _ptr(y_perm), _ptr(y_shared), _ptr(diag), _ptr(ws),
+                                    ws_bytes, _stream(stream)))
+
+
+def moe_cache_stats(cache, state, want_slots: bool = False, stream=None):
+    """(steps, hits, misses, evictions, unplaced) and, with want_slots, each slot's expert (a list)."""
+    out = (C.c_int64 * 5)()
+    se = (C.c_int32 * cache.slots)() if want_slots else None
+    _check(lib().moe_cache_stats(C.byref(cache), _ptr(state), C.cast(out, C.c_void_p),
+                                 C.cast(se, C.c_void_p) if se is not None else None, _stream(stream)))
+    stats = tuple(int(v) for v in out)
+    return (stats, list(se)) if want_slots else stats

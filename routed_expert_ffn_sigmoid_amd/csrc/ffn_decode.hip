@@ -46,7 +46,7 @@ constexpr int DK_GMAX = 16;               // tokens per pass: the MFMA M dimensi
 constexpr int DK_LDS_BUDGET = 150 * 1024; // digit planes + reduction buffer
 
 struct DSlot {
-    int e, I;
+    int e, w, I;  // expert, its weight row, intermediate size
     bool shared;
 };
 
@@ -56,12 +56,16 @@ __device__ __forceinline__ bool dk_slot(const FfnParams &P, int slot, DSlot &s) 
         const int e = P.uniq[slot];
         if (e < 0) return false;
         s.e = e;
+        s.w = weight_row(P, e);
+        if (s.w < 0) return false;  // weights not resident: rows left unwritten
         s.I = P.I;
         s.shared = false;
     } else {
         s.e = 0;
+        s.w = 0;
         s.I = P.Is;
         s.shared = true;
+        if (!P.y_sh) return false;  // the shared expert left out (y_sh = nullptr)
     }
     return s.I > 0;
 }
@@ -391,10 +395,10 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
     const int mrows = MODE == 0 ? s.I : P.d;
     const uint32_t mbytes = (uint32_t)((long)mrows * rb);
     if (MODE == 0) {
-        wr[0] = make_rsrc(W.qg + (long)s.e * s.I * rb, mbytes);
-        wr[NM - 1] = make_rsrc(W.qu + (long)s.e * s.I * rb, mbytes);
+        wr[0] = make_rsrc(W.qg + (long)s.w * s.I * rb, mbytes);
+        wr[NM - 1] = make_rsrc(W.qu + (long)s.w * s.I * rb, mbytes);
     } else {
-        wr[0] = make_rsrc(W.qd + (long)s.e * P.d * rb, mbytes);
+        wr[0] = make_rsrc(W.qd + (long)s.w * P.d * rb, mbytes);
     }
     const uint32_t lane_off = (uint32_t)((long)row * rb) + (uint32_t)(kp * kpart_bytes + 16 * g);
     const int nseg_pad = (nseg + PF - 1) / PF * PF;
@@ -421,10 +425,10 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
     // z of this lane's output row (the same row for every token)
     float zrow[NM];
     if (MODE == 0) {
-        zrow[0] = zp_val(W.zg, WBITS, (long)s.e * s.I + row);
-        zrow[NM - 1] = zp_val(W.zu, WBITS, (long)s.e * s.I + row);
+        zrow[0] = zp_val(W.zg, WBITS, (long)s.w * s.I + row);
+        zrow[NM - 1] = zp_val(W.zu, WBITS, (long)s.w * s.I + row);
     } else {
-        zrow[0] = zp_val(W.zd, WBITS, (long)s.e * P.d + row);
+        zrow[0] = zp_val(W.zd, WBITS, (long)s.w * P.d + row);
     }
     __syncthreads();  // zero_area
 
@@ -509,7 +513,7 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
                     const int i = 4 * g + r;  // token of this register
                     if (i < ng) {
                         if (MODE == 0) {
-                            const long ch = (long)s.e * s.I + o;
+                            const long ch = (long)s.w * s.I + o;
                             const float gf = (float)((double)W.sg[ch] * v[0][r]);
                             const float uf = (float)((double)W.su[ch] * v[NM - 1][r]);
                             const float hv = gf / (1.f + expf(-gf)) * uf;
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
                             else
                                 h[(long)(p0 + g0 + i) * s.I + o] = hv;
                         } else {
-                            const long ch = (long)s.e * P.d + o;
+                            const long ch = (long)s.w * P.d + o;
                             const float y = (float)((double)W.sd[ch] * v[0][r]);
                             if (s.shared)
                                 P.y_sh[(long)(g0 + i) * P.d + o] = y;
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
 // Gate/up stages the digit planes of all T tokens once (slots only remap lanes to tokens); down
 // stages the rows of h of each slot when the slot changes.  Requires T <= DK_GMAX.
 struct DItem {
-    int slot, e, tile, I, kpart_bytes, nseg_pad, row, p0, ng;
+    int slot, e, w, tile, I, kpart_bytes, nseg_pad, row, p0, ng;  // w: weight row (-1: not resident)
     bool shared, row_ok;
 };
 
@@ -736,6 +740,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
                 const int sl = __builtin_amdgcn_readfirstlane(lo);
                 const int q = vs - __builtin_amdgcn_readfirstlane(vpre[sl]);
                 it.e = __builtin_amdgcn_readfirstlane(t_uniq[sl]);
+                it.w = weight_row(P, it.e);
                 it.shared = false;
                 it.I = P.I;
                 const int o0 = __builtin_amdgcn_readfirstlane(t_off[it.e]);
@@ -745,6 +750,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             } else {
                 const int q = vs - nvr;
                 it.e = 0;
+                it.w = P.y_sh ? 0 : -1;  // y_sh = nullptr: the shared expert left out
                 it.shared = true;
                 it.I = P.Is;
                 it.p0 = q * gcap;
@@ -754,6 +760,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             it.slot = i / tiles_r;
             it.tile = i % tiles_r;
             it.e = __builtin_amdgcn_readfirstlane(t_uniq[it.slot]);
+            it.w = weight_row(P, it.e);
             it.shared = false;
             it.I = P.I;
             it.p0 = __builtin_amdgcn_readfirstlane(t_off[it.e]);
@@ -762,6 +769,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             it.slot = nrs;
             it.tile = i - nu * tiles_r;
             it.e = 0;
+            it.w = P.y_sh ? 0 : -1;
             it.shared = true;
             it.I = P.Is;
             it.p0 = 0;
@@ -773,7 +781,8 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         it.nseg_pad = ((it.kpart_bytes + 63) / 64 + PF - 1) / PF * PF;
         it.row = (it.tile * TPW + tile_w) * 16 + j;
         const int u = 2 * i + (j >> 3);  // half tile of this lane's row
-        it.row_ok = it.row < nout && (!HALVES || (u >= u0 && u < u1));
+        it.row_ok = it.row < nout && (!HALVES || (u >= u0 && u < u1)) && it.w >= 0;
+        if (it.w < 0) it.w = 0;  // not resident: reads nothing (row_ok false), writes nothing
         return it;
     };
     auto weights = [&](const DItem &it, rsrc_t (&wr)[NM], uint32_t &lane_off) {
@@ -783,10 +792,10 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         const long rb = (long)K * WBITS / 8;
         const uint32_t mbytes = (uint32_t)((long)nout * rb);
         if (MODE == 0) {
-            wr[0] = make_rsrc(W.qg + (long)it.e * it.I * rb, mbytes);
-            wr[NM - 1] = make_rsrc(W.qu + (long)it.e * it.I * rb, mbytes);
+            wr[0] = make_rsrc(W.qg + (long)it.w * it.I * rb, mbytes);
+            wr[NM - 1] = make_rsrc(W.qu + (long)it.w * it.I * rb, mbytes);
         } else {
-            wr[0] = make_rsrc(W.qd + (long)it.e * P.d * rb, mbytes);
+            wr[0] = make_rsrc(W.qd + (long)it.w * P.d * rb, mbytes);
         }
         // rows past the output or outside this CU's half tiles read nothing
         lane_off = it.row_ok ? (uint32_t)((long)it.row * rb) + (uint32_t)(kp * it.kpart_bytes + 16 * g) : kOOB;
@@ -914,16 +923,16 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         // start the next item (or read nothing), so the epilogue waits only for what it uses
         const QW &W = cur.shared ? P.shared : P.routed;
         const int nout = MODE == 0 ? cur.I : P.d;
-        const int rowc = min(cur.row, nout - 1);
+        const int rowc = cur.row_ok ? min(cur.row, nout - 1) : 0;
         float zrow[NM], srow[NM];
         if (MODE == 0) {
-            const long ch = (long)cur.e * cur.I + rowc;
+            const long ch = (long)cur.w * cur.I + rowc;
             zrow[0] = zp_val(W.zg, WBITS, ch);
             zrow[NM - 1] = zp_val(W.zu, WBITS, ch);
             srow[0] = W.sg[ch];
             srow[NM - 1] = W.su[ch];
         } else {
-            const long ch = (long)cur.e * P.d + rowc;
+            const long ch = (long)cur.w * P.d + rowc;
             zrow[0] = zp_val(W.zd, WBITS, ch);
             srow[0] = W.sd[ch];
         }

@@ -193,8 +193,9 @@ __global__ __launch_bounds__(256) void x16_kernel(FfnParams P, _Float16 *__restr
     };
     if (blockIdx.x >= nrb) {
         // ---- expert exponents: e < E routed, e == E the shared expert
-        const int e = blockIdx.x - nrb;
+        const int e = blockIdx.x - nrb;  // the weight row (routed) or E (shared)
         const bool sh = e == P.E;
+        if (!sh && e >= P.n_wrows) return;  // fewer weight rows than experts (an expert cache's slots)
         const int I = sh ? P.Is : P.I;
         const long base = sh ? 0 : (long)e * I;
         const QW &W = sh ? P.shared : P.routed;
@@ -457,17 +458,22 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         }
         const int slot = __builtin_amdgcn_readfirstlane(lo);
         const bool shared = P.Is > 0 && slot == nslot - 1;
-        int e = 0, p0 = 0, cnt = P.T;
+        int e = 0, wr = 0, p0 = 0, cnt = P.T;
+        bool resident = P.y_sh != nullptr;  // (shared) y_sh = nullptr: the shared expert left out
         if (!shared) {
             e = ld_const(P.uniq, slot);
             p0 = ld_const(P.offsets, e);
             cnt = ld_const(P.offsets, e + 1) - p0;
+            wr = weight_row(P, e);
+            resident = wr >= 0;
+            if (!resident) wr = 0;
         }
         const int mt_n = (cnt + GG_M - 1) / GG_M;
         const int local = tile - __builtin_amdgcn_readfirstlane(s_t0[slot]);
         const int ntile = local / mt_n, mtile = local % mt_n;
         const int r0 = mtile * GG_M;                     // first row of the tile within the slot
-        const int rows = min(GG_M, cnt - r0);
+        // an expert whose weights are not resident: a tile of no rows (reads and writes nothing)
+        const int rows = resident ? min(GG_M, cnt - r0) : 0;
         // row tile number over all slots (the same in both passes: the prefix counts row tiles times
         // tiles_n); it indexes the residual exponents
         const int rt = __builtin_amdgcn_readfirstlane(s_t0[slot]) / tiles_n + mtile;
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                     // one lane per row brings the row's scales (read in the epilogue, after the K loop's barriers;
                     // the previous tile's epilogue is done with them since the barrier that ends it)
                     if ((lane & 7) == 0) {
-                        const int he = G.hexp[shared ? P.E : e];
+                        const int he = G.hexp[shared ? P.E : wr];
                         if (MODE == 0) {
                             rscale[m] = G.xinv[row];
                             hscale[m] = __builtin_ldexpf(1.f, -h_row_exp(he, G.xl[row]));
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         const int nbase = ntile * C::NOUT_G + wv * C::NOUT_W;
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const uint8_t *base = MODE == 0 ? (j == 0 ? W.qg : W.qu) + (long)e * I * rbf : W.qd + (long)e * P.d * rbf;
+            const uint8_t *base = MODE == 0 ? (j == 0 ? W.qg : W.qu) + (long)wr * I * rbf : W.qd + (long)wr * P.d * rbf;
             brs[j] = make_rsrc(base, (uint32_t)(nout * rbf));
         }
 #pragma unroll
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
             const int o = MODE == 0 ? nbase + lr : nbase + 32 * j + lr;
             ocol[j] = o;
             const long ncol = MODE == 0 ? I : P.d;
-            const long ch = (long)e * ncol + min(o, nout - 1);
+            const long ch = (long)wr * ncol + min(o, nout - 1);
             if (MODE == 0) {
                 sc[j] = j == 0 ? W.sg[ch] : W.su[ch];
                 zp[j] = gg_zp(j == 0 ? W.zg : W.zu, WBITS, ch);

@@ -22,11 +22,21 @@ struct FfnParams {
     int wbits, act;
     QW routed, shared;
     const int32_t *offsets, *perm, *uniq, *n_uniq;
+    // routed weight row of expert e: wslot[e] (an expert cache's slot map) or e itself (wslot = nullptr); rows
+    // outside [0, n_wrows) mark an expert whose weights are not resident, and its rows are left unwritten
+    const int32_t *wslot;
+    int n_wrows;
     int n_routed_slots;  // min(E, A): grid slots reserved for routed experts
     bool invariant;      // batch-invariant mode: decode K split fixed by the layer's shape alone
     float *y_perm, *y_sh;
     uint32_t *diag;      // optional counters (nullptr = none): [0] h values not finite in fp16
 };
+
+// Routed weight row of expert e (wave-uniform e), or -1 when that row is outside the weights.
+__device__ __forceinline__ int weight_row(const FfnParams &P, int e) {
+    const int w = P.wslot ? __builtin_amdgcn_readfirstlane(P.wslot[e]) : e;
+    return (unsigned)w < (unsigned)P.n_wrows ? w : -1;
+}
 
 // router.hip
 // nullptr when the router kernels take the shape, else why not (a buffer beyond 32-bit descriptor offsets)
@@ -54,6 +64,17 @@ hipError_t launch_ffn_decode(const FfnParams &P, void *ws, hipStream_t stream);
 bool gemm_supported(const FfnParams &P);
 size_t gemm_workspace_bytes(const FfnParams &P);
 hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream);
+
+// cache.hip: expert residency (slots in HBM over a host tier)
+size_t cache_state_bytes(int E, int S);
+const int32_t *cache_slot_map(const void *state, int E, int S);  // expert -> slot, in the state
+hipError_t launch_cache_init(void *state, int E, int S, int P, int32_t *miss, int32_t *n_miss, hipStream_t stream);
+hipError_t launch_cache_plan(void *state, int E, int S, int P, int policy, const int32_t *uniq, const int32_t *n_uniq,
+                             int32_t *hit, int32_t *n_hit, int32_t *miss, int32_t *n_miss, hipStream_t stream);
+// src: device view of the host tier (E experts); dst: the slots; bytes: per-expert bytes of the nine tensors
+hipError_t launch_cache_fetch(const QW &src, const QW &dst, const long bytes[9], const int32_t *miss,
+                              const int32_t *n_miss, const void *state, int E, int S, int workgroups,
+                              hipStream_t stream);
 
 // dsa_index.hip: sparse-attention indexer scores and top-K causal keys
 size_t index_workspace_bytes(int T, int S);

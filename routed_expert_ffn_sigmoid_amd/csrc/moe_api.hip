@@ -9,6 +9,7 @@
 
 #include "../../include/dsa_index.h"
 #include "../../include/moe.h"
+#include "../../include/moe_cache.h"
 #include "kernels.h"
 
 // Scratch memory of moe_forward_static: one copy per device, at its own address on each, held until the process
@@ -116,6 +117,8 @@ moe::FfnParams ffn_params(const moe_shape *s) {
     P.wbits = s->wbits;
     P.act = s->act_dtype;
     P.n_routed_slots = s->E < P.A ? s->E : P.A;
+    P.wslot = nullptr;
+    P.n_wrows = s->E;
     P.invariant = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
     return P;
 }
@@ -245,9 +248,10 @@ int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, in
 namespace {
 
 // moe_forward's argument checks (all but the workspace); MOE_OK when the call may go ahead
+// (y_shared_optional: y_shared = NULL leaves the shared expert out, as moe_forward_cached allows)
 int check_forward(const char *fn, const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
                   const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
-                  float *y_perm, float *y_shared, uint32_t *diag) {
+                  float *y_perm, float *y_shared, uint32_t *diag, bool y_shared_optional = false) {
     int rc = check_shape(fn, s);
     if (rc) return rc;
     REQUIRE_PTR_T(x, "x");
@@ -256,7 +260,8 @@ int check_forward(const char *fn, const moe_shape *s, const void *x, const moe_q
     if (s->I_shared > 0) {
         rc = check_qffn(fn, shared, "shared");
         if (rc) return rc;
-        REQUIRE_PTR_T(y_shared, "y_shared");
+        if (!y_shared_optional) REQUIRE_PTR_T(y_shared, "y_shared");
+        else if (y_shared && !aligned(y_shared, 16)) return fail(MOE_EALIGN, "%s: y_shared is not 16-byte aligned", fn);
     }
     REQUIRE_PTR(offsets, "offsets");
     REQUIRE_PTR_T(perm, "perm");
@@ -278,11 +283,17 @@ int check_forward(const char *fn, const moe_shape *s, const void *x, const moe_q
 }
 
 // the forward kernels, after check_forward and a workspace check
+// (wslot, n_wrows: the routed weights are an expert cache's n_wrows slots, expert e in slot wslot[e])
 int run_forward(const char *fn, const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
                 const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
-                float *y_perm, float *y_shared, uint32_t *diag, void *ws, void *stream) {
+                float *y_perm, float *y_shared, uint32_t *diag, void *ws, void *stream,
+                const int32_t *wslot = nullptr, int n_wrows = 0) {
     if (s->T == 0) return MOE_OK;  // empty batch: no rows to transform
     moe::FfnParams P = ffn_params(s);
+    if (wslot) {
+        P.wslot = wslot;
+        P.n_wrows = n_wrows;
+    }
     P.x = x;
     P.routed = to_qw(routed);
     P.shared = to_qw(s->I_shared > 0 ? shared : nullptr);
@@ -387,6 +398,170 @@ int moe_combine(const moe_shape *s, const float *y_perm, const float *y_shared, 
     if (s->T == 0) return MOE_OK;  // empty batch
     return launch_status(fn, moe::launch_combine(y_perm, y_shared, inv, topk_w, s->T, s->d, s->k, y,
                                                  (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_cache_shape(const char *fn, const moe_cache_shape *c) {
+    if (!c) return fail(MOE_EINVAL, "%s: cache shape is NULL", fn);
+    if (c->E < 1 || c->E > 1024) return fail(MOE_EINVAL, "%s: cache E=%d must be in [1, 1024]", fn, c->E);
+    if (c->slots < 1 || c->slots > c->E) return fail(MOE_EINVAL, "%s: slots=%d must be in [1, E]", fn, c->slots);
+    if (c->pinned < 0 || c->pinned >= c->slots)
+        return fail(MOE_EINVAL, "%s: pinned=%d must be in [0, slots)", fn, c->pinned);
+    if (c->policy != MOE_CACHE_WEIGHTED_LRU && c->policy != MOE_CACHE_LRU)
+        return fail(MOE_EINVAL, "%s: unknown policy %d", fn, c->policy);
+    return MOE_OK;
+}
+
+// Per-expert bytes of the nine tensors, in moe_qffn's order.
+void expert_tensor_bytes(const moe_shape *s, long b[9]) {
+    const long d = s->d, I = s->I, wb = s->wbits, zb = s->wbits == 8 ? 1 : 4;
+    b[0] = b[1] = I * d * wb / 8;
+    b[2] = d * I * wb / 8;
+    b[3] = b[4] = 4 * I;
+    b[5] = 4 * d;
+    b[6] = b[7] = zb * I;
+    b[8] = zb * d;
+}
+
+// Device address of a host-tier pointer: pinned host memory (its device view) or device memory.
+int tier_address(const char *fn, const void *p, const char *name, const void **out) {
+    hipPointerAttribute_t a;
+    const hipError_t err = hipPointerGetAttributes(&a, p);
+    if (err != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of the failed lookup
+        return fail(MOE_EINVAL, "%s: host_tier.%s is neither pinned host memory nor device memory", fn, name);
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer) {
+        *out = a.devicePointer;
+    } else if (a.type == hipMemoryTypeDevice) {
+        *out = p;
+    } else {
+        return fail(MOE_EINVAL, "%s: host_tier.%s is neither pinned host memory nor device memory", fn, name);
+    }
+    return MOE_OK;
+}
+
+constexpr int kFetchWorkgroups = 128;
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_cache_state_size(const moe_cache_shape *c) {
+    if (check_cache_shape("moe_cache_state_size", c) != MOE_OK) return 0;
+    return (moe::cache_state_bytes(c->E, c->slots) + 255) & ~(size_t)255;
+}
+
+int moe_cache_init(const moe_cache_shape *c, const int32_t *pinned_ids, void *state, int32_t *miss, int32_t *n_miss,
+                   void *stream) {
+    const char *fn = "moe_cache_init";
+    int rc = check_cache_shape(fn, c);
+    if (rc) return rc;
+    REQUIRE_PTR(state, "state");
+    REQUIRE_PTR(miss, "miss");
+    REQUIRE_PTR(n_miss, "n_miss");
+    if (c->pinned > 0) {
+        if (!pinned_ids) return fail(MOE_EINVAL, "%s: pinned_ids is NULL", fn);
+        unsigned char seen[1024] = {0};
+        for (int i = 0; i < c->pinned; i++) {
+            const int e = pinned_ids[i];
+            if (e < 0 || e >= c->E) return fail(MOE_EINVAL, "%s: pinned_ids[%d]=%d outside [0, E)", fn, i, e);
+            if (seen[e]) return fail(MOE_EINVAL, "%s: expert %d pinned twice", fn, e);
+            seen[e] = 1;
+        }
+        const hipError_t err = hipMemcpyAsync(miss, pinned_ids, sizeof(int32_t) * (size_t)c->pinned,
+                                              hipMemcpyHostToDevice, (hipStream_t)stream);
+        if (err != hipSuccess) return fail(MOE_EDEVICE, "%s: copy of the pinned ids: %s", fn, hipGetErrorString(err));
+    }
+    hipError_t err = moe::launch_cache_init(state, c->E, c->slots, c->pinned, miss, n_miss, (hipStream_t)stream);
+    if (err == hipSuccess) err = hipStreamSynchronize((hipStream_t)stream);
+    return launch_status(fn, err);
+}
+
+int moe_cache_plan(const moe_cache_shape *c, int32_t T, int32_t k, const int32_t *uniq, const int32_t *n_uniq,
+                   void *state, int32_t *hit, int32_t *n_hit, int32_t *miss, int32_t *n_miss, void *stream) {
+    const char *fn = "moe_cache_plan";
+    int rc = check_cache_shape(fn, c);
+    if (rc) return rc;
+    if (T < 0 || k < 1) return fail(MOE_EINVAL, "%s: T >= 0 and k >= 1", fn);
+    const long need = (long)T * k < c->E ? (long)T * k : c->E;
+    if (c->slots - c->pinned < need)
+        return fail(MOE_EINVAL, "%s: %d unpinned slots cannot take a step of up to %ld missing experts", fn,
+                    c->slots - c->pinned, need);
+    REQUIRE_PTR(uniq, "uniq");
+    REQUIRE_PTR(n_uniq, "n_uniq");
+    REQUIRE_PTR(state, "state");
+    REQUIRE_PTR(hit, "hit");
+    REQUIRE_PTR(n_hit, "n_hit");
+    REQUIRE_PTR(miss, "miss");
+    REQUIRE_PTR(n_miss, "n_miss");
+    return launch_status(fn, moe::launch_cache_plan(state, c->E, c->slots, c->pinned, c->policy, uniq, n_uniq, hit,
+                                                    n_hit, miss, n_miss, (hipStream_t)stream));
+}
+
+int moe_cache_fetch(const moe_shape *s, const moe_cache_shape *c, const moe_qffn *host_tier, const moe_qffn *slots,
+                    const void *state, const int32_t *miss, const int32_t *n_miss, void *stream) {
+    const char *fn = "moe_cache_fetch";
+    int rc = check_shape(fn, s);
+    if (rc) return rc;
+    rc = check_cache_shape(fn, c);
+    if (rc) return rc;
+    if (s->E != c->E) return fail(MOE_EINVAL, "%s: layer E=%d and cache E=%d differ", fn, s->E, c->E);
+    rc = check_qffn(fn, host_tier, "host_tier");
+    if (rc) return rc;
+    rc = check_qffn(fn, slots, "slots");
+    if (rc) return rc;
+    REQUIRE_PTR(state, "state");
+    REQUIRE_PTR(miss, "miss");
+    REQUIRE_PTR(n_miss, "n_miss");
+    const void *hp[9] = {host_tier->q_gate, host_tier->q_up, host_tier->q_down, host_tier->s_gate, host_tier->s_up,
+                         host_tier->s_down, host_tier->z_gate, host_tier->z_up, host_tier->z_down};
+    static const char *names[9] = {"q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down"};
+    const void *dv[9];
+    for (int j = 0; j < 9; j++) {
+        rc = tier_address(fn, hp[j], names[j], &dv[j]);
+        if (rc) return rc;
+    }
+    moe_qffn src = {dv[0], dv[1], dv[2], (const float *)dv[3], (const float *)dv[4], (const float *)dv[5],
+                    dv[6], dv[7], dv[8]};
+    long bytes[9];
+    expert_tensor_bytes(s, bytes);
+    return launch_status(fn, moe::launch_cache_fetch(to_qw(&src), to_qw(slots), bytes, miss, n_miss, state, c->E,
+                                                     c->slots, kFetchWorkgroups, (hipStream_t)stream));
+}
+
+int moe_forward_cached(const moe_shape *s, const moe_cache_shape *c, const void *x, const moe_qffn *slots,
+                       const void *state, const moe_qffn *shared, const int32_t *offsets, const int32_t *perm,
+                       const int32_t *list, const int32_t *n_list, float *y_perm, float *y_shared, uint32_t *diag,
+                       void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_forward_cached";
+    int rc = check_cache_shape(fn, c);
+    if (rc) return rc;
+    rc = check_forward(fn, s, x, slots, shared, offsets, perm, list, n_list, y_perm, y_shared, diag, true);
+    if (rc) return rc;
+    if (s->E != c->E) return fail(MOE_EINVAL, "%s: layer E=%d and cache E=%d differ", fn, s->E, c->E);
+    REQUIRE_PTR(state, "state");
+    rc = check_ws(fn, s, ws, ws_bytes);
+    if (rc) return rc;
+    return run_forward(fn, s, x, slots, shared, offsets, perm, list, n_list, y_perm, y_shared, diag, ws, stream,
+                       moe::cache_slot_map(state, c->E, c->slots), c->slots);
+}
+
+int moe_cache_stats(const moe_cache_shape *c, const void *state, int64_t out[5], int32_t *slot_expert, void *stream) {
+    const char *fn = "moe_cache_stats";
+    int rc = check_cache_shape(fn, c);
+    if (rc) return rc;
+    REQUIRE_PTR(state, "state");
+    if (!out) return fail(MOE_EINVAL, "%s: out is NULL", fn);
+    hipError_t err = hipMemcpyAsync(out, state, 5 * sizeof(int64_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (err == hipSuccess && slot_expert)
+        err = hipMemcpyAsync(slot_expert, (const uint8_t *)state + 64, sizeof(int32_t) * (size_t)c->slots,
+                             hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (err == hipSuccess) err = hipStreamSynchronize((hipStream_t)stream);
+    return launch_status(fn, err);
 }
 
 }  // extern "C"

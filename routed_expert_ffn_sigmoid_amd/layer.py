@@ -76,15 +76,16 @@ def upload_shared(spec: synth.LayerSpec, seed: int, layer: int, device) -> Optio
 
 
 class DeviceLayerWeights:
-    """Router and expert weights of one layer in HBM."""
+    """Router and expert weights of one layer in HBM (routed=False: router and shared expert only, the routed
+    experts living in a host tier)."""
 
-    def __init__(self, spec: synth.LayerSpec, seed: int = 0, layer: int = 0, device="cuda"):
+    def __init__(self, spec: synth.LayerSpec, seed: int = 0, layer: int = 0, device="cuda", routed: bool = True):
         self.spec = spec
         self.W_r = _dev(synth.gen_router(spec, seed, layer), device)
         self.bias = _dev(synth.gen_bias(spec, seed, layer), device)
-        self.routed = upload_routed(spec, seed, layer, device)
+        self.routed = upload_routed(spec, seed, layer, device) if routed else None
         self.shared = upload_shared(spec, seed, layer, device)
-        self.routed_q = self.routed.qffn()
+        self.routed_q = self.routed.qffn() if routed else None
         self.shared_q = self.shared.qffn() if self.shared is not None else None
 
 
@@ -144,3 +145,77 @@ def upload_x(spec: synth.LayerSpec, x: np.ndarray, device="cuda") -> torch.Tenso
     if spec.act == synth.ACT_BF16:
         t = t.view(torch.int16).view(torch.bfloat16)
     return t.to(device)
+
+
+class HostTier(DeviceExperts):
+    """The E routed experts of a layer in pinned host memory, the tier that an expert cache's slots are filled
+    from (read by the GPU over the host link)."""
+
+    def __init__(self, spec: synth.LayerSpec, seed: int = 0, layer: int = 0):
+        super().__init__(spec, spec.E, spec.I, "cpu")
+        for name in ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down"):
+            setattr(self, name, getattr(self, name).pin_memory())
+        for e in range(spec.E):
+            self.set(e, synth.gen_expert(spec, e, seed, layer))
+
+
+class CachedMoeRun(MoeRun):
+    """One layer's expert cache (slots in HBM over a HostTier) and its step: route, permute and plan on the
+    current stream; the missed experts copied on a second stream while the resident ones and the shared expert
+    compute; then the missed experts and the combine."""
+
+    def __init__(self, spec: synth.LayerSpec, T: int, slots: int, pinned=(), policy: int = B.MOE_CACHE_WEIGHTED_LRU,
+                 device="cuda", path: int = B.MOE_PATH_AUTO, copy_stream=None):
+        super().__init__(spec, T, device, path)
+        E = spec.E
+        self.cache = B.make_cache_shape(E, slots, len(pinned), policy)
+        self.pinned = [int(e) for e in pinned]
+        self.state = torch.empty(B.moe_cache_state_size(self.cache), dtype=torch.uint8, device=device)
+        self.slots = DeviceExperts(spec, slots, spec.I, device)
+        self.slots_q = self.slots.qffn()
+        i32 = dict(dtype=torch.int32, device=device)
+        self.hit, self.n_hit = torch.empty(E, **i32), torch.empty(1, **i32)
+        self.miss, self.n_miss = torch.empty(E, **i32), torch.empty(1, **i32)
+        self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device=device)
+
+    def init(self, tier: HostTier, stream=None):
+        """Empties the cache and loads the pinned experts (waits for them)."""
+        B.moe_cache_init(self.cache, self.pinned, self.state, self.miss, self.n_miss, stream=stream)
+        B.moe_cache_fetch(self.shape, self.cache, tier.qffn(), self.slots_q, self.state, self.miss, self.n_miss,
+                          stream=stream)
+        torch.cuda.synchronize()
+
+    def plan(self, stream=None):
+        B.moe_cache_plan(self.cache, self.T, self.spec.k, self.uniq, self.n_uniq, self.state, self.hit, self.n_hit,
+                         self.miss, self.n_miss, stream=stream)
+
+    def step(self, x, W: DeviceLayerWeights, tier: HostTier, tier_q: Optional[B.moe_qffn] = None, fetch_events=None):
+        """One layer call on the current stream (and the copy stream); returns y.  fetch_events: optional pair of
+        timing events recorded on the copy stream around the copy."""
+        cs = torch.cuda.current_stream()
+        tier_q = tier.qffn() if tier_q is None else tier_q
+        self.route(x, W, cs)
+        self.permute(cs)
+        self.plan(cs)
+        planned = torch.cuda.Event()
+        planned.record(cs)
+        self.copy_stream.wait_event(planned)
+        if fetch_events is not None:
+            fetch_events[0].record(self.copy_stream)
+        B.moe_cache_fetch(self.shape, self.cache, tier_q, self.slots_q, self.state, self.miss, self.n_miss,
+                          stream=self.copy_stream)
+        if fetch_events is not None:
+            fetch_events[1].record(self.copy_stream)
+        fetched = torch.cuda.Event()
+        fetched.record(self.copy_stream)
+        B.moe_forward_cached(self.shape, self.cache, x, self.slots_q, self.state, W.shared_q, self.offsets,
+                             self.perm, self.hit, self.n_hit, self.y_perm, self.y_shared, self.diag, self.ws,
+                             stream=cs)
+        cs.wait_event(fetched)
+        B.moe_forward_cached(self.shape, self.cache, x, self.slots_q, self.state, W.shared_q, self.offsets,
+                             self.perm, self.miss, self.n_miss, self.y_perm, None, self.diag, self.ws, stream=cs)
+        self.combine(cs)
+        return self.y
+
+    def stats(self, want_slots: bool = False):
+        return B.moe_cache_stats(self.cache, self.state, want_slots)

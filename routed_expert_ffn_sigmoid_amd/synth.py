@@ -143,6 +143,22 @@ def gen_x(spec: LayerSpec, T: int, seed: int = 0, batch: int = 0) -> np.ndarray:
     return x
 
 
+def gen_x_correlated(spec: LayerSpec, n: int, rho: float, seed: int = 0, batch: int = 0) -> np.ndarray:
+    """n consecutive token activations [n][d] as a first-order autoregressive sequence, x_0 ~ N(0, 1) and
+    x_t = rho x_{t-1} + sqrt(1 - rho^2) e_t with e_t ~ N(0, 1) (every x_t is N(0, 1)): neighbouring tokens
+    with similar activations, hence similar experts.  fp32, or bf16 bits like gen_x."""
+    rng = _rng(seed, spec.family, 0, _T_X, (1 << 16) + batch)
+    e = rng.standard_normal((n, spec.d), dtype=np.float32)
+    x = np.empty_like(e)
+    c = np.float32(math.sqrt(1.0 - rho * rho))
+    x[0] = e[0]
+    for t in range(1, n):
+        x[t] = np.float32(rho) * x[t - 1] + c * e[t]
+    if spec.act == ACT_BF16:
+        return round_to_bf16_bits(x).reshape(n, spec.d)
+    return x
+
+
 def gen_router(spec: LayerSpec, seed: int = 0, layer: int = 0) -> np.ndarray:
     """W_r [d][E] fp32, entries N(0, 0.02^2)."""
     rng = _rng(seed, _ROUTER_FAMILY.get(spec.family, spec.family), layer, _T_WR)

@@ -263,3 +263,61 @@ def test_index_shape_checked():
     assert "k is NULL" in str(ei.value)
     B.dsa_index_topk(B.dsa_index_shape(T=0, S=100, H=64, D=128, K=16, pos0=0), None, None, FAKE, FAKE, None, None,
                      FAKE, HUGE_WS, stream=0)
+
+
+def test_cache_shape_checked():
+    assert B.moe_cache_state_size(B.make_cache_shape(256, 32, 4)) >= 64 + 4 * (3 * 32 + 256)
+    for bad in (B.make_cache_shape(0, 1), B.make_cache_shape(2048, 32), B.make_cache_shape(8, 9),
+                B.make_cache_shape(8, 0), B.make_cache_shape(8, 4, 4), B.make_cache_shape(8, 4, -1),
+                B.make_cache_shape(8, 4, 0, 2)):
+        assert B.moe_cache_state_size(bad) == 0
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_cache_plan(bad, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+        assert ei.value.code == B.MOE_EINVAL
+
+
+def test_cache_plan_needs_slots_for_a_step():
+    c = B.make_cache_shape(256, 36, 4)  # 32 unpinned slots
+    args = [FAKE] * 7
+    B.lib()  # a step of T*k <= 32 experts would be accepted (not run here: it would enqueue)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_cache_plan(c, 5, 8, *args, stream=0)  # up to 40 missing experts
+    assert ei.value.code == B.MOE_EINVAL and "unpinned slots" in str(ei.value)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_cache_plan(c, 4, 8, FAKE, None, *args[2:], stream=0)  # n_uniq NULL
+    assert ei.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_cache_plan(c, 4, 8, FAKE + 4, *args[1:], stream=0)  # misaligned
+    assert ei.value.code == B.MOE_EALIGN
+
+
+def test_cache_init_checks_pinned_ids_on_the_host():
+    c = B.make_cache_shape(16, 8, 3)
+    for ids in ([1, 2, 2], [1, 2, 16], [-1, 2, 3]):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_cache_init(c, ids, FAKE, FAKE, FAKE, stream=0)
+        assert ei.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_cache_init(c, None, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.code == B.MOE_EINVAL
+
+
+def test_cached_forward_and_fetch_check_shapes():
+    s = shape(E=8, k=2)
+    q = B.moe_qffn(*([FAKE] * 9))
+    with pytest.raises(B.MoeError) as ei:  # cache E differs from the layer's
+        B.moe_cache_fetch(s, B.make_cache_shape(16, 4), q, q, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_cached(s, B.make_cache_shape(16, 4), FAKE, q, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, None, FAKE, 1 << 30, stream=0)
+    assert ei.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as ei:  # state NULL
+        B.moe_forward_cached(s, B.make_cache_shape(8, 4), FAKE, q, None, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, None, FAKE, 1 << 30, stream=0)
+    assert ei.value.code == B.MOE_EINVAL
+    sh = shape(E=8, k=2, I_shared=256)
+    with pytest.raises(B.MoeError) as ei:  # the shared weights stay required with y_shared = NULL
+        B.moe_forward_cached(sh, B.make_cache_shape(8, 4), FAKE, q, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, None, FAKE, 1 << 30, stream=0)
+    assert ei.value.code == B.MOE_EINVAL
