@@ -1,12 +1,13 @@
 """MoE-layer forward benchmark on one MI355X.
 
-One step = one pass of the whole layer (moe_route -> moe_permute ->
-moe_forward -> moe_combine) over one batch of seeded synthetic tokens, with
+One step = one pass of the whole layer (moe_route_permute, i.e. the router
+and the permutation -> moe_forward -> moe_combine) over one batch of seeded
+synthetic tokens, with
 all inputs already resident in HBM.  Decode workloads rotate over several
 resident layers and a pool of activation batches so that neither the 256 MB
 Infinity Cache nor L2 holds the expert weights between steps.
 
-Each step of the rotation is captured once as a HIP graph (the four ABI
+Each step of the rotation is captured once as a HIP graph (the three ABI
 calls) and replayed, so host launch overhead does not enter the timing.
 
 Prints ONE JSON line (the driver's contract).  The top level is the headline
@@ -228,6 +229,11 @@ def measure(spec, T, args, dev):
         for i in range(cycle):
             x, W = operands(i)
             runs[i].route(x, W)
+    rp_graph = torch.cuda.CUDAGraph()  # router and permutation in one call
+    with torch.cuda.graph(rp_graph, stream=side):
+        for i in range(cycle):
+            x, W = operands(i)
+            runs[i].route_permute(x, W)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -266,6 +272,13 @@ def measure(spec, T, args, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     route_us = e0.elapsed_time(e1) * 1e3 / n_fwd
+    rp_graph.replay()
+    e0.record(stream)
+    for _ in range(fwd_reps):
+        rp_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rp_us = e0.elapsed_time(e1) * 1e3 / n_fwd
 
     # distribution of the step time: each step's graph replay between its own pair of events (a separate
     # pass after the timed one, so the events do not enter the reported throughput)
@@ -315,13 +328,14 @@ def measure(spec, T, args, dev):
                    "mean_unique_experts": round(float(np.mean([n_uniq[i % cycle] for i in steps_idx])), 2),
                    "assignments_per_unique_expert": round(T * spec.k / float(np.mean(n_uniq)), 2),
                    "permute_us_alone": round(perm_us, 2), "route_us_alone": round(route_us, 2),
+                   "route_permute_us_alone": round(rp_us, 2),
                    "router": args.router, "capacity_factor": args.capacity_factor,
-                   "timing": "HIP graph per step (the four ABI calls), replayed",
+                   "timing": "HIP graph per step (moe_route_permute, moe_forward, moe_combine), replayed",
                    "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
                    "path": args.path, "batch_invariant": bool(args.invariant), "setup_s": round(setup_s, 1)},
         "roofline": roof,
     }
-    del runs, step_graphs, fwd_graph, perm_graph, route_graph, layers, pool
+    del runs, step_graphs, fwd_graph, perm_graph, route_graph, rp_graph, layers, pool
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res

@@ -29,7 +29,10 @@
  *   - `ws` is a caller-owned device workspace of at least
  *     moe_workspace_size(shape) bytes, 256-byte aligned.  Calls that share a
  *     workspace must be ordered (same stream); concurrent calls need their
- *     own workspaces.  Workspace contents need no initialisation.
+ *     own workspaces.  Its first 256 bytes hold counters: they must be zero
+ *     before the workspace's first use (allocate it zeroed, or call
+ *     moe_workspace_clear once), and every call leaves them zero.  The rest
+ *     needs no initialisation.
  *   - Return value: MOE_OK (0) or a negative MOE_E* code.  All arguments
  *     are validated before anything is enqueued, so a failed call leaves
  *     every output untouched.  moe_last_error() gives a message for the
@@ -172,6 +175,9 @@ typedef struct moe_qffn {
  */
 MOE_API size_t moe_workspace_size(const moe_shape *shape);
 
+/* Zeroes the workspace's counters (its first 256 bytes) with a kernel on `stream`; ws_bytes >= 256. */
+MOE_API int moe_workspace_clear(void *ws, size_t ws_bytes, void *stream);
+
 /*
  * Router ("25GB 内存跑 744B GLM-5.2 模型" page, sections 三.1 and 四.3).
  *   z[t][e]   = sum_i x[t][i] * W_r[i][e]            (fp64 accumulation)
@@ -209,6 +215,19 @@ MOE_API int moe_route(const moe_shape *shape, const void *x, const float *W_r, c
  */
 MOE_API int moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t *counts, int32_t *offsets, int32_t *perm,
                 int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_route followed by moe_permute, with the same arguments, outputs and
+ * checks as the two calls.  For decode batches (T <= 4, the top-k routers
+ * without capacity) the permutation runs inside the selection's launch: the
+ * workgroup that selects last (one per token) sorts the assignments, so the
+ * permutation costs no launch of its own.  The outputs have the same bits as
+ * the two calls'.
+ */
+MOE_API int moe_route_permute(const moe_shape *shape, const void *x, const float *W_r, const float *bias,
+                              int32_t *topk_idx, float *topk_w, double *gap, int32_t *counts, int32_t *offsets,
+                              int32_t *perm, int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws,
+                              size_t ws_bytes, void *stream);
 
 /*
  * Routed and shared SwiGLU experts (walk-through page, section 3.4):

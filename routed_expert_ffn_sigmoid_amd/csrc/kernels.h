@@ -45,9 +45,17 @@ __device__ __forceinline__ int weight_row(const FfnParams &P, int e) {
 // tokens per expert for expert choice)
 const char *router_unsupported(int T, int d, int E, int act, bool inv);
 size_t router_workspace_bytes(int T, int d, int E, bool inv, int k, int router, bool capacity);
+// The permutation's outputs, for the router's fused form.
+struct PermOut {
+    int32_t *counts, *offsets, *perm, *inv, *uniq, *n_uniq;
+};
+// true when the selection's launch also takes the permutation (given PermOut): T <= 4, top-k routers without
+// capacity
+bool router_fused(int T, int E, bool inv, int router, int C);
+// ticket: a zeroed counter the fused form uses and leaves zeroed (nullptr: never fuse); po: also sort (fused form)
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
                          float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
-                         hipStream_t stream);
+                         hipStream_t stream, unsigned *ticket, const PermOut *po);
 
 // permute.hip
 size_t permute_lds_bytes(int E);

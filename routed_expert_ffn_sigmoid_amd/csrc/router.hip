@@ -16,6 +16,7 @@
 // unless two selection scores agree to ~1e-16.
 #include "common.h"
 #include "kernels.h"
+#include "permute_dev.h"
 #include "topk.h"
 
 #include <type_traits>
@@ -151,6 +152,12 @@ constexpr int RSK_EB = 32;                // experts per workgroup column block
 constexpr int RSK_WGS = 256;              // workgroups aimed at
 constexpr int RSK_MAXR = 12;              // W_r rows per thread (1024 threads: 128 VGPRs each)
 constexpr int RSK_MAX_ROWS = 2048;        // rows per block (LDS holds RS_TMAX x rows activations)
+// The selection kernel's permutation (moe_route_permute at T <= RS_TMAX): when perm is set, the last of the T
+// workgroups (a ticket from a zeroed counter, left zeroed) sorts the assignments after every token's choice.
+struct FusedPerm {
+    unsigned *ticket;
+    int32_t *counts, *offsets, *perm, *inv, *uniq, *n_uniq;  // perm = nullptr: no permutation
+};
 
 // Sum of a over the lanes whose index is congruent to this lane's modulo nq (a power of two <= 64), every
 // lane getting the result, in a fixed order: neighbours and pairs inside quads (DPP quad permutes), lanes 4
@@ -187,6 +194,201 @@ __device__ __forceinline__ double sum_congruent(double a, int nq) {
     if (nq <= 16) a = swap_add_f64(a, true);
     if (nq <= 32) a = swap_add_f64(a, false);
     return a;
+}
+
+// (v, id) is better than (v2, id2): larger score, then lower id
+__device__ __forceinline__ bool better(double v, int id, double v2, int id2) {
+    return v > v2 || (v == v2 && id < id2);
+}
+
+// One DPP step of a wave-wide argmax of (v, id): take the partner's pair when it is better.
+// bound_ctrl off and old = own value: lanes without a partner keep what they have.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(double &v, int &id) {
+    const int2 b = __builtin_bit_cast(int2, v);
+    const int lo = __builtin_amdgcn_update_dpp(b.x, b.x, CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(b.y, b.y, CTRL, ROW_MASK, 0xF, false);
+    const int oid = __builtin_amdgcn_update_dpp(id, id, CTRL, ROW_MASK, 0xF, false);
+    const double ov = __builtin_bit_cast(double, make_int2(lo, hi));
+    if (better(ov, oid, v, id)) {
+        v = ov;
+        id = oid;
+    }
+}
+
+// Wave-wide argmax (larger v, then lower id); the result is returned to every lane.
+__device__ __forceinline__ void wave_argmax(double &v, int &id) {
+    argmax_step<0xB1, 0xF>(v, id);   // quad_perm [1,0,3,2]
+    argmax_step<0x4E, 0xF>(v, id);   // quad_perm [2,3,0,1]
+    argmax_step<0x141, 0xF>(v, id);  // row_half_mirror
+    argmax_step<0x140, 0xF>(v, id);  // row_mirror: lane 15 of each row holds the row's best
+    argmax_step<0x142, 0xA>(v, id);  // row_bcast15: rows 1 and 3 take the last lane of rows 0 and 2
+    argmax_step<0x143, 0xC>(v, id);  // row_bcast31: rows 2 and 3 take lane 31
+    const int2 b = __builtin_bit_cast(int2, v);
+    v = __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(b.x, 63), __builtin_amdgcn_readlane(b.y, 63)));
+    id = __builtin_amdgcn_readlane(id, 63);
+}
+
+// One workgroup (1024 threads) per token.  Thread (e, g) sums the splits s = g, g+4, ... of expert e
+// (fixed order); thread (e, 0) adds the four groups in order and takes sigmoid and bias (one expert per
+// thread, so the code holds one copy of exp and the sigmoids run in parallel); then the first wavefront
+// picks the top k+1.  Each lane holds EJ experts (e = lane + 64 j), sorts them once, and exposes its
+// best unchosen one; each round is one wave-wide argmax and the winning lane moves to its next.
+constexpr int RSEL_THREADS = 1024;
+constexpr int RSEL_LOADS = 8;
+
+// mode 0: sigmoid scores, selection by s + bias.  mode 1: softmax gate, selection by the logits and weights
+// lambda * exp(z_j - z_max) / sum over the selected (the max-subtracted softmax renormalised over them).
+// Token t's selection by a workgroup of RSEL_THREADS threads (all of them call it); zs: LDS of 4 E doubles.
+// keys (optional, LDS or global): receives idx[t][0 .. k).
+template <int EJ>
+__device__ inline void select_token(const double *__restrict__ part, int nsplit, int T, int E, int k,
+                                    const float *__restrict__ bias, float lambda, int mode, int t,
+                                    int32_t *__restrict__ idx, float *__restrict__ w, double *__restrict__ gap,
+                                    double *zs, int32_t *keys) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ept = (E + 255) / 256;  // experts per thread column
+    const rsrc_t psrc = make_rsrc(part, (uint32_t)((long)nsplit * T * E * 8));
+    const float bz = (mode == 0 && tid < E) ? bias[tid] : 0.f;  // requested now, used after the sums (E <= RSEL_THREADS)
+    for (int j = 0; j < ept; j++) {
+        const int e = (tid & 255) + 256 * j;
+        const int g = tid >> 8;
+        if (e >= E) continue;
+        double z = 0.0;
+        int sp = g;
+        // batches of RSEL_LOADS independent loads, added in split order
+        for (; sp < nsplit; sp += 4 * RSEL_LOADS) {
+            double a[RSEL_LOADS];
+#pragma unroll
+            for (int m = 0; m < RSEL_LOADS; m++) {
+                const int s2 = sp + 4 * m;
+                a[m] = buf_load_f64(psrc, s2 < nsplit ? (uint32_t)((((long)s2 * T + t) * E + e) * 8) : kOOB);
+            }
+#pragma unroll
+            for (int m = 0; m < RSEL_LOADS; m++) z += a[m];
+        }
+        zs[g * E + e] = z;
+    }
+    __syncthreads();
+    // s and sel of expert e replace its first two partial sums (each thread touches only its own entries)
+    if (tid < E) {
+        const int e = tid;
+        const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
+        if (mode == 0) {
+            const double sv = 1.0 / (1.0 + exp(-z));
+            zs[e] = sv;
+            zs[E + e] = sv + (double)bz;
+        } else {
+            zs[e] = z;
+            zs[E + e] = z;
+        }
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    // this lane's candidates, sorted best first
+    double cv[EJ], cs[EJ];
+    int ci[EJ];
+#pragma unroll
+    for (int j = 0; j < EJ; j++) {
+        const int e = lane + 64 * j;
+        cv[j] = -INFINITY;
+        cs[j] = 0.0;
+        ci[j] = 0x7fffffff;
+        if (e < E) {
+            cs[j] = zs[e];
+            cv[j] = zs[E + e];
+            ci[j] = e;
+        }
+    }
+#pragma unroll
+    for (int a2 = 0; a2 < EJ; a2++)  // insertion sort, fully unrolled (EJ <= 16)
+#pragma unroll
+        for (int b2 = EJ - 1; b2 > a2; b2--)
+            if (better(cv[b2], ci[b2], cv[b2 - 1], ci[b2 - 1])) {
+                const double tv = cv[b2], ts = cs[b2];
+                const int ti = ci[b2];
+                cv[b2] = cv[b2 - 1];
+                cs[b2] = cs[b2 - 1];
+                ci[b2] = ci[b2 - 1];
+                cv[b2 - 1] = tv;
+                cs[b2 - 1] = ts;
+                ci[b2 - 1] = ti;
+            }
+    int head = 0;  // next unchosen candidate of this lane
+    double sum_s = 0.0, prev_v = 0.0, top_z = 0.0;
+    double my_s = 0.0;  // lane r < k keeps the score of choice r
+    int my_id = 0;
+    const int rounds = (k < E) ? k + 1 : k;
+    for (int r = 0; r < rounds; r++) {
+        double hv = -INFINITY, hs = 0.0;
+        int hid = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < EJ; j++)
+            if (head == j) {
+                hv = cv[j];
+                hs = cs[j];
+                hid = ci[j];
+            }
+        double bv = hv;
+        int bid = hid;
+        wave_argmax(bv, bid);
+        const int wl = bid & 63;  // lane that owns the winner
+        const int2 sb = __builtin_bit_cast(int2, hs);
+        const double bs = __builtin_bit_cast(
+            double, make_int2(__builtin_amdgcn_readlane(sb.x, wl), __builtin_amdgcn_readlane(sb.y, wl)));
+        if (r < k) {
+            if (lane == wl) head++;
+            // the weight's numerator: the sigmoid score, or exp(z - z_max) of the softmax gate
+            if (mode == 1 && r == 0) top_z = bs;
+            const double u = mode == 0 ? bs : exp(bs - top_z);
+            sum_s += u;
+            if (lane == r) {
+                my_s = u;
+                my_id = bid;
+            }
+            prev_v = bv;
+        } else if (lane == 0 && gap) {
+            gap[t] = prev_v - bv;
+        }
+    }
+    if (lane == 0 && gap && k >= E) gap[t] = INFINITY;
+    if (lane < k) {
+        idx[(long)t * k + lane] = my_id;
+        w[(long)t * k + lane] = (float)((double)lambda * my_s / sum_s);
+        if (keys) keys[t * k + lane] = my_id;
+    }
+}
+
+// One workgroup per token.  With F.perm set (T <= RS_TMAX), the workgroup that selects last also sorts the
+// assignments: directly from LDS when T = 1, else after a ticket (one agent-scope fence per workgroup publishes its
+// choices; the last one's fence makes the others' visible to it).
+template <int EJ, int MODE>
+__global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const double *__restrict__ part, int nsplit,
+                                                                     int T, int E, int k,
+                                                                     const float *__restrict__ bias, float lambda,
+                                                                     int32_t *__restrict__ idx,
+                                                                     float *__restrict__ w,
+                                                                     double *__restrict__ gap, FusedPerm F) {
+    extern __shared__ double zs[];  // [4][E], then (with F.perm) the sort's LDS and this token's k ids
+    int32_t *psm = (int32_t *)(zs + 4 * E);
+    int32_t *keys = psm + (F.perm ? 18 * E + 1 : 0);
+    select_token<EJ>(part, nsplit, T, E, k, bias, lambda, MODE, blockIdx.x, idx, w, gap, zs, F.perm ? keys : nullptr);
+    if (!F.perm) return;
+    __syncthreads();
+    if (T > 1) {
+        __shared__ int s_last;
+        if (threadIdx.x == 0) {
+            __threadfence();
+            s_last = atomicAdd(F.ticket, 1u) == (unsigned)T - 1u;
+            if (s_last) {
+                __threadfence();
+                atomicExch(F.ticket, 0u);
+            }
+        }
+        __syncthreads();
+        if (!s_last) return;
+    }
+    permute_block(T > 1 ? idx : keys, T * k, E, F.counts, F.offsets, F.perm, F.inv, F.uniq, F.n_uniq, psm);
 }
 
 // grid: (row blocks, expert column blocks, token groups of RS_TMAX); each token's arithmetic depends only on
@@ -262,170 +464,6 @@ __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const
             part[((long)blockIdx.x * T + tg + t) * E + e0 + tid] = z;
         }
         __syncthreads();
-    }
-}
-
-// (v, id) is better than (v2, id2): larger score, then lower id
-__device__ __forceinline__ bool better(double v, int id, double v2, int id2) {
-    return v > v2 || (v == v2 && id < id2);
-}
-
-// One DPP step of a wave-wide argmax of (v, id): take the partner's pair when it is better.
-// bound_ctrl off and old = own value: lanes without a partner keep what they have.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void argmax_step(double &v, int &id) {
-    const int2 b = __builtin_bit_cast(int2, v);
-    const int lo = __builtin_amdgcn_update_dpp(b.x, b.x, CTRL, ROW_MASK, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(b.y, b.y, CTRL, ROW_MASK, 0xF, false);
-    const int oid = __builtin_amdgcn_update_dpp(id, id, CTRL, ROW_MASK, 0xF, false);
-    const double ov = __builtin_bit_cast(double, make_int2(lo, hi));
-    if (better(ov, oid, v, id)) {
-        v = ov;
-        id = oid;
-    }
-}
-
-// Wave-wide argmax (larger v, then lower id); the result is returned to every lane.
-__device__ __forceinline__ void wave_argmax(double &v, int &id) {
-    argmax_step<0xB1, 0xF>(v, id);   // quad_perm [1,0,3,2]
-    argmax_step<0x4E, 0xF>(v, id);   // quad_perm [2,3,0,1]
-    argmax_step<0x141, 0xF>(v, id);  // row_half_mirror
-    argmax_step<0x140, 0xF>(v, id);  // row_mirror: lane 15 of each row holds the row's best
-    argmax_step<0x142, 0xA>(v, id);  // row_bcast15: rows 1 and 3 take the last lane of rows 0 and 2
-    argmax_step<0x143, 0xC>(v, id);  // row_bcast31: rows 2 and 3 take lane 31
-    const int2 b = __builtin_bit_cast(int2, v);
-    v = __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(b.x, 63), __builtin_amdgcn_readlane(b.y, 63)));
-    id = __builtin_amdgcn_readlane(id, 63);
-}
-
-// One workgroup (1024 threads) per token.  Thread (e, g) sums the splits s = g, g+4, ... of expert e
-// (fixed order); thread (e, 0) adds the four groups in order and takes sigmoid and bias (one expert per
-// thread, so the code holds one copy of exp and the sigmoids run in parallel); then the first wavefront
-// picks the top k+1.  Each lane holds EJ experts (e = lane + 64 j), sorts them once, and exposes its
-// best unchosen one; each round is one wave-wide argmax and the winning lane moves to its next.
-constexpr int RSEL_THREADS = 1024;
-constexpr int RSEL_LOADS = 8;
-
-// MODE 0: sigmoid scores, selection by s + bias.  MODE 1: softmax gate, selection by the logits and weights
-// lambda * exp(z_j - z_max) / sum over the selected (the max-subtracted softmax renormalised over them).
-template <int EJ, int MODE>
-__global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const double *__restrict__ part, int nsplit,
-                                                                     int T, int E, int k,
-                                                                     const float *__restrict__ bias, float lambda,
-                                                                     int32_t *__restrict__ idx,
-                                                                     float *__restrict__ w,
-                                                                     double *__restrict__ gap) {
-    extern __shared__ double zs[];  // [4][E]
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int ept = (E + 255) / 256;  // experts per thread column
-    const rsrc_t psrc = make_rsrc(part, (uint32_t)((long)nsplit * T * E * 8));
-    const float bz = (MODE == 0 && tid < E) ? bias[tid] : 0.f;  // requested now, used after the sums (E <= RSEL_THREADS)
-    for (int j = 0; j < ept; j++) {
-        const int e = (tid & 255) + 256 * j;
-        const int g = tid >> 8;
-        if (e >= E) continue;
-        double z = 0.0;
-        int sp = g;
-        // batches of RSEL_LOADS independent loads, added in split order
-        for (; sp < nsplit; sp += 4 * RSEL_LOADS) {
-            double a[RSEL_LOADS];
-#pragma unroll
-            for (int m = 0; m < RSEL_LOADS; m++) {
-                const int s2 = sp + 4 * m;
-                a[m] = buf_load_f64(psrc, s2 < nsplit ? (uint32_t)((((long)s2 * T + t) * E + e) * 8) : kOOB);
-            }
-#pragma unroll
-            for (int m = 0; m < RSEL_LOADS; m++) z += a[m];
-        }
-        zs[g * E + e] = z;
-    }
-    __syncthreads();
-    // s and sel of expert e replace its first two partial sums (each thread touches only its own entries)
-    if (tid < E) {
-        const int e = tid;
-        const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
-        if (MODE == 0) {
-            const double sv = 1.0 / (1.0 + exp(-z));
-            zs[e] = sv;
-            zs[E + e] = sv + (double)bz;
-        } else {
-            zs[e] = z;
-            zs[E + e] = z;
-        }
-    }
-    __syncthreads();
-    if (tid >= 64) return;
-    // this lane's candidates, sorted best first
-    double cv[EJ], cs[EJ];
-    int ci[EJ];
-#pragma unroll
-    for (int j = 0; j < EJ; j++) {
-        const int e = lane + 64 * j;
-        cv[j] = -INFINITY;
-        cs[j] = 0.0;
-        ci[j] = 0x7fffffff;
-        if (e < E) {
-            cs[j] = zs[e];
-            cv[j] = zs[E + e];
-            ci[j] = e;
-        }
-    }
-#pragma unroll
-    for (int a2 = 0; a2 < EJ; a2++)  // insertion sort, fully unrolled (EJ <= 16)
-#pragma unroll
-        for (int b2 = EJ - 1; b2 > a2; b2--)
-            if (better(cv[b2], ci[b2], cv[b2 - 1], ci[b2 - 1])) {
-                const double tv = cv[b2], ts = cs[b2];
-                const int ti = ci[b2];
-                cv[b2] = cv[b2 - 1];
-                cs[b2] = cs[b2 - 1];
-                ci[b2] = ci[b2 - 1];
-                cv[b2 - 1] = tv;
-                cs[b2 - 1] = ts;
-                ci[b2 - 1] = ti;
-            }
-    int head = 0;  // next unchosen candidate of this lane
-    double sum_s = 0.0, prev_v = 0.0, top_z = 0.0;
-    double my_s = 0.0;  // lane r < k keeps the score of choice r
-    int my_id = 0;
-    const int rounds = (k < E) ? k + 1 : k;
-    for (int r = 0; r < rounds; r++) {
-        double hv = -INFINITY, hs = 0.0;
-        int hid = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < EJ; j++)
-            if (head == j) {
-                hv = cv[j];
-                hs = cs[j];
-                hid = ci[j];
-            }
-        double bv = hv;
-        int bid = hid;
-        wave_argmax(bv, bid);
-        const int wl = bid & 63;  // lane that owns the winner
-        const int2 sb = __builtin_bit_cast(int2, hs);
-        const double bs = __builtin_bit_cast(
-            double, make_int2(__builtin_amdgcn_readlane(sb.x, wl), __builtin_amdgcn_readlane(sb.y, wl)));
-        if (r < k) {
-            if (lane == wl) head++;
-            // the weight's numerator: the sigmoid score, or exp(z - z_max) of the softmax gate
-            if (MODE == 1 && r == 0) top_z = bs;
-            const double u = MODE == 0 ? bs : exp(bs - top_z);
-            sum_s += u;
-            if (lane == r) {
-                my_s = u;
-                my_id = bid;
-            }
-            prev_v = bv;
-        } else if (lane == 0 && gap) {
-            gap[t] = prev_v - bv;
-        }
-    }
-    if (lane == 0 && gap && k >= E) gap[t] = INFINITY;
-    if (lane < k) {
-        idx[(long)t * k + lane] = my_id;
-        w[(long)t * k + lane] = (float)((double)lambda * my_s / sum_s);
     }
 }
 
@@ -583,9 +621,15 @@ size_t router_workspace_bytes(int T, int d, int E, bool inv, int k, int router, 
            variant_bytes(T, E, k, router, capacity);
 }
 
+bool router_fused(int T, int E, bool inv, int router, int C) {
+    (void)E;
+    (void)inv;
+    return T >= 1 && T <= RS_TMAX && router != 2 && C <= 0;
+}
+
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
                          float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
-                         hipStream_t stream) {
+                         hipStream_t stream, unsigned *ticket, const PermOut *po) {
     double *part = (double *)ws;
     char *vws = (char *)ws + r_al256((size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double));
     int nsplit;
@@ -617,18 +661,24 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
         hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(EC_THREADS), 0, stream, pT, T, E, C, lambda, idx, w, gap);
         return hipGetLastError();
     }
-    const size_t lds = 4 * E * sizeof(double);
+    const bool fuse = ticket && po && router_fused(T, E, inv, router, C);
+    FusedPerm F{};
+    size_t lds = 4 * E * sizeof(double);
+    if (fuse) {
+        F = FusedPerm{ticket, po->counts, po->offsets, po->perm, po->inv, po->uniq, po->n_uniq};
+        lds += sizeof(int32_t) * ((size_t)18 * E + 1 + (size_t)k);
+    }
     auto select = [&](auto mode) {
         constexpr int M = decltype(mode)::value;
         if (E <= 64)
             hipLaunchKernelGGL((router_select_kernel<1, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
-                               E, k, bias, lambda, idx, w, gap);
+                               E, k, bias, lambda, idx, w, gap, F);
         else if (E <= 256)
             hipLaunchKernelGGL((router_select_kernel<4, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
-                               E, k, bias, lambda, idx, w, gap);
+                               E, k, bias, lambda, idx, w, gap, F);
         else
             hipLaunchKernelGGL((router_select_kernel<16, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit,
-                               T, E, k, bias, lambda, idx, w, gap);
+                               T, E, k, bias, lambda, idx, w, gap, F);
     };
     if (router == 1)
         select(std::integral_constant<int, 1>{});

@@ -113,7 +113,8 @@ class MoeRun:
         self.y_perm = torch.empty((A, d), dtype=torch.float32, device=device)
         self.y_shared = torch.empty((T, d), dtype=torch.float32, device=device) if spec.I_shared > 0 else None
         self.y = torch.empty((T, d), dtype=torch.float32, device=device)
-        self.ws = torch.empty(max(B.moe_workspace_size(self.shape), 256), dtype=torch.uint8, device=device)
+        # zeroed: the workspace's first 256 bytes are counters that must start at zero (the calls keep them there)
+        self.ws = torch.zeros(max(B.moe_workspace_size(self.shape), 256), dtype=torch.uint8, device=device)
         # moe_forward's diagnostic counters (uint32 in the ABI), added to by every forward call
         self.diag = torch.zeros(B.MOE_DIAG_COUNT, dtype=torch.int32, device=device)
 
@@ -131,9 +132,12 @@ class MoeRun:
     def combine(self, stream=None):
         B.moe_combine(self.shape, self.y_perm, self.y_shared, self.inv, self.w, self.y, stream=stream)
 
+    def route_permute(self, x, W: DeviceLayerWeights, stream=None):
+        B.moe_route_permute(self.shape, x, W.W_r, W.bias, self.idx, self.w, self.gap, self.counts, self.offsets,
+                            self.perm, self.inv, self.uniq, self.n_uniq, self.ws, stream=stream)
+
     def run(self, x, W: DeviceLayerWeights, stream=None):
-        self.route(x, W, stream)
-        self.permute(stream)
+        self.route_permute(x, W, stream)
         self.forward(x, W, stream)
         self.combine(stream)
         return self.y

@@ -321,3 +321,29 @@ def test_cached_forward_and_fetch_check_shapes():
         B.moe_forward_cached(sh, B.make_cache_shape(8, 4), FAKE, q, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                              None, None, FAKE, 1 << 30, stream=0)
     assert ei.value.code == B.MOE_EINVAL
+
+
+def test_route_permute_and_workspace_clear_checks():
+    s = shape(T=2)
+    need = B.moe_workspace_size(s)
+    assert need >= 256 + 8 * 1024  # the counters, then the calls' areas
+    args = dict(x=FAKE, W_r=FAKE, bias=FAKE, topk_idx=FAKE, topk_w=FAKE, gap=None, counts=FAKE, offsets=FAKE,
+                perm=FAKE, inv=FAKE, uniq=FAKE, n_uniq=FAKE, ws=FAKE)
+    for miss in ("counts", "offsets", "perm", "inv", "uniq", "n_uniq", "W_r", "topk_idx"):
+        a = dict(args)
+        a[miss] = None
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_route_permute(s, **a, ws_bytes=need, stream=0)
+        assert ei.value.code == B.MOE_EINVAL, miss
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route_permute(s, **args, ws_bytes=need - 1, stream=0)
+    assert ei.value.code == B.MOE_EWORKSPACE
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_workspace_clear(None, 1024, stream=0)
+    assert ei.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_workspace_clear(FAKE + 16, 1024, stream=0)
+    assert ei.value.code == B.MOE_EALIGN
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_workspace_clear(FAKE, 255, stream=0)
+    assert ei.value.code == B.MOE_EWORKSPACE
