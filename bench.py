@@ -18,7 +18,10 @@ stream the kernels run on around replays of a graph of moe_forward calls.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 With the default workload, `additional_workloads` holds the same figures for
 the 256-expert layer at T = 1 (HBM roof) and at T = 8192 with int4 weights
-(MFMA roof), each timed the same way in the same run.
+(MFMA roof), each timed the same way in the same run, then the residency
+tier (decode from pinned host memory behind a per-layer HBM expert cache,
+`--tiered`) and the sparse-attention indexer at decode and prefill
+(`--index`).
 """
 from __future__ import annotations
 
@@ -391,7 +394,7 @@ def measure_index(args, dev):
             "steps": reps * pool, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "int8-qk/f64-score", "data": "synthetic (seeded)",
             "config": {"workload": f"indexer top-{K}: T={T} queries at the end of S={S} keys, H={H}, D={D}",
-                       "key_caches_rotated": pool}, "roofline": roof}
+                       "T": T, "S": S, "H": H, "D": D, "K": K, "key_caches_rotated": pool}, "roofline": roof}
 
 
 PEAK_PCIE_GBS = 64.0  # the host link, PCIe 5.0 x16, one direction
@@ -527,6 +530,28 @@ def measure_tiered(args, dev):
             "hit_rates_by_policy": rates}
 
 
+def index_cpu_baseline(sub, target_s):
+    """The oracle's indexer (scores of every visible key, full sort) on queries of the same shape: the last query
+    of the batch, repeated for about target_s."""
+    from oracle import oracle as orc
+    from routed_expert_ffn_sigmoid_amd import synth
+    T, S = sub["config"]["T"], sub["config"]["S"]
+    H, D, K = sub["config"]["H"], sub["config"]["D"], sub["config"]["K"]
+    inp = synth.gen_index(1, S, H, D, seed=0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.index_topk(inp.q, inp.w, inp.k, inp.kscale, K, S - 1)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    cores = orc.max_threads()
+    return {"value": round(reps / el, 3), "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{reps} oracle calls of one query at the end of S={S} keys (H={H}, D={D}, K={K}), "
+                      f"{el:.1f} s, fp64 C with OpenMP over queries (one query: one thread)"}
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -588,13 +613,21 @@ def main(argv=None):
             sub = {"metric": "MoE-layer tokens/s", "unit": "tokens/s", "steps": args.steps, "warmup": args.warmup,
                    **sub}
             extra.append((name, Tw, sub))
-        out["additional_workloads"] = [s for _, _, s in extra]
+        # the hot path's other rows: the residency tier (decode from a host tier behind the HBM cache) and the
+        # sparse-attention indexer (decode and a prefill chunk)
+        rows = [measure_tiered(argparse.Namespace(**{**vars(args), "T": 1, "layers": None}), dev)]
+        for ix in ("1,32768", "512,16384"):
+            rows.append(measure_index(argparse.Namespace(**{**vars(args), "index": ix}), dev))
+        out["additional_workloads"] = [s for _, _, s in extra] + rows
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, T, args.cpu_seconds)
         for name, Tw, sub in extra:
             sub["cpu_baseline"] = cpu_baseline(synth.CONFIGS[name], Tw, args.cpu_seconds)
         if default_run:
             out["cpu_baseline"]["one_thread"] = one_thread_oracle()
+            for sub in out["additional_workloads"]:
+                if sub.get("metric") == "indexer queries/s":
+                    sub["cpu_baseline"] = index_cpu_baseline(sub, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
