@@ -243,7 +243,9 @@ MOE_API int moe_route_permute(const moe_shape *shape, const void *x, const float
  * scale per row and 32 channels.  The matrix-core path takes x as fp16
  * under one power-of-two scale per token (its largest magnitude put into
  * [2^14, 2^15)), exact for every bf16 value above 2^-29 of the row's
- * largest, so no range of activations overflows fp16.  The decode path
+ * largest, so no range of activations overflows fp16; fp32 activations as
+ * two fp16 values hi + lo (about 22 significant bits), every weight step
+ * multiplied with both.  The decode path
  * takes each token's K part as 24-bit fixed point under one power-of-two
  * scale.  `routed` describes E experts, `shared` one.
  *

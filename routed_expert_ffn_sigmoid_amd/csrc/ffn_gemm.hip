@@ -170,7 +170,10 @@ __device__ __forceinline__ int exp_bound(float v) {
     return ex + 1;
 }
 
-template <int WBITS>
+// ACT 1: x bf16 -> x16 [T][d].  ACT 0: x fp32 -> x16 [T][2 d], per K step of 64 inputs the 64 values of
+// hi = fp16(x 2^e) and then the 64 of lo = fp16(x 2^e - hi) (x 2^e - hi is exact in fp32), about 22 significant
+// bits in all; the gate/up pass runs every weight step against both.
+template <int WBITS, int ACT>
 __global__ __launch_bounds__(256) void x16_kernel(FfnParams P, _Float16 *__restrict__ x16, float *__restrict__ xinv,
                                                   int *__restrict__ xl, int *__restrict__ hexp, int nrb,
                                                   int *__restrict__ tile_ctr) {
@@ -221,6 +224,59 @@ __global__ __launch_bounds__(256) void x16_kernel(FfnParams P, _Float16 *__restr
     // the tile queues of the two GEMM launches that follow start empty
     if (blockIdx.x == 0 && tid < 2 * GG_XCDS) tile_ctr[tid] = 0;
     const int d = P.d, nch = d / 8;
+    auto order8 = [](const _Float16 (&v)[8]) -> h8_t {
+        if (WBITS == 4) return (h8_t){v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};
+        return (h8_t){v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+    };
+    auto row_exp = [](float m) {  // 2^e puts the row maximum m into [2^14, 2^15); see below
+        int e = 0;
+        if (m > 0.f && m <= 3.4e38f) {
+            int ex;
+            frexpf(m, &ex);
+            e = min(max(15 - ex, -120), 120);
+        }
+        return e;
+    };
+    if constexpr (ACT == 0) {
+        const float *xf = (const float *)P.x;
+        for (int t = blockIdx.x; t < P.T; t += nrb) {
+            const float4 *row = (const float4 *)(xf + (long)t * d);
+            float m = 0.f, unused = 0.f;
+            for (int c = tid; c < 2 * nch; c += 256) {
+                const float4 v = row[c];
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            block_max2(m, unused);
+            const int e = row_exp(m);
+            const float sc = __builtin_ldexpf(1.f, e);
+            float l1 = 0.f;
+            h8_t *out = (h8_t *)(x16 + (long)t * 2 * d);
+            for (int c = tid; c < nch; c += 256) {
+                const float4 a = row[2 * c], b = row[2 * c + 1];
+                const float v[8] = {a.x * sc, a.y * sc, a.z * sc, a.w * sc, b.x * sc, b.y * sc, b.z * sc, b.w * sc};
+                _Float16 hi[8], lo[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    hi[i] = (_Float16)v[i];
+                    lo[i] = (_Float16)(v[i] - (float)hi[i]);
+                    l1 += fabsf(v[i]);
+                }
+                // K step c / 8 holds 8 chunks of hi, then 8 of lo
+                out[16 * (c >> 3) + (c & 7)] = order8(hi);
+                out[16 * (c >> 3) + 8 + (c & 7)] = order8(lo);
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) l1 += __shfl_xor(l1, o, 64);
+            if (lane == 0) wred[0][wv] = l1;
+            __syncthreads();
+            if (tid == 0) {
+                xinv[t] = __builtin_ldexpf(1.f, -e);
+                xl[t] = exp_bound((wred[0][0] + wred[0][1]) + (wred[0][2] + wred[0][3])) - e;
+            }
+            __syncthreads();  // wred is rewritten by the next row
+        }
+        return;
+    }
     const uint16_t *x = (const uint16_t *)P.x;
     for (int t = blockIdx.x; t < P.T; t += nrb) {
         const uint4 *row = (const uint4 *)(x + (long)t * d);
@@ -360,7 +416,10 @@ struct GgCfg {
 // its fp32 zero points are integral), it is folded into the dequantisation (B = q - z, exact in fp16);
 // otherwise B = q and the epilogue subtracts z times the row sum of the activations, summed from the
 // staged tiles.
-template <int MODE, int WBITS>
+// XLO (gate/up with fp32 activations): x16 holds each row as 2d fp16 values, K step by K step the step's 64
+// values of hi = fp16(x) and then of lo = fp16(x - hi) (about 22 significant bits together); the K loop runs
+// twice the steps and virtual step v multiplies weight step v / 2, so every weight fragment meets hi and lo.
+template <int MODE, int WBITS, bool XLO>
 __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, GemmBufs G, int tiles_n) {
     using C = GgCfg<MODE, WBITS>;
     constexpr bool RES = C::RES;
@@ -479,8 +538,9 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         const int rt = __builtin_amdgcn_readfirstlane(s_t0[slot]) / tiles_n + mtile;
         const int I = shared ? P.Is : P.I;
         const int KK = MODE == 0 ? P.d : I;              // contraction length
+        const int KX = MODE == 0 && XLO ? 2 * KK : KK;   // activation values per row (hi and lo with XLO)
         const int nout = MODE == 0 ? I : P.d;
-        const int nsteps = KK / GG_K;
+        const int nsteps = KX / GG_K;
         // field by field: a reference into the by-value parameter block would make the compiler copy it
         // to private memory and read these pointers back into vector registers
         QW W;
@@ -503,7 +563,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
         uint32_t asrc[2], alsrc = kOOB, scsrc = kOOB;
         {
             if (MODE == 0) {
-                ars = make_rsrc(G.x16, (uint32_t)((long)P.T * P.d * 2));
+                ars = make_rsrc(G.x16, (uint32_t)((long)P.T * KX * 2));
                 alrs = scrs = ars;  // unused
             } else {
                 const long nr = shared ? P.T : P.A;
@@ -523,7 +583,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
                     long row;
                     if (MODE == 0) row = shared ? (r0 + m) : (P.perm[p0 + r0 + m] / P.k);
                     else row = (long)(shared ? 0 : p0) + r0 + m;
-                    off = (uint32_t)(row * KK * 2) + 16 * alc;
+                    off = (uint32_t)(row * KX * 2) + 16 * alc;
                     // one lane per row brings the row's scales (read in the epilogue, after the K loop's barriers;
                     // the previous tile's epilogue is done with them since the barrier that ends it)
                     if ((lane & 7) == 0) {
@@ -649,7 +709,7 @@ __global__ __launch_bounds__(GG_WAVES * 64, 1) void gemm_kernel(FfnParams P, Gem
 #pragma unroll
                 for (int i = 0; i < NLB; i++)
                     dma16(brs[WBITS == 4 ? i : i >> 1], sb + Y::A_BYTES + wv * GG_NW * RB + i * 1024,
-                          src(bsrc[i], (uint32_t)(step * RB)));
+                          src(bsrc[i], (uint32_t)((XLO ? step >> 1 : step) * RB)));
             };
             f32x16v_t acc[MU][2];
 #pragma unroll
@@ -1002,21 +1062,24 @@ static long gg_row_tiles(const FfnParams &P) {
 static long gg_ksmax(const FfnParams &P) { return (P.I > P.Is ? P.I : P.Is) / GG_K; }
 static size_t gg_hsc_bytes(const FfnParams &P) { return (size_t)gg_row_tiles(P) * gg_ksmax(P) * 256; }
 
+// fp16 activation values per row: d, or 2 d (hi and lo) for fp32 activations
+static long gg_xrow(const FfnParams &P) { return P.act == 1 ? P.d : 2L * P.d; }
+
 size_t gemm_workspace_bytes(const FfnParams &P) {
-    return al256((size_t)P.T * P.d * 2) + 2 * al256((size_t)P.T * 4) + al256((size_t)(P.E + 1) * 4) +
+    return al256((size_t)P.T * gg_xrow(P) * 2) + 2 * al256((size_t)P.T * 4) + al256((size_t)(P.E + 1) * 4) +
            al256((size_t)P.A * P.I * 2) + al256((size_t)P.A * P.I) +
            al256((size_t)P.T * P.Is * 2) + al256((size_t)P.T * P.Is) + al256(gg_hsc_bytes(P)) +
            al256(2 * GG_XCDS * sizeof(int));
 }
 
 bool gemm_supported(const FfnParams &P) {
-    if (P.act != 1) return false;  // bf16 activations
+    if (P.act != 0 && P.act != 1) return false;  // fp32 or bf16 activations
     if (P.d % GG_K || P.I % GG_K || (P.Is > 0 && P.Is % GG_K)) return false;
     if (P.n_routed_slots + 1 > GG_MAXSLOTS) return false;
     // 32-bit buffer offsets
     const long Imax = P.I > P.Is ? P.I : P.Is;
     if (Imax * ((long)P.d * P.wbits / 8) > 0x7FFFFFFFL) return false;
-    if ((long)P.A * Imax * 2 > 0x7FFFFFFFL || (long)P.T * P.d * 2 > 0x7FFFFFFFL) return false;
+    if ((long)P.A * Imax * 2 > 0x7FFFFFFFL || (long)P.T * gg_xrow(P) * 2 > 0x7FFFFFFFL) return false;
     if ((long)gg_hsc_bytes(P) > 0x7FFFFFFFL) return false;
     // epilogue stores: 32-bit offsets within one 128-row tile (out-of-range marker added on top)
     if ((long)GG_M * Imax * 2 > 0x7FFFFFFFL || (long)GG_M * P.d * 4 > 0x7FFFFFFFL) return false;
@@ -1031,13 +1094,13 @@ static int gg_cus() {
     return n;
 }
 
-template <int MODE, int WBITS>
+template <int MODE, int WBITS, bool XLO>
 static hipError_t gg_launch_mode(const FfnParams &P, const GemmBufs &G, hipStream_t stream) {
     using C = GgCfg<MODE, WBITS>;
     const int Imax = P.I > P.Is ? P.I : P.Is;
     const int tiles_n = ((MODE == 0 ? Imax : P.d) + C::NOUT_G - 1) / C::NOUT_G;
     const size_t lds = GG_RING;  // every tile shape lays its stages (and the junk area) out in the ring
-    auto fn = gemm_kernel<MODE, WBITS>;
+    auto fn = gemm_kernel<MODE, WBITS, XLO>;
     hipError_t err = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(fn, dim3(gg_cus()), dim3(GG_WAVES * 64), lds, stream, P, G, tiles_n);
@@ -1049,13 +1112,17 @@ static hipError_t gg_launch(const FfnParams &P, const GemmBufs &G, hipStream_t s
     long nrb = P.T;  // row workgroups, a row per workgroup at a time; then one per expert
     if (nrb > (long)gg_cus() * 8) nrb = (long)gg_cus() * 8;
     const long grid = nrb + P.E + (P.Is > 0 ? 1 : 0);
-    hipLaunchKernelGGL(x16_kernel<WBITS>, dim3((unsigned)grid), dim3(256), 0, stream, P, (_Float16 *)G.x16, G.xinv,
-                       G.xl, G.hexp, (int)nrb, G.tile_ctr);
+    if (P.act == 1)
+        hipLaunchKernelGGL((x16_kernel<WBITS, 1>), dim3((unsigned)grid), dim3(256), 0, stream, P, (_Float16 *)G.x16,
+                           G.xinv, G.xl, G.hexp, (int)nrb, G.tile_ctr);
+    else
+        hipLaunchKernelGGL((x16_kernel<WBITS, 0>), dim3((unsigned)grid), dim3(256), 0, stream, P, (_Float16 *)G.x16,
+                           G.xinv, G.xl, G.hexp, (int)nrb, G.tile_ctr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    err = gg_launch_mode<0, WBITS>(P, G, stream);
+    err = P.act == 1 ? gg_launch_mode<0, WBITS, false>(P, G, stream) : gg_launch_mode<0, WBITS, true>(P, G, stream);
     if (err != hipSuccess) return err;
-    return gg_launch_mode<1, WBITS>(P, G, stream);
+    return gg_launch_mode<1, WBITS, false>(P, G, stream);
 }
 
 hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream) {
@@ -1063,7 +1130,7 @@ hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream) {
     char *p = (char *)ws;
     GemmBufs G;
     G.x16 = (const _Float16 *)p;
-    p += al256((size_t)P.T * P.d * 2);
+    p += al256((size_t)P.T * gg_xrow(P) * 2);
     G.xinv = (float *)p;
     p += al256((size_t)P.T * 4);
     G.xl = (int *)p;

@@ -68,7 +68,7 @@ const char *decode_unsupported(const FfnParams &P);  // nullptr when the decode 
 size_t decode_workspace_bytes(const FfnParams &P);
 hipError_t launch_ffn_decode(const FfnParams &P, void *ws, hipStream_t stream);
 
-// ffn_gemm.hip: MFMA grouped-GEMM path (bf16 activations, d and I multiples of 64)
+// ffn_gemm.hip: MFMA grouped-GEMM path (d and I multiples of 64; fp32 activations as fp16 hi + lo)
 bool gemm_supported(const FfnParams &P);
 size_t gemm_workspace_bytes(const FfnParams &P);
 hipError_t launch_ffn_gemm(const FfnParams &P, void *ws, hipStream_t stream);

@@ -327,7 +327,7 @@ int check_forward(const char *fn, const moe_shape *s, const void *x, const moe_q
     if (forward_path(s) == MOE_PATH_GEMM) {
         if (!moe::gemm_supported(P))
             return fail(MOE_EUNSUPPORTED,
-                        "%s: the matrix-core path takes bf16 activations, d, I and I_shared multiples of 64 and "
+                        "%s: the matrix-core path takes d, I and I_shared multiples of 64 and "
                         "buffers below 2^31 bytes", fn);
     } else if (const char *why = moe::decode_unsupported(P)) {
         return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);

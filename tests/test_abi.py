@@ -187,9 +187,10 @@ def test_decode_expert_matrix_beyond_32_bit_offsets_rejected():
 
 
 def test_matrix_core_path_refuses_what_it_cannot_take():
-    """MOE_PATH_GEMM with fp32 activations, or with sizes that are not multiples of 64, is refused with a
+    """MOE_PATH_GEMM with sizes that are not multiples of 64 (bf16 or fp32 activations) is refused with a
     message; MOE_PATH_AUTO sends such shapes to the decode kernels instead."""
-    for kw in (dict(act_dtype=B.MOE_ACT_F32), dict(act_dtype=B.MOE_ACT_BF16, d=272, wbits=8)):
+    for kw in (dict(act_dtype=B.MOE_ACT_F32, d=272, wbits=8), dict(act_dtype=B.MOE_ACT_BF16, d=272, wbits=8),
+               dict(act_dtype=B.MOE_ACT_F32, I=528)):
         s = shape(T=64, path=B.MOE_PATH_GEMM, **kw)
         with pytest.raises(B.MoeError) as ei:
             _forward(s)

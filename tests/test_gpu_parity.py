@@ -120,8 +120,8 @@ def test_small_layer_parity(orc, dev, case):
     run_full_case(orc, dev, spec, T, label=case)
 
 
-# the matrix-core grouped GEMM path (bf16 activations; d, I multiples of 64): several 128-row tiles per
-# expert with ragged ends, experts with a handful of rows, I_shared above and below I
+# the matrix-core grouped GEMM path (d, I multiples of 64): several 128-row tiles per expert with ragged ends,
+# experts with a handful of rows, I_shared above and below I, bf16 and fp32 activations
 GEMM = {
     "gemm_int4_shared": (dict(d=512, E=16, k=4, I=384, I_shared=192, routed_scale=2.5), 70),
     "gemm_int8_shared": (dict(d=768, E=8, k=2, I=512, I_shared=256, wbits=8, routed_scale=2.5), 200),
@@ -129,6 +129,11 @@ GEMM = {
     "gemm_int8_one_expert_many_rows": (dict(d=128, E=2, k=1, I=64, I_shared=64, wbits=8), 400),
     "gemm_int4_shared_wider": (dict(d=320, E=8, k=3, I=128, I_shared=320), 45),
     "gemm_int4_T1": (dict(d=512, E=64, k=6, I=256, I_shared=256, routed_scale=2.5), 1),
+    # fp32 activations: x as fp16 hi + lo, every weight step run against both
+    "gemm_f32_int8_shared": (dict(d=768, E=8, k=2, I=512, I_shared=256, wbits=8, act=synth.ACT_F32,
+                                  routed_scale=2.5), 150),
+    "gemm_f32_int4_row_tiles": (dict(d=256, E=4, k=2, I=256, act=synth.ACT_F32), 300),
+    "gemm_f32_int4_shared_ragged": (dict(d=320, E=8, k=3, I=128, I_shared=320, act=synth.ACT_F32), 45),
 }
 
 
@@ -151,7 +156,8 @@ def _fractional_zero_points(inp):
 
 
 @pytest.mark.parametrize("case,path", [("gemm_int4_shared", B.MOE_PATH_GEMM), ("gemm_int4_row_tiles", B.MOE_PATH_GEMM),
-                                       ("gemm_int4_shared_wider", B.MOE_PATH_GEMV)])
+                                       ("gemm_int4_shared_wider", B.MOE_PATH_GEMV),
+                                       ("gemm_f32_int4_row_tiles", B.MOE_PATH_GEMM)])
 def test_fractional_int4_zero_points(orc, dev, case, path):
     kw, T = GEMM[case]
     run_full_case(orc, dev, spec_of(**kw), T, path=path, tweak=_fractional_zero_points, label=case + "_frac_zp")
@@ -499,9 +505,10 @@ def weights_for(spec, dev, layer=0):
     return W
 
 
-# (workload, T, sampled tokens for y (None: all), forward path).  The large_zipf T = 512 case also runs on the
-# token-group decode kernel (MOE_PATH_GEMV), the path bf16 activations above T = 16 take when forced.
+# (workload, T, sampled tokens for y (None: all), forward path).  The large_zipf T = 512 and the mid T = 64 cases
+# also run on the token-group decode kernel (MOE_PATH_GEMV), which the matrix-core path replaces above T = 16.
 FULL = [("mid", 1, None, B.MOE_PATH_AUTO), ("mid", 4, None, B.MOE_PATH_AUTO), ("mid", 64, None, B.MOE_PATH_AUTO),
+        ("mid", 64, None, B.MOE_PATH_GEMV), ("mid", 512, 64, B.MOE_PATH_AUTO),
         ("large", 1, None, B.MOE_PATH_AUTO), ("large_zipf", 4, None, B.MOE_PATH_AUTO),
         ("large_zipf", 512, 64, B.MOE_PATH_AUTO), ("large_zipf", 512, 64, B.MOE_PATH_GEMV),
         ("prefill_int4_uniform", 8192, 64, B.MOE_PATH_AUTO), ("prefill_int4_zipf", 8192, 64, B.MOE_PATH_AUTO),
@@ -563,7 +570,7 @@ def test_full_workload_parity(orc, dev, name, T, nsample, path):
     assert int(run.n_uniq.item()) == p.n_uniq
     say(f"   indices+permutation bit-exact; n_uniq={p.n_uniq} max count={p.counts.max()}")
 
-    gemm = path == B.MOE_PATH_GEMM or (path == B.MOE_PATH_AUTO and T > 16 and spec.act == synth.ACT_BF16)
+    gemm = path == B.MOE_PATH_GEMM or (path == B.MOE_PATH_AUTO and T > 16)
     block = 128 if gemm else 16
     so = sampled_oracle(orc, spec)
     yp = run.y_perm.cpu().numpy()
