@@ -104,34 +104,181 @@ __device__ __forceinline__ double from_ordered_f64(uint64_t o) {
 }
 
 // One workgroup per query: the top K of its n = min(S, pos0 + t + 1) visible keys, by ascending position.
+//
+// The K-th largest score is found in two rounds.  First a histogram of IX_NB buckets spaced evenly between the
+// query's smallest and largest score, bucket(s) = floor((s - min) * IX_NB / (max - min)): the map is monotonic in
+// s (a subtraction and a product by a positive constant, each rounded), so every key of a higher bucket has a
+// larger or equal score, and equal scores share a bucket.  A scan from the top finds the bucket b* holding the
+// K-th largest and the count above it; the keys of b* (a few dozen for scores spread like these) are copied to
+// LDS and the exact radix selection of topk.h finds, among them, the K-th largest key and how many of its equals
+// are taken.  Queries whose b* holds more than TOPK_CAND keys (many equal scores, or a range that does not
+// spread) take the radix selection over all keys instead.  Either way the ordered visit writes the positions.
+constexpr int IX_NB = 4096;
+constexpr int IX_UN = 16;  // scores loaded together per thread in the streaming passes
+
+__device__ __forceinline__ int ix_bucket(double s, double mn, double scale) {
+    const double f = (s - mn) * scale;
+    return f >= 0.0 ? (f < (double)(IX_NB - 1) ? (int)f : IX_NB - 1) : 0;
+}
+
+// The bucket holding the K-th largest key (K <= the keys counted): thread tid sums buckets IX_NB - BPT tid - 1 ..
+// IX_NB - BPT tid - BPT (from the top); an inclusive scan over the threads gives the keys above each thread's
+// buckets.  Writes the bucket, the keys in buckets above it and its own count.  scan: LDS of the wavefront totals.
+__device__ void ix_find_bucket(const int *bhist, int K, int *scan, int *bstar, int *above, int *nb) {
+    constexpr int BPT = IX_NB / IX_SEL_THREADS;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int c[BPT], sum = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; q++) {
+        c[q] = bhist[IX_NB - 1 - BPT * tid - q];
+        sum += c[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t2 = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t2;
+    }
+    if (lane == 63) scan[wv] = incl;
+    __syncthreads();
+    int before = incl - sum;
+    for (int w2 = 0; w2 < wv; w2++) before += scan[w2];
+    if (before < K && before + sum >= K) {
+        int acc = before, q = 0;
+        while (acc + c[q] < K) acc += c[q++];
+        *bstar = IX_NB - 1 - BPT * tid - q;
+        *above = acc;
+        *nb = c[q];
+    }
+}
+
 __global__ __launch_bounds__(IX_SEL_THREADS) void index_select_kernel(const double *__restrict__ scores, int S,
                                                                       int K, int pos0, int32_t *__restrict__ top,
                                                                       double *__restrict__ gap) {
+    __shared__ int bhist[IX_NB];
+    __shared__ uint64_t bkeys[TOPK_CAND];
     __shared__ int hist[256];
     __shared__ int scan[IX_SEL_THREADS / 64 + 1];
     __shared__ TopkState st;
     __shared__ uint64_t cand[TOPK_CAND];
-    __shared__ int ncand;
+    __shared__ int ncand, s_nb, s_bstar, s_above;
+    __shared__ double s_mn[IX_SEL_THREADS / 64], s_mx[IX_SEL_THREADS / 64];
     __shared__ unsigned long long below;  // ordered key of the largest score not taken
-    const int t = blockIdx.x;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     long nl = (long)pos0 + t + 1;
     const int n = (int)(nl < 0 ? 0 : (nl > S ? S : nl));
     int32_t *out = top + (long)t * K;
     const double *sc = scores + (long)t * S;
     if (n <= K) {  // every visible key
-        for (int i = threadIdx.x; i < K; i += IX_SEL_THREADS) out[i] = i < n ? i : -1;
-        if (threadIdx.x == 0 && gap) gap[t] = INFINITY;
+        for (int i = tid; i < K; i += IX_SEL_THREADS) out[i] = i < n ? i : -1;
+        if (tid == 0 && gap) gap[t] = INFINITY;
         return;
     }
     auto key = [&](int i) { return ordered_f64(sc[i]); };
-    if (threadIdx.x == 0) below = 0ull;
-    const TopkState s = radix_kth_largest<IX_SEL_THREADS, 64>(key, n, K, hist, &st, cand, &ncand);
+    if (tid == 0) below = 0ull;
+    // ---- the query's range of scores
+    double mn = INFINITY, mx = -INFINITY;
+    for (int i0 = tid; i0 < n; i0 += IX_SEL_THREADS * IX_UN) {
+        double v[IX_UN];
+#pragma unroll
+        for (int u = 0; u < IX_UN; u++) v[u] = i0 + u * IX_SEL_THREADS < n ? sc[i0 + u * IX_SEL_THREADS] : sc[0];
+#pragma unroll
+        for (int u = 0; u < IX_UN; u++) {
+            mn = fmin(mn, v[u]);
+            mx = fmax(mx, v[u]);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o, 64));
+        mx = fmax(mx, __shfl_xor(mx, o, 64));
+    }
+    if (lane == 0) {
+        s_mn[wv] = mn;
+        s_mx[wv] = mx;
+    }
+    for (int b = tid; b < IX_NB; b += IX_SEL_THREADS) bhist[b] = 0;
+    __syncthreads();
+    mn = s_mn[0];
+    mx = s_mx[0];
+    for (int w2 = 1; w2 < IX_SEL_THREADS / 64; w2++) {
+        mn = fmin(mn, s_mn[w2]);
+        mx = fmax(mx, s_mx[w2]);
+    }
+    const double scale = (double)IX_NB / (mx - mn);
+    bool spread = mx > mn && scale > 0.0 && scale < INFINITY;  // uniform over the workgroup
+    TopkState s;
+    if (spread) {
+        // ---- histogram of the buckets
+        for (int i0 = tid; i0 < n; i0 += IX_SEL_THREADS * IX_UN) {
+            double v[IX_UN];
+#pragma unroll
+            for (int u = 0; u < IX_UN; u++) v[u] = i0 + u * IX_SEL_THREADS < n ? sc[i0 + u * IX_SEL_THREADS] : 0.0;
+#pragma unroll
+            for (int u = 0; u < IX_UN; u++)
+                if (i0 + u * IX_SEL_THREADS < n) atomicAdd(&bhist[ix_bucket(v[u], mn, scale)], 1);
+        }
+        __syncthreads();
+        ix_find_bucket(bhist, K, scan, &s_bstar, &s_above, &s_nb);
+        if (tid == 0) ncand = 0;
+        __syncthreads();
+        spread = s_nb <= TOPK_CAND;
+    }
+    if (spread) {
+        // ---- the keys of bucket b* into LDS (any order), then the exact selection among them
+        const int bstar = s_bstar;
+        for (int i0 = tid; i0 < n; i0 += IX_SEL_THREADS * IX_UN) {
+            double v[IX_UN];
+#pragma unroll
+            for (int u = 0; u < IX_UN; u++) v[u] = i0 + u * IX_SEL_THREADS < n ? sc[i0 + u * IX_SEL_THREADS] : 0.0;
+#pragma unroll
+            for (int u = 0; u < IX_UN; u++) {
+                const bool in = i0 + u * IX_SEL_THREADS < n && ix_bucket(v[u], mn, scale) == bstar;
+                const uint64_t bal = __ballot(in);
+                int base = 0;
+                if (bal) {
+                    const int leader = __builtin_ctzll(bal);
+                    if (lane == leader) base = atomicAdd(&ncand, __popcll(bal));
+                    base = __shfl(base, leader, 64);
+                }
+                const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+                if (in) bkeys[base + __popcll(bal & lower)] = ordered_f64(v[u]);
+            }
+        }
+        __syncthreads();
+        const int nb = s_nb, kb = K - s_above;  // the kb-th largest of the bucket's nb keys
+        if (nb <= IX_SEL_THREADS) {
+            // few candidates: each thread counts the candidates above and equal to its own; the one with
+            // (above < kb <= above + equal) is the K-th largest key
+            if (tid < nb) {
+                const uint64_t mk = bkeys[tid];
+                int gt = 0, eq = 0;
+                for (int j = 0; j < nb; j++) {
+                    const uint64_t o = bkeys[j];
+                    gt += o > mk;
+                    eq += o == mk;
+                }
+                if (gt < kb && kb <= gt + eq) {  // every thread holding this key writes the same values
+                    st.v = mk;
+                    st.need = kb - gt;
+                    st.eq = eq;
+                }
+            }
+            __syncthreads();
+            s = st;
+        } else {
+            s = radix_kth_largest<IX_SEL_THREADS, 64>([&](int i) { return bkeys[i]; }, nb, kb, hist, &st, cand,
+                                                      &ncand);
+        }
+    } else {
+        s = radix_kth_largest<IX_SEL_THREADS, 64>(key, n, K, hist, &st, cand, &ncand);
+    }
     uint64_t mine = 0;  // this thread's largest key not taken
     visit_topk<IX_SEL_THREADS>(key, n, s, scan, [&](int i, int rank) { out[rank] = i; },
                                [&](int, uint64_t ki) { mine = ki > mine ? ki : mine; });
     block_max_u64(mine, &below);
     __syncthreads();
-    if (threadIdx.x == 0 && gap)
+    if (tid == 0 && gap)
         gap[t] = s.eq > s.need ? 0.0 : from_ordered_f64(s.v) - from_ordered_f64(below);
 }
 

@@ -24,8 +24,22 @@ def dev():
     return torch.device("cuda:0")
 
 
+def _all_zero_queries(inp):
+    inp.q[:] = 0  # every score 0: no spread between the smallest and the largest score
+
+
+def _big_tie_block(inp):
+    # 6000 copies of one key under one scale: the K-th largest falls in a bucket of more than 4096 equal scores
+    inp.k[1000:7000] = inp.k[0]
+    inp.kscale[1000:7000] = inp.kscale[0]
+
+
+TWEAKS = {"all_scores_equal": _all_zero_queries, "tie_block_beyond_lds": _big_tie_block}
+
 # (T, S, H, D, K, pos0, duplicated keys)
 CASES = {
+    "all_scores_equal": (2, 5000, 16, 64, 2048, 4998, False),
+    "tie_block_beyond_lds": (2, 9000, 16, 64, 2048, 8998, False),
     "decode_32k_context": (1, 32768, 64, 128, 2048, 32767, False),
     "prefill_chunk_64_of_8192": (64, 8192, 64, 128, 2048, 8192 - 64, False),
     "short_context_padding": (8, 1000, 64, 128, 2048, 0, False),
@@ -41,6 +55,8 @@ def test_index_topk_parity(orc, dev, case):
     T, S, H, D, K, pos0, dup = CASES[case]
     say(f"[index] {case} T={T} S={S} H={H} D={D} K={K} pos0={pos0}")
     inp = synth.gen_index(T, S, H, D, seed=len(case), dup_keys=dup)
+    if case in TWEAKS:
+        TWEAKS[case](inp)
     shape = B.dsa_index_shape(T, S, H, D, K, pos0)
     ws = torch.empty(B.dsa_index_workspace_size(shape), dtype=torch.uint8, device=dev)
     top = torch.full((T, K), -7, dtype=torch.int32, device=dev)
@@ -57,5 +73,5 @@ def test_index_topk_parity(orc, dev, case):
         np.testing.assert_array_equal(sc[t, :n], ref.scores[t, :n], err_msg=f"scores of query {t}")
     ties = int(np.sum(ref.gap == 0))
     say(f"   positions and scores bit-exact; {ties} queries with a tie at the K-th place")
-    if dup:
+    if dup or case in TWEAKS:
         assert ties > 0
