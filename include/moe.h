@@ -29,10 +29,7 @@
  *   - `ws` is a caller-owned device workspace of at least
  *     moe_workspace_size(shape) bytes, 256-byte aligned.  Calls that share a
  *     workspace must be ordered (same stream); concurrent calls need their
- *     own workspaces.  Its first 256 bytes hold counters: they must be zero
- *     before the workspace's first use (allocate it zeroed, or call
- *     moe_workspace_clear once), and every call leaves them zero.  The rest
- *     needs no initialisation.
+ *     own workspaces.  Workspace contents need no initialisation.
  *   - Return value: MOE_OK (0) or a negative MOE_E* code.  All arguments
  *     are validated before anything is enqueued, so a failed call leaves
  *     every output untouched.  moe_last_error() gives a message for the
@@ -175,9 +172,6 @@ typedef struct moe_qffn {
  */
 MOE_API size_t moe_workspace_size(const moe_shape *shape);
 
-/* Zeroes the workspace's counters (its first 256 bytes) with a kernel on `stream`; ws_bytes >= 256. */
-MOE_API int moe_workspace_clear(void *ws, size_t ws_bytes, void *stream);
-
 /*
  * Router ("25GB 内存跑 744B GLM-5.2 模型" page, sections 三.1 and 四.3).
  *   z[t][e]   = sum_i x[t][i] * W_r[i][e]            (fp64 accumulation)
@@ -218,10 +212,10 @@ MOE_API int moe_permute(const moe_shape *shape, const int32_t *topk_idx, int32_t
 
 /*
  * moe_route followed by moe_permute, with the same arguments, outputs and
- * checks as the two calls.  For decode batches (T <= 4, the top-k routers
+ * checks as the two calls.  For a single token (T = 1, the top-k routers
  * without capacity) the permutation runs inside the selection's launch: the
- * workgroup that selects last (one per token) sorts the assignments, so the
- * permutation costs no launch of its own.  The outputs have the same bits as
+ * workgroup that selects the token's experts then sorts the assignments, so
+ * the permutation costs no launch of its own.  The outputs have the same bits as
  * the two calls'.
  */
 MOE_API int moe_route_permute(const moe_shape *shape, const void *x, const float *W_r, const float *bias,

@@ -47,7 +47,7 @@ MOE_CACHE_LRU = 1
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_static", "moe_combine",
            "moe_last_error", "moe_abi_version", "dsa_index_workspace_size", "dsa_index_topk",
            "moe_cache_state_size", "moe_cache_init", "moe_cache_plan", "moe_cache_fetch", "moe_forward_cached",
-           "moe_cache_stats", "moe_route_permute", "moe_workspace_clear")
+           "moe_cache_stats", "moe_route_permute")
 
 MOE_STATIC_SCRATCH_BYTES = 64 << 20  # moe_forward_static's scratch
 
@@ -119,8 +119,6 @@ def lib():
             getattr(L, f).restype = C.c_int
         L.moe_route_permute.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
         L.moe_route_permute.restype = C.c_int
-        L.moe_workspace_clear.argtypes = [P, C.c_size_t, P]
-        L.moe_workspace_clear.restype = C.c_int
         _lib = L
     return _lib
 
@@ -203,11 +201,6 @@ def moe_route_permute(shape, x, W_r, bias, topk_idx, topk_w, gap, counts, offset
     _check(lib().moe_route_permute(C.byref(shape), _ptr(x), _ptr(W_r), _ptr(bias), _ptr(topk_idx), _ptr(topk_w),
                                    _ptr(gap), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(uniq),
                                    _ptr(n_uniq), _ptr(ws), ws_bytes, _stream(stream)))
-
-
-def moe_workspace_clear(ws, ws_bytes=None, stream=None) -> None:
-    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
-    _check(lib().moe_workspace_clear(_ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_combine(shape, y_perm, y_shared, inv, topk_w, y, stream=None) -> None:

@@ -52,10 +52,10 @@ struct PermOut {
 // true when the selection's launch also takes the permutation (given PermOut): T <= 4, top-k routers without
 // capacity
 bool router_fused(int T, int E, bool inv, int router, int C);
-// ticket: a zeroed counter the fused form uses and leaves zeroed (nullptr: never fuse); po: also sort (fused form)
+// po: also sort the assignments, inside the selection's launch when router_fused (nullptr: no permutation)
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
                          float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
-                         hipStream_t stream, unsigned *ticket, const PermOut *po);
+                         hipStream_t stream, const PermOut *po);
 
 // permute.hip
 size_t permute_lds_bytes(int E);

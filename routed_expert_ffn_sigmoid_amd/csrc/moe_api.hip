@@ -19,14 +19,6 @@ static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
-// The workspace starts with kWsHead bytes of counters (the router's fused-form ticket at offset 0), zero before
-// the first call and left zero by every call; the kernels' own areas follow.
-constexpr size_t kWsHead = 256;
-void *ws_body(void *ws) { return ws ? (char *)ws + kWsHead : nullptr; }
-unsigned *ws_ticket(void *ws) { return (unsigned *)ws; }
-
-__global__ void ws_clear_kernel(unsigned *head) { head[threadIdx.x] = 0u; }
-
 thread_local char g_err[512] = "";
 
 int fail(int code, const char *fmt, ...) {
@@ -208,16 +200,7 @@ size_t moe_workspace_size(const moe_shape *s) {
     if (m > need) need = m;
     const size_t pm = moe::permute_workspace_bytes(s->T * s->k, s->E);
     if (pm > need) need = pm;
-    return kWsHead + ((need + 255) & ~(size_t)255);
-}
-
-int moe_workspace_clear(void *ws, size_t ws_bytes, void *stream) {
-    const char *fn = "moe_workspace_clear";
-    if (!ws) return fail(MOE_EINVAL, "%s: workspace is NULL", fn);
-    if (!aligned(ws, 256)) return fail(MOE_EALIGN, "%s: workspace is not 256-byte aligned", fn);
-    if (ws_bytes < kWsHead) return fail(MOE_EWORKSPACE, "%s: workspace has %zu bytes, %zu at least", fn, ws_bytes, kWsHead);
-    hipLaunchKernelGGL(ws_clear_kernel, dim3(1), dim3(kWsHead / 4), 0, (hipStream_t)stream, ws_ticket(ws));
-    return launch_status(fn, hipGetLastError());
+    return (need + 255) & ~(size_t)255;
 }
 
 int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *bias, int32_t *topk_idx,
@@ -238,8 +221,8 @@ int moe_route(const moe_shape *s, const void *x, const float *W_r, const float *
     if (const char *why = moe::router_unsupported(s->T, s->d, s->E, s->act_dtype, inv))
         return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
     return launch_status(fn, moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
-                                                topk_idx, topk_w, gap, ws_body(ws), inv, s->router, router_capacity(s),
-                                                (hipStream_t)stream, ws_ticket(ws), nullptr));
+                                                topk_idx, topk_w, gap, ws, inv, s->router, router_capacity(s),
+                                                (hipStream_t)stream, nullptr));
 }
 
 int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, int32_t *offsets, int32_t *perm,
@@ -257,7 +240,7 @@ int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, in
     rc = check_ws(fn, s, ws, ws_bytes);
     if (rc) return rc;
     return launch_status(fn, moe::launch_permute(topk_idx, s->T * s->k, s->E, counts, offsets, perm, inv, uniq,
-                                                 n_uniq, ws_body(ws), (hipStream_t)stream));
+                                                 n_uniq, ws, (hipStream_t)stream));
 }
 
 int moe_route_permute(const moe_shape *s, const void *x, const float *W_r, const float *bias, int32_t *topk_idx,
@@ -287,13 +270,13 @@ int moe_route_permute(const moe_shape *s, const void *x, const float *W_r, const
             return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
         const moe::PermOut po{counts, offsets, perm, inv, uniq, n_uniq};
         hipError_t err = moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
-                                            topk_idx, topk_w, gap, ws_body(ws), invariant, s->router, C,
-                                            (hipStream_t)stream, ws_ticket(ws), &po);
+                                            topk_idx, topk_w, gap, ws, invariant, s->router, C,
+                                            (hipStream_t)stream, &po);
         if (err != hipSuccess) return launch_status(fn, err);
         if (moe::router_fused(s->T, s->E, invariant, s->router, C)) return launch_status(fn, hipSuccess);
     }
     return launch_status(fn, moe::launch_permute(topk_idx, s->T * s->k, s->E, counts, offsets, perm, inv, uniq,
-                                                 n_uniq, ws_body(ws), (hipStream_t)stream));
+                                                 n_uniq, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -357,9 +340,8 @@ int run_forward(const char *fn, const moe_shape *s, const void *x, const moe_qff
     P.y_perm = y_perm;
     P.y_sh = s->I_shared > 0 ? y_shared : nullptr;
     P.diag = diag;
-    void *wb = ws_body(ws);
-    const hipError_t err = forward_path(s) == MOE_PATH_GEMM ? moe::launch_ffn_gemm(P, wb, (hipStream_t)stream)
-                                                             : moe::launch_ffn_decode(P, wb, (hipStream_t)stream);
+    const hipError_t err = forward_path(s) == MOE_PATH_GEMM ? moe::launch_ffn_gemm(P, ws, (hipStream_t)stream)
+                                                             : moe::launch_ffn_decode(P, ws, (hipStream_t)stream);
     return launch_status(fn, err);
 }
 
@@ -384,7 +366,7 @@ int moe_forward_static(const moe_shape *s, const void *x, const moe_qffn *routed
     const char *fn = "moe_forward_static";
     int rc = check_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag);
     if (rc) return rc;
-    const size_t need = kWsHead + forward_workspace_bytes(s);
+    const size_t need = forward_workspace_bytes(s);
     if (need > (size_t)MOE_STATIC_SCRATCH_BYTES)
         return fail(MOE_EWORKSPACE, "%s: this shape needs %zu bytes of scratch, above the static %u", fn, need,
                     (unsigned)MOE_STATIC_SCRATCH_BYTES);

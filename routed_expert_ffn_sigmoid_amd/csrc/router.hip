@@ -152,10 +152,11 @@ constexpr int RSK_EB = 32;                // experts per workgroup column block
 constexpr int RSK_WGS = 256;              // workgroups aimed at
 constexpr int RSK_MAXR = 12;              // W_r rows per thread (1024 threads: 128 VGPRs each)
 constexpr int RSK_MAX_ROWS = 2048;        // rows per block (LDS holds RS_TMAX x rows activations)
-// The selection kernel's permutation (moe_route_permute at T <= RS_TMAX): when perm is set, the last of the T
-// workgroups (a ticket from a zeroed counter, left zeroed) sorts the assignments after every token's choice.
+// The selection kernel's permutation (moe_route_permute at T <= RS_FUSE_TMAX): with perm set, one workgroup selects
+// every token and sorts the assignments.  The tokens' selections then run one after another, each adding about the
+// cost of a separate sort launch, so only the single-token call is fused.
+constexpr int RS_FUSE_TMAX = 1;
 struct FusedPerm {
-    unsigned *ticket;
     int32_t *counts, *offsets, *perm, *inv, *uniq, *n_uniq;  // perm = nullptr: no permutation
 };
 
@@ -359,9 +360,9 @@ __device__ inline void select_token(const double *__restrict__ part, int nsplit,
     }
 }
 
-// One workgroup per token.  With F.perm set (T <= RS_TMAX), the workgroup that selects last also sorts the
-// assignments: directly from LDS when T = 1, else after a ticket (one agent-scope fence per workgroup publishes its
-// choices; the last one's fence makes the others' visible to it).
+// One workgroup per token; with F.perm set (T <= RS_FUSE_TMAX) one workgroup selects the T tokens one after the other
+// and then sorts the assignments from LDS, so the permutation needs no launch of its own and no workgroup waits
+// for another.
 template <int EJ, int MODE>
 __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const double *__restrict__ part, int nsplit,
                                                                      int T, int E, int k,
@@ -369,30 +370,20 @@ __global__ __launch_bounds__(RSEL_THREADS) void router_select_kernel(const doubl
                                                                      int32_t *__restrict__ idx,
                                                                      float *__restrict__ w,
                                                                      double *__restrict__ gap, FusedPerm F) {
-    extern __shared__ double zs[];  // [4][E], then (with F.perm) the sort's LDS and this token's k ids
-    int32_t *psm = (int32_t *)(zs + 4 * E);
-    int32_t *keys = psm + (F.perm ? 18 * E + 1 : 0);
-    select_token<EJ>(part, nsplit, T, E, k, bias, lambda, MODE, blockIdx.x, idx, w, gap, zs, F.perm ? keys : nullptr);
-    if (!F.perm) return;
-    __syncthreads();
-    if (T > 1) {
-        __shared__ int s_last;
-        if (threadIdx.x == 0) {
-            __threadfence();
-            s_last = atomicAdd(F.ticket, 1u) == (unsigned)T - 1u;
-            if (s_last) {
-                __threadfence();
-                atomicExch(F.ticket, 0u);
-            }
-        }
-        __syncthreads();
-        if (!s_last) return;
+    extern __shared__ double zs[];  // [4][E], then (with F.perm) the sort's LDS and the T k chosen ids
+    if (!F.perm) {
+        select_token<EJ>(part, nsplit, T, E, k, bias, lambda, MODE, blockIdx.x, idx, w, gap, zs, nullptr);
+        return;
     }
-    permute_block(T > 1 ? idx : keys, T * k, E, F.counts, F.offsets, F.perm, F.inv, F.uniq, F.n_uniq, psm);
+    int32_t *psm = (int32_t *)(zs + 4 * E);
+    int32_t *keys = psm + 18 * E + 1;
+    for (int t = 0; t < T; t++) {
+        select_token<EJ>(part, nsplit, T, E, k, bias, lambda, MODE, t, idx, w, gap, zs, keys);
+        __syncthreads();  // zs is reused; the ids are complete
+    }
+    permute_block(keys, T * k, E, F.counts, F.offsets, F.perm, F.inv, F.uniq, F.n_uniq, psm);
 }
 
-// grid: (row blocks, expert column blocks, token groups of RS_TMAX); each token's arithmetic depends only on
-// (d, E, rows), not on T or on the other tokens of its group.
 template <int ACT>
 __global__ __launch_bounds__(RSK_THREADS) void router_logits_skinny_kernel(const void *__restrict__ x,
                                                                            const float *__restrict__ Wr, int T,
@@ -624,12 +615,12 @@ size_t router_workspace_bytes(int T, int d, int E, bool inv, int k, int router, 
 bool router_fused(int T, int E, bool inv, int router, int C) {
     (void)E;
     (void)inv;
-    return T >= 1 && T <= RS_TMAX && router != 2 && C <= 0;
+    return T >= 1 && T <= RS_FUSE_TMAX && router != 2 && C <= 0;
 }
 
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
                          float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
-                         hipStream_t stream, unsigned *ticket, const PermOut *po) {
+                         hipStream_t stream, const PermOut *po) {
     double *part = (double *)ws;
     char *vws = (char *)ws + r_al256((size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double));
     int nsplit;
@@ -661,23 +652,24 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
         hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(EC_THREADS), 0, stream, pT, T, E, C, lambda, idx, w, gap);
         return hipGetLastError();
     }
-    const bool fuse = ticket && po && router_fused(T, E, inv, router, C);
+    const bool fuse = po && router_fused(T, E, inv, router, C);
     FusedPerm F{};
     size_t lds = 4 * E * sizeof(double);
     if (fuse) {
-        F = FusedPerm{ticket, po->counts, po->offsets, po->perm, po->inv, po->uniq, po->n_uniq};
-        lds += sizeof(int32_t) * ((size_t)18 * E + 1 + (size_t)k);
+        F = FusedPerm{po->counts, po->offsets, po->perm, po->inv, po->uniq, po->n_uniq};
+        lds += sizeof(int32_t) * ((size_t)18 * E + 1 + (size_t)T * k);
     }
+    const dim3 sgrid(fuse ? 1 : T);
     auto select = [&](auto mode) {
         constexpr int M = decltype(mode)::value;
         if (E <= 64)
-            hipLaunchKernelGGL((router_select_kernel<1, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
+            hipLaunchKernelGGL((router_select_kernel<1, M>), sgrid, dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
                                E, k, bias, lambda, idx, w, gap, F);
         else if (E <= 256)
-            hipLaunchKernelGGL((router_select_kernel<4, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
+            hipLaunchKernelGGL((router_select_kernel<4, M>), sgrid, dim3(RSEL_THREADS), lds, stream, part, nsplit, T,
                                E, k, bias, lambda, idx, w, gap, F);
         else
-            hipLaunchKernelGGL((router_select_kernel<16, M>), dim3(T), dim3(RSEL_THREADS), lds, stream, part, nsplit,
+            hipLaunchKernelGGL((router_select_kernel<16, M>), sgrid, dim3(RSEL_THREADS), lds, stream, part, nsplit,
                                T, E, k, bias, lambda, idx, w, gap, F);
     };
     if (router == 1)

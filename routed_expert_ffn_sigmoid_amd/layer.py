@@ -113,8 +113,7 @@ class MoeRun:
         self.y_perm = torch.empty((A, d), dtype=torch.float32, device=device)
         self.y_shared = torch.empty((T, d), dtype=torch.float32, device=device) if spec.I_shared > 0 else None
         self.y = torch.empty((T, d), dtype=torch.float32, device=device)
-        # zeroed: the workspace's first 256 bytes are counters that must start at zero (the calls keep them there)
-        self.ws = torch.zeros(max(B.moe_workspace_size(self.shape), 256), dtype=torch.uint8, device=device)
+        self.ws = torch.empty(max(B.moe_workspace_size(self.shape), 256), dtype=torch.uint8, device=device)
         # moe_forward's diagnostic counters (uint32 in the ABI), added to by every forward call
         self.diag = torch.zeros(B.MOE_DIAG_COUNT, dtype=torch.int32, device=device)
 

@@ -324,10 +324,9 @@ def test_cached_forward_and_fetch_check_shapes():
     assert ei.value.code == B.MOE_EINVAL
 
 
-def test_route_permute_and_workspace_clear_checks():
+def test_route_permute_checks():
     s = shape(T=2)
     need = B.moe_workspace_size(s)
-    assert need >= 256 + 8 * 1024  # the counters, then the calls' areas
     args = dict(x=FAKE, W_r=FAKE, bias=FAKE, topk_idx=FAKE, topk_w=FAKE, gap=None, counts=FAKE, offsets=FAKE,
                 perm=FAKE, inv=FAKE, uniq=FAKE, n_uniq=FAKE, ws=FAKE)
     for miss in ("counts", "offsets", "perm", "inv", "uniq", "n_uniq", "W_r", "topk_idx"):
@@ -338,13 +337,4 @@ def test_route_permute_and_workspace_clear_checks():
         assert ei.value.code == B.MOE_EINVAL, miss
     with pytest.raises(B.MoeError) as ei:
         B.moe_route_permute(s, **args, ws_bytes=need - 1, stream=0)
-    assert ei.value.code == B.MOE_EWORKSPACE
-    with pytest.raises(B.MoeError) as ei:
-        B.moe_workspace_clear(None, 1024, stream=0)
-    assert ei.value.code == B.MOE_EINVAL
-    with pytest.raises(B.MoeError) as ei:
-        B.moe_workspace_clear(FAKE + 16, 1024, stream=0)
-    assert ei.value.code == B.MOE_EALIGN
-    with pytest.raises(B.MoeError) as ei:
-        B.moe_workspace_clear(FAKE, 255, stream=0)
     assert ei.value.code == B.MOE_EWORKSPACE
