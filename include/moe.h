@@ -301,6 +301,23 @@ MOE_API int moe_forward_static(const moe_shape *shape, const void *x, const moe_
 MOE_API int moe_combine(const moe_shape *shape, const float *y_perm, const float *y_shared, const int32_t *inv,
                 const float *topk_w, float *y, void *stream);
 
+/*
+ * The whole layer in one call: moe_route_permute, moe_forward and
+ * moe_combine on the same arguments, with the same checks, writing the same
+ * outputs with the same bits (every intermediate output included).  For a
+ * single token on the decode path with a top-k router and no capacity, the
+ * selection and the sort of the chosen experts (GLM-5.2 page, sections 三.1
+ * and 三.4) run inside the forward's first launch: every workgroup of that
+ * launch selects the token's experts from the router's partial sums for
+ * itself, so neither needs a launch of its own.  Otherwise the call runs the
+ * three calls' kernels in turn.  ws: moe_workspace_size(shape) bytes.
+ */
+MOE_API int moe_layer(const moe_shape *shape, const void *x, const float *W_r, const float *bias,
+                      const moe_qffn *routed, const moe_qffn *shared, int32_t *topk_idx, float *topk_w,
+                      double *gap, int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *uniq,
+                      int32_t *n_uniq, float *y_perm, float *y_shared, float *y, uint32_t *diag, void *ws,
+                      size_t ws_bytes, void *stream);
+
 /* Message describing the calling thread's last failed call ("" if none). */
 MOE_API const char *moe_last_error(void);
 

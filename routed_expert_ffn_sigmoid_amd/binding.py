@@ -47,7 +47,7 @@ MOE_CACHE_LRU = 1
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_static", "moe_combine",
            "moe_last_error", "moe_abi_version", "dsa_index_workspace_size", "dsa_index_topk",
            "moe_cache_state_size", "moe_cache_init", "moe_cache_plan", "moe_cache_fetch", "moe_forward_cached",
-           "moe_cache_stats", "moe_route_permute")
+           "moe_cache_stats", "moe_route_permute", "moe_layer")
 
 MOE_STATIC_SCRATCH_BYTES = 64 << 20  # moe_forward_static's scratch
 
@@ -119,6 +119,8 @@ def lib():
             getattr(L, f).restype = C.c_int
         L.moe_route_permute.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
         L.moe_route_permute.restype = C.c_int
+        L.moe_layer.argtypes = [S, P, P, P, Q, Q, P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_layer.restype = C.c_int
         _lib = L
     return _lib
 
@@ -201,6 +203,15 @@ def moe_route_permute(shape, x, W_r, bias, topk_idx, topk_w, gap, counts, offset
     _check(lib().moe_route_permute(C.byref(shape), _ptr(x), _ptr(W_r), _ptr(bias), _ptr(topk_idx), _ptr(topk_w),
                                    _ptr(gap), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(uniq),
                                    _ptr(n_uniq), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer(shape, x, W_r, bias, routed: moe_qffn, shared: Optional[moe_qffn], topk_idx, topk_w, gap, counts,
+              offsets, perm, inv, uniq, n_uniq, y_perm, y_shared, y, diag, ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().moe_layer(C.byref(shape), _ptr(x), _ptr(W_r), _ptr(bias), C.byref(routed),
+                           C.byref(shared) if shared is not None else None, _ptr(topk_idx), _ptr(topk_w), _ptr(gap),
+                           _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(uniq), _ptr(n_uniq),
+                           _ptr(y_perm), _ptr(y_shared), _ptr(y), _ptr(diag), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_combine(shape, y_perm, y_shared, inv, topk_w, y, stream=None) -> None:

@@ -36,6 +36,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "select_dev.h"
 
 namespace moe {
 
@@ -564,6 +565,68 @@ __host__ __device__ inline int dkp_tab_words(int mode, int n_routed_slots, int E
     return 1 + n_routed_slots + E + 1 + (mode == 0 ? A : 0);
 }
 
+// One token's routing inside the gate/up launch (FfnParams::route): its scores from the router's split partial
+// sums, the top k by wavefront 0 (the selection kernel's order of sums and picks, so the same bits), and the
+// permutation of those k distinct experts straight into the LDS routing table.  For one token the stable
+// counting sort reduces to ranks: choice j goes to place r_j = the number of chosen ids below its own, uniq
+// lists the chosen ids in increasing order, and offsets[e] counts the chosen ids below e.  Workgroup 0 also
+// writes the routing outputs.  zs: LDS of 4 E doubles and k ints, free until the table barrier.  Every thread
+// calls it; E <= 256, k <= 64.
+__device__ void route_one_token(const FfnParams &P, int *tab, double *zs) {
+    const FfnParams::Route &R = P.route;
+    const int E = P.E, k = P.k;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const bool out = blockIdx.x == 0;
+    token_scores<DKP_WAVES * 64>(R.part, R.nsplit, 1, E, R.bias, R.mode, 0, zs);  // ends with a barrier
+    int *ids = (int *)(zs + 4 * E);
+    if (tid < 64) {
+        int id;
+        float wt;
+        double gp;
+        topk_pick<4>(zs, E, k, R.lambda, R.mode, id, wt, gp);
+        if (lane < k) ids[lane] = id;
+        if (out) {
+            if (lane < k) {
+                R.idx[lane] = id;
+                R.w[lane] = wt;
+            }
+            if (lane == 0 && R.gap) R.gap[0] = gp;
+        }
+    }
+    __syncthreads();
+    int *t_uniq = tab + 1, *t_off = tab + 1 + k, *t_perm = tab + 2 + k + E;  // n_routed_slots = k for one token
+    if (tid < k) {
+        const int id = ids[tid];
+        int r = 0;
+        for (int i = 0; i < k; i++) r += ids[i] < id;
+        t_uniq[r] = id;
+        t_perm[r] = tid;
+        if (out) {
+            R.uniq[r] = id;
+            R.perm[r] = tid;
+            R.inv[tid] = r;
+        }
+    }
+    for (int e = tid; e <= E; e += DKP_WAVES * 64) {
+        int c = 0, chosen = 0;
+        for (int i = 0; i < k; i++) {
+            const int v = ids[i];
+            c += v < e;
+            chosen |= v == e;
+        }
+        t_off[e] = c;
+        if (out) {
+            R.offsets[e] = c;
+            if (e < E) R.counts[e] = chosen;
+            if (e >= k && e < E) R.uniq[e] = -1;
+        }
+    }
+    if (tid == 0) {
+        tab[0] = k;
+        if (out) *R.n_uniq = k;
+    }
+}
+
 // PASSES (down only): the digit planes hold gcap < T token rows, so a slot with more rows is taken as
 // several virtual slots of at most gcap rows each, in row order, each streaming the expert's rows again
 // (the mid workload's down pass at T = 4: 3 x 14336 inputs of planes fit the LDS, 4 do not).
@@ -604,7 +667,12 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     const int kd = MODE == 0 ? P.d : 0;
     const rsrc_t xsrc0 = make_rsrc(P.x, (uint32_t)((long)T * P.d * (SRC == 0 ? 4 : 2)));
     StageRaw<SRCX> raw0;
-    {
+    if (MODE == 0 && P.route.part) {
+        // one token routed here: its activation row is requested first, then the partial sums
+        const int kpart = kd / S;
+        stage_issue<SRCX>(xsrc0, (long)tile_w * kd + kp * kpart, tile_w < T ? 0 : kpad, kpad / 8, kpart, raw0);
+        route_one_token(P, tab, (double *)(dk_lds + pl0));
+    } else {
         const rsrc_t r_nu = make_rsrc(P.n_uniq, 4), r_uq = make_rsrc(P.uniq, (uint32_t)nrs * 4);
         const rsrc_t r_of = make_rsrc(P.offsets, (uint32_t)(P.E + 1) * 4);
         const rsrc_t r_pm = make_rsrc(P.perm, (uint32_t)P.A * 4);
@@ -1197,26 +1265,49 @@ static hipError_t dkp_launch_pass(const FfnParams &P, float *h, float *h_sh, int
 
 // Launches the persistent kernel if the digit planes of all T tokens fit (for the down pass: of at least one
 // token, the slots then taken in passes); *done tells whether it did.
-template <int MODE, int WBITS, int SRC>
-static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t stream, bool *done) {
-    *done = false;
+// The persistent kernel's K split, padded K part and token rows per pass for pass `mode`; false when the
+// token-group kernel takes the pass instead.
+struct DkpPlan {
+    int S, kpad, gcap;
+};
+static bool dkp_plan(int mode, const FfnParams &P, DkpPlan *pl) {
+    const int wbits = P.wbits;
     const int Imax = P.I > P.Is ? P.I : P.Is;
-    const int K = MODE == 0 ? P.d : Imax;
-    const int Kmin = MODE == 0 ? P.d : (P.Is > 0 && P.Is < P.I ? P.Is : P.I);
-    const int nout = MODE == 0 ? Imax : P.d;
+    const int K = mode == 0 ? P.d : Imax;
+    const int Kmin = mode == 0 ? P.d : (P.Is > 0 && P.Is < P.I ? P.Is : P.I);
+    const int nout = mode == 0 ? Imax : P.d;
     const int slots = P.n_routed_slots + (P.Is > 0 ? 1 : 0);
     const double uniq_exp = (double)P.E * (1.0 - std::pow(1.0 - (double)P.k / P.E, (double)P.T));
     const double slots_exp = std::min((double)P.n_routed_slots, uniq_exp) + (P.Is > 0 ? 1 : 0);
     // routed and shared expert split alike: the split must divide both K ranges
-    int S = P.invariant ? decode_pinned_s(MODE, P) : dkp_pick_s(MODE, K, nout, slots, slots_exp, WBITS, device_cus());
-    while (S > 1 && (Kmin % (S * (WBITS == 8 ? 16 : 32)))) S >>= 1;
-    const int kpad = pad_k(K / S, WBITS);
-    if (P.T > DK_GMAX || dkp_tab_words(MODE, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64)
-        return hipSuccess;
+    int S = P.invariant ? decode_pinned_s(mode, P) : dkp_pick_s(mode, K, nout, slots, slots_exp, wbits, device_cus());
+    while (S > 1 && (Kmin % (S * (wbits == 8 ? 16 : 32)))) S >>= 1;
+    const int kpad = pad_k(K / S, wbits);
+    if (P.T > DK_GMAX || dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64)
+        return false;
     // token rows the planes hold: all T, or (down) fewer, with the slots taken in passes
     int gcap = P.T;
-    while (gcap > 0 && dkp_lds_bytes(MODE, S, P, kpad, gcap) > DKP_LDS_BUDGET) gcap--;
-    if (gcap < 1 || (MODE == 0 && gcap < P.T)) return hipSuccess;
+    while (gcap > 0 && dkp_lds_bytes(mode, S, P, kpad, gcap) > DKP_LDS_BUDGET) gcap--;
+    if (gcap < 1 || (mode == 0 && gcap < P.T)) return false;
+    *pl = DkpPlan{S, kpad, gcap};
+    return true;
+}
+
+bool decode_routes(const FfnParams &P) {
+    DkpPlan pl;
+    if (P.T != 1 || P.E > 256 || P.k > 64 || !dkp_plan(0, P, &pl)) return false;
+    // the selection's scores and ids borrow the digit planes' LDS before the activations are staged
+    return (size_t)pl.S * 3 * pl.gcap * (pl.kpad + 16) >= (size_t)32 * P.E + (size_t)4 * P.k;
+}
+
+template <int MODE, int WBITS, int SRC>
+static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t stream, bool *done) {
+    *done = false;
+    DkpPlan pl;
+    if (!dkp_plan(MODE, P, &pl)) return hipSuccess;
+    const int Imax = P.I > P.Is ? P.I : P.Is;
+    const int K = MODE == 0 ? P.d : Imax;
+    const int S = pl.S, kpad = pl.kpad, gcap = pl.gcap;
     *done = true;
     constexpr int PFA = MODE == 0 ? 8 : 16, PFB = MODE == 0 ? 7 : 14;
     const bool deep = dkp_pf(MODE, (K / S * WBITS / 8 + 63) / 64) == PFA;
@@ -1252,6 +1343,7 @@ static hipError_t dk_launch_s(const FfnParams &P, float *h, float *h_sh, int kpa
 
 template <int MODE, int WBITS, int SRC>
 static hipError_t dk_launch_mode(const FfnParams &P, float *h, float *h_sh, hipStream_t stream) {
+    if (MODE == 0 && P.route.part && !decode_routes(P)) return hipErrorInvalidValue;  // only the persistent kernel routes
     bool done = false;
     hipError_t err = dkp_try<MODE, WBITS, SRC>(P, h, h_sh, stream, &done);
     if (done || err != hipSuccess) return err;

@@ -30,6 +30,21 @@ struct FfnParams {
     bool invariant;      // batch-invariant mode: decode K split fixed by the layer's shape alone
     float *y_perm, *y_sh;
     uint32_t *diag;      // optional counters (nullptr = none): [0] h values not finite in fp16
+    // Routing inside the decode gate/up launch (one token, top-k routers without capacity; the decode path
+    // only).  part = nullptr: the routing tables are read from offsets, perm, uniq and n_uniq.  Otherwise
+    // every workgroup selects the token's experts from the router's split partial sums part[nsplit][1][E]
+    // and sorts them for itself, and workgroup 0 writes the routing outputs below (offsets, uniq and n_uniq
+    // are the buffers the down launch then reads).
+    struct Route {
+        const double *part;
+        int nsplit, mode;  // mode 0 sigmoid + bias, 1 softmax gate
+        const float *bias;
+        float lambda;
+        int32_t *idx;
+        float *w;
+        double *gap;  // optional
+        int32_t *counts, *offsets, *perm, *inv, *uniq, *n_uniq;
+    } route;
 };
 
 // Routed weight row of expert e (wave-uniform e), or -1 when that row is outside the weights.
@@ -49,9 +64,14 @@ size_t router_workspace_bytes(int T, int d, int E, bool inv, int k, int router, 
 struct PermOut {
     int32_t *counts, *offsets, *perm, *inv, *uniq, *n_uniq;
 };
-// true when the selection's launch also takes the permutation (given PermOut): T <= 4, top-k routers without
+// true when the selection's launch also takes the permutation (given PermOut): T = 1, top-k routers without
 // capacity
 bool router_fused(int T, int E, bool inv, int router, int C);
+// The logits kernel alone: split partial sums part[nsplit][T][E] of x . W_r in fp64 (the select kernel's input);
+// returns nsplit through *nsplit.
+hipError_t launch_router_logits(int act, const void *x, const float *Wr, int T, int d, int E, bool inv, double *part,
+                                int *nsplit, hipStream_t stream);
+size_t router_partials_bytes(int T, int d, int E, bool inv);
 // po: also sort the assignments, inside the selection's launch when router_fused (nullptr: no permutation)
 hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
                          float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
@@ -66,6 +86,8 @@ hipError_t launch_permute(const int32_t *idx, int A, int E, int32_t *counts, int
 // ffn_decode.hip: decode path, int8 MFMA with exact integer accumulation (h kept in fp32 in the workspace)
 const char *decode_unsupported(const FfnParams &P);  // nullptr when the decode kernels take the shape
 size_t decode_workspace_bytes(const FfnParams &P);
+// true when the decode launches can route a single token inside the gate/up launch (FfnParams::route)
+bool decode_routes(const FfnParams &P);
 hipError_t launch_ffn_decode(const FfnParams &P, void *ws, hipStream_t stream);
 
 // ffn_gemm.hip: MFMA grouped-GEMM path (d and I multiples of 64; fp32 activations as fp16 hi + lo)

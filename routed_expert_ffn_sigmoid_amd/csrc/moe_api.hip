@@ -200,6 +200,11 @@ size_t moe_workspace_size(const moe_shape *s) {
     if (m > need) need = m;
     const size_t pm = moe::permute_workspace_bytes(s->T * s->k, s->E);
     if (pm > need) need = pm;
+    // moe_layer with the routing inside the forward: the router's partial sums after the forward's workspace
+    if (s->T == 1) {
+        const size_t lr = g + moe::router_partials_bytes(s->T, s->d, s->E, inv);
+        if (lr > need) need = lr;
+    }
     return (need + 255) & ~(size_t)255;
 }
 
@@ -243,10 +248,14 @@ int moe_permute(const moe_shape *s, const int32_t *topk_idx, int32_t *counts, in
                                                  n_uniq, ws, (hipStream_t)stream));
 }
 
-int moe_route_permute(const moe_shape *s, const void *x, const float *W_r, const float *bias, int32_t *topk_idx,
-                      float *topk_w, double *gap, int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
-                      int32_t *uniq, int32_t *n_uniq, void *ws, size_t ws_bytes, void *stream) {
-    const char *fn = "moe_route_permute";
+}  // extern "C"
+
+namespace {
+
+// moe_route_permute's argument checks (all but the workspace)
+int check_route_permute(const char *fn, const moe_shape *s, const void *x, const float *W_r, const float *bias,
+                        int32_t *topk_idx, float *topk_w, double *gap, int32_t *counts, int32_t *offsets,
+                        int32_t *perm, int32_t *inv, int32_t *uniq, int32_t *n_uniq) {
     int rc = check_shape(fn, s);
     if (rc) return rc;
     REQUIRE_PTR_T(x, "x");
@@ -261,22 +270,46 @@ int moe_route_permute(const moe_shape *s, const void *x, const float *W_r, const
     REQUIRE_PTR_T(inv, "inv");
     REQUIRE_PTR(uniq, "uniq");
     REQUIRE_PTR(n_uniq, "n_uniq");
-    rc = check_ws(fn, s, ws, ws_bytes);
-    if (rc) return rc;
+    if (s->T > 0) {
+        const bool invariant = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
+        if (const char *why = moe::router_unsupported(s->T, s->d, s->E, s->act_dtype, invariant))
+            return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
+    }
+    return MOE_OK;
+}
+
+// moe_route_permute's kernels, after its checks
+hipError_t run_route_permute(const moe_shape *s, const void *x, const float *W_r, const float *bias,
+                             int32_t *topk_idx, float *topk_w, double *gap, int32_t *counts, int32_t *offsets,
+                             int32_t *perm, int32_t *inv, int32_t *uniq, int32_t *n_uniq, void *ws, void *stream) {
     const bool invariant = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
     const int C = router_capacity(s);
     if (s->T > 0) {
-        if (const char *why = moe::router_unsupported(s->T, s->d, s->E, s->act_dtype, invariant))
-            return fail(MOE_EUNSUPPORTED, "%s: %s", fn, why);
         const moe::PermOut po{counts, offsets, perm, inv, uniq, n_uniq};
         hipError_t err = moe::launch_router(s->act_dtype, x, W_r, bias, s->T, s->d, s->E, s->k, s->routed_scale,
                                             topk_idx, topk_w, gap, ws, invariant, s->router, C,
                                             (hipStream_t)stream, &po);
-        if (err != hipSuccess) return launch_status(fn, err);
-        if (moe::router_fused(s->T, s->E, invariant, s->router, C)) return launch_status(fn, hipSuccess);
+        if (err != hipSuccess || moe::router_fused(s->T, s->E, invariant, s->router, C)) return err;
     }
-    return launch_status(fn, moe::launch_permute(topk_idx, s->T * s->k, s->E, counts, offsets, perm, inv, uniq,
-                                                 n_uniq, ws, (hipStream_t)stream));
+    return moe::launch_permute(topk_idx, s->T * s->k, s->E, counts, offsets, perm, inv, uniq, n_uniq, ws,
+                               (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route_permute(const moe_shape *s, const void *x, const float *W_r, const float *bias, int32_t *topk_idx,
+                      float *topk_w, double *gap, int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                      int32_t *uniq, int32_t *n_uniq, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_route_permute";
+    int rc = check_route_permute(fn, s, x, W_r, bias, topk_idx, topk_w, gap, counts, offsets, perm, inv, uniq,
+                                 n_uniq);
+    if (rc) return rc;
+    rc = check_ws(fn, s, ws, ws_bytes);
+    if (rc) return rc;
+    return launch_status(fn, run_route_permute(s, x, W_r, bias, topk_idx, topk_w, gap, counts, offsets, perm, inv,
+                                               uniq, n_uniq, ws, stream));
 }
 
 }  // extern "C"
@@ -318,18 +351,10 @@ int check_forward(const char *fn, const moe_shape *s, const void *x, const moe_q
     return MOE_OK;
 }
 
-// the forward kernels, after check_forward and a workspace check
-// (wslot, n_wrows: the routed weights are an expert cache's n_wrows slots, expert e in slot wslot[e])
-int run_forward(const char *fn, const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
-                const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
-                float *y_perm, float *y_shared, uint32_t *diag, void *ws, void *stream,
-                const int32_t *wslot = nullptr, int n_wrows = 0) {
-    if (s->T == 0) return MOE_OK;  // empty batch: no rows to transform
+moe::FfnParams forward_params(const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                              const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                              float *y_perm, float *y_shared, uint32_t *diag) {
     moe::FfnParams P = ffn_params(s);
-    if (wslot) {
-        P.wslot = wslot;
-        P.n_wrows = n_wrows;
-    }
     P.x = x;
     P.routed = to_qw(routed);
     P.shared = to_qw(s->I_shared > 0 ? shared : nullptr);
@@ -340,6 +365,30 @@ int run_forward(const char *fn, const moe_shape *s, const void *x, const moe_qff
     P.y_perm = y_perm;
     P.y_sh = s->I_shared > 0 ? y_shared : nullptr;
     P.diag = diag;
+    return P;
+}
+
+// moe_layer routes inside the forward's gate/up launch: one token on the decode path, a top-k router without
+// capacity (the selection the router's own fused form takes)
+bool layer_routes_in_forward(const moe_shape *s) {
+    if (s->T != 1 || forward_path(s) != MOE_PATH_GEMV) return false;
+    if (!moe::router_fused(s->T, s->E, (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0, s->router, router_capacity(s)))
+        return false;
+    return moe::decode_routes(ffn_params(s));
+}
+
+// the forward kernels, after check_forward and a workspace check
+// (wslot, n_wrows: the routed weights are an expert cache's n_wrows slots, expert e in slot wslot[e])
+int run_forward(const char *fn, const moe_shape *s, const void *x, const moe_qffn *routed, const moe_qffn *shared,
+                const int32_t *offsets, const int32_t *perm, const int32_t *uniq, const int32_t *n_uniq,
+                float *y_perm, float *y_shared, uint32_t *diag, void *ws, void *stream,
+                const int32_t *wslot = nullptr, int n_wrows = 0) {
+    if (s->T == 0) return MOE_OK;  // empty batch: no rows to transform
+    moe::FfnParams P = forward_params(s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag);
+    if (wslot) {
+        P.wslot = wslot;
+        P.n_wrows = n_wrows;
+    }
     const hipError_t err = forward_path(s) == MOE_PATH_GEMM ? moe::launch_ffn_gemm(P, ws, (hipStream_t)stream)
                                                              : moe::launch_ffn_decode(P, ws, (hipStream_t)stream);
     return launch_status(fn, err);
@@ -434,6 +483,48 @@ int moe_combine(const moe_shape *s, const float *y_perm, const float *y_shared, 
     if (s->T == 0) return MOE_OK;  // empty batch
     return launch_status(fn, moe::launch_combine(y_perm, y_shared, inv, topk_w, s->T, s->d, s->k, y,
                                                  (hipStream_t)stream));
+}
+
+int moe_layer(const moe_shape *s, const void *x, const float *W_r, const float *bias, const moe_qffn *routed,
+              const moe_qffn *shared, int32_t *topk_idx, float *topk_w, double *gap, int32_t *counts,
+              int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *uniq, int32_t *n_uniq, float *y_perm,
+              float *y_shared, float *y, uint32_t *diag, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_layer";
+    int rc = check_route_permute(fn, s, x, W_r, bias, topk_idx, topk_w, gap, counts, offsets, perm, inv, uniq,
+                                 n_uniq);
+    if (rc) return rc;
+    rc = check_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag);
+    if (rc) return rc;
+    REQUIRE_PTR_T(y, "y");
+    rc = check_ws(fn, s, ws, ws_bytes);
+    if (rc) return rc;
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t err;
+    if (layer_routes_in_forward(s)) {
+        // logits, then the gate/up launch selects and sorts for itself (workgroup 0 writes the routing
+        // outputs), the down launch, the combine; the partial sums sit past the forward's workspace
+        moe::FfnParams P = forward_params(s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag);
+        double *part = (double *)((char *)ws + moe::decode_workspace_bytes(P));
+        const bool invariant = (s->flags & MOE_FLAG_BATCH_INVARIANT) != 0;
+        int nsplit = 0;
+        err = moe::launch_router_logits(s->act_dtype, x, W_r, s->T, s->d, s->E, invariant, part, &nsplit, st);
+        if (err != hipSuccess) return launch_status(fn, err);
+        P.route = moe::FfnParams::Route{part, nsplit, s->router == MOE_ROUTER_SOFTMAX ? 1 : 0, bias,
+                                        s->routed_scale, topk_idx, topk_w, gap, counts, offsets, perm, inv, uniq,
+                                        n_uniq};
+        err = moe::launch_ffn_decode(P, ws, st);
+    } else {
+        err = run_route_permute(s, x, W_r, bias, topk_idx, topk_w, gap, counts, offsets, perm, inv, uniq, n_uniq, ws,
+                                stream);
+        if (err != hipSuccess) return launch_status(fn, err);
+        if (s->T == 0) return launch_status(fn, hipSuccess);
+        rc = run_forward(fn, s, x, routed, shared, offsets, perm, uniq, n_uniq, y_perm, y_shared, diag, ws, stream);
+        if (rc) return rc;
+        err = hipSuccess;
+    }
+    if (err != hipSuccess) return launch_status(fn, err);
+    return launch_status(fn, moe::launch_combine(y_perm, s->I_shared > 0 ? y_shared : nullptr, inv, topk_w, s->T,
+                                                 s->d, s->k, y, st));
 }
 
 }  // extern "C"

@@ -17,6 +17,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "permute_dev.h"
+#include "select_dev.h"
 #include "topk.h"
 
 #include <type_traits>
@@ -160,83 +161,12 @@ struct FusedPerm {
     int32_t *counts, *offsets, *perm, *inv, *uniq, *n_uniq;  // perm = nullptr: no permutation
 };
 
-// Sum of a over the lanes whose index is congruent to this lane's modulo nq (a power of two <= 64), every
-// lane getting the result, in a fixed order: neighbours and pairs inside quads (DPP quad permutes), lanes 4
-// and 8 apart inside rows of 16 (DPP row rotations), then the other row of each 32 and the other half of the
-// wavefront (16- and 32-lane swaps).  All steps are register moves; the steps below nq are skipped.
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double a) {
-    const int2 b = __builtin_bit_cast(int2, a);
-    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_update_dpp(0, b.x, CTRL, 0xF, 0xF, false),
-                                                __builtin_amdgcn_update_dpp(0, b.y, CTRL, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ double swap_add_f64(double a, bool sixteen) {
-    const int2 b = __builtin_bit_cast(int2, a);
-    int2 p, q;
-    if (sixteen) {
-        const auto x = __builtin_amdgcn_permlane16_swap((uint32_t)b.x, (uint32_t)b.x, false, false);
-        const auto y = __builtin_amdgcn_permlane16_swap((uint32_t)b.y, (uint32_t)b.y, false, false);
-        p = make_int2((int)x[0], (int)y[0]);
-        q = make_int2((int)x[1], (int)y[1]);
-    } else {
-        const auto x = __builtin_amdgcn_permlane32_swap((uint32_t)b.x, (uint32_t)b.x, false, false);
-        const auto y = __builtin_amdgcn_permlane32_swap((uint32_t)b.y, (uint32_t)b.y, false, false);
-        p = make_int2((int)x[0], (int)y[0]);
-        q = make_int2((int)x[1], (int)y[1]);
-    }
-    // the two results hold this lane's value and its partner's, the lower row or half first
-    return __builtin_bit_cast(double, p) + __builtin_bit_cast(double, q);
-}
-__device__ __forceinline__ double sum_congruent(double a, int nq) {
-    if (nq <= 1) a += dpp_f64<0xB1>(a);   // quad_perm 1,0,3,2
-    if (nq <= 2) a += dpp_f64<0x4E>(a);   // quad_perm 2,3,0,1
-    if (nq <= 4) a += dpp_f64<0x124>(a);  // row_ror:4
-    if (nq <= 8) a += dpp_f64<0x128>(a);  // row_ror:8
-    if (nq <= 16) a = swap_add_f64(a, true);
-    if (nq <= 32) a = swap_add_f64(a, false);
-    return a;
-}
-
-// (v, id) is better than (v2, id2): larger score, then lower id
-__device__ __forceinline__ bool better(double v, int id, double v2, int id2) {
-    return v > v2 || (v == v2 && id < id2);
-}
-
-// One DPP step of a wave-wide argmax of (v, id): take the partner's pair when it is better.
-// bound_ctrl off and old = own value: lanes without a partner keep what they have.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void argmax_step(double &v, int &id) {
-    const int2 b = __builtin_bit_cast(int2, v);
-    const int lo = __builtin_amdgcn_update_dpp(b.x, b.x, CTRL, ROW_MASK, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(b.y, b.y, CTRL, ROW_MASK, 0xF, false);
-    const int oid = __builtin_amdgcn_update_dpp(id, id, CTRL, ROW_MASK, 0xF, false);
-    const double ov = __builtin_bit_cast(double, make_int2(lo, hi));
-    if (better(ov, oid, v, id)) {
-        v = ov;
-        id = oid;
-    }
-}
-
-// Wave-wide argmax (larger v, then lower id); the result is returned to every lane.
-__device__ __forceinline__ void wave_argmax(double &v, int &id) {
-    argmax_step<0xB1, 0xF>(v, id);   // quad_perm [1,0,3,2]
-    argmax_step<0x4E, 0xF>(v, id);   // quad_perm [2,3,0,1]
-    argmax_step<0x141, 0xF>(v, id);  // row_half_mirror
-    argmax_step<0x140, 0xF>(v, id);  // row_mirror: lane 15 of each row holds the row's best
-    argmax_step<0x142, 0xA>(v, id);  // row_bcast15: rows 1 and 3 take the last lane of rows 0 and 2
-    argmax_step<0x143, 0xC>(v, id);  // row_bcast31: rows 2 and 3 take lane 31
-    const int2 b = __builtin_bit_cast(int2, v);
-    v = __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(b.x, 63), __builtin_amdgcn_readlane(b.y, 63)));
-    id = __builtin_amdgcn_readlane(id, 63);
-}
-
 // One workgroup (1024 threads) per token.  Thread (e, g) sums the splits s = g, g+4, ... of expert e
 // (fixed order); thread (e, 0) adds the four groups in order and takes sigmoid and bias (one expert per
 // thread, so the code holds one copy of exp and the sigmoids run in parallel); then the first wavefront
 // picks the top k+1.  Each lane holds EJ experts (e = lane + 64 j), sorts them once, and exposes its
 // best unchosen one; each round is one wave-wide argmax and the winning lane moves to its next.
 constexpr int RSEL_THREADS = 1024;
-constexpr int RSEL_LOADS = 8;
 
 // mode 0: sigmoid scores, selection by s + bias.  mode 1: softmax gate, selection by the logits and weights
 // lambda * exp(z_j - z_max) / sum over the selected (the max-subtracted softmax renormalised over them).
@@ -247,115 +177,17 @@ __device__ inline void select_token(const double *__restrict__ part, int nsplit,
                                     const float *__restrict__ bias, float lambda, int mode, int t,
                                     int32_t *__restrict__ idx, float *__restrict__ w, double *__restrict__ gap,
                                     double *zs, int32_t *keys) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int ept = (E + 255) / 256;  // experts per thread column
-    const rsrc_t psrc = make_rsrc(part, (uint32_t)((long)nsplit * T * E * 8));
-    const float bz = (mode == 0 && tid < E) ? bias[tid] : 0.f;  // requested now, used after the sums (E <= RSEL_THREADS)
-    for (int j = 0; j < ept; j++) {
-        const int e = (tid & 255) + 256 * j;
-        const int g = tid >> 8;
-        if (e >= E) continue;
-        double z = 0.0;
-        int sp = g;
-        // batches of RSEL_LOADS independent loads, added in split order
-        for (; sp < nsplit; sp += 4 * RSEL_LOADS) {
-            double a[RSEL_LOADS];
-#pragma unroll
-            for (int m = 0; m < RSEL_LOADS; m++) {
-                const int s2 = sp + 4 * m;
-                a[m] = buf_load_f64(psrc, s2 < nsplit ? (uint32_t)((((long)s2 * T + t) * E + e) * 8) : kOOB);
-            }
-#pragma unroll
-            for (int m = 0; m < RSEL_LOADS; m++) z += a[m];
-        }
-        zs[g * E + e] = z;
-    }
-    __syncthreads();
-    // s and sel of expert e replace its first two partial sums (each thread touches only its own entries)
-    if (tid < E) {
-        const int e = tid;
-        const double z = ((zs[e] + zs[E + e]) + zs[2 * E + e]) + zs[3 * E + e];
-        if (mode == 0) {
-            const double sv = 1.0 / (1.0 + exp(-z));
-            zs[e] = sv;
-            zs[E + e] = sv + (double)bz;
-        } else {
-            zs[e] = z;
-            zs[E + e] = z;
-        }
-    }
-    __syncthreads();
-    if (tid >= 64) return;
-    // this lane's candidates, sorted best first
-    double cv[EJ], cs[EJ];
-    int ci[EJ];
-#pragma unroll
-    for (int j = 0; j < EJ; j++) {
-        const int e = lane + 64 * j;
-        cv[j] = -INFINITY;
-        cs[j] = 0.0;
-        ci[j] = 0x7fffffff;
-        if (e < E) {
-            cs[j] = zs[e];
-            cv[j] = zs[E + e];
-            ci[j] = e;
-        }
-    }
-#pragma unroll
-    for (int a2 = 0; a2 < EJ; a2++)  // insertion sort, fully unrolled (EJ <= 16)
-#pragma unroll
-        for (int b2 = EJ - 1; b2 > a2; b2--)
-            if (better(cv[b2], ci[b2], cv[b2 - 1], ci[b2 - 1])) {
-                const double tv = cv[b2], ts = cs[b2];
-                const int ti = ci[b2];
-                cv[b2] = cv[b2 - 1];
-                cs[b2] = cs[b2 - 1];
-                ci[b2] = ci[b2 - 1];
-                cv[b2 - 1] = tv;
-                cs[b2 - 1] = ts;
-                ci[b2 - 1] = ti;
-            }
-    int head = 0;  // next unchosen candidate of this lane
-    double sum_s = 0.0, prev_v = 0.0, top_z = 0.0;
-    double my_s = 0.0;  // lane r < k keeps the score of choice r
-    int my_id = 0;
-    const int rounds = (k < E) ? k + 1 : k;
-    for (int r = 0; r < rounds; r++) {
-        double hv = -INFINITY, hs = 0.0;
-        int hid = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < EJ; j++)
-            if (head == j) {
-                hv = cv[j];
-                hs = cs[j];
-                hid = ci[j];
-            }
-        double bv = hv;
-        int bid = hid;
-        wave_argmax(bv, bid);
-        const int wl = bid & 63;  // lane that owns the winner
-        const int2 sb = __builtin_bit_cast(int2, hs);
-        const double bs = __builtin_bit_cast(
-            double, make_int2(__builtin_amdgcn_readlane(sb.x, wl), __builtin_amdgcn_readlane(sb.y, wl)));
-        if (r < k) {
-            if (lane == wl) head++;
-            // the weight's numerator: the sigmoid score, or exp(z - z_max) of the softmax gate
-            if (mode == 1 && r == 0) top_z = bs;
-            const double u = mode == 0 ? bs : exp(bs - top_z);
-            sum_s += u;
-            if (lane == r) {
-                my_s = u;
-                my_id = bid;
-            }
-            prev_v = bv;
-        } else if (lane == 0 && gap) {
-            gap[t] = prev_v - bv;
-        }
-    }
-    if (lane == 0 && gap && k >= E) gap[t] = INFINITY;
+    token_scores<RSEL_THREADS>(part, nsplit, T, E, bias, mode, t, zs);
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    int my_id;
+    float my_w;
+    double g;
+    topk_pick<EJ>(zs, E, k, lambda, mode, my_id, my_w, g);
+    if (lane == 0 && gap) gap[t] = g;
     if (lane < k) {
         idx[(long)t * k + lane] = my_id;
-        w[(long)t * k + lane] = (float)((double)lambda * my_s / sum_s);
+        w[(long)t * k + lane] = my_w;
         if (keys) keys[t * k + lane] = my_id;
     }
 }
@@ -618,11 +450,12 @@ bool router_fused(int T, int E, bool inv, int router, int C) {
     return T >= 1 && T <= RS_FUSE_TMAX && router != 2 && C <= 0;
 }
 
-hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
-                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
-                         hipStream_t stream, const PermOut *po) {
-    double *part = (double *)ws;
-    char *vws = (char *)ws + r_al256((size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double));
+size_t router_partials_bytes(int T, int d, int E, bool inv) {
+    return r_al256((size_t)router_nsplit(T, d, E, inv) * (size_t)T * (size_t)E * sizeof(double));
+}
+
+hipError_t launch_router_logits(int act, const void *x, const float *Wr, int T, int d, int E, bool inv, double *part,
+                                int *nsplit_out, hipStream_t stream) {
     int nsplit;
     if (use_skinny(T, E, inv)) {
         const int rows = skinny_rows(d, E);
@@ -643,7 +476,17 @@ hipError_t launch_router(int act, const void *x, const float *Wr, const float *b
         else
             hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, stream, x, Wr, T, d, E, chunk, part);
     }
-    hipError_t err = hipGetLastError();
+    *nsplit_out = nsplit;
+    return hipGetLastError();
+}
+
+hipError_t launch_router(int act, const void *x, const float *Wr, const float *bias, int T, int d, int E, int k,
+                         float lambda, int32_t *idx, float *w, double *gap, void *ws, bool inv, int router, int C,
+                         hipStream_t stream, const PermOut *po) {
+    double *part = (double *)ws;
+    char *vws = (char *)ws + router_partials_bytes(T, d, E, inv);
+    int nsplit = 0;
+    hipError_t err = launch_router_logits(act, x, Wr, T, d, E, inv, part, &nsplit, stream);
     if (err != hipSuccess) return err;
     if (router == 2) {
         // expert choice: per-token softmax, then per expert the C tokens of largest probability

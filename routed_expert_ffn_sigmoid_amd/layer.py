@@ -135,7 +135,18 @@ class MoeRun:
         B.moe_route_permute(self.shape, x, W.W_r, W.bias, self.idx, self.w, self.gap, self.counts, self.offsets,
                             self.perm, self.inv, self.uniq, self.n_uniq, self.ws, stream=stream)
 
+    def layer(self, x, W: DeviceLayerWeights, stream=None):
+        B.moe_layer(self.shape, x, W.W_r, W.bias, W.routed_q, W.shared_q, self.idx, self.w, self.gap, self.counts,
+                    self.offsets, self.perm, self.inv, self.uniq, self.n_uniq, self.y_perm, self.y_shared, self.y,
+                    self.diag, self.ws, stream=stream)
+
     def run(self, x, W: DeviceLayerWeights, stream=None):
+        """The layer in one call (moe_layer); the same bits as run_calls."""
+        self.layer(x, W, stream)
+        return self.y
+
+    def run_calls(self, x, W: DeviceLayerWeights, stream=None):
+        """The layer as the three calls moe_route_permute, moe_forward, moe_combine."""
         self.route_permute(x, W, stream)
         self.forward(x, W, stream)
         self.combine(stream)

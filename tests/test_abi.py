@@ -338,3 +338,36 @@ def test_route_permute_checks():
     with pytest.raises(B.MoeError) as ei:
         B.moe_route_permute(s, **args, ws_bytes=need - 1, stream=0)
     assert ei.value.code == B.MOE_EWORKSPACE
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_layer_checks(T):
+    """moe_layer refuses what any of its three calls refuses, before anything is enqueued (the fake pointers are
+    never dereferenced), and needs the workspace moe_workspace_size gives: at T = 1 that covers the router's
+    partial sums beside the forward's area."""
+    s = shape(T=T, I_shared=256)
+    need = B.moe_workspace_size(s)
+    q = B.make_qffn(*([FAKE] * 9))
+    args = dict(x=FAKE, W_r=FAKE, bias=FAKE, routed=q, shared=q, topk_idx=FAKE, topk_w=FAKE, gap=None, counts=FAKE,
+                offsets=FAKE, perm=FAKE, inv=FAKE, uniq=FAKE, n_uniq=FAKE, y_perm=FAKE, y_shared=FAKE, y=FAKE,
+                diag=None, ws=FAKE)
+    for miss in ("x", "W_r", "bias", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "uniq", "n_uniq",
+                 "y_perm", "y_shared", "y", "ws"):
+        a = dict(args)
+        a[miss] = None
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_layer(s, **a, ws_bytes=need, stream=0)
+        assert ei.value.code == (B.MOE_EWORKSPACE if miss == "ws" else B.MOE_EINVAL), miss
+    a = dict(args)
+    a["shared"] = B.make_qffn(*([FAKE] * 8 + [None]))
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer(s, **a, ws_bytes=need, stream=0)
+    assert ei.value.code == B.MOE_EINVAL
+    a = dict(args)
+    a["y"] = FAKE + 4
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer(s, **a, ws_bytes=need, stream=0)
+    assert ei.value.code == B.MOE_EALIGN
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer(s, **args, ws_bytes=need - 1, stream=0)
+    assert ei.value.code == B.MOE_EWORKSPACE
