@@ -1,14 +1,14 @@
 """MoE-layer forward benchmark on one MI355X.
 
-One step = one pass of the whole layer (moe_route_permute, i.e. the router
-and the permutation -> moe_forward -> moe_combine) over one batch of seeded
-synthetic tokens, with
-all inputs already resident in HBM.  Decode workloads rotate over several
+One step = one pass of the whole layer (moe_layer: the router, the
+permutation, moe_forward and moe_combine in one call; a single token is
+routed inside the forward's first launch) over one batch of seeded
+synthetic tokens, with all inputs already resident in HBM.  Decode workloads rotate over several
 resident layers and a pool of activation batches so that neither the 256 MB
 Infinity Cache nor L2 holds the expert weights between steps.
 
-Each step of the rotation is captured once as a HIP graph (the three ABI
-calls) and replayed, so host launch overhead does not enter the timing.
+Each step of the rotation is captured once as a HIP graph (the moe_layer
+call) and replayed, so host launch overhead does not enter the timing.
 
 Prints ONE JSON line (the driver's contract).  The top level is the headline
 workload (mid layer, T = 1 by default): `value` is MoE-layer tokens/s.
@@ -208,7 +208,7 @@ def measure(spec, T, args, dev):
         n_uniq[i] = int(runs[i].n_uniq.item())
     torch.cuda.synchronize()
 
-    # HIP graphs: one per step of the rotation (the four ABI calls), and one of a whole rotation of
+    # HIP graphs: one per step of the rotation (the moe_layer call), and one of a whole rotation of
     # moe_forward calls for the expert-FFN stage timing
     side = torch.cuda.Stream()
     step_graphs = []

@@ -1,10 +1,11 @@
 """moe_layer against moe_route_permute, moe_forward and moe_combine called in turn: the same bits for every output.
 
 For one token on the decode path with a top-k router and no capacity, moe_layer selects and sorts inside the
-forward's first launch (every workgroup for itself, the first writing the routing outputs); elsewhere it runs
-the three calls' kernels.  The cases cover both forms: sigmoid and softmax routers, a non-power-of-two E (the
-matrix-core logits kernel), int4 and int8 weights, bf16 and fp32 activations, with and without a shared expert,
-the batch-invariant mode, k = E (soft routing), capacity, and the empty batch.
+forward's first launch (every workgroup for itself from the logits kernel's partial sums, the first writing the
+routing outputs); elsewhere it runs the three calls' kernels.  The cases cover both forms: sigmoid and softmax
+routers, E from 4 to 256 (every block shape of the single-token logits kernel) and a non-power-of-two E (the
+matrix-core logits kernel), int4 and int8 weights, bf16 and fp32 activations, with and without a shared
+expert, the batch-invariant mode, k = E (soft routing), capacity, and the empty batch.
 """
 import pytest
 import torch
@@ -40,6 +41,10 @@ CASES = {
     "E8_k2_int8_f32_T1": (dict(d=4096, E=8, k=2, I=512, I_shared=0, wbits=8, act=synth.ACT_F32, routed_scale=1.0,
                                 bias="uniform0.01"), 1, 0, 0, 0.0),
     "E64_T1": (dict(), 1, 0, 0, 0.0),
+    "tiny_E8_k2_int8_f32_T1": (dict(d=256, E=8, k=2, I=512, I_shared=0, wbits=8, act=synth.ACT_F32,
+                                    routed_scale=1.0, bias="uniform0.01"), 1, 0, 0, 0.0),
+    "E4_k2_T1": (dict(d=512, E=4, k=2), 1, 0, 0, 0.0),
+    "E32_k4_f32_T1": (dict(d=2048, E=32, k=4, act=synth.ACT_F32), 1, 0, 0, 0.0),
     "E64_noshared_T1": (dict(I_shared=0), 1, 0, 0, 0.0),
     "softmax_E64_T1": (dict(), 1, B.MOE_ROUTER_SOFTMAX, 0, 0.0),
     "E12_k3_T1": (dict(E=12, k=3), 1, 0, 0, 0.0),
