@@ -630,7 +630,13 @@ __device__ void route_one_token(const FfnParams &P, int *tab, double *zs) {
 // PASSES (down only): the digit planes hold gcap < T token rows, so a slot with more rows is taken as
 // several virtual slots of at most gcap rows each, in row order, each streaming the expert's rows again
 // (the mid workload's down pass at T = 4: 3 x 14336 inputs of planes fit the LDS, 4 do not).
-template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES>
+// COMB (down only, one token, FfnParams::comb_y set): the combine runs in this launch.  The h rows of all
+// nsl = n_uniq + shared slots are staged at once (planes row s = slot s, gcap = nsl), items are numbered
+// tile-major (item i = tile i / nsl of slot i % nsl) and ranges are cut at tiles, so a workgroup takes every
+// slot of its rows in turn.  The wavefront that finishes a row of a slot keeps its output in LDS; after the
+// tile's last slot it adds, as the combine kernel does, y = y_shared + w_0 Y_0 + w_1 Y_1 + ... in fp32 fmaf
+// (choice j's output is slot inv[j]'s: one row per slot at T = 1).
+template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES, bool COMB>
 __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(FfnParams P, float *__restrict__ h,
                                                                            float *__restrict__ h_sh, int kpad,
                                                                            int tiles_r, int tiles_s, int ncu,
@@ -643,6 +649,10 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     __shared__ int wexpo[NW][DK_GMAX];
     __shared__ double wxsum[NW][DK_GMAX];
     __shared__ uint32_t zero_area[8];
+    // COMB: each wavefront's outputs of its 16 rows per slot, and the token's choices (inv, w)
+    __shared__ float ycomb[COMB ? NW : 1][COMB ? DK_GMAX : 1][16];
+    __shared__ int c_inv[COMB ? DK_GMAX : 1];
+    __shared__ float c_w[COMB ? DK_GMAX : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave indices stay scalar
     const int tile_w = wv / S, kp = wv % S;
@@ -655,7 +665,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     int *tab = (int *)dk_lds;
     const int *t_uniq = tab + 1, *t_off = tab + 1 + nrs, *t_perm = tab + 2 + nrs + P.E;
     const int stride = kpad + 16;
-    const long pb = (long)(PASSES ? gcap : T) * stride;  // bytes per digit plane of one K part
+    const long pb = (long)(PASSES || COMB ? gcap : T) * stride;  // bytes per digit plane of one K part
     const int vwords = PASSES ? nrs + 2 : 0;               // first virtual slot of each slot (PASSES)
     int *vpre = tab + tab_words;
     const long pl0 = ((long)(tab_words + vwords) * 4 + 15) & ~15L;
@@ -695,6 +705,10 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             const int kpart = kd / S;
             const long ro = (long)tile_w * kd + kp * kpart;
             stage_issue<SRCX>(xsrc0, ro, tile_w < T ? 0 : kpad, kpad / 8, kpart, raw0);
+        }
+        if (COMB && tid < P.k) {
+            c_inv[tid] = P.comb_inv[tid];
+            c_w[tid] = P.comb_w[tid];
         }
 #pragma unroll
         for (int q = 0; q < DKP_TAB_PER_THREAD; q++) {
@@ -741,14 +755,15 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         nvs = P.Is > 0 ? (T + gcap - 1) / gcap : 0;
     }
     // item counts stay far below 2^31 / ncu (at most 1025 slots x 2^16 tiles), so 32-bit index math
-    const int N = nvr * tiles_r + nvs * tiles_s;
+    const int nsl = nu + (P.Is > 0 ? 1 : 0);  // COMB: slots per tile
+    const int N = COMB ? tiles_r : nvr * tiles_r + nvs * tiles_s;  // COMB: ranges count tiles
     // With one tile per item (S = NW) the ranges are cut in half tiles (8 rows): every CU gets the same
     // number of rows to within 8, and a range may begin or end in the middle of a tile, whose rows
     // outside it read and store nothing.  Otherwise the ranges are cut in items.
     constexpr bool HALVES = TPW == 1;
     const int NU = HALVES ? 2 * N : N;
     int u0, u1;
-    if (MODE == 0 || HALVES) {
+    if (MODE == 0 || HALVES || COMB) {
         const int G = gridDim.x, b = blockIdx.x;
         if (G % ncu == 0 && NU >= G) {
             const int m = G / ncu, c = b % ncu, r = b / ncu;
@@ -789,12 +804,31 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         u0 = bound(blockIdx.x);
         u1 = bound(blockIdx.x + 1);
     }
-    const int i0 = HALVES ? u0 >> 1 : u0, i1 = HALVES ? (u1 + 1) >> 1 : u1;
+    const int i0 = (HALVES ? u0 >> 1 : u0) * (COMB ? nsl : 1), i1 = (HALVES ? (u1 + 1) >> 1 : u1) * (COMB ? nsl : 1);
     if (i0 >= i1) return;  // uniform over the workgroup
 
     auto decode = [&](int i) {
         DItem it;
-        if (PASSES) {
+        const int tile = COMB ? i / nsl : 0;
+        if (COMB) {
+            const int sl = i - tile * nsl;
+            it.slot = sl;
+            it.tile = tile;
+            it.ng = 1;
+            if (sl < nu) {
+                it.e = __builtin_amdgcn_readfirstlane(t_uniq[sl]);
+                it.w = weight_row(P, it.e);
+                it.shared = false;
+                it.I = P.I;
+                it.p0 = __builtin_amdgcn_readfirstlane(t_off[it.e]);
+            } else {
+                it.e = 0;
+                it.w = 0;
+                it.shared = true;
+                it.I = P.Is;
+                it.p0 = 0;
+            }
+        } else if (PASSES) {
             const int vs = i / tiles_r;
             it.slot = vs;
             it.tile = i % tiles_r;
@@ -848,7 +882,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         it.kpart_bytes = K / S * WBITS / 8;
         it.nseg_pad = ((it.kpart_bytes + 63) / 64 + PF - 1) / PF * PF;
         it.row = (it.tile * TPW + tile_w) * 16 + j;
-        const int u = 2 * i + (j >> 3);  // half tile of this lane's row
+        const int u = 2 * (COMB ? tile : i) + (j >> 3);  // half tile of this lane's row
         it.row_ok = it.row < nout && (!HALVES || (u >= u0 && u < u1)) && it.w >= 0;
         if (it.w < 0) it.w = 0;  // not resident: reads nothing (row_ok false), writes nothing
         return it;
@@ -905,6 +939,38 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < PF; b++) ld(b, wr_cur, off_cur, cur.kpart_bytes, b);
+    } else if (COMB) {
+        // the h rows of every slot, planes row r = slot r: each wavefront stages rows tile_w and
+        // tile_w + TPW (the host keeps nsl <= 2 TPW), both requested before the weights
+        auto row_src = [&](int r, rsrc_t &src, long &ro, int &kpart) {
+            const bool sh = r >= nu;
+            const int I = sh ? P.Is : P.I;
+            kpart = I / S;
+            const long p0 = sh ? 0 : __builtin_amdgcn_readfirstlane(t_off[__builtin_amdgcn_readfirstlane(t_uniq[r])]);
+            src = make_rsrc(sh ? h_sh : h, (uint32_t)((long)(sh ? T : P.A) * I * 4));
+            ro = p0 * I + kp * kpart;
+        };
+        const int r1 = tile_w, r2 = tile_w + TPW;
+        const bool st1 = r1 < nsl, st2 = r2 < nsl;
+        rsrc_t src1, src2;
+        long ro1, ro2;
+        int kpart1, kpart2;
+        row_src(st1 ? r1 : 0, src1, ro1, kpart1);
+        row_src(st2 ? r2 : 0, src2, ro2, kpart2);
+        StageRaw<SRCX> raw1, raw2;
+        stage_issue<SRCX>(src1, ro1, st1 ? 0 : kpad, kpad / 8, kpart1, raw1);
+        stage_issue<SRCX>(src2, ro2, st2 ? 0 : kpad, kpad / 8, kpart2, raw2);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < PF; b++) ld(b, wr_cur, off_cur, cur.kpart_bytes, b);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st1)
+            stage_finish<WBITS, SRCX>(raw1, src1, ro1, r1, kpad / 8, kpart1, stride, pb, planes, wexpo[kp],
+                                      wxsum[kp]);
+        if (st2)
+            stage_finish<WBITS, SRCX>(raw2, src2, ro2, r2, kpad / 8, kpart2, stride, pb, planes, wexpo[kp],
+                                      wxsum[kp]);
     } else {
         // Rows of h: those of the slot are known only after the table round.  Each staging wavefront's
         // first row is requested before any wavefront starts its weights (when fewer rows than tiles
@@ -947,7 +1013,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             off_nxt = off_cur;
         }
         // ---- down: the rows of h of a new slot
-        if (MODE == 1 && cur.slot != staged_slot) {
+        if (MODE == 1 && !COMB && cur.slot != staged_slot) {
             const rsrc_t src = h_src(cur);
             const int kpart = cur.I / S;
             const long base = cur.p0;
@@ -965,7 +1031,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
 
         // ---- A-operand row of this lane: the token (gate/up) or slot row (down) at position j
         int trow = -1;
-        if (j < cur.ng) trow = MODE == 0 ? (cur.shared ? j : t_perm[cur.p0 + j] / P.k) : j;
+        if (j < cur.ng) trow = MODE == 0 ? (cur.shared ? j : t_perm[cur.p0 + j] / P.k) : (COMB ? cur.slot : j);
         const bool tok_ok = trow >= 0;
         const int8_t *xrow = tok_ok ? planes + (long)trow * stride : (const int8_t *)zero_area;
         const long pstep = tok_ok ? pb : 0;
@@ -1020,7 +1086,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         for (int r = 0; r < 4; r++) {
             const int i2 = 4 * g + r;
             const bool ok = i2 < cur.ng;
-            const int pr = ok ? (MODE == 0 ? (cur.shared ? i2 : t_perm[cur.p0 + i2] / P.k) : i2) : 0;
+            const int pr = ok ? (MODE == 0 ? (cur.shared ? i2 : t_perm[cur.p0 + i2] / P.k) : (COMB ? cur.slot : i2)) : 0;
             const double unit = ok ? ldexp(1.0, -wexpo[kp][pr]) : 0.0;
             const double xs = ok ? wxsum[kp][pr] : 0.0;
 #pragma unroll
@@ -1067,6 +1133,18 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
                             P.y_sh[(long)(cur.p0 + i2) * P.d + o] = y;
                         else
                             P.y_perm[(long)(cur.p0 + i2) * P.d + o] = y;
+                        if (COMB) {
+                            // the same lane holds row o for every slot of the tile: the last slot combines
+                            ycomb[wv][cur.slot][j] = y;
+                            if (cur.slot == nsl - 1) {
+                                float acc = P.Is > 0 ? ycomb[wv][nu][j] : 0.f;
+                                for (int c = 0; c < P.k; c++) {
+                                    const int p = c_inv[c];
+                                    if (p >= 0 && p < nu) acc = fmaf(c_w[c], ycomb[wv][p][j], acc);
+                                }
+                                P.comb_y[o] = acc;
+                            }
+                        }
                     }
                 }
             }
@@ -1223,13 +1301,13 @@ static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad, int g
     return tab + (size_t)S * 3 * g * (kpad + 16) + dkp_red_bytes(mode);
 }
 
-template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES>
+template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES, bool COMB = false>
 static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, int gcap, hipStream_t stream) {
     const int rows_per_item = 16 * (DKP_WAVES / S);
     const int tiles_r = ((MODE == 0 ? P.I : P.d) + rows_per_item - 1) / rows_per_item;
     const int tiles_s = P.Is > 0 ? ((MODE == 0 ? P.Is : P.d) + rows_per_item - 1) / rows_per_item : 0;
     const size_t lds = dkp_lds_bytes(MODE, S, P, kpad, gcap);
-    auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S, PF, PASSES>;
+    auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S, PF, PASSES, COMB>;
     hipError_t err = allow_lds(fn, lds);
     if (err != hipSuccess) return err;
     const int ncu = device_cus();
@@ -1263,10 +1341,9 @@ static hipError_t dkp_launch_pass(const FfnParams &P, float *h, float *h_sh, int
     }
 }
 
-// Launches the persistent kernel if the digit planes of all T tokens fit (for the down pass: of at least one
-// token, the slots then taken in passes); *done tells whether it did.
 // The persistent kernel's K split, padded K part and token rows per pass for pass `mode`; false when the
-// token-group kernel takes the pass instead.
+// token-group kernel takes the pass instead.  With the combine in the down launch (P.comb_y), the planes hold
+// the rows of every slot of the token, and false means that form does not fit.
 struct DkpPlan {
     int S, kpad, gcap;
 };
@@ -1285,12 +1362,29 @@ static bool dkp_plan(int mode, const FfnParams &P, DkpPlan *pl) {
     const int kpad = pad_k(K / S, wbits);
     if (P.T > DK_GMAX || dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64)
         return false;
+    if (mode == 1 && P.comb_y) {
+        // each wavefront stages at most two rows (nsl <= 2 TPW), and the ranges, cut at tiles so that a
+        // workgroup holds every slot of its rows, give the busiest CU no more items than the plain split
+        const int nsl = P.n_routed_slots + (P.Is > 0 ? 1 : 0);
+        const int tpw = DKP_WAVES / S, ncu = device_cus();
+        const long tiles = (P.d + 16 * tpw - 1) / (16 * tpw), units = tpw == 1 ? 2 * tiles : tiles;
+        if (P.T != 1 || nsl > DK_GMAX || nsl > 2 * tpw || dkp_lds_bytes(1, S, P, kpad, nsl) > DKP_LDS_BUDGET)
+            return false;
+        if ((units + ncu - 1) / ncu * nsl > (units * nsl + ncu - 1) / ncu) return false;
+        *pl = DkpPlan{S, kpad, nsl};
+        return true;
+    }
     // token rows the planes hold: all T, or (down) fewer, with the slots taken in passes
     int gcap = P.T;
     while (gcap > 0 && dkp_lds_bytes(mode, S, P, kpad, gcap) > DKP_LDS_BUDGET) gcap--;
     if (gcap < 1 || (mode == 0 && gcap < P.T)) return false;
     *pl = DkpPlan{S, kpad, gcap};
     return true;
+}
+
+bool decode_combines(const FfnParams &P) {
+    DkpPlan pl;
+    return P.T == 1 && P.comb_y && P.k <= DK_GMAX && dkp_plan(1, P, &pl);
 }
 
 bool decode_routes(const FfnParams &P) {
@@ -1300,6 +1394,8 @@ bool decode_routes(const FfnParams &P) {
     return (size_t)pl.S * 3 * pl.gcap * (pl.kpad + 16) >= (size_t)32 * P.E + (size_t)4 * P.k;
 }
 
+// Launches the persistent kernel if the digit planes of all T tokens fit (for the down pass: of at least one
+// token, the slots then taken in passes); *done tells whether it did.
 template <int MODE, int WBITS, int SRC>
 static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t stream, bool *done) {
     *done = false;
@@ -1312,6 +1408,20 @@ static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t
     constexpr int PFA = MODE == 0 ? 8 : 16, PFB = MODE == 0 ? 7 : 14;
     const bool deep = dkp_pf(MODE, (K / S * WBITS / 8 + 63) / 64) == PFA;
     if (MODE == 1 && gcap < P.T) return dkp_launch_pass<MODE, WBITS, SRC>(P, h, h_sh, kpad, gcap, S, deep, stream);
+    if constexpr (MODE == 1) {
+        if (P.comb_y) {
+            switch (S) {
+                case 8: return deep ? dkp_launch_s<1, WBITS, SRC, 8, PFA, false, true>(P, h, h_sh, kpad, gcap, stream)
+                                    : dkp_launch_s<1, WBITS, SRC, 8, PFB, false, true>(P, h, h_sh, kpad, gcap, stream);
+                case 4: return deep ? dkp_launch_s<1, WBITS, SRC, 4, PFA, false, true>(P, h, h_sh, kpad, gcap, stream)
+                                    : dkp_launch_s<1, WBITS, SRC, 4, PFB, false, true>(P, h, h_sh, kpad, gcap, stream);
+                case 2: return deep ? dkp_launch_s<1, WBITS, SRC, 2, PFA, false, true>(P, h, h_sh, kpad, gcap, stream)
+                                    : dkp_launch_s<1, WBITS, SRC, 2, PFB, false, true>(P, h, h_sh, kpad, gcap, stream);
+                default: return deep ? dkp_launch_s<1, WBITS, SRC, 1, PFA, false, true>(P, h, h_sh, kpad, gcap, stream)
+                                     : dkp_launch_s<1, WBITS, SRC, 1, PFB, false, true>(P, h, h_sh, kpad, gcap, stream);
+            }
+        }
+    }
     switch (S) {
         case 8: return deep ? dkp_launch_s<MODE, WBITS, SRC, 8, PFA, false>(P, h, h_sh, kpad, gcap, stream)
                             : dkp_launch_s<MODE, WBITS, SRC, 8, PFB, false>(P, h, h_sh, kpad, gcap, stream);
@@ -1343,7 +1453,9 @@ static hipError_t dk_launch_s(const FfnParams &P, float *h, float *h_sh, int kpa
 
 template <int MODE, int WBITS, int SRC>
 static hipError_t dk_launch_mode(const FfnParams &P, float *h, float *h_sh, hipStream_t stream) {
-    if (MODE == 0 && P.route.part && !decode_routes(P)) return hipErrorInvalidValue;  // only the persistent kernel routes
+    // only the persistent kernel routes, and combines
+    if (MODE == 0 && P.route.part && !decode_routes(P)) return hipErrorInvalidValue;
+    if (MODE == 1 && P.comb_y && !decode_combines(P)) return hipErrorInvalidValue;
     bool done = false;
     hipError_t err = dkp_try<MODE, WBITS, SRC>(P, h, h_sh, stream, &done);
     if (done || err != hipSuccess) return err;

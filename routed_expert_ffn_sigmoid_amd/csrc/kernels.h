@@ -45,6 +45,11 @@ struct FfnParams {
         double *gap;  // optional
         int32_t *counts, *offsets, *perm, *inv, *uniq, *n_uniq;
     } route;
+    // The combine inside the decode down launch (one token): y = y_sh + sum_j comb_w[j] y_perm[comb_inv[j]],
+    // written to comb_y (nullptr: no combine here).
+    const int32_t *comb_inv;
+    const float *comb_w;
+    float *comb_y;
 };
 
 // Routed weight row of expert e (wave-uniform e), or -1 when that row is outside the weights.
@@ -88,6 +93,8 @@ const char *decode_unsupported(const FfnParams &P);  // nullptr when the decode 
 size_t decode_workspace_bytes(const FfnParams &P);
 // true when the decode launches can route a single token inside the gate/up launch (FfnParams::route)
 bool decode_routes(const FfnParams &P);
+// true when the decode down launch can also combine (FfnParams::comb_y; one token, its slots' rows in LDS)
+bool decode_combines(const FfnParams &P);
 hipError_t launch_ffn_decode(const FfnParams &P, void *ws, hipStream_t stream);
 
 // ffn_gemm.hip: MFMA grouped-GEMM path (d and I multiples of 64; fp32 activations as fp16 hi + lo)

@@ -512,7 +512,13 @@ int moe_layer(const moe_shape *s, const void *x, const float *W_r, const float *
         P.route = moe::FfnParams::Route{part, nsplit, s->router == MOE_ROUTER_SOFTMAX ? 1 : 0, bias,
                                         s->routed_scale, topk_idx, topk_w, gap, counts, offsets, perm, inv, uniq,
                                         n_uniq};
+        // the combine in the down launch when the token's slots fit its LDS
+        P.comb_inv = inv;
+        P.comb_w = topk_w;
+        P.comb_y = y;
+        if (!moe::decode_combines(P)) P.comb_y = nullptr;
         err = moe::launch_ffn_decode(P, ws, st);
+        if (err != hipSuccess || P.comb_y) return launch_status(fn, err);
     } else {
         err = run_route_permute(s, x, W_r, bias, topk_idx, topk_w, gap, counts, offsets, perm, inv, uniq, n_uniq, ws,
                                 stream);

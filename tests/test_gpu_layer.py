@@ -2,7 +2,8 @@
 
 For one token on the decode path with a top-k router and no capacity, moe_layer selects and sorts inside the
 forward's first launch (every workgroup for itself from the logits kernel's partial sums, the first writing the
-routing outputs); elsewhere it runs the three calls' kernels.  The cases cover both forms: sigmoid and softmax
+routing outputs), and where the token's slots fit and balance, the combine inside the down launch; elsewhere it
+runs the three calls' kernels.  The cases cover both forms: sigmoid and softmax
 routers, E from 4 to 256 (every block shape of the single-token logits kernel) and a non-power-of-two E (the
 matrix-core logits kernel), int4 and int8 weights, bf16 and fp32 activations, with and without a shared
 expert, the batch-invariant mode, k = E (soft routing), capacity, and the empty batch.
@@ -41,6 +42,10 @@ CASES = {
     "E8_k2_int8_f32_T1": (dict(d=4096, E=8, k=2, I=512, I_shared=0, wbits=8, act=synth.ACT_F32, routed_scale=1.0,
                                 bias="uniform0.01"), 1, 0, 0, 0.0),
     "E64_T1": (dict(), 1, 0, 0, 0.0),
+    # down launches that also combine: two slots per token over 256 tiles of 32 rows
+    "combine_E8_k2_T1": (dict(d=8192, E=8, k=2, I=4096, I_shared=0), 1, 0, 0, 0.0),
+    "combine_E8_k1_shared_T1": (dict(d=8192, E=8, k=1, I=4096, I_shared=4096), 1, 0, 0, 0.0),
+    "combine_softmax_E8_k2_T1": (dict(d=8192, E=8, k=2, I=4096, I_shared=0), 1, B.MOE_ROUTER_SOFTMAX, 0, 0.0),
     "tiny_E8_k2_int8_f32_T1": (dict(d=256, E=8, k=2, I=512, I_shared=0, wbits=8, act=synth.ACT_F32,
                                     routed_scale=1.0, bias="uniform0.01"), 1, 0, 0, 0.0),
     "E4_k2_T1": (dict(d=512, E=4, k=2), 1, 0, 0, 0.0),
