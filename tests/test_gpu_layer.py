@@ -6,7 +6,7 @@ routing outputs), and where the token's slots fit and balance, the combine insid
 runs the three calls' kernels.  The cases cover both forms: sigmoid and softmax
 routers, E from 4 to 256 (every block shape of the single-token logits kernel) and a non-power-of-two E (the
 matrix-core logits kernel), int4 and int8 weights, bf16 and fp32 activations, with and without a shared
-expert, the batch-invariant mode, k = E (soft routing), capacity, and the empty batch.
+expert, the batch-invariant mode, k = E (soft routing), capacity, and the empty batch and T > 1.
 """
 import pytest
 import torch
@@ -57,6 +57,8 @@ CASES = {
     "invariant_E256_T1": (dict(d=7168, E=256, k=8, I=128, I_shared=128), 1, 0, B.MOE_FLAG_BATCH_INVARIANT, 0.0),
     "capacity_T1": (dict(), 1, 0, 0, 1.25),
     "unfused_T3": (dict(), 3, 0, 0, 0.0),
+    "E256_k8_shared_T4": (dict(d=7168, E=256, k=8, I=128, I_shared=128), 4, 0, 0, 0.0),
+    "E12_k3_T6": (dict(E=12, k=3), 6, 0, 0, 0.0),
     "unfused_gemm_T40": (dict(d=1024, E=16, k=4, I=256, I_shared=256), 40, 0, 0, 0.0),
     "empty_T0": (dict(), 0, 0, 0, 0.0),
 }
