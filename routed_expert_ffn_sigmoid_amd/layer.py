@@ -1,4 +1,5 @@
-"""Device-resident MoE layer: uploads seeded synthetic inputs and runs the four ABI calls.
+"""Device-resident MoE layer: uploads seeded synthetic inputs and runs the ABI calls (the four steps one by one,
+or the whole layer in one moe_layer call).
 
 torch provides device memory and the stream; every step of the layer runs in
 libmoe_hip.so through the binding.

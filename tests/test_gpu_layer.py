@@ -54,6 +54,8 @@ CASES = {
     "softmax_E64_T1": (dict(), 1, B.MOE_ROUTER_SOFTMAX, 0, 0.0),
     "E12_k3_T1": (dict(E=12, k=3), 1, 0, 0, 0.0),
     "soft_k_eq_E_T1": (dict(E=16, k=16, I=128), 1, B.MOE_ROUTER_SOFTMAX, 0, 0.0),
+    "E64_k24_T1": (dict(E=64, k=24, I=128), 1, 0, 0, 0.0),
+    "E512_k8_T1": (dict(d=1024, E=512, k=8, I=64), 1, 0, 0, 0.0),  # beyond the in-launch selection: three calls
     "invariant_E256_T1": (dict(d=7168, E=256, k=8, I=128, I_shared=128), 1, 0, B.MOE_FLAG_BATCH_INVARIANT, 0.0),
     "capacity_T1": (dict(), 1, 0, 0, 1.25),
     "unfused_T3": (dict(), 3, 0, 0, 0.0),
