@@ -321,7 +321,8 @@ MOE_API int moe_layer(const moe_shape *shape, const void *x, const float *W_r, c
 /* Message describing the calling thread's last failed call ("" if none). */
 MOE_API const char *moe_last_error(void);
 
-/* ABI version: increases when a signature or a layout changes. */
+/* ABI version: increases when an entry point is added or removed, or a signature or a layout changes
+ * (4: moe_layer). */
 MOE_API int moe_abi_version(void);
 
 #ifdef __cplusplus

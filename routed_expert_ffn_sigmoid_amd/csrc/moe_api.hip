@@ -185,7 +185,7 @@ int launch_status(const char *fn, hipError_t err) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 const char *moe_last_error(void) { return g_err; }
 

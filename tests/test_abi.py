@@ -371,3 +371,7 @@ def test_layer_checks(T):
     with pytest.raises(B.MoeError) as ei:
         B.moe_layer(s, **args, ws_bytes=need - 1, stream=0)
     assert ei.value.code == B.MOE_EWORKSPACE
+
+
+def test_abi_version():
+    assert B.moe_abi_version() == 4
