@@ -1,15 +1,19 @@
 // Sigmoid + bias top-k router ("25GB 内存跑 744B GLM-5.2 模型" page, sections 三.1 and 四.3).
 //
 // Two kernels:
-//   logits  z = x . W_r in fp64, split over blocks of d rows so that even one
-//           token spreads the W_r read over the whole chip.  T <= 4: each
-//           workgroup streams a block of >= 64 KB of W_r rows once for all tokens;
-//           larger T: 64 tokens x 64 experts register tiles.  At most 32 blocks
-//           at small T, so the partials are few.  Partial sums per
-//           block go to the workspace (no atomics: the reduction order is fixed).
-//   select  one workgroup per token: adds the partials in a fixed order, takes
-//           the sigmoid, adds the bias, and picks the top k+1 by repeated
-//           wave-wide argmax with ties to the lower id.
+//   logits  z = x . W_r in fp64, split over blocks of d rows (and, for few
+//           tokens, of 32 experts) so that even one token spreads the W_r read
+//           over the whole chip.  T <= 4: 1024-thread workgroups each stream a
+//           block of at least 8 KB of W_r once for all tokens, at most 32 row
+//           blocks so the partials are few; larger T: fp64 matrix cores on tiles
+//           of 64 tokens x 256 experts.  Partial sums per block go to the
+//           workspace (no atomics: the reduction order is fixed).
+//   select  one workgroup per token (for one token whose permutation is asked
+//           for, that workgroup also sorts): adds the partials in a fixed order,
+//           takes the sigmoid, adds the bias, and picks the top k+1 by repeated
+//           wave-wide argmax with ties to the lower id.  The selection's device
+//           code (select_dev.h) also serves the decode gate/up launch that
+//           routes one token itself.
 // Products of an fp32/bf16 activation and an fp32 weight are exact in fp64,
 // so the logit differs from any other fp64 summation order only by fp64
 // rounding; the choice of experts therefore matches a plain fp64 evaluation
