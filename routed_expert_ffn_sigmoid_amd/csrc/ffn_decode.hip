@@ -9,8 +9,9 @@
 // Arithmetic.  For an output row with quantised weights q, zero point z and
 // scale s, and an input row x:
 //     out = s * (sum_k q_k x_k  -  z * sum_k x_k).
-// The input row is put into 24-bit fixed point with a per-token power-of-two
-// scale, x_k ~= X_k * 2^-e (|X_k| < 2^22), and X_k is written as three signed
+// The input row is put into 24-bit fixed point with a power-of-two scale per
+// token and K part (the inputs one wavefront covers), x_k ~= X_k * 2^-e
+// (|X_k| < 2^22), and X_k is written as three signed
 // 8-bit digits, X = 65536 D2 + 256 D1 + D0.  sum_k q_k X_k is then three
 // v_mfma_i32_16x16x64_i8 products with exact int32 accumulation: int8 weights
 // feed the MFMA as loaded, int4 weights need two bit operations per 8
@@ -25,11 +26,16 @@
 //   segment, 16 rows x 64 contiguous bytes per instruction);
 //   the activation digits for token l%16 come from LDS at the same inputs;
 //   C[token i][row j] lands in lane 16*(i/4) + j, register i%4.
-// A workgroup is 4 wavefronts covering TPW = 4/S tiles of 16 rows; the S
-// wavefronts of a tile split K and add their fp64 partials in a fixed order.
-// The first PF segments of every row are requested before the slot's token
-// list is read and before the activations are staged; the segment loop is
-// padded to a multiple of PF with out-of-range (zero) loads, so it is
+// Two kernels use this arithmetic.  decode_persistent_kernel (the default up to
+// 16 tokens, when the digit planes of every token fit the LDS) runs one
+// workgroup of 8 wavefronts per CU over a range of (slot, tile) items with the
+// weight stream running across items; with the routing of one token given to
+// it, its gate/up launch also selects and sorts, and its down launch may also
+// combine.  decode_kernel (further tokens, or planes beyond the LDS) runs a
+// grid of (row block, slot) workgroups of 4 wavefronts covering TPW = 4/S
+// tiles of 16 rows, tokens in passes.  In both, the S wavefronts of a tile
+// split K and add their fp64 partials in a fixed order, and the segment loop
+// is padded to a multiple of PF with out-of-range (zero) loads, so it is
 // straight-line code with PF segments in flight per row.
 #include <algorithm>
 #include <cmath>

@@ -10,9 +10,10 @@
 // Weights are the integers q of the per-channel quantisation (page "企业官网建设流程全解析", section
 // 3.4): w = s (q - z).  They enter the MFMA as fp16 values of q, exact for int8 and int4, dequantised in
 // registers from the packed bytes; the zero point is applied once per output through the row sum of the
-// activations, and the scale in the epilogue.  Activations: x is bf16 and is converted once to fp16 under
-// a power-of-two scale per token (exact for every value above 2^-29 of the row's largest; any range fits),
-// undone in the gate/up epilogue.  h is stored under a power-of-two scale per row, 2^-r, chosen from a bound
+// activations, and the scale in the epilogue.  Activations: bf16 x is converted once to fp16 under a
+// power-of-two scale per token (exact for every value above 2^-29 of the row's largest; any range fits),
+// undone in the gate/up epilogue; fp32 x becomes two fp16 values hi + lo under that scale (about 22
+// significant bits), and gate/up runs every weight step against both.  h is stored under a power-of-two scale per row, 2^-r, chosen from a bound
 // on |h| that x's L1 norm and the expert's scales give (see x16_kernel), so it never overflows fp16 either;
 // the down epilogue multiplies by 2^r.  h enters the down GEMM as an fp16 plane plus the residual
 // h - fp16(h) in fp6 e2m3 under one E8M0 exponent per row and 32 channels (the block form of the scaled
