@@ -678,11 +678,75 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     int8_t *planes = (int8_t *)dk_lds + pl0 + (long)kp * 3 * pb;
     double *red = (double *)(dk_lds + pl0 + (long)S * 3 * pb);
 
+    // ---- this workgroup's range of units [ra, rb) for nu_ routed slots (nvr_ and nvs_ routed and shared virtual
+    // slots).  With one tile per item (S = NW) the ranges are cut in half tiles (8 rows): every CU gets the same
+    // number of rows to within 8, and a range may begin or end in the middle of a tile, whose rows outside it
+    // read and store nothing.  Otherwise the ranges are cut in items.
+    constexpr bool HALVES = TPW == 1;
+    auto urange = [&](int nu_, int nvr_, int nvs_, int &ra, int &rb) {
+        const int N = COMB ? tiles_r : nvr_ * tiles_r + nvs_ * tiles_s;  // COMB: ranges count tiles
+        const int NU = HALVES ? 2 * N : N;
+        if (MODE == 0 || HALVES || COMB) {
+            const int G = gridDim.x, b = blockIdx.x;
+            if (G % ncu == 0 && NU >= G) {
+                const int m = G / ncu, c = b % ncu, r = b / ncu;
+                const int c0 = c * NU / ncu, c1 = (c + 1) * NU / ncu;
+                ra = c0 + r * (c1 - c0) / m;
+                rb = c0 + (r + 1) * (c1 - c0) / m;
+            } else {
+                ra = b * NU / G;
+                rb = (b + 1) * NU / G;
+            }
+        } else {
+            // Down with items of several tiles: it restages the rows of h whenever a range moves to another
+            // slot, and that request would queue behind the weights already in flight, a long delay next to
+            // coarse items.  So the range boundaries are moved to slot starts: each slot is shared by the
+            // workgroups whose plain boundary c * NU / G falls inside it, in equal parts; a slot that no
+            // boundary falls into goes to the workgroup before it.  (With half-tile units the plain split is
+            // kept: it balances to 8 rows, and one restage per crossing range costs less than the rounding
+            // of slot-aligned shares.)
+            const int G = gridDim.x;
+            const int ur = HALVES ? 2 * tiles_r : tiles_r;
+            const int us = P.Is > 0 ? (HALVES ? 2 * tiles_s : tiles_s) : 0;
+            auto bound = [&](int c) -> int {
+                if (c <= 0 || NU == 0) return 0;
+                if (c >= G) return NU;
+                const int p = (int)((long)c * NU / G);
+                int st, len;
+                if (PASSES || p < nu_ * ur) {
+                    st = p / ur * ur;
+                    len = ur;
+                } else {
+                    st = nu_ * ur;
+                    len = us;
+                }
+                const int first = (int)(((long)st * G + NU - 1) / NU);
+                const int n = (int)(((long)(st + len) * G + NU - 1) / NU) - first;  // >= 1: c is one of them
+                return st + (int)((long)(c - first) * len / n);
+            };
+            ra = bound(blockIdx.x);
+            rb = bound(blockIdx.x + 1);
+        }
+    };
+
     // ---- first memory round trip: routing table and (gate/up) this wavefront's first activation row, all
     // requested before any of them is waited for
     const int kd = MODE == 0 ? P.d : 0;
     const rsrc_t xsrc0 = make_rsrc(P.x, (uint32_t)((long)T * P.d * (SRC == 0 ? 4 : 2)));
     StageRaw<SRCX> raw0;
+    // Down at one token: slot s's row of h is row s (each chosen expert has the one assignment, so offsets of the
+    // slot's expert is s), and the shared expert's is row 0 of its own.  So the rows of h this wavefront stages
+    // first are requested with the routing table, for the range it would have with every routed slot used; they
+    // are checked against the real ones once the table is in.  raw1 / raw2: the rows' data; e_ro1 / e_ro2: their
+    // element offsets (-1: none requested) and e_sh1 / e_sh2 whether they are the shared expert's.
+    const bool early = MODE == 1 && !PASSES && T == 1;
+    StageRaw<SRCX> raw1, raw2;
+    long e_ro1 = -1, e_ro2 = -1;
+    bool e_sh1 = false, e_sh2 = false;
+    int eu0 = 0, eu1 = 0;
+    auto h_row_src = [&](bool sh) {
+        return make_rsrc(sh ? h_sh : h, (uint32_t)((long)(sh ? T : P.A) * (sh ? P.Is : P.I) * 4));
+    };
     if (MODE == 0 && P.route.part) {
         // one token routed here: its activation row is requested first, then the partial sums
         const int kpart = kd / S;
@@ -711,6 +775,23 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             const int kpart = kd / S;
             const long ro = (long)tile_w * kd + kp * kpart;
             stage_issue<SRCX>(xsrc0, ro, tile_w < T ? 0 : kpad, kpad / 8, kpart, raw0);
+        }
+        if (early) {
+            auto issue = [&](int slot, StageRaw<SRCX> &raw, bool &sh, long &ro) {
+                sh = slot >= nrs;
+                const int I = sh ? P.Is : P.I;
+                ro = (sh ? 0 : (long)slot * I) + kp * (I / S);
+                stage_issue<SRCX>(h_row_src(sh), ro, 0, kpad / 8, I / S, raw);
+            };
+            const int nsl_all = nrs + (P.Is > 0 ? 1 : 0);
+            if (COMB) {  // planes row r = slot r: rows tile_w and tile_w + TPW
+                if (tile_w < nsl_all) issue(tile_w, raw1, e_sh1, e_ro1);
+                if (tile_w + TPW < nsl_all) issue(tile_w + TPW, raw2, e_sh2, e_ro2);
+            } else {  // the first item's slot, staged by the wavefronts of token row 0
+                urange(nrs, nrs, P.Is > 0 ? 1 : 0, eu0, eu1);
+                const int i0p = HALVES ? eu0 >> 1 : eu0;
+                if (eu0 < eu1 && tile_w == 0) issue(i0p < nrs * tiles_r ? i0p / tiles_r : nrs, raw1, e_sh1, e_ro1);
+            }
         }
         if (COMB && tid < P.k) {
             c_inv[tid] = P.comb_inv[tid];
@@ -762,53 +843,12 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     }
     // item counts stay far below 2^31 / ncu (at most 1025 slots x 2^16 tiles), so 32-bit index math
     const int nsl = nu + (P.Is > 0 ? 1 : 0);  // COMB: slots per tile
-    const int N = COMB ? tiles_r : nvr * tiles_r + nvs * tiles_s;  // COMB: ranges count tiles
-    // With one tile per item (S = NW) the ranges are cut in half tiles (8 rows): every CU gets the same
-    // number of rows to within 8, and a range may begin or end in the middle of a tile, whose rows
-    // outside it read and store nothing.  Otherwise the ranges are cut in items.
-    constexpr bool HALVES = TPW == 1;
-    const int NU = HALVES ? 2 * N : N;
     int u0, u1;
-    if (MODE == 0 || HALVES || COMB) {
-        const int G = gridDim.x, b = blockIdx.x;
-        if (G % ncu == 0 && NU >= G) {
-            const int m = G / ncu, c = b % ncu, r = b / ncu;
-            const int c0 = c * NU / ncu, c1 = (c + 1) * NU / ncu;
-            u0 = c0 + r * (c1 - c0) / m;
-            u1 = c0 + (r + 1) * (c1 - c0) / m;
-        } else {
-            u0 = b * NU / G;
-            u1 = (b + 1) * NU / G;
-        }
+    if (early && nu == nrs && !COMB) {
+        u0 = eu0;  // the range the early rows were requested for
+        u1 = eu1;
     } else {
-        // Down with items of several tiles: it restages the rows of h whenever a range moves to another
-        // slot, and that request would queue behind the weights already in flight, a long delay next to
-        // coarse items.  So the range boundaries are moved to slot starts: each slot is shared by the
-        // workgroups whose plain boundary c * NU / G falls inside it, in equal parts; a slot that no
-        // boundary falls into goes to the workgroup before it.  (With half-tile units the plain split is
-        // kept: it balances to 8 rows, and one restage per crossing range costs less than the rounding
-        // of slot-aligned shares.)
-        const int G = gridDim.x;
-        const int ur = HALVES ? 2 * tiles_r : tiles_r;
-        const int us = P.Is > 0 ? (HALVES ? 2 * tiles_s : tiles_s) : 0;
-        auto bound = [&](int c) -> int {
-            if (c <= 0 || NU == 0) return 0;
-            if (c >= G) return NU;
-            const int p = (int)((long)c * NU / G);
-            int st, len;
-            if (PASSES || p < nu * ur) {
-                st = p / ur * ur;
-                len = ur;
-            } else {
-                st = nu * ur;
-                len = us;
-            }
-            const int first = (int)(((long)st * G + NU - 1) / NU);
-            const int n = (int)(((long)(st + len) * G + NU - 1) / NU) - first;  // >= 1: c is one of them
-            return st + (int)((long)(c - first) * len / n);
-        };
-        u0 = bound(blockIdx.x);
-        u1 = bound(blockIdx.x + 1);
+        urange(nu, nvr, nvs, u0, u1);
     }
     const int i0 = (HALVES ? u0 >> 1 : u0) * (COMB ? nsl : 1), i1 = (HALVES ? (u1 + 1) >> 1 : u1) * (COMB ? nsl : 1);
     if (i0 >= i1) return;  // uniform over the workgroup
@@ -963,9 +1003,11 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         int kpart1, kpart2;
         row_src(st1 ? r1 : 0, src1, ro1, kpart1);
         row_src(st2 ? r2 : 0, src2, ro2, kpart2);
-        StageRaw<SRCX> raw1, raw2;
-        stage_issue<SRCX>(src1, ro1, st1 ? 0 : kpad, kpad / 8, kpart1, raw1);
-        stage_issue<SRCX>(src2, ro2, st2 ? 0 : kpad, kpad / 8, kpart2, raw2);
+        // rows requested with the table (one token) are used when they are the ones needed
+        if (!(st1 && e_ro1 == ro1 && e_sh1 == (r1 >= nu)))
+            stage_issue<SRCX>(src1, ro1, st1 ? 0 : kpad, kpad / 8, kpart1, raw1);
+        if (!(st2 && e_ro2 == ro2 && e_sh2 == (r2 >= nu)))
+            stage_issue<SRCX>(src2, ro2, st2 ? 0 : kpad, kpad / 8, kpart2, raw2);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -986,10 +1028,11 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         const rsrc_t src = h_src(cur);
         const int kpart = cur.I / S;
         const long base = cur.p0;
-        StageRaw<SRCX> raw1;
         const bool st1 = tile_w < cur.ng;
         const long ro1 = (base + tile_w) * cur.I + kp * kpart;
-        stage_issue<SRCX>(src, ro1, st1 ? 0 : kpad, kpad / 8, kpart, raw1);
+        // the row requested with the table (one token) is used when it is the one needed
+        if (!(st1 && e_ro1 == ro1 && e_sh1 == cur.shared))
+            stage_issue<SRCX>(src, ro1, st1 ? 0 : kpad, kpad / 8, kpart, raw1);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
