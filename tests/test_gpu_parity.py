@@ -279,8 +279,12 @@ def test_invalid_expert_ids_end_to_end(orc, dev):
     """Invalid ids written into topk_idx between moe_route and moe_permute: moe_permute drops them (inv = -1,
     n_uniq = -1), moe_forward still applies every valid expert, and moe_combine leaves the dropped choices out.
     Checked against the oracle's expert and combine functions on the valid assignments, on the persistent decode
-    kernel, the token-group kernel and the matrix-core path."""
-    cases = [(dict(d=512, E=16, k=4, I=352, I_shared=96, routed_scale=2.5), 7, B.MOE_PATH_AUTO),
+    kernel, the token-group kernel and the matrix-core path.  The one-token cases use fewer slots than the routed
+    ones, so the down launch's rows of h requested with the routing table (for every routed slot used) do not all
+    match and are requested again."""
+    cases = [(dict(d=512, E=16, k=4, I=352, I_shared=96, routed_scale=2.5), 1, B.MOE_PATH_AUTO),
+             (dict(d=7168, E=256, k=8, I=128, I_shared=128, routed_scale=2.5), 1, B.MOE_PATH_AUTO),
+             (dict(d=512, E=16, k=4, I=352, I_shared=96, routed_scale=2.5), 7, B.MOE_PATH_AUTO),
              (dict(d=256, E=8, k=3, I=128, I_shared=128, act=synth.ACT_F32), 40, B.MOE_PATH_AUTO),
              (dict(d=512, E=16, k=4, I=384, I_shared=192, routed_scale=2.5), 70, B.MOE_PATH_GEMM)]
     for kw, T, path in cases:
@@ -295,6 +299,7 @@ def test_invalid_expert_ids_end_to_end(orc, dev):
         bad = rng.random(idx.shape) < 0.15
         bad[0, 0] = True
         idx[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, spec.E + 3)
+        idx[0, 0] = spec.E + 3  # at least one id out of range (an empty slot, -1, is not an error)
         run.idx.copy_(torch.from_numpy(idx))
         run.y_perm.fill_(float("nan"))
         run.permute()
