@@ -1350,6 +1350,30 @@ static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad, int g
     return tab + (size_t)S * 3 * g * (kpad + 16) + dkp_red_bytes(mode);
 }
 
+// Gate/up split outside the batch-invariant mode.  The weight stream is the bound, and it runs at full rate
+// while most CUs stream, so fewer and longer items win (less per-item work: the cross-wavefront sum of the K
+// parts, the epilogue, the refill across items) as long as the last round of items keeps most CUs busy.
+// One token (the slot count is exact): the smallest S in {1, 2, 4} whose items per CU, R = items / CUs, are at
+// least 1.5 with the last round at least 3/4 full.  The mid workload's token (2 slots of 14336 rows) takes
+// S = 2, R = 1.75; the 256-expert layer's (9 slots of 2048 rows) keeps S = 8, whose half-tile ranges balance to
+// 8 rows where S = 4 would leave a last round a quarter full.  Several tokens (the slot count is an estimate,
+// which skewed routing lowers): S = 4 while R >= 3 at the expected slot count.  Measured at 2 to 16 tokens on
+// both layers, S = 4 beat S = 8 by 2-4 % up to 8 tokens and tied at 16; S = 1 and S = 2 each lost to S = 8 on
+// one of them.  0: none qualifies (dkp_pick_s decides).  The planes must fit the LDS.
+static int dkp_pick_s0(const FfnParams &P, double slots) {
+    const int chunk = P.wbits == 8 ? 16 : 32, ncu = device_cus();
+    const double shared = P.Is > 0 ? 1.0 : 0.0;
+    for (int S = P.T == 1 ? 1 : 4; S <= 4; S <<= 1) {
+        if (P.d % (S * chunk)) continue;
+        const int rows = 16 * (DKP_WAVES / S);
+        const double items = (slots - shared) * ((P.I + rows - 1) / rows) + shared * ((P.Is + rows - 1) / rows);
+        const double R = items / ncu, fill = R - std::floor(R);
+        const bool ok = P.T == 1 ? R >= 1.5 && (fill == 0.0 || fill >= 0.75) : R >= 3.0;
+        if (ok && dkp_lds_bytes(0, S, P, pad_k(P.d / S, P.wbits), P.T) <= DKP_LDS_BUDGET) return S;
+    }
+    return 0;
+}
+
 template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES, bool COMB = false>
 static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, int gcap, hipStream_t stream) {
     const int rows_per_item = 16 * (DKP_WAVES / S);
@@ -1406,7 +1430,9 @@ static bool dkp_plan(int mode, const FfnParams &P, DkpPlan *pl) {
     const double uniq_exp = (double)P.E * (1.0 - std::pow(1.0 - (double)P.k / P.E, (double)P.T));
     const double slots_exp = std::min((double)P.n_routed_slots, uniq_exp) + (P.Is > 0 ? 1 : 0);
     // routed and shared expert split alike: the split must divide both K ranges
-    int S = P.invariant ? decode_pinned_s(mode, P) : dkp_pick_s(mode, K, nout, slots, slots_exp, wbits, device_cus());
+    int S = P.invariant || mode == 1 ? 0 : dkp_pick_s0(P, P.T == 1 ? slots : slots_exp);
+    if (S == 0)
+        S = P.invariant ? decode_pinned_s(mode, P) : dkp_pick_s(mode, K, nout, slots, slots_exp, wbits, device_cus());
     while (S > 1 && (Kmin % (S * (wbits == 8 ? 16 : 32)))) S >>= 1;
     const int kpad = pad_k(K / S, wbits);
     if (P.T > DK_GMAX || dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64)
