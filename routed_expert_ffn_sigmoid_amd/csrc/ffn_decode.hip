@@ -1327,7 +1327,7 @@ static int dkp_pick_s(int mode, int K, int nout, int slots, double slots_exp, in
     return best;
 }
 
-// K split of pass `mode` in the batch-invariant mode: the split the persistent kernel picks for one token, capped
+// K split of pass `mode` in the batch-invariant mode: the split dkp_pick_s's cost rule gives for one token, capped
 // at 4 (the token-group kernel's largest), and dividing both the routed and the shared K range.  It depends on the
 // layer's shape alone, so a token's staged fixed point and its order of sums are the same at every T.
 static int decode_pinned_s(int mode, const FfnParams &P) {

@@ -110,6 +110,12 @@ SMALL = {
     "down_token_passes": (dict(d=256, E=4, k=2, I=14336, I_shared=14336, wbits=8, act=synth.ACT_F32), 6),
     # 256 experts with a short hidden size: four experts per lane in the selection, few W_r rows per split
     "E256_d128_T4": (dict(d=128, E=256, k=8, I=64, I_shared=64, routed_scale=2.5), 4),
+    # gate/up K splits taken for long items on a 256-CU chip, each with a ragged last tile: one token whose
+    # 4 x 112 items of 128 rows fill 1.75 rounds (S = 1); one token with a shared expert, 4 x 110 + 47 items of
+    # 64 rows (S = 2); three tokens at 4.6 expected slots of 188 items of 32 rows, plus the shared expert (S = 4)
+    "T1_gateup_split1": (dict(d=256, E=8, k=4, I=14288, wbits=8, act=synth.ACT_F32), 1),
+    "T1_gateup_split2": (dict(d=512, E=16, k=4, I=7008, I_shared=3008, routed_scale=2.5), 1),
+    "T3_gateup_split4": (dict(d=256, E=8, k=2, I=6016, I_shared=992, wbits=8, act=synth.ACT_F32), 3),
 }
 
 
