@@ -1358,8 +1358,10 @@ static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad, int g
 // S = 2, R = 1.75; the 256-expert layer's (9 slots of 2048 rows) keeps S = 8, whose half-tile ranges balance to
 // 8 rows where S = 4 would leave a last round a quarter full.  Several tokens (the slot count is an estimate,
 // which skewed routing lowers): S = 4 while R >= 3 at the expected slot count.  Measured at 2 to 16 tokens on
-// both layers, S = 4 beat S = 8 by 2-4 % up to 8 tokens and tied at 16; S = 1 and S = 2 each lost to S = 8 on
-// one of them.  0: none qualifies (dkp_pick_s decides).  The planes must fit the LDS.
+// both layers, S = 4 beat S = 8 by 1.6-4 % at 2 and 4 tokens and on the mid layer at 8, and tied elsewhere;
+// S = 2 also beat S = 8, by less than S = 4 on the mid layer; S = 1 lost up to 7 % to S = 8 on the mid layer
+// (it won on the 256-expert layer at 4 tokens).  0: none qualifies (dkp_pick_s decides).  The planes must fit
+// the LDS.
 static int dkp_pick_s0(const FfnParams &P, double slots) {
     const int chunk = P.wbits == 8 ? 16 : 32, ncu = device_cus();
     const double shared = P.Is > 0 ? 1.0 : 0.0;
