@@ -39,7 +39,8 @@ typedef struct dsa_index_shape {
     int32_t pos0; /* position of query 0 (>= 0): query t sees keys s <= pos0 + t */
 } dsa_index_shape;
 
-/* Workspace bytes for this shape (T * S fp64 scores); 0 for a shape that fails the checks. */
+/* Workspace bytes for this shape (T * S fp64 scores, then two fp64 per query and block of 64 keys: the score
+ * range of each scoring workgroup); 0 for a shape that fails the checks. */
 MOE_API size_t dsa_index_workspace_size(const dsa_index_shape *shape);
 
 /*

@@ -37,8 +37,10 @@ __global__ __launch_bounds__(IX_WAVES * 64) void index_score_kernel(const int8_t
                                                                     const int8_t *__restrict__ k,
                                                                     const float *__restrict__ kscale, int T, int S,
                                                                     int H, int D, int pos0, int nkb,
-                                                                    double *__restrict__ scores) {
+                                                                    double *__restrict__ scores,
+                                                                    double *__restrict__ range) {
     extern __shared__ __align__(16) uint8_t qs[];  // [IX_QB][H][D + IX_QPAD]
+    __shared__ double s_rng[IX_WAVES][IX_QB][2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
@@ -46,7 +48,12 @@ __global__ __launch_bounds__(IX_WAVES * 64) void index_score_kernel(const int8_t
     const int t0 = blockIdx.y * IX_QB;
     const int tlast = min(T - 1, t0 + IX_QB - 1);
     const int kb0 = blockIdx.x * nkb * IX_KEYS;  // first key of this workgroup
-    if (kb0 > pos0 + tlast) return;  // no query of the group sees these keys (uniform)
+    // range[t][x] = {smallest, largest} score of query t among workgroup x's keys (+inf, -inf: none)
+    double *rng = range + ((long)t0 * gridDim.x + blockIdx.x) * 2;
+    if (kb0 > pos0 + tlast) {  // no query of the group sees these keys (uniform)
+        if (tid < 2 * IX_QB && t0 + tid / 2 < T) rng[(long)(tid / 2) * gridDim.x * 2 + (tid & 1)] = tid & 1 ? -INFINITY : INFINITY;
+        return;
+    }
     // the group's query rows into LDS (rows of queries past T are zeros)
     const int nq16 = IX_QB * H * D / 16;
     for (int c = tid; c < nq16; c += IX_WAVES * 64) {
@@ -61,6 +68,7 @@ __global__ __launch_bounds__(IX_WAVES * 64) void index_score_kernel(const int8_t
     const uint8_t *arow = qs + (long)((j >> 2) * H + (j & 3)) * pitch + 16 * g;
     const int t = t0 + g;  // this lane's chain: query t, key s0 + j
     const float *wt = w + (long)(t < T ? t : 0) * H;
+    double lmn = INFINITY, lmx = -INFINITY;  // this lane's scores' range
     for (int kb = 0; kb < nkb; kb++) {
         const int s0 = kb0 + kb * IX_KEYS + 16 * wv;
         if (s0 > pos0 + tlast || s0 >= S) break;  // uniform over the wavefront
@@ -89,7 +97,29 @@ __global__ __launch_bounds__(IX_WAVES * 64) void index_score_kernel(const int8_t
             acc = __builtin_fma((double)w4.w, (double)(c[3] > 0 ? c[3] : 0), acc);
         }
         const int key = s0 + j;
-        if (t < T && key < S && key <= pos0 + t) scores[(long)t * S + key] = (double)kscale[key] * acc;
+        if (t < T && key < S && key <= pos0 + t) {
+            const double sc = (double)kscale[key] * acc;
+            scores[(long)t * S + key] = sc;
+            lmn = fmin(lmn, sc);
+            lmx = fmax(lmx, sc);
+        }
+    }
+    // the range of each query over the workgroup's keys: the 16 lanes of its lane group, then the wavefronts
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+        lmn = fmin(lmn, __shfl_xor(lmn, o, 64));
+        lmx = fmax(lmx, __shfl_xor(lmx, o, 64));
+    }
+    if (j == 0) {
+        s_rng[wv][g][0] = lmn;
+        s_rng[wv][g][1] = lmx;
+    }
+    __syncthreads();
+    if (tid < 2 * IX_QB && t0 + tid / 2 < T) {
+        const int gq = tid / 2, hi = tid & 1;
+        double v = s_rng[0][gq][hi];
+        for (int w2 = 1; w2 < IX_WAVES; w2++) v = hi ? fmax(v, s_rng[w2][gq][hi]) : fmin(v, s_rng[w2][gq][hi]);
+        rng[(long)gq * gridDim.x * 2 + hi] = v;
     }
 }
 
@@ -154,7 +184,8 @@ __device__ void ix_find_bucket(const int *bhist, int K, int *scan, int *bstar, i
 
 __global__ __launch_bounds__(IX_SEL_THREADS) void index_select_kernel(const double *__restrict__ scores, int S,
                                                                       int K, int pos0, int32_t *__restrict__ top,
-                                                                      double *__restrict__ gap) {
+                                                                      double *__restrict__ gap,
+                                                                      const double *__restrict__ range, int nbx) {
     __shared__ int bhist[IX_NB];
     __shared__ uint64_t bkeys[TOPK_CAND];
     __shared__ int hist[256];
@@ -176,17 +207,11 @@ __global__ __launch_bounds__(IX_SEL_THREADS) void index_select_kernel(const doub
     }
     auto key = [&](int i) { return ordered_f64(sc[i]); };
     if (tid == 0) below = 0ull;
-    // ---- the query's range of scores
+    // ---- the query's range of scores, from the scoring workgroups' ranges
     double mn = INFINITY, mx = -INFINITY;
-    for (int i0 = tid; i0 < n; i0 += IX_SEL_THREADS * IX_UN) {
-        double v[IX_UN];
-#pragma unroll
-        for (int u = 0; u < IX_UN; u++) v[u] = i0 + u * IX_SEL_THREADS < n ? sc[i0 + u * IX_SEL_THREADS] : sc[0];
-#pragma unroll
-        for (int u = 0; u < IX_UN; u++) {
-            mn = fmin(mn, v[u]);
-            mx = fmax(mx, v[u]);
-        }
+    for (int i = tid; i < nbx; i += IX_SEL_THREADS) {
+        mn = fmin(mn, range[((long)t * nbx + i) * 2]);
+        mx = fmax(mx, range[((long)t * nbx + i) * 2 + 1]);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -282,7 +307,10 @@ __global__ __launch_bounds__(IX_SEL_THREADS) void index_select_kernel(const doub
         gap[t] = s.eq > s.need ? 0.0 : from_ordered_f64(s.v) - from_ordered_f64(below);
 }
 
-size_t index_workspace_bytes(int T, int S) { return (size_t)T * (size_t)S * sizeof(double); }
+// scores [T][S], then the scoring workgroups' ranges [T][at most ceil(S / IX_KEYS)][2]
+size_t index_workspace_bytes(int T, int S) {
+    return (size_t)T * (size_t)S * sizeof(double) + (size_t)T * (size_t)((S + IX_KEYS - 1) / IX_KEYS) * 16;
+}
 
 const char *index_unsupported(int T, int S, int H, int D) {
     if ((long)S * D >= kMaxDescBytes) return "the keys (S*D bytes) exceed 2^31 bytes";
@@ -294,6 +322,8 @@ hipError_t launch_index_topk(const int8_t *q, const float *w, const int8_t *k, c
                              int H, int D, int K, int pos0, int32_t *top, double *gap, void *ws,
                              hipStream_t stream) {
     double *scores = (double *)ws;
+    double *range = scores + (long)T * S;
+    int nbx = 0;  // scoring workgroups along the keys
     // key blocks up to the last query's position
     long vis = (long)pos0 + T;
     if (vis > S) vis = S;
@@ -303,7 +333,8 @@ hipError_t launch_index_topk(const int8_t *q, const float *w, const int8_t *k, c
         const int groups = (T + IX_QB - 1) / IX_QB;
         const int nkb = groups >= 16 ? 8 : 1;
         const long blocks = (vis + IX_KEYS - 1) / IX_KEYS;
-        const dim3 grid((unsigned)((blocks + nkb - 1) / nkb), (unsigned)groups);
+        nbx = (int)((blocks + nkb - 1) / nkb);
+        const dim3 grid((unsigned)nbx, (unsigned)groups);
         const size_t lds = (size_t)IX_QB * H * (D + IX_QPAD);
         if (lds > 65536) {
             const hipError_t e = hipFuncSetAttribute((const void *)index_score_kernel,
@@ -311,11 +342,12 @@ hipError_t launch_index_topk(const int8_t *q, const float *w, const int8_t *k, c
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(index_score_kernel, grid, dim3(IX_WAVES * 64), lds, stream, q, w, k, kscale, T, S, H, D,
-                           pos0, nkb, scores);
+                           pos0, nkb, scores, range);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(index_select_kernel, dim3(T), dim3(IX_SEL_THREADS), 0, stream, scores, S, K, pos0, top, gap);
+    hipLaunchKernelGGL(index_select_kernel, dim3(T), dim3(IX_SEL_THREADS), 0, stream, scores, S, K, pos0, top, gap,
+                       range, nbx);
     return hipGetLastError();
 }
 
