@@ -633,9 +633,10 @@ __device__ void route_one_token(const FfnParams &P, int *tab, double *zs) {
     }
 }
 
-// PASSES (down only): the digit planes hold gcap < T token rows, so a slot with more rows is taken as
-// several virtual slots of at most gcap rows each, in row order, each streaming the expert's rows again
-// (the mid workload's down pass at T = 4: 3 x 14336 inputs of planes fit the LDS, 4 do not).
+// PASSES: the digit planes hold gcap < T token rows, so a slot with more rows is taken as several virtual slots
+// of at most gcap rows each, in row order, each streaming the expert's rows again (the mid workload's down pass at
+// T = 4: 3 x 14336 inputs of planes fit the LDS, 4 do not; gate/up of the 256-expert layer at T = 8: 5 x 7168).
+// Down stages the virtual slot's rows of h, gate/up its tokens' activation rows (planes row r = its r-th row).
 // COMB (down only, one token, FfnParams::comb_y set): the combine runs in this launch.  The h rows of all
 // nsl = n_uniq + shared slots are staged at once (planes row s = slot s, gcap = nsl), items are numbered
 // tile-major (item i = tile i / nsl of slot i % nsl) and ranges are cut at tiles, so a workgroup takes every
@@ -774,7 +775,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             // token row tile_w (if any), this wavefront's K part
             const int kpart = kd / S;
             const long ro = (long)tile_w * kd + kp * kpart;
-            stage_issue<SRCX>(xsrc0, ro, tile_w < T ? 0 : kpad, kpad / 8, kpart, raw0);
+            stage_issue<SRCX>(xsrc0, ro, tile_w < T && !PASSES ? 0 : kpad, kpad / 8, kpart, raw0);
         }
         if (early) {
             auto issue = [&](int slot, StageRaw<SRCX> &raw, bool &sh, long &ro) {
@@ -953,6 +954,12 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         return make_rsrc(it.shared ? h_sh : h, (uint32_t)((long)(it.shared ? T : P.A) * it.I * 4));
     };
 
+    // gate/up with token passes: the token of row r of an item's virtual slot (the shared expert's rows are the
+    // tokens in order; a routed slot's are its assignments' tokens)
+    auto gu_token = [&](const DItem &it, int r) -> int {
+        return it.shared ? it.p0 + r : __builtin_amdgcn_readfirstlane(t_perm[it.p0 + r]) / P.k;
+    };
+
     DItem cur = decode(i0);
     rsrc_t wr_cur[NM], wr_nxt[NM];
     uint32_t off_cur, off_nxt;
@@ -967,7 +974,19 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
     // ---- activations of the first item and the weight stream.  Gate/up stages first (its rows were
     // requested with the table): the staging code is cold at launch, and fetching it behind the whole
     // chip's first burst of weight requests costs more than the short gap before the stream starts.
-    if (MODE == 0) {
+    if (MODE == 0 && PASSES) {
+        // token passes: the planes hold the rows of the first item's virtual slot (row r = its r-th token)
+        const int kpart = kd / S;
+        for (int r = tile_w; r < cur.ng; r += TPW) {
+            const long ro = (long)gu_token(cur, r) * kd + kp * kpart;
+            StageRaw<SRCX> raw;
+            stage_issue<SRCX>(xsrc0, ro, 0, kpad / 8, kpart, raw);
+            stage_finish<WBITS, SRCX>(raw, xsrc0, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp], wxsum[kp]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < PF; b++) ld(b, wr_cur, off_cur, cur.kpart_bytes, b);
+    } else if (MODE == 0) {
         // rows tile_w, tile_w + TPW, ...: the next row is requested before this one is turned into digits
         const int kpart = kd / S;
         StageRaw<SRCX> rb;
@@ -1061,6 +1080,19 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
             for (int m = 0; m < NM; m++) wr_nxt[m] = wr_cur[m];
             off_nxt = off_cur;
         }
+        // ---- gate/up with token passes: the activation rows of a new virtual slot
+        if (MODE == 0 && PASSES && cur.slot != staged_slot) {
+            const int kpart = kd / S;
+            __syncthreads();  // every wavefront is done reading the previous planes
+            for (int r = tile_w; r < cur.ng; r += TPW) {
+                const long ro = (long)gu_token(cur, r) * kd + kp * kpart;
+                StageRaw<SRCX> raw;
+                stage_issue<SRCX>(xsrc0, ro, 0, kpad / 8, kpart, raw);
+                stage_finish<WBITS, SRCX>(raw, xsrc0, ro, r, kpad / 8, kpart, stride, pb, planes, wexpo[kp],
+                                          wxsum[kp]);
+            }
+            __syncthreads();
+        }
         // ---- down: the rows of h of a new slot
         if (MODE == 1 && !COMB && cur.slot != staged_slot) {
             const rsrc_t src = h_src(cur);
@@ -1080,7 +1112,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
 
         // ---- A-operand row of this lane: the token (gate/up) or slot row (down) at position j
         int trow = -1;
-        if (j < cur.ng) trow = MODE == 0 ? (cur.shared ? j : t_perm[cur.p0 + j] / P.k) : (COMB ? cur.slot : j);
+        if (j < cur.ng) trow = MODE == 0 && !PASSES ? (cur.shared ? j : t_perm[cur.p0 + j] / P.k) : (COMB ? cur.slot : j);
         const bool tok_ok = trow >= 0;
         const int8_t *xrow = tok_ok ? planes + (long)trow * stride : (const int8_t *)zero_area;
         const long pstep = tok_ok ? pb : 0;
@@ -1135,7 +1167,8 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
         for (int r = 0; r < 4; r++) {
             const int i2 = 4 * g + r;
             const bool ok = i2 < cur.ng;
-            const int pr = ok ? (MODE == 0 ? (cur.shared ? i2 : t_perm[cur.p0 + i2] / P.k) : (COMB ? cur.slot : i2)) : 0;
+            const int pr = ok ? (MODE == 0 && !PASSES ? (cur.shared ? i2 : t_perm[cur.p0 + i2] / P.k) : (COMB ? cur.slot : i2))
+                              : 0;
             const double unit = ok ? ldexp(1.0, -wexpo[kp][pr]) : 0.0;
             const double xs = ok ? wxsum[kp][pr] : 0.0;
 #pragma unroll
@@ -1173,7 +1206,7 @@ __global__ __launch_bounds__(DKP_WAVES * 64, 1) void decode_persistent_kernel(Ff
                         const float uf = (float)((double)srow[NM - 1] * v[NM - 1][r]);
                         const float hv = gf / (1.f + expf(-gf)) * uf;
                         if (cur.shared)
-                            h_sh[(long)i2 * cur.I + o] = hv;
+                            h_sh[(long)(cur.p0 + i2) * cur.I + o] = hv;
                         else
                             h[(long)(cur.p0 + i2) * cur.I + o] = hv;
                     } else {
@@ -1379,8 +1412,11 @@ static int dkp_pick_s0(const FfnParams &P, double slots) {
 template <int MODE, int WBITS, int SRC, int S, int PF, bool PASSES, bool COMB = false>
 static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kpad, int gcap, hipStream_t stream) {
     const int rows_per_item = 16 * (DKP_WAVES / S);
-    const int tiles_r = ((MODE == 0 ? P.I : P.d) + rows_per_item - 1) / rows_per_item;
-    const int tiles_s = P.Is > 0 ? ((MODE == 0 ? P.Is : P.d) + rows_per_item - 1) / rows_per_item : 0;
+    int tiles_r = ((MODE == 0 ? P.I : P.d) + rows_per_item - 1) / rows_per_item;
+    int tiles_s = P.Is > 0 ? ((MODE == 0 ? P.Is : P.d) + rows_per_item - 1) / rows_per_item : 0;
+    // token passes number every virtual slot's items alike: gate/up counts the larger of the two expert widths
+    if (MODE == 0 && PASSES && tiles_s > tiles_r) tiles_r = tiles_s;
+    if (MODE == 0 && PASSES && tiles_s > 0) tiles_s = tiles_r;
     const size_t lds = dkp_lds_bytes(MODE, S, P, kpad, gcap);
     auto fn = decode_persistent_kernel<MODE, WBITS, SRC, S, PF, PASSES, COMB>;
     hipError_t err = allow_lds(fn, lds);
@@ -1400,19 +1436,16 @@ static hipError_t dkp_launch_s(const FfnParams &P, float *h, float *h_sh, int kp
 template <int MODE, int WBITS, int SRC>
 static hipError_t dkp_launch_pass(const FfnParams &P, float *h, float *h_sh, int kpad, int gcap, int S, bool deep,
                                   hipStream_t stream) {
-    if constexpr (MODE != 1) {
-        return hipErrorNotSupported;
-    } else {
-        switch (S) {
-            case 8: return deep ? dkp_launch_s<1, WBITS, SRC, 8, 16, true>(P, h, h_sh, kpad, gcap, stream)
-                                : dkp_launch_s<1, WBITS, SRC, 8, 14, true>(P, h, h_sh, kpad, gcap, stream);
-            case 4: return deep ? dkp_launch_s<1, WBITS, SRC, 4, 16, true>(P, h, h_sh, kpad, gcap, stream)
-                                : dkp_launch_s<1, WBITS, SRC, 4, 14, true>(P, h, h_sh, kpad, gcap, stream);
-            case 2: return deep ? dkp_launch_s<1, WBITS, SRC, 2, 16, true>(P, h, h_sh, kpad, gcap, stream)
-                                : dkp_launch_s<1, WBITS, SRC, 2, 14, true>(P, h, h_sh, kpad, gcap, stream);
-            default: return deep ? dkp_launch_s<1, WBITS, SRC, 1, 16, true>(P, h, h_sh, kpad, gcap, stream)
-                                 : dkp_launch_s<1, WBITS, SRC, 1, 14, true>(P, h, h_sh, kpad, gcap, stream);
-        }
+    constexpr int PFA = MODE == 0 ? 8 : 16, PFB = MODE == 0 ? 7 : 14;
+    switch (S) {
+        case 8: return deep ? dkp_launch_s<MODE, WBITS, SRC, 8, PFA, true>(P, h, h_sh, kpad, gcap, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 8, PFB, true>(P, h, h_sh, kpad, gcap, stream);
+        case 4: return deep ? dkp_launch_s<MODE, WBITS, SRC, 4, PFA, true>(P, h, h_sh, kpad, gcap, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 4, PFB, true>(P, h, h_sh, kpad, gcap, stream);
+        case 2: return deep ? dkp_launch_s<MODE, WBITS, SRC, 2, PFA, true>(P, h, h_sh, kpad, gcap, stream)
+                            : dkp_launch_s<MODE, WBITS, SRC, 2, PFB, true>(P, h, h_sh, kpad, gcap, stream);
+        default: return deep ? dkp_launch_s<MODE, WBITS, SRC, 1, PFA, true>(P, h, h_sh, kpad, gcap, stream)
+                             : dkp_launch_s<MODE, WBITS, SRC, 1, PFB, true>(P, h, h_sh, kpad, gcap, stream);
     }
 }
 
@@ -1451,10 +1484,10 @@ static bool dkp_plan(int mode, const FfnParams &P, DkpPlan *pl) {
         *pl = DkpPlan{S, kpad, nsl};
         return true;
     }
-    // token rows the planes hold: all T, or (down) fewer, with the slots taken in passes
+    // token rows the planes hold: all T, or fewer, with the slots taken in passes
     int gcap = P.T;
     while (gcap > 0 && dkp_lds_bytes(mode, S, P, kpad, gcap) > DKP_LDS_BUDGET) gcap--;
-    if (gcap < 1 || (mode == 0 && gcap < P.T)) return false;
+    if (gcap < 1) return false;
     *pl = DkpPlan{S, kpad, gcap};
     return true;
 }
@@ -1484,7 +1517,7 @@ static hipError_t dkp_try(const FfnParams &P, float *h, float *h_sh, hipStream_t
     *done = true;
     constexpr int PFA = MODE == 0 ? 8 : 16, PFB = MODE == 0 ? 7 : 14;
     const bool deep = dkp_pf(MODE, (K / S * WBITS / 8 + 63) / 64) == PFA;
-    if (MODE == 1 && gcap < P.T) return dkp_launch_pass<MODE, WBITS, SRC>(P, h, h_sh, kpad, gcap, S, deep, stream);
+    if (gcap < P.T) return dkp_launch_pass<MODE, WBITS, SRC>(P, h, h_sh, kpad, gcap, S, deep, stream);
     if constexpr (MODE == 1) {
         if (P.comb_y) {
             switch (S) {

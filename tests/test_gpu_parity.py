@@ -116,6 +116,11 @@ SMALL = {
     "T1_gateup_split1": (dict(d=256, E=8, k=4, I=14288, wbits=8, act=synth.ACT_F32), 1),
     "T1_gateup_split2": (dict(d=512, E=16, k=4, I=7008, I_shared=3008, routed_scale=2.5), 1),
     "T3_gateup_split4": (dict(d=256, E=8, k=2, I=6016, I_shared=992, wbits=8, act=synth.ACT_F32), 3),
+    # gate/up whose digit planes hold fewer token rows than the batch (3 T d bytes over the LDS budget): slots and
+    # the shared expert taken in token passes, each restaging its tokens' activation rows
+    "gateup_token_passes": (dict(d=8192, E=4, k=2, I=256, I_shared=256, routed_scale=2.5), 6),
+    "gateup_token_passes_int8_f32": (dict(d=6144, E=8, k=2, I=512, wbits=8, act=synth.ACT_F32), 12),
+    "gateup_token_passes_wide_shared": (dict(d=8192, E=4, k=1, I=128, I_shared=384), 5),
 }
 
 
@@ -521,6 +526,7 @@ def weights_for(spec, dev, layer=0):
 FULL = [("mid", 1, None, B.MOE_PATH_AUTO), ("mid", 4, None, B.MOE_PATH_AUTO), ("mid", 64, None, B.MOE_PATH_AUTO),
         ("mid", 64, None, B.MOE_PATH_GEMV), ("mid", 512, 64, B.MOE_PATH_AUTO),
         ("large", 1, None, B.MOE_PATH_AUTO), ("large_zipf", 4, None, B.MOE_PATH_AUTO),
+        ("large_zipf", 8, None, B.MOE_PATH_AUTO),
         ("large_zipf", 512, 64, B.MOE_PATH_AUTO), ("large_zipf", 512, 64, B.MOE_PATH_GEMV),
         ("prefill_int4_uniform", 8192, 64, B.MOE_PATH_AUTO), ("prefill_int4_zipf", 8192, 64, B.MOE_PATH_AUTO),
         ("prefill_int8_uniform", 8192, 64, B.MOE_PATH_AUTO), ("prefill_int8_zipf", 8192, 64, B.MOE_PATH_AUTO)]
