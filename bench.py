@@ -321,9 +321,10 @@ def measure(spec, T, args, dev):
     # the roof that binds: HBM when the expert FFNs do fewer flops per expert-weight byte than the ridge
     # point of the two peaks (2516.6 TFLOP/s / 8 TB/s = 315 flop/B), the matrix cores otherwise
     ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    # the auto path runs the matrix-core GEMM for T > 16 (outside the invariant mode)
-    gemm = args.path == "gemm" or (args.path == "auto" and not args.invariant and T > 16)
-    traffic = None if args.invariant or args.path == "gemv" and T > 16 else measured_traffic(spec.name, T, gemm)
+    # the auto path runs the matrix-core GEMM above B.MOE_AUTO_DECODE_MAX_T tokens (outside the invariant mode)
+    gemm = args.path == "gemm" or (args.path == "auto" and not args.invariant and T > B.MOE_AUTO_DECODE_MAX_T)
+    traffic = (None if args.invariant or args.path == "gemv" and T > B.MOE_AUTO_DECODE_MAX_T
+               else measured_traffic(spec.name, T, gemm))
     if flops_per_step / bytes_per_fwd < ridge:
         achieved = bytes_per_fwd / (fwd_s / n_fwd) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

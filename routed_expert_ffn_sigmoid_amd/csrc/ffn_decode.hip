@@ -26,14 +26,14 @@
 //   segment, 16 rows x 64 contiguous bytes per instruction);
 //   the activation digits for token l%16 come from LDS at the same inputs;
 //   C[token i][row j] lands in lane 16*(i/4) + j, register i%4.
-// Two kernels use this arithmetic.  decode_persistent_kernel (the default up to
-// 16 tokens, when the digit planes of every token fit the LDS) runs one
-// workgroup of 8 wavefronts per CU over a range of (slot, tile) items with the
-// weight stream running across items; with the routing of one token given to
-// it, its gate/up launch also selects and sorts, and its down launch may also
-// combine.  decode_kernel (further tokens, or planes beyond the LDS) runs a
-// grid of (row block, slot) workgroups of 4 wavefronts covering TPW = 4/S
-// tiles of 16 rows, tokens in passes.  In both, the S wavefronts of a tile
+// Two kernels use this arithmetic.  decode_persistent_kernel (the default)
+// runs one workgroup of 8 wavefronts per CU over a range of (slot, tile) items
+// with the weight stream running across items; a slot with more tokens than
+// its digit planes hold (at most 16) is taken in token passes.  With the
+// routing of one token given to it, its gate/up launch also selects and sorts,
+// and its down launch may also combine.  decode_kernel (routing tables beyond
+// the persistent kernel's LDS) runs a grid of (row block, slot) workgroups of
+// 4 wavefronts covering TPW = 4/S tiles of 16 rows, tokens in passes.  In both, the S wavefronts of a tile
 // split K and add their fp64 partials in a fixed order, and the segment loop
 // is padded to a multiple of PF with out-of-range (zero) loads, so it is
 // straight-line code with PF segments in flight per row.
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(DK_THREADS, 3) void decode_kernel(FfnParams P, floa
 //
 // Start-up takes two memory round trips: the routing tables (unique list, offsets, permutation) go to
 // LDS in one round together with the first activation rows; the weight stream starts right after.
-// Gate/up stages the digit planes of all T tokens once (slots only remap lanes to tokens); down
-// stages the rows of h of each slot when the slot changes.  Requires T <= DK_GMAX.
+// Gate/up stages the digit planes of all T tokens once where they fit (slots only remap lanes to tokens); down,
+// and gate/up in token passes, stage the rows of each (virtual) slot when it changes.
 struct DItem {
     int slot, e, w, tile, I, kpart_bytes, nseg_pad, row, p0, ng;  // w: weight row (-1: not resident)
     bool shared, row_ok;
@@ -1470,8 +1470,7 @@ static bool dkp_plan(int mode, const FfnParams &P, DkpPlan *pl) {
         S = P.invariant ? decode_pinned_s(mode, P) : dkp_pick_s(mode, K, nout, slots, slots_exp, wbits, device_cus());
     while (S > 1 && (Kmin % (S * (wbits == 8 ? 16 : 32)))) S >>= 1;
     const int kpad = pad_k(K / S, wbits);
-    if (P.T > DK_GMAX || dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64)
-        return false;
+    if (dkp_tab_words(mode, P.n_routed_slots, P.E, P.A) > DKP_TAB_PER_THREAD * DKP_WAVES * 64) return false;
     if (mode == 1 && P.comb_y) {
         // each wavefront stages at most two rows (nsl <= 2 TPW), and the ranges, cut at tiles so that a
         // workgroup holds every slot of its rows, give the busiest CU no more items than the plain split
@@ -1484,8 +1483,8 @@ static bool dkp_plan(int mode, const FfnParams &P, DkpPlan *pl) {
         *pl = DkpPlan{S, kpad, nsl};
         return true;
     }
-    // token rows the planes hold: all T, or fewer, with the slots taken in passes
-    int gcap = P.T;
+    // token rows the planes hold: all T, or fewer (at most DK_GMAX, the MFMA rows), with the slots taken in passes
+    int gcap = P.T < DK_GMAX ? P.T : DK_GMAX;
     while (gcap > 0 && dkp_lds_bytes(mode, S, P, kpad, gcap) > DKP_LDS_BUDGET) gcap--;
     if (gcap < 1) return false;
     *pl = DkpPlan{S, kpad, gcap};

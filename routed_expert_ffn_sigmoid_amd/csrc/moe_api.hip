@@ -124,13 +124,14 @@ moe::FfnParams ffn_params(const moe_shape *s) {
 }
 
 // Path the forward call takes for this shape: the matrix-core grouped GEMM once there are enough rows
-// per expert to reuse each weight (more than 16 tokens), the bandwidth-bound decode kernels otherwise; the
-// batch-invariant mode keeps every T on the decode kernels, so a token's bits never depend on the batch.
+// per expert to reuse each weight (more than MOE_AUTO_DECODE_MAX_T tokens), the bandwidth-bound decode kernels
+// otherwise; the batch-invariant mode keeps every T on the decode kernels, so a token's bits never depend on the
+// batch.
 int forward_path(const moe_shape *s) {
     if (s->path != MOE_PATH_AUTO) return s->path;
     if (s->flags & MOE_FLAG_BATCH_INVARIANT) return MOE_PATH_GEMV;
     moe::FfnParams P = ffn_params(s);
-    if (s->T > 16 && moe::gemm_supported(P)) return MOE_PATH_GEMM;
+    if (s->T > MOE_AUTO_DECODE_MAX_T && moe::gemm_supported(P)) return MOE_PATH_GEMM;
     return MOE_PATH_GEMV;
 }
 

@@ -131,6 +131,20 @@ def test_small_layer_parity(orc, dev, case):
     run_full_case(orc, dev, spec, T, label=case)
 
 
+# the decode kernels above 16 tokens (MOE_PATH_GEMV): slots with more tokens than the MFMA's 16 rows, in passes
+SMALL_GEMV = {
+    "gemv_T40_int4_shared": (dict(d=512, E=16, k=4, I=352, I_shared=96, routed_scale=2.5), 40),
+    "gemv_T24_int8_f32": (dict(d=1024, E=8, k=2, I=1536, wbits=8, act=synth.ACT_F32), 24),
+    "gemv_T33_planes_passes": (dict(d=8192, E=4, k=2, I=256, I_shared=256), 33),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL_GEMV))
+def test_small_layer_parity_decode_above_16(orc, dev, case):
+    kw, T = SMALL_GEMV[case]
+    run_full_case(orc, dev, spec_of(**kw), T, path=B.MOE_PATH_GEMV, label=case)
+
+
 # the matrix-core grouped GEMM path (d, I multiples of 64): several 128-row tiles per expert with ragged ends,
 # experts with a handful of rows, I_shared above and below I, bf16 and fp32 activations
 GEMM = {
@@ -587,7 +601,7 @@ def test_full_workload_parity(orc, dev, name, T, nsample, path):
     assert int(run.n_uniq.item()) == p.n_uniq
     say(f"   indices+permutation bit-exact; n_uniq={p.n_uniq} max count={p.counts.max()}")
 
-    gemm = path == B.MOE_PATH_GEMM or (path == B.MOE_PATH_AUTO and T > 16)
+    gemm = path == B.MOE_PATH_GEMM or (path == B.MOE_PATH_AUTO and T > B.MOE_AUTO_DECODE_MAX_T)
     block = 128 if gemm else 16
     so = sampled_oracle(orc, spec)
     yp = run.y_perm.cpu().numpy()
