@@ -1393,8 +1393,8 @@ static size_t dkp_lds_bytes(int mode, int S, const FfnParams &P, int kpad, int g
 // which skewed routing lowers): S = 4 while R >= 3 at the expected slot count.  Measured at 2 to 16 tokens on
 // both layers, S = 4 beat S = 8 by 1.6-4 % at 2 and 4 tokens and on the mid layer at 8, and tied elsewhere;
 // S = 2 also beat S = 8, by less than S = 4 on the mid layer; S = 1 lost up to 7 % to S = 8 on the mid layer
-// (it won on the 256-expert layer at 4 tokens).  0: none qualifies (dkp_pick_s decides).  The planes must fit
-// the LDS.
+// (it won on the 256-expert layer at 4 tokens).  0: none qualifies (dkp_pick_s decides).  The planes must hold
+// one token row; tokens beyond what they hold are taken in passes.
 static int dkp_pick_s0(const FfnParams &P, double slots) {
     const int chunk = P.wbits == 8 ? 16 : 32, ncu = device_cus();
     const double shared = P.Is > 0 ? 1.0 : 0.0;
@@ -1404,7 +1404,8 @@ static int dkp_pick_s0(const FfnParams &P, double slots) {
         const double items = (slots - shared) * ((P.I + rows - 1) / rows) + shared * ((P.Is + rows - 1) / rows);
         const double R = items / ncu, fill = R - std::floor(R);
         const bool ok = P.T == 1 ? R >= 1.5 && (fill == 0.0 || fill >= 0.75) : R >= 3.0;
-        if (ok && dkp_lds_bytes(0, S, P, pad_k(P.d / S, P.wbits), P.T) <= DKP_LDS_BUDGET) return S;
+        // the planes must hold one token row at least (more tokens than fit are taken in passes)
+        if (ok && dkp_lds_bytes(0, S, P, pad_k(P.d / S, P.wbits), 1) <= DKP_LDS_BUDGET) return S;
     }
     return 0;
 }
