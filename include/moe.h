@@ -98,8 +98,8 @@ extern "C" {
 #define MOE_PATH_GEMM 2 /* MFMA grouped GEMM (prefill) */
 /* MOE_PATH_AUTO runs the decode kernels up to this T and the matrix-core path above it where that path applies
  * (measured crossover: the decode kernels, taking each expert's tokens in passes of at most 16, are faster at
- * T = 32 on the mid and 256-expert layers and slower from about T = 48). */
-#define MOE_AUTO_DECODE_MAX_T 32
+ * T = 40 on the mid and 256-expert layers; at T = 48 the mid layer's matrix-core path is 3 % faster). */
+#define MOE_AUTO_DECODE_MAX_T 40
 
 /*
  * Batch-shape-invariant mode.  Quantised integer kernels may round differently
@@ -115,7 +115,7 @@ extern "C" {
  *     (MOE_PATH_GEMM stays on the matrix-core path, whose rows are
  *     independent of each other too, and gives its own, different bits);
  *   - moe_combine is per token already.
- * Cost: the decode split is the one chosen for T = 1, so T <= 32 runs as fast
+ * Cost: the decode split is the one chosen for T = 1, so T <= 40 runs as fast
  * or a little slower; above T = 16 the decode kernels take each expert's tokens
  * in passes of at most 16 and stream its weights again per pass, so at large T
  * they are far slower than the matrix-core path.

@@ -39,7 +39,7 @@ MOE_ROUTER_EXPERT_CHOICE = 2
 MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_GEMM = 2
-MOE_AUTO_DECODE_MAX_T = 32  # MOE_PATH_AUTO: the decode kernels up to this T, the matrix-core path above
+MOE_AUTO_DECODE_MAX_T = 40  # MOE_PATH_AUTO: the decode kernels up to this T, the matrix-core path above
 
 MOE_CACHE_WEIGHTED_LRU = 0
 MOE_CACHE_LRU = 1

@@ -42,7 +42,7 @@ CASES = {
     # decode batch on the three calls' kernels
     "E64_T4": (dict(), 4),
     # the matrix-core path
-    "gemm_T40": (dict(d=1024, E=16, k=4, I=256, I_shared=256), 40),
+    "gemm_T48": (dict(d=1024, E=16, k=4, I=256, I_shared=256), 48),
 }
 
 

@@ -61,7 +61,7 @@ CASES = {
     "unfused_T3": (dict(), 3, 0, 0, 0.0),
     "E256_k8_shared_T4": (dict(d=7168, E=256, k=8, I=128, I_shared=128), 4, 0, 0, 0.0),
     "E12_k3_T6": (dict(E=12, k=3), 6, 0, 0, 0.0),
-    "unfused_gemm_T40": (dict(d=1024, E=16, k=4, I=256, I_shared=256), 40, 0, 0, 0.0),
+    "unfused_gemm_T48": (dict(d=1024, E=16, k=4, I=256, I_shared=256), 48, 0, 0, 0.0),
     "empty_T0": (dict(), 0, 0, 0, 0.0),
 }
 
